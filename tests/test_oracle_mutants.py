@@ -1,0 +1,57 @@
+"""Plant one plausible mistake at a time in a copy of the oracle and check that
+at least one pin catches it (CPU only; the oracle source itself is untouched)."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text, planted mistake[, number of sites])
+MUTANTS = [
+    ("router_tie_to_higher", "if (l[e] > l[i0]) i0 = e;", "if (l[e] >= l[i0]) i0 = e;"),
+    ("router_second_tie", "if (e != i0 && l[e] > l[i1]) i1 = e;", "if (e != i0 && l[e] >= l[i1]) i1 = e;"),
+    ("router_no_renorm", "g[2 * t] = (float)(p0 / (p0 + p1));", "g[2 * t] = (float)p0;"),
+    ("router_slots_swapped", "idx[2 * t] = i0;\n        idx[2 * t + 1] = i1;",
+     "idx[2 * t] = i1;\n        idx[2 * t + 1] = i0;"),
+    ("router_Wr_transposed", "ld(Wr, j * (int64_t)E + e, dt)", "ld(Wr, (int64_t)e * d + j, dt)"),
+    ("router_softmax_sign", "double p1 = exp(l[i1] - l[i0]) / den;", "double p1 = exp(l[i0] - l[i1]) / den;"),
+    ("switch_sign", "double v = w - Dold + Dnew;", "double v = w + Dold + Dnew;"),
+    ("switch_drop_old", "double v = w - Dold + Dnew;", "double v = w + Dnew;"),
+    ("switch_no_scale", "D += s * (double)g[k] * acc;", "D += (double)g[k] * acc;"),
+    ("switch_no_gate", "D += s * (double)g[k] * acc;", "D += s * acc;"),
+    ("switch_B_transposed", "ld(B, ((int64_t)e * d_out + i) * r + rho, dt)",
+     "ld(B, ((int64_t)e * r + rho) * d_out + i, dt)"),
+    ("switch_one_slot", "double D = 0.0;\n    for (int k = 0; k < 2; ++k) {",
+     "double D = 0.0;\n    for (int k = 0; k < 1; ++k) {"),
+    ("switch_A_index", "ld(A, ((int64_t)e * r + rho) * d_in + j, dt);\n            acc += b * a;",
+     "ld(A, ((int64_t)e * r + rho) * d_in + (d_in - 1 - j), dt);\n            acc += b * a;"),
+    ("round_truncate", "double nr = nearbyint(n);", "double nr = trunc(n);"),
+    ("round_ties_away", "double nr = nearbyint(n);", "double nr = round(n);"),
+    ("round_subnormal", "if (qexp < -133) qexp = -133;", "if (qexp < -126) qexp = -126;"),
+    ("sgmm_no_gate", "double c = s * (double)g[2 * t + k];", "double c = s;"),
+    ("sgmm_B_wrong_expert", "double b = ld(B, ((int64_t)e * d_out + o) * r + rho, dt);",
+     "double b = ld(B, ((int64_t)idx[2 * t] * d_out + o) * r + rho, dt);"),
+    ("sgmm_x_row", "double p = ld(x, t * d_in + j, dt) * ld(A,", "double p = ld(x, 0 * d_in + j, dt) * ld(A,"),
+    ("sgmm_v_slot", "acc += v[k * r + rho] * b;", "acc += v[rho] * b;"),
+    # an empty slot (-1) read as expert 0 everywhere it is tested
+    ("empty_slot_as_expert0", "if (e < 0) continue;", "if (e < 0) e = 0;", 3),
+]
+
+
+MUTANTS = [m if len(m) == 4 else m + (1,) for m in MUTANTS]
+
+
+@pytest.mark.parametrize("name,orig,bad,count", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, orig, bad, count, tmp_path):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(orig) == count, f"mutation site for {name} not found {count} time(s)"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(orig, bad))
+    so = oracle.build(str(path), str(tmp_path / f"lib{name}.so"))
+    lib = oracle.load(so)
+    caught = oracle_pins.failing_pins(lib)
+    assert caught, f"planted mistake {name} passed every pin"
