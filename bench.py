@@ -1,0 +1,271 @@
+"""Benchmark of the pre-gated dynamic-LoRA hot path on one MI355X.
+
+Headline (value): fused-switch weight throughput on the 7B-shaped decode
+workload (32 layers x q/k/v/o 4096x4096, gate/up 4096->11008, down
+11008->4096, bf16; E=8 experts of rank 16, scale 2; 256 tokens).  One step is
+one pass over the token batch: the router for the 256 tokens, then the 256
+fused switches (token t-1's set -> token t's set, every adapted weight of
+every layer in one launch each), all with inputs resident in HBM.
+value = weight bytes read + written per second (GB/s).
+
+Beside it, in the same JSON line: SGMM tokens/s on the prefill workload (4096
+tokens x 7 projections, Zipf(1.1) pairs) and on the mixed decode workload
+(64 rows x 32 layers x 7 projections, 128 Markov steps); the switch kernel's
+roofline (HIP-event timing of each launch on its stream, against 8 TB/s); and
+the CPU oracle timed on a bounded sample of the headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12
+
+
+def _src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+SWITCH_SOURCES = ["dynamic_lora_moe_amd/csrc/switch.hip", "dynamic_lora_moe_amd/csrc/gfx950.hpp",
+                  "dynamic_lora_moe_amd/csrc/internal.hpp"]
+
+
+def _traffic(kernel_key, algo_bytes_per_launch):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    ent = t.get(kernel_key)
+    if not ent or ent.get("source_hash") != _src_hash(SWITCH_SOURCES):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def bench_switch(torch, dlm, synth, steps, warmup, log):
+    wl = synth.WORKLOADS["7b-decode"]
+    log(f"building {wl.name}: {wl.n_mats} weights, {wl.switch_w_elems() * 2 / 1e9:.2f} GB bf16")
+    model = synth.switch_model(wl)
+    x, Wr = synth.router_inputs(wl)
+    L = dlm.Layers([(W, A, B) for _, _, W, A, B in model], wl.E, wl.r, wl.scale)
+    stream = torch.cuda.current_stream()
+    T = wl.T
+
+    def one_step(events=None):
+        idx, g = dlm.pregate(x, Wr)
+        L.switch(None, (idx[0], g[0]))
+        for t in range(1, T):
+            if events is not None:
+                events[t - 1][0].record(stream)
+            L.switch((idx[t - 1], g[t - 1]), (idx[t], g[t]))
+            if events is not None:
+                events[t - 1][1].record(stream)
+        return idx
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(T - 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        one_step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for e in ev for a, b in e]
+    assert L.status() == dlm.DLM_OK
+    w_bytes = wl.switch_w_elems() * 2 * 2                      # read + write
+    # A/B slices of the distinct experts of old and new (at most 4 experts)
+    slice_bytes_per_expert = wl.layers * sum((o + i) * wl.r * 2 for _, o, i in wl.projs)
+    algo_bytes = w_bytes + 4 * slice_bytes_per_expert          # router sets are top-2 distinct
+    n_switch = steps * T
+    ms_per_step = wall * 1e3 / steps
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    res = {
+        "ms_per_step": ms_per_step,
+        "weight_GBps": w_bytes * n_switch / wall / 1e9,
+        "algo_GBps": algo_bytes * n_switch / wall / 1e9,
+        "switch_ms": avg_launch_s * 1e3,
+        "switch_ms_p50": sorted(launch_ms)[len(launch_ms) // 2],
+        "algo_bytes_per_launch": algo_bytes,
+        "weight_bytes_per_launch": w_bytes,
+        "launches_per_switch": L.launches_per_switch(),
+        "achieved_launch_GBps": algo_bytes / avg_launch_s / 1e9,
+    }
+    L.close()
+    del model
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_sgmm(torch, dlm, synth, name, reps, log):
+    wl = synth.WORKLOADS[name]
+    log(f"building {name}")
+    probs = synth.sgmm_problems(wl)
+    idx, g = synth.batched_sets(wl)
+    grp = dlm.SgmmGroup([(x, A, B, y) for _, _, x, A, B, y in probs], wl.E, wl.r, wl.scale)
+    ws = grp.workspace(wl.T)
+    if name == "sgmm-prefill":
+        sets = [(idx.cuda(), g.cuda())]
+    else:
+        sets = [(idx[s].cuda(), g[s].cuda()) for s in range(wl.steps)]
+    stream = torch.cuda.current_stream()
+
+    def one():
+        for i, gg in sets:
+            grp.run(i, gg, workspace=ws)
+
+    one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        one()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    tokens = wl.T * len(sets)
+    # algorithmic bytes: x once, y read + write, A/B of the experts used, idx/g
+    used = torch.zeros(wl.E, dtype=torch.bool)
+    nbytes = 0
+    for i, _ in sets:
+        u = torch.unique(i.cpu())
+        u = u[u >= 0]
+        per_step = 0
+        for _, _, x, A, B, y in probs:
+            d_in, d_out = x.shape[1], y.shape[1]
+            per_step += wl.T * d_in * 2 + 2 * wl.T * d_out * 2 + len(u) * wl.r * (d_in + d_out) * 2
+        nbytes += per_step + wl.T * 16
+        used[u.long()] = True
+    res = {"tokens_per_s": tokens / sec, "ms_per_pass": sec * 1e3, "GBps": nbytes / sec / 1e9,
+           "frac_of_hbm_peak": nbytes / sec / HBM_PEAK, "algo_bytes_per_pass": nbytes}
+    grp.close()
+    del probs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(torch, synth, target_s, log):
+    """The oracle (as it stands) on a bounded sample of the headline workload:
+    the switch of every adapted weight of one layer, on an evenly spaced subset
+    of rows sized to take about `target_s` seconds; scaled to weight GB/s."""
+    import numpy as np
+
+    import oracle
+    wl = synth.WORKLOADS["7b-decode"]
+    model = synth.switch_model(wl, layers=[0])
+    threads = oracle.threads()
+    old = ([1, 5], [0.6, 0.4])
+    new = ([2, 5], [0.7, 0.3])
+
+    # calibrate on a small sample, then size the measured sample
+    def timed(stride):
+        tot = 0.0
+        elems = 0
+        for _, _, W, A, B in model:
+            rows = np.arange(0, W.shape[0], stride)
+            Wr = W[torch.from_numpy(rows).cuda()].cpu()
+            Ac, Bc = A.cpu(), B.cpu()
+            t1 = time.perf_counter()
+            oracle.switch_rows(Wr, rows, Ac, Bc, W.shape[0], wl.scale, old, new)
+            tot += time.perf_counter() - t1
+            elems += rows.size * W.shape[1]
+        return elems, tot
+
+    e, t = timed(512)
+    per_elem = t / max(e, 1)
+    layer_elems = sum(o * i for _, o, i in wl.projs)
+    stride = max(1, int(np.ceil(layer_elems * per_elem / target_s)))
+    e, t = timed(stride)
+    log(f"cpu oracle: {e} elements in {t:.1f} s on {threads} threads")
+    gbps = e * 4 / t / 1e9
+    return {"value": gbps, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"switch (old {old} -> new {new}) of all 7 adapted weights of layer 0 of the "
+                      f"7B-shaped workload, every {stride}th row ({e} elements, {t:.1f} s); weight "
+                      f"bytes read+written per second, binary64 oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--sgmm-reps", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sgmm", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the hot path here runs on a single GPU with no "
+              "sharding or collectives; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dynamic_lora_moe_amd as dlm
+    import synth
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    torch.cuda.set_device(0)
+    sw = bench_switch(torch, dlm, synth, args.steps, args.warmup, log)
+    log(f"switch: {sw}")
+    sg = {}
+    if not args.no_sgmm:
+        sg["prefill"] = bench_sgmm(torch, dlm, synth, "sgmm-prefill", args.sgmm_reps, log)
+        log(f"sgmm prefill: {sg['prefill']}")
+        sg["mixed_decode"] = bench_sgmm(torch, dlm, synth, "mixed-decode", max(1, args.sgmm_reps // 5), log)
+        log(f"sgmm mixed decode: {sg['mixed_decode']}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, synth, args.cpu_seconds, log)
+    achieved = sw["achieved_launch_GBps"]
+    out = {
+        "metric": "fused-switch weight GB/s + SGMM tokens/s; fraction of MI355X HBM peak",
+        "value": round(sw["weight_GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sw["ms_per_step"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "7b-decode: 32 layers x 7 adapted projections (q,k,v,o 4096x4096; "
+                               "gate,up 4096->11008; down 11008->4096), E=8, r=16, scale 2, "
+                               "256 tokens batch 1; step = router + 256 fused switches",
+                   "tokens_per_step": 256, "weights_per_switch": 224},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(achieved * 1e9 / HBM_PEAK, 4),
+                     "traffic": _traffic("switch_bf16_7b", sw["algo_bytes_per_launch"]),
+                     "kernel": "switch_bf16_kernel<1,256>",
+                     "avg_launch_ms": round(sw["switch_ms"], 4),
+                     "algo_bytes_per_launch": sw["algo_bytes_per_launch"]},
+        "cpu_baseline": cpu,
+        "switch": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in sw.items()},
+        "sgmm": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                 for k, v in sg.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,273 @@
+"""MI355X (gfx950) hot path of token-level pre-gated dynamic LoRA adapters.
+
+A thin ctypes binding of libdlm.so (declared in include/dlm.h).  It only
+marshals torch tensors (device memory) and the current HIP stream into the
+C ABI; every step of the path runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or fails to load, importing the ops raises.
+
+  pregate(x, Wr)                  -> (idx [T][2] int32, g [T][2] fp32)
+  Layers([(W, A, B), ...], E, r, scale).switch(old, new)   # in place, one launch
+  sgmm(x, idx, g, A, B, y, scale)                          # y updated in place
+  SgmmGroup([(x, A, B, y), ...], E, r, scale).run(idx, g)
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdlm.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "dlm.h")
+
+DLM_OK, DLM_EINVAL, DLM_ESHAPE, DLM_EDTYPE, DLM_EALIGN = 0, -1, -2, -3, -4
+DLM_EWORKSPACE, DLM_EHIP, DLM_EDEVICE, DLM_ENOMEM = -5, -6, -7, -8
+DLM_F32, DLM_BF16 = 0, 1
+STATUS_NAMES = {0: "DLM_OK", -1: "DLM_EINVAL", -2: "DLM_ESHAPE", -3: "DLM_EDTYPE",
+                -4: "DLM_EALIGN", -5: "DLM_EWORKSPACE", -6: "DLM_EHIP", -7: "DLM_EDEVICE",
+                -8: "DLM_ENOMEM"}
+
+
+class DLMError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class dlm_proj(C.Structure):
+    _fields_ = [("W", C.c_void_p), ("A", C.c_void_p), ("B", C.c_void_p),
+                ("d_out", C.c_int64), ("d_in", C.c_int64)]
+
+
+class dlm_sgmm_problem(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("A", C.c_void_p), ("B", C.c_void_p), ("y", C.c_void_p),
+                ("d_in", C.c_int64), ("d_out", C.c_int64)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libdlm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with dynamic_lora_moe_amd/build.py")
+    lib = C.CDLL(path)
+    P, I64, I32, F = C.c_void_p, C.c_int64, C.c_int32, C.c_float
+    sig = {
+        "dlm_last_error": ([], C.c_char_p),
+        "dlm_version": ([], C.c_char_p),
+        "dlm_pregate": ([P, P, I64, I64, I32, I32, P, P, P], C.c_int),
+        "dlm_layers_create": ([P, I32, I32, I32, F, I32, P], C.c_int),
+        "dlm_layers_destroy": ([P], C.c_int),
+        "dlm_switch": ([P, P, P, P, P, P], C.c_int),
+        "dlm_switch_launches": ([P], C.c_int),
+        "dlm_layers_status": ([P, P, P], C.c_int),
+        "dlm_sgmm_workspace_size": ([I64, I32, I32, I32, P], C.c_int),
+        "dlm_sgmm": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, F, I32, P, C.c_size_t, P], C.c_int),
+        "dlm_sgmm_group_create": ([P, I32, I32, I32, F, I32, P], C.c_int),
+        "dlm_sgmm_group_destroy": ([P], C.c_int),
+        "dlm_sgmm_group_run": ([P, P, P, I64, P, C.c_size_t, P], C.c_int),
+        "dlm_sgmm_status": ([P, P, P], C.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions include/dlm.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dlm_\w+)\s*\(", text, flags=re.M)))
+
+
+def _check(rc: int, what: str):
+    if rc != DLM_OK:
+        raise DLMError(rc, f"{what}: {load().dlm_last_error().decode()}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DLM_F32
+    if t.dtype == torch.bfloat16:
+        return DLM_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---- router -------------------------------------------------------------------
+
+def pregate(x: torch.Tensor, Wr: torch.Tensor, idx=None, g=None, stream=None):
+    """Top-2 pre-gate: x [T][d], Wr [d][E] -> idx [T][2] int32, g [T][2] fp32 (device)."""
+    _need(x, "x")
+    _need(Wr, "Wr")
+    T, d = x.shape
+    E = Wr.shape[1]
+    if Wr.shape[0] != d or Wr.dtype != x.dtype:
+        raise ValueError("Wr must be [d][E] with x's dtype")
+    if idx is None:
+        idx = torch.empty((T, 2), dtype=torch.int32, device=x.device)
+    if g is None:
+        g = torch.empty((T, 2), dtype=torch.float32, device=x.device)
+    _check(load().dlm_pregate(_p(x), _p(Wr), T, d, E, _dt(x), _p(idx), _p(g), _stream(stream)),
+           "dlm_pregate")
+    return idx, g
+
+
+# ---- fused switch ---------------------------------------------------------------
+
+def _set_ptrs(s):
+    if s is None:
+        return None, None
+    i, g = s
+    _need(i, "set idx")
+    _need(g, "set g")
+    if i.dtype != torch.int32 or g.dtype != torch.float32 or i.numel() < 2 or g.numel() < 2:
+        raise ValueError("a set is (int32 idx[2], fp32 g[2]) on the device")
+    return _p(i), _p(g)
+
+
+class Layers:
+    """Every adapted weight of every layer, switched together by one launch."""
+
+    def __init__(self, projs, E: int, r: int, scale: float):
+        self._keep = list(projs)
+        arr = (dlm_proj * len(self._keep))()
+        dt = None
+        for k, (W, A, B) in enumerate(self._keep):
+            for t, nm in ((W, "W"), (A, "A"), (B, "B")):
+                _need(t, nm)
+            dt = _dt(W) if dt is None else dt
+            arr[k] = dlm_proj(W.data_ptr(), A.data_ptr(), B.data_ptr(), W.shape[0], W.shape[1])
+        h = C.c_void_p()
+        _check(load().dlm_layers_create(arr, len(self._keep), E, r, float(scale), dt, C.byref(h)),
+               "dlm_layers_create")
+        self._h = h
+        self.E, self.r, self.scale = E, r, scale
+
+    def switch(self, old=None, new=None, stream=None):
+        """old/new: (idx int32[2], g fp32[2]) device tensors, or None for the empty set."""
+        oi, og = _set_ptrs(old)
+        ni, ng = _set_ptrs(new)
+        _check(load().dlm_switch(self._h, oi, og, ni, ng, _stream(stream)), "dlm_switch")
+
+    def status(self, stream=None) -> int:
+        code = C.c_int32(0)
+        _check(load().dlm_layers_status(self._h, C.byref(code), _stream(stream)), "dlm_layers_status")
+        return code.value
+
+    def launches_per_switch(self) -> int:
+        return load().dlm_switch_launches(self._h)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _check(load().dlm_layers_destroy(self._h), "dlm_layers_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+
+# ---- SGMM ------------------------------------------------------------------------
+
+def sgmm_workspace_size(T: int, E: int, r: int, n_problems: int = 1) -> int:
+    b = C.c_size_t(0)
+    _check(load().dlm_sgmm_workspace_size(T, E, r, n_problems, C.byref(b)), "dlm_sgmm_workspace_size")
+    return b.value
+
+
+def sgmm_workspace(T: int, E: int, r: int, n_problems: int = 1, device="cuda") -> torch.Tensor:
+    n = sgmm_workspace_size(T, E, r, n_problems)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def sgmm(x, idx, g, A, B, y, scale: float, workspace=None, stream=None):
+    """y += sum_k s g_k (x A_k^T) B_k^T row by row, in place (returns y)."""
+    for t, nm in ((x, "x"), (idx, "idx"), (g, "g"), (A, "A"), (B, "B"), (y, "y")):
+        _need(t, nm)
+    T, d_in = x.shape
+    E, r, _ = A.shape
+    d_out = B.shape[1]
+    if workspace is None:
+        workspace = sgmm_workspace(T, E, r, 1, x.device)
+    _check(load().dlm_sgmm(_p(x), _p(idx), _p(g), _p(A), _p(B), _p(y), T, d_in, d_out, E, r,
+                           float(scale), _dt(x), _p(workspace), workspace.numel(), _stream(stream)),
+           "dlm_sgmm")
+    return y
+
+
+def sgmm_status(workspace, stream=None) -> int:
+    code = C.c_int32(0)
+    _check(load().dlm_sgmm_status(_p(workspace), C.byref(code), _stream(stream)), "dlm_sgmm_status")
+    return code.value
+
+
+class SgmmGroup:
+    """Many (x, A, B, y) problems run on the same rows' expert sets (decide once)."""
+
+    def __init__(self, problems, E: int, r: int, scale: float):
+        self._keep = list(problems)
+        arr = (dlm_sgmm_problem * len(self._keep))()
+        dt = None
+        for k, (x, A, B, y) in enumerate(self._keep):
+            for t, nm in ((x, "x"), (A, "A"), (B, "B"), (y, "y")):
+                _need(t, nm)
+            dt = _dt(x) if dt is None else dt
+            arr[k] = dlm_sgmm_problem(x.data_ptr(), A.data_ptr(), B.data_ptr(), y.data_ptr(),
+                                      x.shape[1], y.shape[1])
+        h = C.c_void_p()
+        _check(load().dlm_sgmm_group_create(arr, len(self._keep), E, r, float(scale), dt, C.byref(h)),
+               "dlm_sgmm_group_create")
+        self._h = h
+        self.E, self.r, self.n = E, r, len(self._keep)
+
+    def workspace(self, T: int, device="cuda"):
+        return sgmm_workspace(T, self.E, self.r, self.n, device)
+
+    def run(self, idx, g, T: int | None = None, workspace=None, stream=None):
+        _need(idx, "idx")
+        _need(g, "g")
+        T = idx.shape[0] if T is None else T
+        if workspace is None:
+            workspace = self.workspace(T, idx.device)
+        _check(load().dlm_sgmm_group_run(self._h, _p(idx), _p(g), T, _p(workspace),
+                                         workspace.numel(), _stream(stream)), "dlm_sgmm_group_run")
+        return workspace
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _check(load().dlm_sgmm_group_destroy(self._h), "dlm_sgmm_group_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass

@@ -1,0 +1,397 @@
+// Host side of the C ABI declared in include/dlm.h: argument validation (no GPU
+// call before it passes), device descriptor tables, launches and status words.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "dlm.h"
+#include "internal.hpp"
+
+using namespace dlm;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = 0;
+    return DLM_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(DLM_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == DLM_F32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) { return dtype == DLM_F32 || dtype == DLM_BF16; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+// --------------------------------------------------------------- handles ----
+
+struct dlm_layers {
+    SwDesc* d_descs = nullptr;
+    int32_t* d_err = nullptr;
+    int32_t n = 0;
+    int32_t E = 0, r = 0;
+    float scale = 1.f;
+    int32_t dtype = 0;
+    SwTile tile{};
+    int64_t n_tiles = 0, n_elems = 0, per_xcd = 0;
+};
+
+struct dlm_sgmm_group {
+    SgDesc* d_descs = nullptr;
+    std::vector<SgDesc> h_descs;
+    int32_t n = 0;
+    int32_t E = 0, r = 0;
+    float scale = 1.f;
+    int32_t dtype = 0;
+    int64_t total_cb = 0, d_out_max = 0;
+};
+
+extern "C" {
+
+const char* dlm_last_error(void) { return g_err; }
+
+const char* dlm_version(void) { return "dlm 0.1.0 (gfx950)"; }
+
+// ---------------------------------------------------------------- router ----
+
+int dlm_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int32_t E, int32_t dtype,
+                int32_t* idx, float* g, void* stream) {
+    if (T < 0 || T > ((int64_t)1 << 31)) return fail(DLM_ESHAPE, "pregate: T=%lld out of range", (long long)T);
+    if (d < 1 || d > kMaxDim) return fail(DLM_ESHAPE, "pregate: d=%lld out of range", (long long)d);
+    if (E < 2 || E > DLM_MAX_EXPERTS) return fail(DLM_ESHAPE, "pregate: E=%d not in [2, %d]", E, DLM_MAX_EXPERTS);
+    if (!valid_dtype(dtype)) return fail(DLM_EDTYPE, "pregate: unknown dtype %d", dtype);
+    if (T == 0) return ok();
+    if (!x || !Wr || !idx || !g) return fail(DLM_EINVAL, "pregate: null pointer");
+    hipError_t e = launch_pregate(x, Wr, T, d, E, dtype, idx, g, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "pregate launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------- switch ----
+
+int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, float scale,
+                      int32_t dtype, dlm_layers** out) {
+    if (!out) return fail(DLM_EINVAL, "layers_create: out is null");
+    *out = nullptr;
+    if (!projs) return fail(DLM_EINVAL, "layers_create: projs is null");
+    if (n < 1) return fail(DLM_EINVAL, "layers_create: n=%d", n);
+    if (E < 1 || E > DLM_MAX_EXPERTS) return fail(DLM_ESHAPE, "layers_create: E=%d not in [1, %d]", E, DLM_MAX_EXPERTS);
+    if (r < 1 || r > DLM_MAX_RANK) return fail(DLM_ESHAPE, "layers_create: r=%d not in [1, %d]", r, DLM_MAX_RANK);
+    if (!valid_dtype(dtype)) return fail(DLM_EDTYPE, "layers_create: unknown dtype %d", dtype);
+    if (!std::isfinite(scale)) return fail(DLM_EINVAL, "layers_create: scale is not finite");
+    const SwTile tile = switch_tile_for_rank(r);
+    std::vector<SwDesc> h(n);
+    int64_t tiles = 0, elems = 0;
+    for (int i = 0; i < n; ++i) {
+        const dlm_proj& p = projs[i];
+        if (!p.W || !p.A || !p.B) return fail(DLM_EINVAL, "layers_create: proj %d has a null pointer", i);
+        if (p.d_out < 1 || p.d_in < 1 || p.d_out > kMaxDim || p.d_in > kMaxDim)
+            return fail(DLM_ESHAPE, "layers_create: proj %d shape %lldx%lld out of range", i,
+                        (long long)p.d_out, (long long)p.d_in);
+        if (dtype == DLM_BF16) {
+            if (!aligned16(p.W) || !aligned16(p.A) || !aligned16(p.B))
+                return fail(DLM_EALIGN, "layers_create: proj %d pointer not 16-byte aligned", i);
+            if (p.d_in % 8 != 0)
+                return fail(DLM_EALIGN, "layers_create: proj %d d_in=%lld not a multiple of 8", i, (long long)p.d_in);
+        }
+        SwDesc& d = h[i];
+        d.W = p.W;
+        d.A = p.A;
+        d.B = p.B;
+        d.d_out = (int32_t)p.d_out;
+        d.d_in = (int32_t)p.d_in;
+        d.n_rt = (int32_t)((p.d_out + tile.rt - 1) / tile.rt);
+        d.n_ct = (int32_t)((p.d_in + tile.ct - 1) / tile.ct);
+        d.tile0 = tiles;
+        d.elem0 = elems;
+        tiles += (int64_t)d.n_rt * d.n_ct;
+        elems += p.d_out * p.d_in;
+    }
+    dlm_layers* hd = new (std::nothrow) dlm_layers();
+    if (!hd) return fail(DLM_ENOMEM, "layers_create: host allocation failed");
+    hd->n = n;
+    hd->E = E;
+    hd->r = r;
+    hd->scale = scale;
+    hd->dtype = dtype;
+    hd->tile = tile;
+    hd->n_tiles = tiles;
+    hd->n_elems = elems;
+    hd->per_xcd = (tiles + 7) / 8;
+    hipError_t e = hipMalloc((void**)&hd->d_descs, sizeof(SwDesc) * n);
+    if (e == hipSuccess) e = hipMalloc((void**)&hd->d_err, 256);
+    if (e == hipSuccess) e = hipMemcpy(hd->d_descs, h.data(), sizeof(SwDesc) * n, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(hd->d_err, 0, 256);
+    if (e != hipSuccess) {
+        if (hd->d_descs) (void)hipFree(hd->d_descs);
+        if (hd->d_err) (void)hipFree(hd->d_err);
+        delete hd;
+        return hip_fail(e, "layers_create");
+    }
+    *out = hd;
+    return ok();
+}
+
+int dlm_layers_destroy(dlm_layers* h) {
+    if (!h) return fail(DLM_EINVAL, "layers_destroy: null handle");
+    hipError_t e = hipDeviceSynchronize();
+    if (h->d_descs) (void)hipFree(h->d_descs);
+    if (h->d_err) (void)hipFree(h->d_err);
+    delete h;
+    if (e != hipSuccess) return hip_fail(e, "layers_destroy");
+    return ok();
+}
+
+int dlm_switch(dlm_layers* h, const int32_t* old_idx, const float* old_g, const int32_t* new_idx,
+               const float* new_g, void* stream) {
+    if (!h) return fail(DLM_EINVAL, "switch: null handle");
+    if ((old_idx && !old_g) || (new_idx && !new_g))
+        return fail(DLM_EINVAL, "switch: a set has indices but no gates");
+    SwitchArgs a;
+    a.descs = h->d_descs;
+    a.n_desc = h->n;
+    a.E = h->E;
+    a.r = h->r;
+    a.scale = h->scale;
+    a.old_idx = old_idx;
+    a.old_g = old_g;
+    a.new_idx = new_idx;
+    a.new_g = new_g;
+    a.err = h->d_err;
+    hipError_t e;
+    if (h->dtype == DLM_BF16) {
+        a.n_units = h->n_tiles;
+        a.per_xcd = h->per_xcd;
+        e = launch_switch_bf16(a, h->tile, (hipStream_t)stream);
+    } else {
+        a.n_units = h->n_elems;
+        a.per_xcd = 0;
+        e = launch_switch_generic(a, h->dtype, (hipStream_t)stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "switch launch");
+    return ok();
+}
+
+int dlm_switch_launches(const dlm_layers* h) { return h ? 1 : 0; }
+
+int dlm_layers_status(dlm_layers* h, int32_t* code, void* stream) {
+    if (!h || !code) return fail(DLM_EINVAL, "layers_status: null argument");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    int32_t v = 0;
+    if (e == hipSuccess) e = hipMemcpy(&v, h->d_err, sizeof v, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && v != 0) e = hipMemset(h->d_err, 0, sizeof v);
+    if (e != hipSuccess) return hip_fail(e, "layers_status");
+    *code = v ? DLM_EDEVICE : DLM_OK;
+    return ok();
+}
+
+// ------------------------------------------------------------------ SGMM ----
+
+int dlm_sgmm_workspace_size(int64_t T, int32_t E, int32_t r, int32_t n_problems, size_t* bytes) {
+    if (!bytes) return fail(DLM_EINVAL, "sgmm_workspace_size: bytes is null");
+    if (T < 0 || T > ((int64_t)1 << 30)) return fail(DLM_ESHAPE, "sgmm_workspace_size: T=%lld", (long long)T);
+    if (E < 1 || E > DLM_MAX_EXPERTS) return fail(DLM_ESHAPE, "sgmm_workspace_size: E=%d", E);
+    if (r < 1 || r > DLM_MAX_RANK) return fail(DLM_ESHAPE, "sgmm_workspace_size: r=%d", r);
+    if (n_problems < 1) return fail(DLM_EINVAL, "sgmm_workspace_size: n_problems=%d", n_problems);
+    *bytes = sgmm_layout(T, E, r, n_problems).total;
+    return ok();
+}
+
+namespace {
+
+int check_problem(const dlm_sgmm_problem& p, int dtype, int i) {
+    if (!p.x || !p.A || !p.B || !p.y) return fail(DLM_EINVAL, "sgmm: problem %d has a null pointer", i);
+    if (p.d_in < 1 || p.d_out < 1 || p.d_in > kMaxDim || p.d_out > kMaxDim)
+        return fail(DLM_ESHAPE, "sgmm: problem %d shape d_in=%lld d_out=%lld", i, (long long)p.d_in,
+                    (long long)p.d_out);
+    if (dtype == DLM_BF16) {
+        if (!aligned16(p.x) || !aligned16(p.A) || !aligned16(p.B) || !aligned16(p.y))
+            return fail(DLM_EALIGN, "sgmm: problem %d pointer not 16-byte aligned", i);
+        if (p.d_in % 8 != 0 || p.d_out % 8 != 0)
+            return fail(DLM_EALIGN, "sgmm: problem %d d_in/d_out not multiples of 8", i);
+    }
+    return DLM_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, const SgLayout& L) {
+    if (!ws) return fail(DLM_EWORKSPACE, "sgmm: workspace is null");
+    if (((uintptr_t)ws & 255u) != 0) return fail(DLM_EALIGN, "sgmm: workspace not 256-byte aligned");
+    if (ws_bytes < L.total)
+        return fail(DLM_EWORKSPACE, "sgmm: workspace %zu bytes < %zu needed", ws_bytes, L.total);
+    return DLM_OK;
+}
+
+int run_sgmm(const SgDesc* d_descs, const SgDesc& single, int n_prob, int64_t total_cb,
+             int64_t d_out_max, const int32_t* idx, const float* g, int64_t T, int E, int r,
+             float scale, int dtype, void* ws, const SgLayout& L, hipStream_t s) {
+    SgmmArgs a;
+    a.descs = d_descs;
+    a.single = single;
+    a.n_prob = n_prob;
+    a.n_expand_units = L.tiles_max * total_cb;
+    a.total_cb = total_cb;
+    a.d_out_max = d_out_max;
+    a.idx = idx;
+    a.g = g;
+    a.T = T;
+    a.E = E;
+    a.r = r;
+    a.scale = scale;
+    a.ws = (char*)ws;
+    a.L = L;
+    hipError_t e = launch_sgmm(a, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "sgmm launch");
+    return ok();
+}
+
+}  // namespace
+
+int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, const void* B,
+             void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E, int32_t r, float scale,
+             int32_t dtype, void* workspace, size_t ws_bytes, void* stream) {
+    if (T < 0 || T > ((int64_t)1 << 30)) return fail(DLM_ESHAPE, "sgmm: T=%lld out of range", (long long)T);
+    if (E < 1 || E > DLM_MAX_EXPERTS) return fail(DLM_ESHAPE, "sgmm: E=%d not in [1, %d]", E, DLM_MAX_EXPERTS);
+    if (r < 1 || r > DLM_MAX_RANK) return fail(DLM_ESHAPE, "sgmm: r=%d not in [1, %d]", r, DLM_MAX_RANK);
+    if (!valid_dtype(dtype)) return fail(DLM_EDTYPE, "sgmm: unknown dtype %d", dtype);
+    if (!std::isfinite(scale)) return fail(DLM_EINVAL, "sgmm: scale is not finite");
+    dlm_sgmm_problem p{x, A, B, y, d_in, d_out};
+    int rc = check_problem(p, dtype, 0);
+    if (rc != DLM_OK) return rc;
+    if (T == 0) return ok();
+    if (!idx || !g) return fail(DLM_EINVAL, "sgmm: idx or g is null");
+    const size_t es = esize(dtype);
+    if (overlap(x, (size_t)T * d_in * es, y, (size_t)T * d_out * es))
+        return fail(DLM_EINVAL, "sgmm: x and y overlap");
+    const SgLayout L = sgmm_layout(T, E, r, 1);
+    rc = check_ws(workspace, ws_bytes, L);
+    if (rc != DLM_OK) return rc;
+    SgDesc d{};
+    d.x = x;
+    d.A = A;
+    d.B = B;
+    d.y = y;
+    d.d_in = (int32_t)d_in;
+    d.d_out = (int32_t)d_out;
+    d.n_cb = (int32_t)((d_out + 255) / 256);
+    d.unit0 = 0;
+    return run_sgmm(nullptr, d, 1, d.n_cb, d_out, idx, g, T, E, r, scale, dtype, workspace, L,
+                    (hipStream_t)stream);
+}
+
+int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, int32_t r,
+                          float scale, int32_t dtype, dlm_sgmm_group** out) {
+    if (!out) return fail(DLM_EINVAL, "sgmm_group_create: out is null");
+    *out = nullptr;
+    if (!probs || n < 1 || n > 65535) return fail(DLM_EINVAL, "sgmm_group_create: bad problem list (n=%d)", n);
+    if (E < 1 || E > DLM_MAX_EXPERTS) return fail(DLM_ESHAPE, "sgmm_group_create: E=%d", E);
+    if (r < 1 || r > DLM_MAX_RANK) return fail(DLM_ESHAPE, "sgmm_group_create: r=%d", r);
+    if (!valid_dtype(dtype)) return fail(DLM_EDTYPE, "sgmm_group_create: unknown dtype %d", dtype);
+    if (!std::isfinite(scale)) return fail(DLM_EINVAL, "sgmm_group_create: scale is not finite");
+    dlm_sgmm_group* h = new (std::nothrow) dlm_sgmm_group();
+    if (!h) return fail(DLM_ENOMEM, "sgmm_group_create: host allocation failed");
+    h->h_descs.resize(n);
+    int64_t cb = 0, dmax = 0;
+    for (int i = 0; i < n; ++i) {
+        const int rc = check_problem(probs[i], dtype, i);
+        if (rc != DLM_OK) {
+            delete h;
+            return rc;
+        }
+        SgDesc& d = h->h_descs[i];
+        d = SgDesc{};
+        d.x = probs[i].x;
+        d.A = probs[i].A;
+        d.B = probs[i].B;
+        d.y = probs[i].y;
+        d.d_in = (int32_t)probs[i].d_in;
+        d.d_out = (int32_t)probs[i].d_out;
+        d.n_cb = (int32_t)((probs[i].d_out + 255) / 256);
+        d.unit0 = cb;
+        cb += d.n_cb;
+        if (probs[i].d_out > dmax) dmax = probs[i].d_out;
+    }
+    h->n = n;
+    h->E = E;
+    h->r = r;
+    h->scale = scale;
+    h->dtype = dtype;
+    h->total_cb = cb;
+    h->d_out_max = dmax;
+    hipError_t e = hipMalloc((void**)&h->d_descs, sizeof(SgDesc) * n);
+    if (e == hipSuccess) e = hipMemcpy(h->d_descs, h->h_descs.data(), sizeof(SgDesc) * n, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (h->d_descs) (void)hipFree(h->d_descs);
+        delete h;
+        return hip_fail(e, "sgmm_group_create");
+    }
+    *out = h;
+    return ok();
+}
+
+int dlm_sgmm_group_destroy(dlm_sgmm_group* h) {
+    if (!h) return fail(DLM_EINVAL, "sgmm_group_destroy: null handle");
+    hipError_t e = hipDeviceSynchronize();
+    if (h->d_descs) (void)hipFree(h->d_descs);
+    delete h;
+    if (e != hipSuccess) return hip_fail(e, "sgmm_group_destroy");
+    return ok();
+}
+
+int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, int64_t T,
+                       void* workspace, size_t ws_bytes, void* stream) {
+    if (!h) return fail(DLM_EINVAL, "sgmm_group_run: null handle");
+    if (T < 0 || T > ((int64_t)1 << 30)) return fail(DLM_ESHAPE, "sgmm_group_run: T=%lld", (long long)T);
+    if (T == 0) return ok();
+    if (!idx || !g) return fail(DLM_EINVAL, "sgmm_group_run: idx or g is null");
+    const size_t es = esize(h->dtype);
+    for (int i = 0; i < h->n; ++i) {
+        const SgDesc& d = h->h_descs[i];
+        if (overlap(d.x, (size_t)T * d.d_in * es, d.y, (size_t)T * d.d_out * es))
+            return fail(DLM_EINVAL, "sgmm_group_run: problem %d x and y overlap", i);
+    }
+    const SgLayout L = sgmm_layout(T, h->E, h->r, h->n);
+    const int rc = check_ws(workspace, ws_bytes, L);
+    if (rc != DLM_OK) return rc;
+    return run_sgmm(h->d_descs, h->h_descs[0], h->n, h->total_cb, h->d_out_max, idx, g, T, h->E,
+                    h->r, h->scale, h->dtype, workspace, L, (hipStream_t)stream);
+}
+
+int dlm_sgmm_status(void* workspace, int32_t* code, void* stream) {
+    if (!workspace || !code) return fail(DLM_EINVAL, "sgmm_status: null argument");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    int32_t v = 0;
+    if (e == hipSuccess) e = hipMemcpy(&v, (char*)workspace + SG_ERR * 4, sizeof v, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && v != 0) e = hipMemset((char*)workspace + SG_ERR * 4, 0, sizeof v);
+    if (e != hipSuccess) return hip_fail(e, "sgmm_status");
+    *code = v ? DLM_EDEVICE : DLM_OK;
+    return ok();
+}
+
+}  // extern "C"

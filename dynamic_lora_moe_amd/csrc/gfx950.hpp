@@ -1,0 +1,64 @@
+// gfx950 (CDNA4) device helpers shared by the kernels of this library:
+// bf16 <-> fp32 conversion, 128-bit global access, the bf16 MFMA shapes used,
+// and wave64 reductions.  Compiled for gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dlm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// A bf16 is the upper half of an fp32: widening is a shift / mask.
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf_to_f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f_to_bf(float a) {
+    return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
+// 128-bit global load/store.  `nt` marks streaming data that is touched once
+// (weights being switched) so it does not evict reused adapter slices.
+__device__ __forceinline__ u32x4 ld128(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x4 ld128_nt(const void* p) {
+    return __builtin_nontemporal_load((const u32x4*)p);
+}
+__device__ __forceinline__ void st128(void* p, u32x4 v) { *(u32x4*)p = v; }
+__device__ __forceinline__ void st128_nt(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, (u32x4*)p);
+}
+
+// D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, 8 consecutive k
+// each (the two half-waves cover the two k halves).  Output register a of lane
+// l holds D[8*(a/4) + 4*(l/32) + a%4][l % 32].
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// Butterfly sum over the 64 lanes; every lane gets the total, in the same
+// fixed order on every run.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+}  // namespace dlm

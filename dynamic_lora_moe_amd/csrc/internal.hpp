@@ -1,0 +1,95 @@
+// Structures shared between the host API (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dlm {
+
+// ---- fused switch ---------------------------------------------------------
+
+// One adapted weight in the device table of a dlm_layers handle.
+struct SwDesc {
+    void* W;            // [d_out][d_in]
+    const void* A;      // [E][r][d_in]
+    const void* B;      // [E][d_out][r]
+    int32_t d_out, d_in;
+    int32_t n_rt, n_ct; // row tiles x column tiles of this weight
+    int64_t tile0;      // index of its first tile in the launch (prefix sum)
+    int64_t elem0;      // index of its first element (generic path)
+};
+
+struct SwitchArgs {
+    const SwDesc* descs;
+    int32_t n_desc;
+    int32_t E, r;
+    float scale;
+    int64_t n_units;    // tiles (MFMA path) or elements (generic path)
+    int64_t per_xcd;    // units per XCD chunk (MFMA path)
+    const int32_t* old_idx;
+    const float* old_g;
+    const int32_t* new_idx;
+    const float* new_g;
+    int32_t* err;
+};
+
+// Tile geometry of the bf16 MFMA switch for a padded rank.
+struct SwTile {
+    int r16;   // padded rank / 16
+    int ct;    // columns per tile
+    int rt;    // rows per tile
+};
+SwTile switch_tile_for_rank(int r);
+
+hipError_t launch_switch_bf16(const SwitchArgs& a, const SwTile& t, hipStream_t s);
+hipError_t launch_switch_generic(const SwitchArgs& a, int dtype, hipStream_t s);
+
+// ---- router ---------------------------------------------------------------
+
+hipError_t launch_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int E,
+                          int dtype, int32_t* idx, float* g, hipStream_t s);
+
+// ---- SGMM -----------------------------------------------------------------
+
+struct SgDesc {
+    const void* x;
+    const void* A;
+    const void* B;
+    void* y;
+    int32_t d_in, d_out;
+    int32_t n_cb;       // 256-column blocks of the expand
+    int32_t pad;
+    int64_t unit0;      // first column block of this problem (prefix sum of n_cb)
+};
+
+// Workspace sections (byte offsets, each 256-aligned).
+struct SgLayout {
+    size_t hdr, perm, rank, key, hist, tmask, v, total;
+    int64_t T, T_pad, n_chunks, n_keys, tiles_max;
+    int r_pad;
+};
+SgLayout sgmm_layout(int64_t T, int E, int r, int n_prob);
+
+// Header words of the workspace.
+enum { SG_ERR = 0, SG_NPOS = 1, SG_NTILES = 2 };
+
+struct SgmmArgs {
+    const SgDesc* descs;   // device table, or nullptr to use `single`
+    SgDesc single;
+    int32_t n_prob;
+    int64_t n_expand_units;  // tiles_max * total_cb
+    int64_t total_cb;        // sum over problems of their 256-column blocks
+    int64_t d_out_max;       // largest d_out over the problems
+    const int32_t* idx;
+    const float* g;
+    int64_t T;
+    int32_t E, r;
+    float scale;
+    char* ws;
+    SgLayout L;
+};
+
+hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s);
+
+}  // namespace dlm

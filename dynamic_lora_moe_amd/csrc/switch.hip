@@ -1,0 +1,333 @@
+// Fused adapter switch (AdaFuse digest, section 2-na "fused adapter
+// switching"): one launch removes the previous token's gated adapters from
+// every adapted weight of every layer and merges the current token's, in
+// place:
+//     W <- round( W - s*sum_old g_k B_k A_k + s*sum_new g_k B_k A_k ).
+// The pages do this with concatenated adapter matrices and a parallel GEMM
+// inside one kernel, updating the backbone in place and hiding load latency
+// with a prefetch buffer.
+//
+// gfx950 design (bf16 path):
+//   * The switch is a stream over W (read once, written once, 4 bytes per
+//     element) with 4r MACs per element: HBM-bound, with the delta on MFMA.
+//   * Work unit = a 256-row x CT-column tile of one weight.  Tiles of all L*P
+//     weights form one launch; a workgroup finds its weight by binary search in
+//     the device descriptor table.  Consecutive tiles go to the same XCD so each
+//     XCD streams a contiguous band of W and its L2 keeps the band's slices.
+//   * The four slots [new0, new1, old0, old1] are the concatenated K = 4r
+//     contraction.  Their A column slices for the tile are staged once in LDS,
+//     transposed to [column][rank] so a lane reads its 8 MFMA k-values with one
+//     16-byte LDS read.  B row slices are already k-contiguous and go straight
+//     from global memory into MFMA operand registers.
+//   * The MFMA runs "transposed": M = W columns, N = W rows.  With the columns
+//     of each 32-column block permuted (perm below) the accumulator of lane l
+//     holds 16 consecutive columns of row l%32, so W is read and written with
+//     two 128-bit accesses per lane and per block, no LDS round trip.
+//   * Each slot has its own fp32 accumulator chain (K = r).  The epilogue
+//     forms S_new = c1*P1 + c0*P0 and S_old the same way (one fma each), then
+//     W - (S_old - S_new) in fp32 and one RNE to bf16.  Identical expressions
+//     for both halves make a switch to the same set an exact no-op; each set's
+//     slots are put in a canonical order first so slot order cannot matter.
+//   * W is touched once: loads and stores carry the nontemporal hint.
+#include "gfx950.hpp"
+#include "internal.hpp"
+
+namespace dlm {
+
+SwTile switch_tile_for_rank(int r) {
+    SwTile t;
+    t.r16 = (r + 15) / 16;
+    t.ct = t.r16 <= 1 ? 256 : (t.r16 <= 2 ? 128 : 64);
+    t.rt = 256;
+    return t;
+}
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRowGroups = 2;  // 32-row groups per wave
+constexpr int kRT = kWaves * kRowGroups * 32;
+
+struct Sets {
+    int e[4];    // experts of [new0, new1, old0, old1]; -1 = empty
+    float c[4];  // s * g of each slot (0 for an empty slot)
+    bool ok;
+};
+
+// Reads both sets from device memory (every thread reads the same words, so
+// every decision below is uniform), validates them and orders each set's two
+// slots canonically by (expert, coefficient).
+__device__ __forceinline__ Sets read_sets(const SwitchArgs& a) {
+    Sets s;
+    s.ok = true;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int32_t* ip = h == 0 ? a.new_idx : a.old_idx;
+        const float* gp = h == 0 ? a.new_g : a.old_g;
+        int e0 = -1, e1 = -1;
+        float c0 = 0.f, c1 = 0.f;
+        if (ip != nullptr) {
+            e0 = ip[0];
+            e1 = ip[1];
+            const float g0 = gp[0], g1 = gp[1];
+            if (e0 < -1 || e0 >= a.E || e1 < -1 || e1 >= a.E) s.ok = false;
+            if (e0 >= 0 && !__builtin_isfinite(g0)) s.ok = false;
+            if (e1 >= 0 && !__builtin_isfinite(g1)) s.ok = false;
+            c0 = e0 >= 0 ? a.scale * g0 : 0.f;
+            c1 = e1 >= 0 ? a.scale * g1 : 0.f;
+            if (e1 < e0 || (e1 == e0 && c1 < c0)) {
+                const int te = e0; e0 = e1; e1 = te;
+                const float tc = c0; c0 = c1; c1 = tc;
+            }
+        }
+        s.e[2 * h] = e0;
+        s.e[2 * h + 1] = e1;
+        s.c[2 * h] = c0;
+        s.c[2 * h + 1] = c1;
+    }
+    return s;
+}
+
+template <bool kByTile>
+__device__ __forceinline__ int find_desc(const SwDesc* __restrict__ d, int n, int64_t u) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int64_t start = kByTile ? d[mid].tile0 : d[mid].elem0;
+        if (start <= u) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Column cc (0..31) of a 32-column block -> the MFMA row index m that carries it.
+// With this order, accumulator register a of lane l holds column 16*(l/32) + a.
+__device__ __forceinline__ int perm_row(int cc) { return 8 * ((cc >> 2) & 3) + 4 * (cc >> 4) + (cc & 3); }
+
+template <int R16, int CT>
+__global__ __launch_bounds__(kWaves* kWave) void switch_bf16_kernel(SwitchArgs a) {
+    constexpr int RPAD = R16 * 16;
+    constexpr int RP = RPAD + 8;   // LDS pitch of one transposed column (elements)
+    constexpr int NCB = CT / 32;   // 32-column MFMA blocks per tile
+    constexpr int NSUB = CT / 64;  // 64-column steps per row group
+    constexpr int SLOT_ELEMS = NCB * 32 * RP;
+    extern __shared__ __attribute__((aligned(16))) uint16_t As[];  // [4][NCB][32][RP]
+
+    const int64_t bid = blockIdx.x;
+    const int64_t t = (bid & 7) * a.per_xcd + (bid >> 3);
+    if (t >= a.n_units) return;
+    const Sets sc = read_sets(a);
+    if (!sc.ok) {
+        if (t == 0 && threadIdx.x == 0) *a.err = 1;
+        return;
+    }
+    const SwDesc D = a.descs[find_desc<true>(a.descs, a.n_desc, t)];
+    const int64_t local = t - D.tile0;
+    const int row_base = (int)(local / D.n_ct) * kRT;
+    const int col_base = (int)(local % D.n_ct) * CT;
+    const int d_out = D.d_out, d_in = D.d_in, r = a.r;
+    const uint16_t* __restrict__ Ab = (const uint16_t*)D.A;
+    const uint16_t* __restrict__ Bb = (const uint16_t*)D.B;
+    uint16_t* __restrict__ W = (uint16_t*)D.W;
+
+    // ---- stage the active slots' A column slices, transposed, into LDS ----
+    constexpr int CHUNKS = CT / 8;  // 8-column (16-byte) chunks per rank row
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+        const int e = sc.e[slot];
+        if (e < 0) continue;
+        uint16_t* dst_slot = As + slot * SLOT_ELEMS;
+        for (int q = threadIdx.x; q < RPAD * CHUNKS; q += kWaves * kWave) {
+            const int rho = q / CHUNKS;
+            const int ch = q - rho * CHUNKS;
+            const int col = col_base + ch * 8;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (rho < r && col < d_in) v = ld128(Ab + ((int64_t)e * r + rho) * d_in + col);
+            uint16_t* dst = dst_slot + (ch >> 2) * 32 * RP + rho;
+            const int cc0 = (ch & 3) * 8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t word = v[j >> 1];
+                dst[perm_row(cc0 + j) * RP] = (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
+    const bool act[4] = {sc.e[0] >= 0, sc.e[1] >= 0, sc.e[2] >= 0, sc.e[3] >= 0};
+    const bool r_vec = (r & 7) == 0;
+
+#pragma unroll 1
+    for (int rg = 0; rg < kRowGroups; ++rg) {
+        const int grp0 = row_base + (w * kRowGroups + rg) * 32;
+        if (grp0 >= d_out) break;
+        const int row = grp0 + n;
+        const bool rv = row < d_out;
+
+        // B row slices: lane holds B[e][row][16ks + 8h .. +8] (MFMA N = row).
+        u32x4 bop[4][R16];
+#pragma unroll
+        for (int slot = 0; slot < 4; ++slot) {
+#pragma unroll
+            for (int ks = 0; ks < R16; ++ks) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                const int rho0 = ks * 16 + 8 * h;
+                if (act[slot] && rv && rho0 < r) {
+                    const uint16_t* bp = Bb + ((int64_t)sc.e[slot] * d_out + row) * r + rho0;
+                    if (r_vec) {
+                        v = ld128(bp);
+                    } else {
+                        uint32_t wd[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t lo = (rho0 + 2 * j < r) ? bp[2 * j] : 0u;
+                            const uint32_t hi = (rho0 + 2 * j + 1 < r) ? bp[2 * j + 1] : 0u;
+                            wd[j] = lo | (hi << 16);
+                        }
+                        v = u32x4{wd[0], wd[1], wd[2], wd[3]};
+                    }
+                }
+                bop[slot][ks] = v;
+            }
+        }
+
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) {
+            const int c0 = col_base + sub * 64;
+            if (c0 >= d_in) break;
+            // lane's W: block b, columns c0 + 32b + 16h + [0,16)
+            u32x4 wv[2][2];
+            uint16_t* wrow = W + (int64_t)row * d_in;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int col = c0 + 32 * b + 16 * h + 8 * q;
+                    wv[b][q] = (rv && col < d_in) ? ld128_nt(wrow + col) : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                f32x16 P[4];
+#pragma unroll
+                for (int slot = 0; slot < 4; ++slot) {
+                    P[slot] = f32x16{};
+                    if (!act[slot]) continue;
+                    const uint16_t* ap = As + slot * SLOT_ELEMS + (sub * 2 + b) * 32 * RP + n * RP + 8 * h;
+#pragma unroll
+                    for (int ks = 0; ks < R16; ++ks)
+                        P[slot] = mfma32(*(const u32x4*)(ap + ks * 16), bop[slot][ks], P[slot]);
+                }
+                uint32_t ow[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const uint32_t word = wv[b][p >> 2][p & 3];
+                    float o2[2];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int i = 2 * p + j;
+                        const float sn = fmaf(sc.c[1], P[1][i], sc.c[0] * P[0][i]);
+                        const float so = fmaf(sc.c[3], P[3][i], sc.c[2] * P[2][i]);
+                        const float wf = j ? bf_hi(word) : bf_lo(word);
+                        o2[j] = wf - (so - sn);
+                    }
+                    ow[p] = pack2_bf16(o2[0], o2[1]);
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int col = c0 + 32 * b + 16 * h + 8 * q;
+                    if (rv && col < d_in)
+                        st128_nt(wrow + col, u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]});
+                }
+            }
+        }
+    }
+}
+
+// ---- element-wise path: fp32 weights (and any shape) ----------------------
+
+template <typename T> __device__ __forceinline__ float ldf(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ldf<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p, int64_t i) {
+    return bf_to_f(p[i]);
+}
+template <typename T> __device__ __forceinline__ void stf(T* p, int64_t i, float v);
+template <> __device__ __forceinline__ void stf<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void stf<uint16_t>(uint16_t* p, int64_t i, float v) {
+    p[i] = f_to_bf(v);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void switch_generic_kernel(SwitchArgs a) {
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= a.n_units) return;
+    const Sets sc = read_sets(a);
+    if (!sc.ok) {
+        if (u == 0) *a.err = 1;
+        return;
+    }
+    const SwDesc D = a.descs[find_desc<false>(a.descs, a.n_desc, u)];
+    const int64_t local = u - D.elem0;
+    const int64_t row = local / D.d_in, col = local % D.d_in;
+    const T* A = (const T*)D.A;
+    const T* B = (const T*)D.B;
+    T* W = (T*)D.W;
+    float P[4];
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+        float acc = 0.f;
+        const int e = sc.e[slot];
+        if (e >= 0)
+            for (int rho = 0; rho < a.r; ++rho)
+                acc = fmaf(ldf(B, ((int64_t)e * D.d_out + row) * a.r + rho),
+                           ldf(A, ((int64_t)e * a.r + rho) * D.d_in + col), acc);
+        P[slot] = acc;
+    }
+    const float sn = fmaf(sc.c[1], P[1], sc.c[0] * P[0]);
+    const float so = fmaf(sc.c[3], P[3], sc.c[2] * P[2]);
+    const int64_t i = row * D.d_in + col;
+    stf(W, i, ldf(W, i) - (so - sn));
+}
+
+template <int R16, int CT>
+hipError_t launch_r(const SwitchArgs& a, hipStream_t s) {
+    constexpr int RP = R16 * 16 + 8;
+    const size_t lds = (size_t)4 * (CT / 32) * 32 * RP * sizeof(uint16_t);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)switch_bf16_kernel<R16, CT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t grid = 8 * a.per_xcd;
+    hipLaunchKernelGGL((switch_bf16_kernel<R16, CT>), dim3((unsigned)grid), dim3(kWaves * kWave),
+                       lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_switch_bf16(const SwitchArgs& a, const SwTile& t, hipStream_t s) {
+    switch (t.r16) {
+        case 1: return launch_r<1, 256>(a, s);
+        case 2: return launch_r<2, 128>(a, s);
+        case 3: return launch_r<3, 64>(a, s);
+        case 4: return launch_r<4, 64>(a, s);
+        case 5: return launch_r<5, 64>(a, s);
+        case 6: return launch_r<6, 64>(a, s);
+        case 7: return launch_r<7, 64>(a, s);
+        case 8: return launch_r<8, 64>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_switch_generic(const SwitchArgs& a, int dtype, hipStream_t s) {
+    const dim3 grid((unsigned)((a.n_units + 255) / 256));
+    if (dtype == 0)
+        hipLaunchKernelGGL(switch_generic_kernel<float>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(switch_generic_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace dlm

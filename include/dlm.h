@@ -1,0 +1,227 @@
+/*
+ * dlm.h -- C ABI of the MI355X (gfx950) hot path of token-level pre-gated
+ * dynamic LoRA adapters (AdaFuse: "Accelerating Dynamic Adapter Inference via
+ * Token-Level Pre-Gating and Fused Kernel Optimization").
+ *
+ * Three operations:
+ *   dlm_pregate  one top-2 routing decision per token, made once and reused by
+ *                every adapted layer (AdaFuse digest, section 2-ga "token-level
+ *                pre-gating"; English abstract, "decide-once, apply-everywhere").
+ *   dlm_switch   one launch that removes the previous token's gated adapters
+ *                from every adapted weight of every layer and merges the current
+ *                token's, in place (digest section 2-na "fused adapter
+ *                switching": concatenated adapters, parallel GEMM in one
+ *                kernel, in-place update, prefetch).
+ *   dlm_sgmm     the unmerged batched form for rows with different expert sets,
+ *                y += sum_k g_k (x A_k^T) B_k^T, segmenting rows by their set
+ *                (digest section 2-na names the SGMM, "segmented gather matrix
+ *                multiplication", kernel).
+ *
+ * Conventions (all calls):
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer and every stream; `stream` is a hipStream_t passed as void*
+ *     (NULL = the legacy default stream).  Calls only enqueue work on `stream`
+ *     and return; device-side failures are reported through the status calls.
+ *   - Layouts are row-major.  Adapted weight W is [d_out][d_in]; expert bank A
+ *     is [E][r][d_in] (A_e = the LoRA "down" matrix), B is [E][d_out][r] (B_e =
+ *     the LoRA "up" matrix); the delta of expert e is B_e A_e.
+ *   - An expert set is two slots (idx[2] int32, g[2] fp32).  idx = -1 is an
+ *     empty slot; a NULL set pointer is the empty set.  Slot order does not
+ *     change results of dlm_switch (the kernel orders the slots itself).
+ *   - dtype: DLM_F32 or DLM_BF16 for every floating tensor of a call (x, Wr,
+ *     W, A, B, y); gates g are always fp32, indices int32.
+ *   - bf16 arithmetic: bf16 operands, fp32 accumulation; results are rounded
+ *     to bf16 once, to nearest even.
+ *   - Every call validates its arguments on the host before touching the GPU;
+ *     on a negative status nothing was enqueued and no memory was changed.
+ *     dlm_last_error() gives a text for the last failure of the calling thread.
+ *   - Thread safety: calls on distinct handles / workspaces may run
+ *     concurrently; one handle or workspace must not be used by two calls in
+ *     flight at once (the caller orders its streams).
+ */
+#ifndef DLM_H
+#define DLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DLM_OK = 0,
+    DLM_EINVAL = -1,     /* null pointer, bad count, bad value */
+    DLM_ESHAPE = -2,     /* a size out of the supported range */
+    DLM_EDTYPE = -3,     /* unknown or unsupported dtype */
+    DLM_EALIGN = -4,     /* a pointer or row pitch not 16-byte aligned (bf16 fast path) */
+    DLM_EWORKSPACE = -5, /* workspace missing or too small */
+    DLM_EHIP = -6,       /* a HIP runtime call failed */
+    DLM_EDEVICE = -7,    /* the device rejected an expert set (index out of range,
+                            non-finite gate); reported by the status calls */
+    DLM_ENOMEM = -8      /* a host or device allocation failed */
+} dlm_status;
+
+typedef enum { DLM_F32 = 0, DLM_BF16 = 1 } dlm_dtype;
+
+/* Limits of this build. */
+#define DLM_MAX_EXPERTS 32
+#define DLM_MAX_RANK 128
+
+/* Text of the calling thread's last non-OK status (static storage). */
+const char* dlm_last_error(void);
+
+/* Library version string. */
+const char* dlm_version(void);
+
+/* ------------------------------------------------------------------ router */
+
+/*
+ * Top-2 pre-gate for T tokens (digest section 2-ga: a lightweight top-2 router
+ * at the first layer selects each token's expert set; the set is then reused by
+ * every layer).
+ *   x  [T][d]  token activations at the first layer (dtype)
+ *   Wr [d][E]  router weight (dtype)
+ *   idx [T][2] out, int32: slot 0 = expert with the largest logit l = x.Wr,
+ *              slot 1 = largest of the rest; equal logits -> lower index.
+ *   g   [T][2] out, fp32: softmax over all E renormalised over the kept two,
+ *              i.e. g0 = 1/(1+exp(l1-l0)), g1 = 1 - g0 (computed in binary64,
+ *              rounded once to fp32).
+ * Logits accumulate in binary64 (the products of fp32/bf16 inputs are exact),
+ * so the decision is exact up to the summation order.  idx is always in
+ * [0, E) and idx[t][0] != idx[t][1], also for non-finite inputs.
+ * Requires 2 <= E <= DLM_MAX_EXPERTS, d >= 1, T >= 0 (T = 0 enqueues nothing).
+ */
+int dlm_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int32_t E,
+                int32_t dtype, int32_t* idx, float* g, void* stream);
+
+/* ------------------------------------------------------------ fused switch */
+
+/* One adapted weight and its expert bank. */
+typedef struct {
+    void* W;        /* [d_out][d_in], updated in place by dlm_switch */
+    const void* A;  /* [E][r][d_in] */
+    const void* B;  /* [E][d_out][r] */
+    int64_t d_out;
+    int64_t d_in;
+} dlm_proj;
+
+typedef struct dlm_layers dlm_layers;
+
+/*
+ * Build the table of every adapted weight of every layer (L*P entries) that
+ * one dlm_switch call updates.  Copies the host descriptors to a small device
+ * table (the only allocation of the switch path, freed by destroy) plus a
+ * device error word.  The buffers themselves stay owned by the caller and must
+ * outlive the handle.
+ *   projs (host) [n]; E in [1, DLM_MAX_EXPERTS]; r in [1, DLM_MAX_RANK];
+ *   scale = the LoRA scale s multiplying every delta.
+ * bf16: every W/A/B pointer 16-byte aligned and every d_in a multiple of 8.
+ * Does not synchronise.  *out (host) receives the handle.
+ */
+int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r,
+                      float scale, int32_t dtype, dlm_layers** out);
+
+/* Free the handle's device table (synchronises the device first). */
+int dlm_layers_destroy(dlm_layers* h);
+
+/*
+ * One fused switch over every weight of the handle, one kernel launch:
+ *   W <- round( W - s*sum_{k in old} g_k B_k A_k + s*sum_{k in new} g_k B_k A_k )
+ * (digest section 2-na: remove the previous token's adapters and merge the
+ * current token's, on concatenated adapter matrices, in place).  The sets are
+ * read from DEVICE memory (idx[2] int32, g[2] fp32; NULL = empty set), so a
+ * router output can feed the switch with no host synchronisation.  Each
+ * slot's product is accumulated separately in fp32 and scaled by s*g_k in
+ * fp32; the old and new halves use the same expression, so a switch to the
+ * same set leaves W bitwise unchanged.
+ * A set with an index outside [-1, E) or a non-finite gate on a used slot is
+ * rejected on the device: no weight is written and the handle's error word is
+ * set (read it with dlm_layers_status).
+ * No allocation; one launch on `stream`.
+ */
+int dlm_switch(dlm_layers* h, const int32_t* old_idx, const float* old_g,
+               const int32_t* new_idx, const float* new_g, void* stream);
+
+/* Number of kernel launches one dlm_switch call makes (always 1). */
+int dlm_switch_launches(const dlm_layers* h);
+
+/*
+ * Synchronise `stream`, then read and clear the handle's device error word:
+ * *code (host) = DLM_OK or DLM_EDEVICE.
+ */
+int dlm_layers_status(dlm_layers* h, int32_t* code, void* stream);
+
+/* ------------------------------------------------------------------- SGMM */
+
+/*
+ * Workspace bytes dlm_sgmm / dlm_sgmm_grouped need for T rows, E experts,
+ * rank r and n_problems problems sharing one set of rows (row segmentation,
+ * per-problem shrink results v [T][2][r] fp32, device status word).
+ * *bytes is host memory.
+ */
+int dlm_sgmm_workspace_size(int64_t T, int32_t E, int32_t r, int32_t n_problems,
+                            size_t* bytes);
+
+/*
+ * Batched unmerged adapters for rows with different expert sets:
+ *   y[t] <- round( y[t] + sum_k s*g[t][k] * B_{idx[t][k]} (A_{idx[t][k]} x[t]) )
+ *   x [T][d_in], y [T][d_out] (in place, must not overlap x),
+ *   idx [T][2] int32 (-1 = empty slot), g [T][2] fp32,
+ *   A [E][r][d_in], B [E][d_out][r].
+ * Three launches: segment (rows sorted by their unordered expert pair,
+ * 32-row tiles, the experts each tile uses), shrink (v = x A^T on the tile's
+ * experts, bf16 MFMA, fp32 result kept in the workspace) and expand
+ * (y += (s g v) B^T, MFMA with v*s*g split into two bf16 terms, fp32 accumulate,
+ * one bf16 rounding of y).  Rows whose two slots are empty are not touched.
+ * A row with an index outside [-1, E) or a non-finite gate on a used slot makes
+ * the whole call a no-op on y and sets the workspace status word (read it with
+ * dlm_sgmm_status).
+ * bf16: x, y, A, B 16-byte aligned; d_in and d_out multiples of 8.
+ * workspace: >= dlm_sgmm_workspace_size(T, E, r, 1) bytes, 256-byte aligned.
+ */
+int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A,
+             const void* B, void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E,
+             int32_t r, float scale, int32_t dtype, void* workspace, size_t ws_bytes,
+             void* stream);
+
+/* One problem of a grouped SGMM: every problem shares the rows' sets. */
+typedef struct {
+    const void* x;  /* [T][d_in] */
+    const void* A;  /* [E][r][d_in] */
+    const void* B;  /* [E][d_out][r] */
+    void* y;        /* [T][d_out], in place */
+    int64_t d_in;
+    int64_t d_out;
+} dlm_sgmm_problem;
+
+typedef struct dlm_sgmm_group dlm_sgmm_group;
+
+/*
+ * Register n problems (e.g. every adapted projection of every layer) that are
+ * run together on the same rows' expert sets: the decide-once routing means
+ * one segmentation serves all of them.  Copies the descriptors (host) to a
+ * small device table; buffers stay owned by the caller.
+ */
+int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, int32_t r,
+                          float scale, int32_t dtype, dlm_sgmm_group** out);
+int dlm_sgmm_group_destroy(dlm_sgmm_group* h);
+
+/*
+ * Run every problem of the group for T rows: one segment launch shared by all
+ * problems, then one shrink and one expand launch covering all problems.
+ * workspace: >= dlm_sgmm_workspace_size(T, E, r, n_problems) bytes.
+ */
+int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, int64_t T,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Synchronise `stream`, then read and clear the workspace status word:
+ * *code (host) = DLM_OK or DLM_EDEVICE.
+ */
+int dlm_sgmm_status(void* workspace, int32_t* code, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLM_H */

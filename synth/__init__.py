@@ -210,3 +210,58 @@ WORKLOADS = {
     "mixed-decode": Workload("mixed-decode", 4, torch.bfloat16, 32, _P7B, 8, 16, 1.0, 4096, 64,
                              steps=128, extra={"p_keep": 0.9}),
 }
+
+
+# --------------------------------------------------------------------------
+# Device-resident inputs of a workload
+# --------------------------------------------------------------------------
+
+def switch_model(wl: Workload, device="cuda", layers=None):
+    """[(layer, proj_name, W, A, B)] for every adapted weight of the decode workloads:
+    W [d_out][d_in] ~ N(0, .02), A [E][r][d_in], B [E][d_out][r] ~ N(0, .02)."""
+    out = []
+    for l in (range(wl.layers) if layers is None else layers):
+        for pi, (name, o, i) in enumerate(wl.projs):
+            W = normal_device((o, i), 0.02, wl.dtype, device, wl.cfg_id, "W", l, pi)
+            A = normal_device((wl.E, wl.r, i), 0.02, wl.dtype, device, wl.cfg_id, "A", l, pi)
+            B = normal_device((wl.E, o, wl.r), 0.02, wl.dtype, device, wl.cfg_id, "B", l, pi)
+            out.append((l, name, W, A, B))
+    return out
+
+
+def refill_switch_weights_(wl: Workload, model):
+    """Regenerate every W of `model` in place (same streams as switch_model)."""
+    for l, name, W, _, _ in model:
+        pi = [p[0] for p in wl.projs].index(name)
+        fill_normal_device_(W, 0.02, wl.cfg_id, "W", l, pi)
+
+
+def router_inputs(wl: Workload, device="cuda"):
+    """x [T][d] ~ N(0, 1) and Wr [d][E] ~ N(0, .02) of the decode workloads."""
+    x = normal_device((wl.T, wl.d_model), 1.0, wl.dtype, device, wl.cfg_id, "x")
+    Wr = normal_device((wl.d_model, wl.E), 0.02, wl.dtype, device, wl.cfg_id, "Wr")
+    return x, Wr
+
+
+def sgmm_problems(wl: Workload, device="cuda"):
+    """[(layer, proj_name, x, A, B, y0)] of the batched workloads: x [T][d_in] ~ N(0, 1),
+    y0 [T][d_out] ~ N(0, .02^2 d_in) standing in for the base output, A/B ~ N(0, .02)."""
+    out = []
+    for l in range(wl.layers):
+        for pi, (name, o, i) in enumerate(wl.projs):
+            x = normal_device((wl.T, i), 1.0, wl.dtype, device, wl.cfg_id, "x", l, pi)
+            A = normal_device((wl.E, wl.r, i), 0.02, wl.dtype, device, wl.cfg_id, "A", l, pi)
+            B = normal_device((wl.E, o, wl.r), 0.02, wl.dtype, device, wl.cfg_id, "B", l, pi)
+            y = normal_device((wl.T, o), 0.02 * i ** 0.5, wl.dtype, device, wl.cfg_id, "y0", l, pi)
+            out.append((l, name, x, A, B, y))
+    return out
+
+
+def batched_sets(wl: Workload):
+    """Expert sets of the batched workloads as CPU tensors:
+    prefill -> idx [T][2], g [T][2]; mixed decode -> idx [steps][T][2], g [steps][T][2]."""
+    if wl.name == "sgmm-prefill":
+        return zipf_pair_sets(wl.T, wl.E, wl.extra["zipf_s"], wl.cfg_id, "sets")
+    if wl.name == "mixed-decode":
+        return markov_pair_sets(wl.steps, wl.T, wl.E, wl.extra["p_keep"], wl.cfg_id, "sets")
+    raise ValueError(wl.name)

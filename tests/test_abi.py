@@ -1,0 +1,154 @@
+"""C-ABI library checks that need no GPU: it loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call
+(every call below fails validation, so no device memory is ever touched)."""
+import ctypes as C
+import os
+
+import pytest
+
+import dynamic_lora_moe_amd as dlm
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dlm.LIB_PATH), reason="libdlm.so not built")
+
+FAKE = 0x100000  # a 256-byte aligned address that validation rejects before use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dlm.load()
+
+
+def test_exports_every_header_function(lib):
+    names = dlm.header_functions()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dlm.h but not exported"
+    assert lib.dlm_version().decode().startswith("dlm")
+
+
+def test_header_status_codes_match_binding():
+    text = open(dlm.HEADER).read()
+    for name, val in [("DLM_OK", 0), ("DLM_EINVAL", -1), ("DLM_ESHAPE", -2), ("DLM_EDTYPE", -3),
+                      ("DLM_EALIGN", -4), ("DLM_EWORKSPACE", -5), ("DLM_EHIP", -6),
+                      ("DLM_EDEVICE", -7), ("DLM_ENOMEM", -8)]:
+        assert f"{name} = {val}" in text
+        assert dlm.STATUS_NAMES[val] == name
+
+
+def _err(lib):
+    return lib.dlm_last_error().decode()
+
+
+def test_pregate_validation(lib):
+    P = C.c_void_p
+    assert lib.dlm_pregate(P(FAKE), P(FAKE), 4, 64, 1, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert "E=1" in _err(lib)
+    assert lib.dlm_pregate(P(FAKE), P(FAKE), 4, 64, 33, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert lib.dlm_pregate(P(FAKE), P(FAKE), 4, 0, 8, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert lib.dlm_pregate(P(FAKE), P(FAKE), -1, 64, 8, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert lib.dlm_pregate(P(FAKE), P(FAKE), 4, 64, 8, 7, P(FAKE), P(FAKE), None) == dlm.DLM_EDTYPE
+    assert lib.dlm_pregate(None, P(FAKE), 4, 64, 8, 1, P(FAKE), P(FAKE), None) == dlm.DLM_EINVAL
+    assert lib.dlm_pregate(P(FAKE), P(FAKE), 4, 64, 8, 1, None, P(FAKE), None) == dlm.DLM_EINVAL
+    # T = 0 is a valid no-op that touches nothing
+    assert lib.dlm_pregate(None, None, 0, 64, 8, 1, None, None, None) == dlm.DLM_OK
+
+
+def _projs(*ps):
+    arr = (dlm.dlm_proj * len(ps))()
+    for i, p in enumerate(ps):
+        arr[i] = dlm.dlm_proj(*p)
+    return arr
+
+
+def test_layers_create_validation(lib):
+    h = C.c_void_p()
+    ok = (FAKE, FAKE, FAKE, 64, 64)
+    assert lib.dlm_layers_create(None, 1, 4, 4, 1.0, 1, C.byref(h)) == dlm.DLM_EINVAL
+    assert lib.dlm_layers_create(_projs(ok), 1, 4, 4, 1.0, 1, None) == dlm.DLM_EINVAL
+    assert lib.dlm_layers_create(_projs(ok), 0, 4, 4, 1.0, 1, C.byref(h)) == dlm.DLM_EINVAL
+    assert lib.dlm_layers_create(_projs(ok), 1, 0, 4, 1.0, 1, C.byref(h)) == dlm.DLM_ESHAPE
+    assert lib.dlm_layers_create(_projs(ok), 1, 33, 4, 1.0, 1, C.byref(h)) == dlm.DLM_ESHAPE
+    assert lib.dlm_layers_create(_projs(ok), 1, 4, 0, 1.0, 1, C.byref(h)) == dlm.DLM_ESHAPE
+    assert lib.dlm_layers_create(_projs(ok), 1, 4, 129, 1.0, 1, C.byref(h)) == dlm.DLM_ESHAPE
+    assert lib.dlm_layers_create(_projs(ok), 1, 4, 4, 1.0, 5, C.byref(h)) == dlm.DLM_EDTYPE
+    assert lib.dlm_layers_create(_projs(ok), 1, 4, 4, float("nan"), 1, C.byref(h)) == dlm.DLM_EINVAL
+    assert lib.dlm_layers_create(_projs((0, FAKE, FAKE, 64, 64)), 1, 4, 4, 1.0, 1, C.byref(h)) == dlm.DLM_EINVAL
+    assert lib.dlm_layers_create(_projs((FAKE, FAKE, FAKE, 0, 64)), 1, 4, 4, 1.0, 1, C.byref(h)) == dlm.DLM_ESHAPE
+    # bf16 fast path needs 16-byte aligned pointers and d_in % 8 == 0; the second
+    # weight of the list is the bad one, so the error names it
+    assert lib.dlm_layers_create(_projs(ok, (FAKE + 2, FAKE, FAKE, 64, 64)), 2, 4, 4, 1.0, 1,
+                                 C.byref(h)) == dlm.DLM_EALIGN
+    assert "proj 1" in _err(lib)
+    assert lib.dlm_layers_create(_projs((FAKE, FAKE, FAKE, 64, 60)), 1, 4, 4, 1.0, 1, C.byref(h)) == dlm.DLM_EALIGN
+    assert h.value is None
+
+
+def test_switch_and_status_validation(lib):
+    P = C.c_void_p
+    assert lib.dlm_switch(None, None, None, None, None, None) == dlm.DLM_EINVAL
+    assert lib.dlm_layers_destroy(None) == dlm.DLM_EINVAL
+    assert lib.dlm_layers_status(None, None, None) == dlm.DLM_EINVAL
+    assert lib.dlm_switch_launches(None) == 0
+    assert lib.dlm_sgmm_status(None, None, None) == dlm.DLM_EINVAL
+    assert lib.dlm_sgmm_group_destroy(None) == dlm.DLM_EINVAL
+    assert lib.dlm_sgmm_group_run(None, P(FAKE), P(FAKE), 4, P(FAKE), 1 << 20, None) == dlm.DLM_EINVAL
+
+
+def test_sgmm_workspace_size(lib):
+    b = C.c_size_t(0)
+    assert lib.dlm_sgmm_workspace_size(4096, 8, 16, 7, C.byref(b)) == dlm.DLM_OK
+    # the per-problem shrink results dominate: 7 problems x 4096 rows x 2 slots x 16 x 4 bytes
+    assert b.value >= 7 * 4096 * 2 * 16 * 4
+    assert b.value % 256 == 0
+    small = C.c_size_t(0)
+    assert lib.dlm_sgmm_workspace_size(64, 8, 16, 1, C.byref(small)) == dlm.DLM_OK
+    assert small.value < b.value
+    assert lib.dlm_sgmm_workspace_size(-1, 8, 16, 1, C.byref(b)) == dlm.DLM_ESHAPE
+    assert lib.dlm_sgmm_workspace_size(64, 0, 16, 1, C.byref(b)) == dlm.DLM_ESHAPE
+    assert lib.dlm_sgmm_workspace_size(64, 8, 0, 1, C.byref(b)) == dlm.DLM_ESHAPE
+    assert lib.dlm_sgmm_workspace_size(64, 8, 16, 0, C.byref(b)) == dlm.DLM_EINVAL
+    assert lib.dlm_sgmm_workspace_size(64, 8, 16, 1, None) == dlm.DLM_EINVAL
+
+
+def test_sgmm_validation(lib):
+    P = C.c_void_p
+    ws = C.c_size_t(0)
+    lib.dlm_sgmm_workspace_size(16, 4, 16, 1, C.byref(ws))
+    X, Y = FAKE, FAKE + (1 << 20)
+
+    def call(x=X, idx=FAKE, g=FAKE, A=FAKE, B=FAKE, y=Y, T=16, d_in=64, d_out=64, E=4, r=16,
+             s=1.0, dt=1, w=FAKE, nb=ws.value):
+        return lib.dlm_sgmm(P(x), P(idx), P(g), P(A), P(B), P(y), T, d_in, d_out, E, r, s, dt,
+                            P(w), nb, None)
+
+    assert call(T=-1) == dlm.DLM_ESHAPE
+    assert call(E=0) == dlm.DLM_ESHAPE
+    assert call(r=200) == dlm.DLM_ESHAPE
+    assert call(dt=3) == dlm.DLM_EDTYPE
+    assert call(s=float("inf")) == dlm.DLM_EINVAL
+    assert call(x=0) == dlm.DLM_EINVAL
+    assert call(idx=0) == dlm.DLM_EINVAL
+    assert call(d_in=0) == dlm.DLM_ESHAPE
+    assert call(d_out=60) == dlm.DLM_EALIGN
+    assert call(A=FAKE + 8) == dlm.DLM_EALIGN
+    assert call(y=X + 64) == dlm.DLM_EINVAL          # y overlaps x
+    assert "overlap" in _err(lib)
+    assert call(w=0) == dlm.DLM_EWORKSPACE
+    assert call(nb=ws.value - 1) == dlm.DLM_EWORKSPACE
+    assert call(w=FAKE + 16) == dlm.DLM_EALIGN       # workspace must be 256-byte aligned
+    assert call(T=0) == dlm.DLM_OK                   # nothing to do, nothing touched
+
+
+def test_sgmm_group_create_validation(lib):
+    h = C.c_void_p()
+    arr = (dlm.dlm_sgmm_problem * 2)()
+    arr[0] = dlm.dlm_sgmm_problem(FAKE, FAKE, FAKE, FAKE + (1 << 20), 64, 64)
+    arr[1] = dlm.dlm_sgmm_problem(FAKE, FAKE, FAKE, FAKE + (1 << 20), 64, 12)
+    assert lib.dlm_sgmm_group_create(None, 1, 4, 16, 1.0, 1, C.byref(h)) == dlm.DLM_EINVAL
+    assert lib.dlm_sgmm_group_create(arr, 0, 4, 16, 1.0, 1, C.byref(h)) == dlm.DLM_EINVAL
+    assert lib.dlm_sgmm_group_create(arr, 2, 4, 16, 1.0, 1, None) == dlm.DLM_EINVAL
+    assert lib.dlm_sgmm_group_create(arr, 2, 40, 16, 1.0, 1, C.byref(h)) == dlm.DLM_ESHAPE
+    # problem 1 has d_out = 12 (not a multiple of 8) for bf16
+    assert lib.dlm_sgmm_group_create(arr, 2, 4, 16, 1.0, 1, C.byref(h)) == dlm.DLM_EALIGN
+    assert "problem 1" in _err(lib)
+    assert h.value is None

@@ -1,0 +1,154 @@
+"""SGMM parity on small and ragged shapes, edge cases and the device error path.
+Inputs are generated; the oracle recomputes every row in binary64."""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_lora_moe_amd as dlm
+import oracle
+import synth
+from gpu_util import check_bf16, check_f32
+
+pytestmark = pytest.mark.gpu
+
+# The expand feeds u = s*g*v to the MFMA as hi + lo bf16 terms: a relative
+# representation error of at most 2^-17 per term on top of fp32 accumulation.
+SPLIT = 2.0 ** -16
+
+
+def _problem(T, d_in, d_out, E, r, dt, key):
+    x = synth.normal_device((T, d_in), 1.0, dt, "cuda", key, "x")
+    A = synth.normal_device((E, r, d_in), 0.02, dt, "cuda", key, "A")
+    B = synth.normal_device((E, d_out, r), 0.02, dt, "cuda", key, "B")
+    y = synth.normal_device((T, d_out), 0.02 * d_in ** 0.5, dt, "cuda", key, "y0")
+    return x, A, B, y
+
+
+def _sets(T, E, rng, p_empty=0.1, p_dup=0.05, p_none=0.05):
+    idx = np.empty((T, 2), np.int32)
+    for t in range(T):
+        idx[t] = rng.choice(E, size=2, replace=E < 2)
+        u = rng.random()
+        if u < p_empty:
+            idx[t, 1] = -1
+        elif u < p_empty + p_dup:
+            idx[t, 1] = idx[t, 0]
+        elif u < p_empty + p_dup + p_none:
+            idx[t] = -1
+    g = rng.random((T, 2)).astype(np.float32)
+    return torch.from_numpy(idx), torch.from_numpy(g)
+
+
+def _check(x, idx, g, A, B, y0, y, scale, what):
+    ref, ex, ab = oracle.sgmm(x.cpu(), idx.cpu(), g.cpu(), A.cpu(), B.cpu(), y0, scale,
+                              with_stats=True)
+    d_in, r = x.shape[1], A.shape[1]
+    n = d_in + 2 * r + 2
+    if y.dtype == torch.float32:
+        return check_f32(y.cpu(), ex, ab, n, what)
+    return check_bf16(y.cpu(), ref, ex, ab, n, extra=SPLIT, what=what)
+
+
+CASES = [
+    # (T, d_in, d_out, E, r, scale, dtype)
+    (16, 64, 64, 4, 4, 1.0, torch.float32),          # tiny fp32 workload shape
+    (33, 96, 40, 3, 5, 2.0, torch.float32),
+    (1, 64, 64, 8, 16, 1.0, torch.bfloat16),
+    (5, 200, 264, 8, 16, 2.0, torch.bfloat16),       # ragged everything
+    (33, 64, 72, 2, 16, 1.0, torch.bfloat16),
+    (100, 136, 520, 8, 4, 1.0, torch.bfloat16),      # r < 16, r % 8 != 0
+    (64, 128, 256, 8, 24, 1.0, torch.bfloat16),
+    (70, 72, 64, 16, 64, 1.0, torch.bfloat16),       # 70B rank, many experts
+    (40, 64, 64, 32, 16, 1.0, torch.bfloat16),       # most experts
+    (20, 64, 96, 4, 128, 0.5, torch.bfloat16),       # largest rank
+    (300, 256, 264, 8, 16, 1.0, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_sgmm_parity(ci):
+    T, d_in, d_out, E, r, scale, dt = CASES[ci]
+    print(f"[sgmm] case {ci}: T={T} d_in={d_in} d_out={d_out} E={E} r={r} {dt}", flush=True)
+    x, A, B, y = _problem(T, d_in, d_out, E, r, dt, 3000 + ci)
+    idx, g = _sets(T, E, np.random.default_rng(ci))
+    y0 = y.cpu().clone()
+    idx_d, g_d = idx.cuda(), g.cuda()
+    ws = dlm.sgmm_workspace(T, E, r)
+    dlm.sgmm(x, idx_d, g_d, A, B, y, scale, ws)
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    st = _check(x, idx, g, A, B, y0, y, scale, f"sgmm case {ci}")
+    print(st, flush=True)
+    # rows whose two slots are empty are not touched
+    none = (idx == -1).all(1)
+    assert torch.equal(y.cpu()[none], y0[none])
+
+
+def test_sgmm_zero_gates_and_slot_swap():
+    T, d_in, d_out, E, r = 48, 128, 136, 8, 16
+    x, A, B, y = _problem(T, d_in, d_out, E, r, torch.bfloat16, 3100)
+    idx, g = _sets(T, E, np.random.default_rng(5), 0, 0, 0)
+    y0 = y.clone()
+    ws = dlm.sgmm_workspace(T, E, r)
+    dlm.sgmm(x, idx.cuda(), torch.zeros_like(g).cuda(), A, B, y, 1.0, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    y1 = y0.clone()
+    dlm.sgmm(x, idx.cuda(), g.cuda(), A, B, y1, 1.0, ws)
+    y2 = y0.clone()
+    dlm.sgmm(x, idx.flip(1).contiguous().cuda(), g.flip(1).contiguous().cuda(), A, B, y2, 1.0, ws)
+    torch.cuda.synchronize()
+    # with the slots swapped a row keeps its pair, hence its tile and union: same bits
+    assert torch.equal(y1, y2)
+
+
+def test_sgmm_single_set_matches_gemm_reference():
+    """All rows on one set: y + s(g0 X A0^T B0^T + g1 X A1^T B1^T), a plain GEMM chain (fp32 CPU)."""
+    T, d_in, d_out, E, r = 96, 256, 192, 8, 16
+    x, A, B, y = _problem(T, d_in, d_out, E, r, torch.bfloat16, 3101)
+    y0 = y.cpu().clone()
+    idx = torch.tensor([[2, 6]] * T, dtype=torch.int32)
+    g = torch.tensor([[0.75, 0.25]] * T, dtype=torch.float32)
+    dlm.sgmm(x, idx.cuda(), g.cuda(), A, B, y, 2.0)
+    torch.cuda.synchronize()
+    X, Ad, Bd = x.cpu().double(), A.cpu().double(), B.cpu().double()
+    ref = y0.double() + 2.0 * (0.75 * (X @ Ad[2].T) @ Bd[2].T + 0.25 * (X @ Ad[6].T) @ Bd[6].T)
+    assert (y.cpu().double() - ref).abs().max().item() < 0.02
+    _check(x, idx, g, A, B, y0, y, 2.0, "single set")
+
+
+def test_sgmm_bad_set_is_a_noop_with_status():
+    T, d_in, d_out, E, r = 40, 64, 64, 4, 16
+    x, A, B, y = _problem(T, d_in, d_out, E, r, torch.bfloat16, 3102)
+    y0 = y.clone()
+    idx, g = _sets(T, E, np.random.default_rng(9), 0, 0, 0)
+    ws = dlm.sgmm_workspace(T, E, r)
+    for bad_i, bad_g in [((7, 0), 4), ((3, 1), -2), ((20, 0), None)]:
+        ii, gg = idx.clone(), g.clone()
+        if bad_g is None:
+            gg[bad_i] = float("nan")
+        else:
+            ii[bad_i] = bad_g
+        dlm.sgmm(x, ii.cuda(), gg.cuda(), A, B, y, 1.0, ws)
+        assert dlm.sgmm_status(ws) == dlm.DLM_EDEVICE
+        assert torch.equal(y, y0)
+    # the status word was cleared; a good call works again on the same workspace
+    dlm.sgmm(x, idx.cuda(), g.cuda(), A, B, y, 1.0, ws)
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    _check(x, idx, g, A, B, y0.cpu(), y, 1.0, "after bad set")
+
+
+def test_sgmm_group_matches_single_calls():
+    T, E, r = 50, 8, 16
+    shapes = [(64, 128), (200, 64), (96, 264)]
+    probs = [_problem(T, i, o, E, r, torch.bfloat16, 3200 + k) for k, (i, o) in enumerate(shapes)]
+    idx, g = _sets(T, E, np.random.default_rng(11))
+    y0s = [p[3].clone() for p in probs]
+    grp = dlm.SgmmGroup(probs, E, r, 2.0)
+    grp.run(idx.cuda(), g.cuda())
+    torch.cuda.synchronize()
+    for k, (x, A, B, y) in enumerate(probs):
+        y1 = y0s[k].clone()
+        dlm.sgmm(x, idx.cuda(), g.cuda(), A, B, y1, 2.0)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y), k
+        _check(x, idx, g, A, B, y0s[k].cpu(), y, 2.0, f"group problem {k}")
