@@ -30,15 +30,25 @@ __device__ __forceinline__ uint16_t f_to_bf(float a) {
     return __builtin_bit_cast(uint16_t, (__bf16)a);
 }
 
+// Global-memory accesses go through address_space(1) pointers so they compile
+// to global_* instructions.  Generic pointers (e.g. read from a descriptor
+// table) would give flat_* instructions, which also count against the LDS
+// wait counter: every LDS wait would then drain all in-flight HBM loads.
+template <typename T> using gptr = __attribute__((address_space(1))) T*;
+template <typename T> using gcptr = __attribute__((address_space(1))) const T*;
+
+template <typename T> __device__ __forceinline__ T gld(const T* p) { return *(gcptr<T>)p; }
+template <typename T> __device__ __forceinline__ void gst(T* p, T v) { *(gptr<T>)p = v; }
+
 // 128-bit global load/store.  `nt` marks streaming data that is touched once
 // (weights being switched) so it does not evict reused adapter slices.
-__device__ __forceinline__ u32x4 ld128(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x4 ld128(const void* p) { return *(gcptr<u32x4>)p; }
 __device__ __forceinline__ u32x4 ld128_nt(const void* p) {
-    return __builtin_nontemporal_load((const u32x4*)p);
+    return __builtin_nontemporal_load((gcptr<u32x4>)p);
 }
-__device__ __forceinline__ void st128(void* p, u32x4 v) { *(u32x4*)p = v; }
+__device__ __forceinline__ void st128(void* p, u32x4 v) { *(gptr<u32x4>)p = v; }
 __device__ __forceinline__ void st128_nt(void* p, u32x4 v) {
-    __builtin_nontemporal_store(v, (u32x4*)p);
+    __builtin_nontemporal_store(v, (gptr<u32x4>)p);
 }
 
 // D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.

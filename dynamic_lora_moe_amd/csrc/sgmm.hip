@@ -187,13 +187,16 @@ __device__ __forceinline__ int find_prob(const SgDesc* __restrict__ d, int n, in
 
 // ---- shrink (bf16, MFMA) -----------------------------------------------------
 
+// N blocks (32 columns of (expert, rank)) accumulated per pass over K.
+constexpr int kNBG = 2;
+
 template <int R16>
 __global__ __launch_bounds__(256) void sgmm_shrink_bf16(SgmmArgs a) {
     constexpr int RPAD = R16 * 16;
     const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
-    if (hdr[SG_ERR]) return;
+    if (gld(hdr + SG_ERR)) return;
     const int tile = blockIdx.x;
-    if (tile >= hdr[SG_NTILES]) return;
+    if (tile >= gld(hdr + SG_NTILES)) return;
     const int prob = blockIdx.y;
     const SgDesc D = a.descs ? a.descs[prob] : a.single;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
@@ -206,12 +209,12 @@ __global__ __launch_bounds__(256) void sgmm_shrink_bf16(SgmmArgs a) {
     __shared__ float s_red[3][kWave][16];
     const int tid = threadIdx.x;
     if (tid < 32) {
-        const int row = perm[tile * 32 + tid];
+        const int row = gld(perm + tile * 32 + tid);
         s_row[tid] = row;
-        s_e0[tid] = row >= 0 ? a.idx[2 * (int64_t)row] : -1;
-        s_e1[tid] = row >= 0 ? a.idx[2 * (int64_t)row + 1] : -1;
+        s_e0[tid] = row >= 0 ? gld(a.idx + 2 * (int64_t)row) : -1;
+        s_e1[tid] = row >= 0 ? gld(a.idx + 2 * (int64_t)row + 1) : -1;
     }
-    if (tid == 0) s_nU = mask_list(tmask[tile], s_U);
+    if (tid == 0) s_nU = mask_list(gld(tmask + tile), s_U);
     __syncthreads();
 
     const int nU = s_nU;
@@ -224,19 +227,19 @@ __global__ __launch_bounds__(256) void sgmm_shrink_bf16(SgmmArgs a) {
     const uint16_t* xr = xrow >= 0 ? x + (int64_t)xrow * d_in : nullptr;
     const int n_kc = (d_in + 63) / 64;
 
-    for (int g0 = 0; g0 < NB; g0 += 4) {
-        const int nbg = NB - g0 < 4 ? NB - g0 : 4;
+    for (int g0 = 0; g0 < NB; g0 += kNBG) {
+        const int nbg = NB - g0 < kNBG ? NB - g0 : kNBG;
         // lane's column of each N block: (expert U[u], rank rho)
-        const uint16_t* arow[4];
+        const uint16_t* arow[kNBG];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kNBG; ++j) {
             const int nn = (g0 + j) * 32 + n;
             const int u = nn / RPAD, rho = nn % RPAD;
             arow[j] = (j < nbg && u < nU && rho < r) ? A + ((int64_t)s_U[u] * r + rho) * d_in : nullptr;
         }
-        f32x16 acc[4];
+        f32x16 acc[kNBG];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+        for (int j = 0; j < kNBG; ++j) acc[j] = f32x16{};
         // K: 64-wide chunks, wave w takes chunks w, w+4, ...; inside a chunk the
         // half-wave h covers k in [32h, 32h+32) as four 8-wide MFMA k-steps, so
         // each lane reads 64 contiguous bytes of x and of each A row.
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(256) void sgmm_shrink_bf16(SgmmArgs a) {
                 xo[s] = (xr && col < d_in) ? ld128(xr + col) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kNBG; ++j) {
                 if (j >= nbg) break;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(256) void sgmm_shrink_bf16(SgmmArgs a) {
         }
         // fixed-order sum of the four waves' partial products, one block at a time
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kNBG; ++j) {
             if (j >= nbg) break;
             if (w > 0) {
 #pragma unroll
@@ -279,8 +282,8 @@ __global__ __launch_bounds__(256) void sgmm_shrink_bf16(SgmmArgs a) {
                         const int m = 8 * (i >> 2) + 4 * h + (i & 3);
                         if (s_row[m] < 0) continue;
                         float* vp = v + ((int64_t)(tile * 32 + m) * 2) * RPAD + rho;
-                        if (s_e0[m] == e) vp[0] = val;
-                        if (s_e1[m] == e) vp[RPAD] = val;
+                        if (s_e0[m] == e) gst(vp, val);
+                        if (s_e1[m] == e) gst(vp + RPAD, val);
                     }
                 }
             }
@@ -297,13 +300,13 @@ template <int R16>
 __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_xcd) {
     constexpr int RPAD = R16 * 16;
     const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
-    if (hdr[SG_ERR]) return;
+    if (gld(hdr + SG_ERR)) return;
     const int64_t bid = blockIdx.x;
     const int64_t t = (bid & 7) * per_xcd + (bid >> 3);
     if (t >= a.n_expand_units) return;
     // work item = (tile, problem, 256-column block), tile-major
     const int tile = (int)(t / a.total_cb);
-    if (tile >= hdr[SG_NTILES]) return;
+    if (tile >= gld(hdr + SG_NTILES)) return;
     const int64_t rem = t - (int64_t)tile * a.total_cb;
     const int prob = a.descs ? find_prob(a.descs, a.n_prob, rem) : 0;
     const SgDesc D = a.descs ? a.descs[prob] : a.single;
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     __shared__ int s_U[32];
     __shared__ int s_nU;
     const int tid = threadIdx.x;
-    if (tid == 0) s_nU = mask_list(tmask[tile], s_U);
+    if (tid == 0) s_nU = mask_list(gld(tmask + tile), s_U);
     __syncthreads();
 
     const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
@@ -327,14 +330,14 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     uint16_t* __restrict__ y = (uint16_t*)D.y;
 
     // this lane's row (MFMA N index = tile row n) and its two slots
-    const int row = perm[tile * 32 + n];
+    const int row = gld(perm + tile * 32 + n);
     int e0 = -1, e1 = -1;
     float c0 = 0.f, c1 = 0.f;
     if (row >= 0) {
-        e0 = a.idx[2 * (int64_t)row];
-        e1 = a.idx[2 * (int64_t)row + 1];
-        c0 = e0 >= 0 ? a.scale * a.g[2 * (int64_t)row] : 0.f;
-        c1 = e1 >= 0 ? a.scale * a.g[2 * (int64_t)row + 1] : 0.f;
+        e0 = gld(a.idx + 2 * (int64_t)row);
+        e1 = gld(a.idx + 2 * (int64_t)row + 1);
+        c0 = e0 >= 0 ? a.scale * gld(a.g + 2 * (int64_t)row) : 0.f;
+        c1 = e1 >= 0 ? a.scale * gld(a.g + 2 * (int64_t)row + 1) : 0.f;
     }
     const float* v0 = v + ((int64_t)(tile * 32 + n) * 2) * RPAD;
     const float* v1 = v0 + RPAD;
@@ -357,14 +360,16 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
 #pragma unroll
             for (int j = 0; j < 8; ++j) uv[j] = 0.f;
             if (m0) {
+                const u32x4 p0 = ld128(v0 + rho0), p1 = ld128(v0 + rho0 + 4);
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    if (rho0 + j < r) uv[j] = c0 * v0[rho0 + j];
+                    if (rho0 + j < r) uv[j] = c0 * __uint_as_float(j < 4 ? p0[j] : p1[j - 4]);
             }
             if (m1) {
+                const u32x4 p0 = ld128(v1 + rho0), p1 = ld128(v1 + rho0 + 4);
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    if (rho0 + j < r) uv[j] = fmaf(c1, v1[rho0 + j], uv[j]);
+                    if (rho0 + j < r) uv[j] = fmaf(c1, __uint_as_float(j < 4 ? p0[j] : p1[j - 4]), uv[j]);
             }
             uint32_t hw[4], lw[4];
 #pragma unroll
@@ -385,8 +390,8 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
                     } else {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const uint32_t lo = (rho0 + 2 * j < r) ? bp[2 * j] : 0u;
-                            const uint32_t hi = (rho0 + 2 * j + 1 < r) ? bp[2 * j + 1] : 0u;
+                            const uint32_t lo = (rho0 + 2 * j < r) ? gld(bp + 2 * j) : 0u;
+                            const uint32_t hi = (rho0 + 2 * j + 1 < r) ? gld(bp + 2 * j + 1) : 0u;
                             ao[j] = lo | (hi << 16);
                         }
                     }

@@ -28,7 +28,8 @@
 //     W - (S_old - S_new) in fp32 and one RNE to bf16.  Identical expressions
 //     for both halves make a switch to the same set an exact no-op; each set's
 //     slots are put in a canonical order first so slot order cannot matter.
-//   * W is touched once: loads and stores carry the nontemporal hint.
+//   * W goes through the caches with default policy: nontemporal hints on this
+//     stream measured ~1.5x slower on MI355X.
 #include "gfx950.hpp"
 #include "internal.hpp"
 
@@ -103,15 +104,208 @@ __device__ __forceinline__ int find_desc(const SwDesc* __restrict__ d, int n, in
 // With this order, accumulator register a of lane l holds column 16*(l/32) + a.
 __device__ __forceinline__ int perm_row(int cc) { return 8 * ((cc >> 2) & 3) + 4 * (cc >> 4) + (cc & 3); }
 
-template <int R16, int CT>
-__global__ __launch_bounds__(kWaves* kWave) void switch_bf16_kernel(SwitchArgs a) {
+// LDS layouts.
+//  A slices: As[slot][cb][m][RPAD] bf16, one row per MFMA row index m (one W
+//    column), RPAD ranks.  The 16-byte chunks of a row are XOR-swizzled so the
+//    8 lanes of each ds_read_b128 phase hit 8 different bank groups.
+//  W scratch: one 32-row x 64-column bf16 block per wave (4 KB), rows of eight
+//    16-byte chunks, chunk index XOR (row & 7): both the row-major (global)
+//    and the MFMA-layout accesses are conflict-free.
+template <int R16>
+__device__ __forceinline__ int a_chunk_swz(int m, int c) {
+    constexpr int P = 2 * R16;                            // chunks per row
+    constexpr int G = (P % 8 == 0) ? 8 : (P % 4 == 0 ? 4 : 2);  // gcd(P, 8)
+    constexpr int PER = 8 / G;
+    return c ^ ((m / PER) % G);
+}
+__device__ __forceinline__ int w_off(int row, int chunk) {  // bf16 element offset
+    return row * 64 + ((chunk ^ (row & 7)) << 3);
+}
+
+// One 256-row x CT-column tile.  FULL = every row, column and rank of the tile
+// is in range (all tiles of model-sized weights): then no load or store carries
+// a guard, so the compiler issues them back to back instead of branching
+// around each one.  Edge tiles run the guarded instance.
+template <int R16, int CT, bool FULL>
+__device__ __forceinline__ void switch_tile(const SwitchArgs& a, const Sets& sc, const SwDesc& D,
+                                            int row_base, int col_base, uint16_t* As, uint16_t* Ws) {
     constexpr int RPAD = R16 * 16;
-    constexpr int RP = RPAD + 8;   // LDS pitch of one transposed column (elements)
     constexpr int NCB = CT / 32;   // 32-column MFMA blocks per tile
     constexpr int NSUB = CT / 64;  // 64-column steps per row group
-    constexpr int SLOT_ELEMS = NCB * 32 * RP;
-    extern __shared__ __attribute__((aligned(16))) uint16_t As[];  // [4][NCB][32][RP]
+    constexpr int U = kRowGroups * NSUB;  // (row group, step) units per wave
+    constexpr int SLOT_ELEMS = NCB * 32 * RPAD;
+    constexpr int CHUNKS = CT / 8;  // 16-byte chunks per rank row of the A slice
+    constexpr int NQ = RPAD * CHUNKS;
+    constexpr int NSTAGE = (NQ + kWaves * kWave - 1) / (kWaves * kWave);
+    const int d_out = D.d_out, d_in = D.d_in, r = a.r;
+    const uint16_t* __restrict__ Ab = (const uint16_t*)D.A;
+    const uint16_t* __restrict__ Bb = (const uint16_t*)D.B;
+    uint16_t* __restrict__ W = (uint16_t*)D.W;
+    const int tid = threadIdx.x, w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
+    const bool act[4] = {sc.e[0] >= 0, sc.e[1] >= 0, sc.e[2] >= 0, sc.e[3] >= 0};
+    const bool r_vec = (r & 7) == 0;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    uint16_t* ws = Ws + w * (32 * 64);  // this wave's W scratch
+    // row-major lane map of a 32x64 block: instruction i covers rows 8i + lane/8,
+    // lane%8 is the 16-byte chunk within the 128-byte row segment
+    const int lr = lane >> 3, lc = lane & 7;
 
+    // 1) A column slices of the active slots: issue every load first.
+    u32x4 av[4][NSTAGE];
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+#pragma unroll
+        for (int i = 0; i < NSTAGE; ++i) {
+            const int q = tid + i * kWaves * kWave;
+            const int rho = q / CHUNKS, col = col_base + (q % CHUNKS) * 8;
+            bool ok = act[slot] && (NQ % (kWaves * kWave) == 0 || q < NQ);
+            if (!FULL) ok = ok && rho < r && col < d_in;
+            av[slot][i] = ok ? ld128(Ab + ((int64_t)sc.e[slot] * r + rho) * d_in + col) : zero;
+        }
+    }
+
+    // row group g of this wave covers rows row_base + (w*kRowGroups + g)*32 + [0,32)
+    auto load_b = [&](u32x4 (&bo)[4][R16], int g) {
+        const int row = row_base + (w * kRowGroups + g) * 32 + n;
+#pragma unroll
+        for (int slot = 0; slot < 4; ++slot)
+#pragma unroll
+            for (int ks = 0; ks < R16; ++ks) {
+                const int rho0 = ks * 16 + 8 * h;
+                const uint16_t* bp = Bb + ((int64_t)sc.e[slot] * d_out + row) * r + rho0;
+                u32x4 v = zero;
+                if (FULL) {
+                    if (act[slot]) v = ld128(bp);
+                } else if (act[slot] && row < d_out && rho0 < r) {
+                    if (r_vec) {
+                        v = ld128(bp);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t lo = (rho0 + 2 * j < r) ? gld(bp + 2 * j) : 0u;
+                            const uint32_t hi = (rho0 + 2 * j + 1 < r) ? gld(bp + 2 * j + 1) : 0u;
+                            v[j] = lo | (hi << 16);
+                        }
+                    }
+                }
+                bo[slot][ks] = v;
+            }
+    };
+    // unit u = (row group u / NSUB, 64-column step u % NSUB), read row-major:
+    // instruction i reads row 8i + lr, columns c0 + 8lc .. +8
+    auto load_w = [&](u32x4 (&wv)[4], int u) {
+        const int row0 = row_base + (w * kRowGroups + u / NSUB) * 32;
+        const int col = col_base + (u % NSUB) * 64 + 8 * lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 8 * i + lr;
+            const uint16_t* p = W + (int64_t)row * d_in + col;
+            if (FULL) wv[i] = ld128(p);
+            else wv[i] = (row < d_out && col < d_in) ? ld128(p) : zero;
+        }
+    };
+
+    u32x4 bcur[4][R16];
+    u32x4 wcur[4], wnxt[4];
+    load_b(bcur, 0);
+    load_w(wcur, 0);
+
+    // 2) transpose the A slices into LDS: As[slot][cb][m][rho] = A[e][rho][col(cb, m)]
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+        if (!act[slot]) continue;
+        uint16_t* dst_slot = As + slot * SLOT_ELEMS;
+#pragma unroll
+        for (int i = 0; i < NSTAGE; ++i) {
+            const int q = tid + i * kWaves * kWave;
+            if (NQ % (kWaves * kWave) != 0 && q >= NQ) continue;
+            const int rho = q / CHUNKS, ch = q % CHUNKS;
+            uint16_t* dst = dst_slot + (ch >> 2) * 32 * RPAD + (rho & 7);
+            const int cc0 = (ch & 3) * 8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int m = perm_row(cc0 + j);
+                const uint32_t word = av[slot][i][j >> 1];
+                dst[m * RPAD + (a_chunk_swz<R16>(m, rho >> 3) << 3)] =
+                    (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
+            }
+        }
+    }
+    __syncthreads();
+
+    // 3) stream the wave's units: the next unit's W is in flight while the
+    //    current unit runs its MFMAs and epilogue; the next row group's B slices
+    //    are fetched right after the last MFMA that reads the current ones.
+#pragma unroll 1
+    for (int u = 0; u < U; ++u) {
+        const int g = u / NSUB, sub = u % NSUB;
+        if (u + 1 < U) load_w(wnxt, u + 1);
+        // row-major registers -> scratch; each block then reads its MFMA layout
+        // (row n, chunks 4b + 2h + q) and writes its result back in place
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4*)(ws + w_off(8 * i + lr, lc)) = wcur[i];
+#pragma unroll 1
+        for (int b = 0; b < 2; ++b) {
+            u32x4 wm[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) wm[q] = *(const u32x4*)(ws + w_off(n, 4 * b + 2 * h + q));
+            f32x16 P[4];
+#pragma unroll
+            for (int slot = 0; slot < 4; ++slot) {
+                P[slot] = f32x16{};
+                if (!act[slot]) continue;
+                const uint16_t* ap = As + slot * SLOT_ELEMS + (sub * 2 + b) * 32 * RPAD + n * RPAD;
+#pragma unroll
+                for (int ks = 0; ks < R16; ++ks)
+                    P[slot] = mfma32(*(const u32x4*)(ap + (a_chunk_swz<R16>(n, 2 * ks + h) << 3)),
+                                     bcur[slot][ks], P[slot]);
+            }
+            if (b == 1 && u + 1 < U && (u + 1) % NSUB == 0) load_b(bcur, (u + 1) / NSUB);
+            uint32_t ow[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t word = wm[p >> 2][p & 3];
+                float o2[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int i = 2 * p + j;
+                    const float sn = fmaf(sc.c[1], P[1][i], sc.c[0] * P[0][i]);
+                    const float so = fmaf(sc.c[3], P[3][i], sc.c[2] * P[2][i]);
+                    const float wf = j ? bf_hi(word) : bf_lo(word);
+                    o2[j] = wf - (so - sn);
+                }
+                ow[p] = pack2_bf16(o2[0], o2[1]);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                *(u32x4*)(ws + w_off(n, 4 * b + 2 * h + q)) =
+                    u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
+        }
+        // scratch -> row-major registers -> global
+        const int row0 = row_base + (w * kRowGroups + g) * 32;
+        const int col = col_base + sub * 64 + 8 * lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 8 * i + lr;
+            const u32x4 v = *(const u32x4*)(ws + w_off(8 * i + lr, lc));
+            if (FULL || (row < d_out && col < d_in)) st128(W + (int64_t)row * d_in + col, v);
+        }
+        if (u + 1 < U) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wcur[i] = wnxt[i];
+        }
+    }
+}
+
+// Rank 16 fits three waves per SIMD without spilling, ranks up to 96 two, larger
+// ranks one.
+template <int R16, int CT>
+__global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(R16 <= 1 ? 3 : (R16 <= 6 ? 2 : 1))))
+void switch_bf16_kernel(SwitchArgs a) {
+    // [4 slots][CT/32][32][R16*16] A slices, then 4 x [32][64] W scratch
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint16_t* As = smem;
+    uint16_t* Ws = smem + 4 * (CT / 32) * 32 * (R16 * 16);
     const int64_t bid = blockIdx.x;
     const int64_t t = (bid & 7) * a.per_xcd + (bid >> 3);
     if (t >= a.n_units) return;
@@ -124,123 +318,11 @@ __global__ __launch_bounds__(kWaves* kWave) void switch_bf16_kernel(SwitchArgs a
     const int64_t local = t - D.tile0;
     const int row_base = (int)(local / D.n_ct) * kRT;
     const int col_base = (int)(local % D.n_ct) * CT;
-    const int d_out = D.d_out, d_in = D.d_in, r = a.r;
-    const uint16_t* __restrict__ Ab = (const uint16_t*)D.A;
-    const uint16_t* __restrict__ Bb = (const uint16_t*)D.B;
-    uint16_t* __restrict__ W = (uint16_t*)D.W;
-
-    // ---- stage the active slots' A column slices, transposed, into LDS ----
-    constexpr int CHUNKS = CT / 8;  // 8-column (16-byte) chunks per rank row
-#pragma unroll
-    for (int slot = 0; slot < 4; ++slot) {
-        const int e = sc.e[slot];
-        if (e < 0) continue;
-        uint16_t* dst_slot = As + slot * SLOT_ELEMS;
-        for (int q = threadIdx.x; q < RPAD * CHUNKS; q += kWaves * kWave) {
-            const int rho = q / CHUNKS;
-            const int ch = q - rho * CHUNKS;
-            const int col = col_base + ch * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (rho < r && col < d_in) v = ld128(Ab + ((int64_t)e * r + rho) * d_in + col);
-            uint16_t* dst = dst_slot + (ch >> 2) * 32 * RP + rho;
-            const int cc0 = (ch & 3) * 8;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t word = v[j >> 1];
-                dst[perm_row(cc0 + j) * RP] = (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
-            }
-        }
-    }
-    __syncthreads();
-
-    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
-    const bool act[4] = {sc.e[0] >= 0, sc.e[1] >= 0, sc.e[2] >= 0, sc.e[3] >= 0};
-    const bool r_vec = (r & 7) == 0;
-
-#pragma unroll 1
-    for (int rg = 0; rg < kRowGroups; ++rg) {
-        const int grp0 = row_base + (w * kRowGroups + rg) * 32;
-        if (grp0 >= d_out) break;
-        const int row = grp0 + n;
-        const bool rv = row < d_out;
-
-        // B row slices: lane holds B[e][row][16ks + 8h .. +8] (MFMA N = row).
-        u32x4 bop[4][R16];
-#pragma unroll
-        for (int slot = 0; slot < 4; ++slot) {
-#pragma unroll
-            for (int ks = 0; ks < R16; ++ks) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                const int rho0 = ks * 16 + 8 * h;
-                if (act[slot] && rv && rho0 < r) {
-                    const uint16_t* bp = Bb + ((int64_t)sc.e[slot] * d_out + row) * r + rho0;
-                    if (r_vec) {
-                        v = ld128(bp);
-                    } else {
-                        uint32_t wd[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t lo = (rho0 + 2 * j < r) ? bp[2 * j] : 0u;
-                            const uint32_t hi = (rho0 + 2 * j + 1 < r) ? bp[2 * j + 1] : 0u;
-                            wd[j] = lo | (hi << 16);
-                        }
-                        v = u32x4{wd[0], wd[1], wd[2], wd[3]};
-                    }
-                }
-                bop[slot][ks] = v;
-            }
-        }
-
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
-            const int c0 = col_base + sub * 64;
-            if (c0 >= d_in) break;
-            // lane's W: block b, columns c0 + 32b + 16h + [0,16)
-            u32x4 wv[2][2];
-            uint16_t* wrow = W + (int64_t)row * d_in;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int col = c0 + 32 * b + 16 * h + 8 * q;
-                    wv[b][q] = (rv && col < d_in) ? ld128_nt(wrow + col) : u32x4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                f32x16 P[4];
-#pragma unroll
-                for (int slot = 0; slot < 4; ++slot) {
-                    P[slot] = f32x16{};
-                    if (!act[slot]) continue;
-                    const uint16_t* ap = As + slot * SLOT_ELEMS + (sub * 2 + b) * 32 * RP + n * RP + 8 * h;
-#pragma unroll
-                    for (int ks = 0; ks < R16; ++ks)
-                        P[slot] = mfma32(*(const u32x4*)(ap + ks * 16), bop[slot][ks], P[slot]);
-                }
-                uint32_t ow[8];
-#pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    const uint32_t word = wv[b][p >> 2][p & 3];
-                    float o2[2];
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int i = 2 * p + j;
-                        const float sn = fmaf(sc.c[1], P[1][i], sc.c[0] * P[0][i]);
-                        const float so = fmaf(sc.c[3], P[3][i], sc.c[2] * P[2][i]);
-                        const float wf = j ? bf_hi(word) : bf_lo(word);
-                        o2[j] = wf - (so - sn);
-                    }
-                    ow[p] = pack2_bf16(o2[0], o2[1]);
-                }
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int col = c0 + 32 * b + 16 * h + 8 * q;
-                    if (rv && col < d_in)
-                        st128_nt(wrow + col, u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]});
-                }
-            }
-        }
-    }
+    const bool full = row_base + kRT <= D.d_out && col_base + CT <= D.d_in && a.r == R16 * 16;
+    if (full)
+        switch_tile<R16, CT, true>(a, sc, D, row_base, col_base, As, Ws);
+    else
+        switch_tile<R16, CT, false>(a, sc, D, row_base, col_base, As, Ws);
 }
 
 // ---- element-wise path: fp32 weights (and any shape) ----------------------
@@ -290,14 +372,11 @@ __global__ __launch_bounds__(256) void switch_generic_kernel(SwitchArgs a) {
 
 template <int R16, int CT>
 hipError_t launch_r(const SwitchArgs& a, hipStream_t s) {
-    constexpr int RP = R16 * 16 + 8;
-    const size_t lds = (size_t)4 * (CT / 32) * 32 * RP * sizeof(uint16_t);
-    static bool attr_set = false;
-    if (!attr_set) {
+    const size_t lds = ((size_t)4 * (CT / 32) * 32 * (R16 * 16) + (size_t)kWaves * 32 * 64) * sizeof(uint16_t);
+    if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)switch_bf16_kernel<R16, CT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int64_t grid = 8 * a.per_xcd;
     hipLaunchKernelGGL((switch_bf16_kernel<R16, CT>), dim3((unsigned)grid), dim3(kWaves * kWave),
