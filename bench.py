@@ -162,42 +162,95 @@ def bench_sgmm(torch, dlm, synth, name, reps, log):
 
 def cpu_baseline(torch, synth, target_s, log):
     """The oracle (as it stands) on a bounded sample of the headline workload:
-    the switch of every adapted weight of one layer, on an evenly spaced subset
-    of rows sized to take about `target_s` seconds; scaled to weight GB/s."""
+    the switch of every adapted weight of the first k layers, k chosen so the
+    oracle runs about `target_s` seconds (at least one layer); scaled to weight
+    GB/s (weight bytes read + written per second)."""
     import numpy as np
 
     import oracle
     wl = synth.WORKLOADS["7b-decode"]
-    model = synth.switch_model(wl, layers=[0])
     threads = oracle.threads()
     old = ([1, 5], [0.6, 0.4])
     new = ([2, 5], [0.7, 0.3])
-
-    # calibrate on a small sample, then size the measured sample
-    def timed(stride):
-        tot = 0.0
-        elems = 0
-        for _, _, W, A, B in model:
-            rows = np.arange(0, W.shape[0], stride)
-            Wr = W[torch.from_numpy(rows).cuda()].cpu()
-            Ac, Bc = A.cpu(), B.cpu()
+    elems, secs, layers = 0, 0.0, 0
+    while layers < wl.layers and (layers == 0 or secs * (layers + 1) / layers <= target_s):
+        for _, _, W, A, B in synth.switch_model(wl, layers=[layers]):
+            Wh, Ah, Bh = W.cpu(), A.cpu(), B.cpu()
+            rows = np.arange(W.shape[0])
             t1 = time.perf_counter()
-            oracle.switch_rows(Wr, rows, Ac, Bc, W.shape[0], wl.scale, old, new)
-            tot += time.perf_counter() - t1
-            elems += rows.size * W.shape[1]
-        return elems, tot
+            oracle.switch_rows(Wh, rows, Ah, Bh, W.shape[0], wl.scale, old, new)
+            secs += time.perf_counter() - t1
+            elems += W.numel()
+        layers += 1
+        torch.cuda.empty_cache()
+    log(f"cpu oracle: {layers} layers, {elems} elements in {secs:.1f} s on {threads} threads")
+    return {"value": elems * 4 / secs / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"switch (old {old} -> new {new}) of all 7 adapted weights of the first "
+                      f"{layers} of 32 layers of the 7B-shaped workload ({elems} elements, "
+                      f"{secs:.1f} s of oracle time); weight bytes read+written per second, "
+                      f"binary64 oracle, OpenMP over rows"}
 
-    e, t = timed(512)
-    per_elem = t / max(e, 1)
-    layer_elems = sum(o * i for _, o, i in wl.projs)
-    stride = max(1, int(np.ceil(layer_elems * per_elem / target_s)))
-    e, t = timed(stride)
-    log(f"cpu oracle: {e} elements in {t:.1f} s on {threads} threads")
-    gbps = e * 4 / t / 1e9
-    return {"value": gbps, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"switch (old {old} -> new {new}) of all 7 adapted weights of layer 0 of the "
-                      f"7B-shaped workload, every {stride}th row ({e} elements, {t:.1f} s); weight "
-                      f"bytes read+written per second, binary64 oracle"}
+
+def profile_kernels(torch, dlm, synth, n_switch, log):
+    """A short run for hardware-counter collection: the router on the 256 tokens,
+    `n_switch` fused switches of the 7B-shaped workload, then one 1 GiB device
+    copy (torch) whose byte count calibrates the FETCH_SIZE/WRITE_SIZE counters."""
+    wl = synth.WORKLOADS["7b-decode"]
+    model = synth.switch_model(wl)
+    x, Wr = synth.router_inputs(wl)
+    L = dlm.Layers([(W, A, B) for _, _, W, A, B in model], wl.E, wl.r, wl.scale)
+    idx, g = dlm.pregate(x, Wr)
+    L.switch(None, (idx[0], g[0]))
+    for t in range(1, n_switch):
+        L.switch((idx[t - 1], g[t - 1]), (idx[t], g[t]))
+    torch.cuda.synchronize()
+    src = torch.empty(2 ** 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"profiled {n_switch} switches and one copy of {src.numel() * 2} bytes")
+
+
+def traffic_from(fetch_csv, write_csv, log):
+    """Per-launch HBM bytes of the switch kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE in KiB per dispatch) of `--profile-kernels`, each
+    scaled by the same counter's reading for the 1 GiB copy (known bytes);
+    written to profiles/traffic.json with a hash of the kernel source."""
+    import csv
+
+    def read(path, counter):
+        sw, cp = [], []
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                v = float(row["Counter_Value"])
+                if "switch_bf16_kernel" in name:
+                    sw.append(v)
+                elif "copy" in name.lower() and "dlm" not in name:
+                    cp.append(v)
+        return sw, cp
+    out = {}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        sw, cp = read(path, counter)
+        copy_kib = max(cp)  # the 1 GiB copy is the largest copy dispatch
+        factor = (2 ** 30 / 1024) / copy_kib
+        out[key] = {"switch_kib_per_launch": sum(sw) / len(sw), "launches": len(sw),
+                    "copy_kib": copy_kib, "scale": factor,
+                    "bytes_per_launch": sum(sw) / len(sw) * 1024 * factor}
+    res = {"switch_bf16_7b": {
+        "source_hash": _src_hash(SWITCH_SOURCES),
+        "bytes_per_launch": out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"],
+        "fetch": out["fetch"], "write": out["write"],
+        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                   "python3 bench.py --profile-kernels"}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    log(f"wrote {path}: {res}")
 
 
 def main():
@@ -209,7 +262,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sgmm", action="store_true")
+    ap.add_argument("--profile-kernels", type=int, nargs="?", const=4, default=0,
+                    help="short run for rocprofv3 counter collection (N switches + 1 GiB copy)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter CSVs")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from, lambda m: print(f"[bench] {m}", file=sys.stderr))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the hot path here runs on a single GPU with no "
               "sharding or collectives; run it with --gpus 1", file=sys.stderr)
@@ -224,6 +284,9 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     torch.cuda.set_device(0)
+    if args.profile_kernels:
+        profile_kernels(torch, dlm, synth, args.profile_kernels, log)
+        return
     sw = bench_switch(torch, dlm, synth, args.steps, args.warmup, log)
     log(f"switch: {sw}")
     sg = {}
