@@ -67,10 +67,11 @@ def load(path: str = LIB_PATH):
         "dlm_switch": ([P, P, P, P, P, P], C.c_int),
         "dlm_switch_launches": ([P], C.c_int),
         "dlm_layers_status": ([P, P, P], C.c_int),
-        "dlm_sgmm_workspace_size": ([I64, I32, I32, I32, P], C.c_int),
+        "dlm_sgmm_workspace_size": ([I64, I64, I32, I32, I32, P], C.c_int),
         "dlm_sgmm": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, F, I32, P, C.c_size_t, P], C.c_int),
         "dlm_sgmm_group_create": ([P, I32, I32, I32, F, I32, P], C.c_int),
         "dlm_sgmm_group_destroy": ([P], C.c_int),
+        "dlm_sgmm_group_repack": ([P, P], C.c_int),
         "dlm_sgmm_group_run": ([P, P, P, I64, P, C.c_size_t, P], C.c_int),
         "dlm_sgmm_status": ([P, P, P], C.c_int),
     }
@@ -197,14 +198,16 @@ class Layers:
 
 # ---- SGMM ------------------------------------------------------------------------
 
-def sgmm_workspace_size(T: int, E: int, r: int, n_problems: int = 1) -> int:
+def sgmm_workspace_size(T: int, d_in_max: int, E: int, r: int, n_problems: int = 1) -> int:
     b = C.c_size_t(0)
-    _check(load().dlm_sgmm_workspace_size(T, E, r, n_problems, C.byref(b)), "dlm_sgmm_workspace_size")
+    _check(load().dlm_sgmm_workspace_size(T, d_in_max, E, r, n_problems, C.byref(b)),
+           "dlm_sgmm_workspace_size")
     return b.value
 
 
-def sgmm_workspace(T: int, E: int, r: int, n_problems: int = 1, device="cuda") -> torch.Tensor:
-    n = sgmm_workspace_size(T, E, r, n_problems)
+def sgmm_workspace(T: int, d_in_max: int, E: int, r: int, n_problems: int = 1,
+                   device="cuda") -> torch.Tensor:
+    n = sgmm_workspace_size(T, d_in_max, E, r, n_problems)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
@@ -216,7 +219,7 @@ def sgmm(x, idx, g, A, B, y, scale: float, workspace=None, stream=None):
     E, r, _ = A.shape
     d_out = B.shape[1]
     if workspace is None:
-        workspace = sgmm_workspace(T, E, r, 1, x.device)
+        workspace = sgmm_workspace(T, d_in, E, r, 1, x.device)
     _check(load().dlm_sgmm(_p(x), _p(idx), _p(g), _p(A), _p(B), _p(y), T, d_in, d_out, E, r,
                            float(scale), _dt(x), _p(workspace), workspace.numel(), _stream(stream)),
            "dlm_sgmm")
@@ -247,9 +250,14 @@ class SgmmGroup:
                "dlm_sgmm_group_create")
         self._h = h
         self.E, self.r, self.n = E, r, len(self._keep)
+        self.d_in_max = max(x.shape[1] for x, _, _, _ in self._keep)
 
     def workspace(self, T: int, device="cuda"):
-        return sgmm_workspace(T, self.E, self.r, self.n, device)
+        return sgmm_workspace(T, self.d_in_max, self.E, self.r, self.n, device)
+
+    def repack(self, stream=None):
+        """Refresh the packed A copies after the A banks were changed in place."""
+        _check(load().dlm_sgmm_group_repack(self._h, _stream(stream)), "dlm_sgmm_group_repack")
 
     def run(self, idx, g, T: int | None = None, workspace=None, stream=None):
         _need(idx, "idx")

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <new>
 #include <vector>
 
@@ -70,7 +71,14 @@ struct dlm_sgmm_group {
     int32_t E = 0, r = 0;
     float scale = 1.f;
     int32_t dtype = 0;
-    int64_t total_cb = 0, d_out_max = 0;
+    int64_t total_cb = 0, total_ks = 0, d_out_max = 0, d_in_max = 0;
+    // packed copies of the distinct A banks (bf16 groups), owned by the handle
+    struct Pack {
+        const void* A;
+        void* Ap;
+        int64_t d_in;
+    };
+    std::vector<Pack> packs;
 };
 
 extern "C" {
@@ -214,13 +222,16 @@ int dlm_layers_status(dlm_layers* h, int32_t* code, void* stream) {
 
 // ------------------------------------------------------------------ SGMM ----
 
-int dlm_sgmm_workspace_size(int64_t T, int32_t E, int32_t r, int32_t n_problems, size_t* bytes) {
+int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r, int32_t n_problems,
+                            size_t* bytes) {
     if (!bytes) return fail(DLM_EINVAL, "sgmm_workspace_size: bytes is null");
     if (T < 0 || T > ((int64_t)1 << 30)) return fail(DLM_ESHAPE, "sgmm_workspace_size: T=%lld", (long long)T);
+    if (d_in_max < 1 || d_in_max > kMaxDim)
+        return fail(DLM_ESHAPE, "sgmm_workspace_size: d_in_max=%lld", (long long)d_in_max);
     if (E < 1 || E > DLM_MAX_EXPERTS) return fail(DLM_ESHAPE, "sgmm_workspace_size: E=%d", E);
     if (r < 1 || r > DLM_MAX_RANK) return fail(DLM_ESHAPE, "sgmm_workspace_size: r=%d", r);
     if (n_problems < 1) return fail(DLM_EINVAL, "sgmm_workspace_size: n_problems=%d", n_problems);
-    *bytes = sgmm_layout(T, E, r, n_problems).total;
+    *bytes = sgmm_layout(T, d_in_max, E, r, n_problems).total;
     return ok();
 }
 
@@ -249,14 +260,16 @@ int check_ws(void* ws, size_t ws_bytes, const SgLayout& L) {
 }
 
 int run_sgmm(const SgDesc* d_descs, const SgDesc& single, int n_prob, int64_t total_cb,
-             int64_t d_out_max, const int32_t* idx, const float* g, int64_t T, int E, int r,
-             float scale, int dtype, void* ws, const SgLayout& L, hipStream_t s) {
+             int64_t total_ks, int64_t d_out_max, const int32_t* idx, const float* g, int64_t T, int E, int r,
+             float scale, int dtype, int packed, void* ws, const SgLayout& L, hipStream_t s) {
     SgmmArgs a;
     a.descs = d_descs;
+    a.packed = packed;
     a.single = single;
     a.n_prob = n_prob;
     a.n_expand_units = L.tiles_max * total_cb;
     a.total_cb = total_cb;
+    a.total_ks = total_ks;
     a.d_out_max = d_out_max;
     a.idx = idx;
     a.g = g;
@@ -289,7 +302,7 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, c
     const size_t es = esize(dtype);
     if (overlap(x, (size_t)T * d_in * es, y, (size_t)T * d_out * es))
         return fail(DLM_EINVAL, "sgmm: x and y overlap");
-    const SgLayout L = sgmm_layout(T, E, r, 1);
+    const SgLayout L = sgmm_layout(T, d_in, E, r, 1);
     rc = check_ws(workspace, ws_bytes, L);
     if (rc != DLM_OK) return rc;
     SgDesc d{};
@@ -299,9 +312,11 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, c
     d.y = y;
     d.d_in = (int32_t)d_in;
     d.d_out = (int32_t)d_out;
-    d.n_cb = (int32_t)((d_out + 255) / 256);
+    d.n_cb = (int32_t)((d_out + kSgmmExpandCols - 1) / kSgmmExpandCols);
     d.unit0 = 0;
-    return run_sgmm(nullptr, d, 1, d.n_cb, d_out, idx, g, T, E, r, scale, dtype, workspace, L,
+    d.n_ks = (int32_t)((d_in + kSgmmKSlice - 1) / kSgmmKSlice);
+    d.ks0 = 0;
+    return run_sgmm(nullptr, d, 1, d.n_cb, d.n_ks, d_out, idx, g, T, E, r, scale, dtype, 0, workspace, L,
                     (hipStream_t)stream);
 }
 
@@ -317,7 +332,7 @@ int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, i
     dlm_sgmm_group* h = new (std::nothrow) dlm_sgmm_group();
     if (!h) return fail(DLM_ENOMEM, "sgmm_group_create: host allocation failed");
     h->h_descs.resize(n);
-    int64_t cb = 0, dmax = 0;
+    int64_t cb = 0, ks = 0, dmax = 0, dimax = 0;
     for (int i = 0; i < n; ++i) {
         const int rc = check_problem(probs[i], dtype, i);
         if (rc != DLM_OK) {
@@ -332,10 +347,14 @@ int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, i
         d.y = probs[i].y;
         d.d_in = (int32_t)probs[i].d_in;
         d.d_out = (int32_t)probs[i].d_out;
-        d.n_cb = (int32_t)((probs[i].d_out + 255) / 256);
+        d.n_cb = (int32_t)((probs[i].d_out + kSgmmExpandCols - 1) / kSgmmExpandCols);
         d.unit0 = cb;
         cb += d.n_cb;
+        d.n_ks = (int32_t)((probs[i].d_in + kSgmmKSlice - 1) / kSgmmKSlice);
+        d.ks0 = ks;
+        ks += d.n_ks;
         if (probs[i].d_out > dmax) dmax = probs[i].d_out;
+        if (probs[i].d_in > dimax) dimax = probs[i].d_in;
     }
     h->n = n;
     h->E = E;
@@ -343,11 +362,34 @@ int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, i
     h->scale = scale;
     h->dtype = dtype;
     h->total_cb = cb;
+    h->total_ks = ks;
     h->d_out_max = dmax;
-    hipError_t e = hipMalloc((void**)&h->d_descs, sizeof(SgDesc) * n);
+    h->d_in_max = dimax;
+    hipError_t e = hipSuccess;
+    if (dtype == DLM_BF16) {
+        // one packed copy per distinct (A, d_in); problems sharing a bank share it
+        std::map<std::pair<const void*, int64_t>, void*> seen;
+        for (int i = 0; i < n && e == hipSuccess; ++i) {
+            SgDesc& d = h->h_descs[i];
+            const auto key = std::make_pair(d.A, (int64_t)d.d_in);
+            auto it = seen.find(key);
+            if (it == seen.end()) {
+                void* ap = nullptr;
+                e = hipMalloc(&ap, (size_t)E * r * d.d_in * 2);
+                if (e != hipSuccess) break;
+                h->packs.push_back({d.A, ap, d.d_in});
+                e = launch_sgmm_pack_a(d.A, ap, E, r, d.d_in, nullptr);
+                it = seen.emplace(key, ap).first;
+            }
+            d.Ap = it->second;
+        }
+        if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+    }
+    if (e == hipSuccess) e = hipMalloc((void**)&h->d_descs, sizeof(SgDesc) * n);
     if (e == hipSuccess) e = hipMemcpy(h->d_descs, h->h_descs.data(), sizeof(SgDesc) * n, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         if (h->d_descs) (void)hipFree(h->d_descs);
+        for (auto& pk : h->packs) (void)hipFree(pk.Ap);
         delete h;
         return hip_fail(e, "sgmm_group_create");
     }
@@ -359,8 +401,18 @@ int dlm_sgmm_group_destroy(dlm_sgmm_group* h) {
     if (!h) return fail(DLM_EINVAL, "sgmm_group_destroy: null handle");
     hipError_t e = hipDeviceSynchronize();
     if (h->d_descs) (void)hipFree(h->d_descs);
+    for (auto& pk : h->packs) (void)hipFree(pk.Ap);
     delete h;
     if (e != hipSuccess) return hip_fail(e, "sgmm_group_destroy");
+    return ok();
+}
+
+int dlm_sgmm_group_repack(dlm_sgmm_group* h, void* stream) {
+    if (!h) return fail(DLM_EINVAL, "sgmm_group_repack: null handle");
+    for (auto& pk : h->packs) {
+        const hipError_t e = launch_sgmm_pack_a(pk.A, pk.Ap, h->E, h->r, pk.d_in, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "sgmm_group_repack");
+    }
     return ok();
 }
 
@@ -376,11 +428,11 @@ int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, in
         if (overlap(d.x, (size_t)T * d.d_in * es, d.y, (size_t)T * d.d_out * es))
             return fail(DLM_EINVAL, "sgmm_group_run: problem %d x and y overlap", i);
     }
-    const SgLayout L = sgmm_layout(T, h->E, h->r, h->n);
+    const SgLayout L = sgmm_layout(T, h->d_in_max, h->E, h->r, h->n);
     const int rc = check_ws(workspace, ws_bytes, L);
     if (rc != DLM_OK) return rc;
-    return run_sgmm(h->d_descs, h->h_descs[0], h->n, h->total_cb, h->d_out_max, idx, g, T, h->E,
-                    h->r, h->scale, h->dtype, workspace, L, (hipStream_t)stream);
+    return run_sgmm(h->d_descs, h->h_descs[0], h->n, h->total_cb, h->total_ks, h->d_out_max, idx, g, T, h->E,
+                    h->r, h->scale, h->dtype, h->packs.empty() ? 0 : 1, workspace, L, (hipStream_t)stream);
 }
 
 int dlm_sgmm_status(void* workspace, int32_t* code, void* stream) {

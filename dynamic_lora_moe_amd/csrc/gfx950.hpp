@@ -61,7 +61,13 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+// Wave index within the workgroup, marked wave-uniform (an SGPR): control flow
+// that depends on it stays scalar instead of running under exec masks.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
+// A value every lane of the wave holds identically (e.g. read from LDS),
+// moved to an SGPR so loops and branches on it stay scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Butterfly sum over the 64 lanes; every lane gets the total, in the same
 // fixed order on every run.

@@ -11,12 +11,13 @@
 //            experts its rows use (a bitmask).  Rows with two empty slots are
 //            left out.  The same segmentation serves every problem of a
 //            grouped call (one routing decision per token for all layers).
-//   shrink   per (tile, problem): v = x_rows A_U^T for the tile's experts U,
-//            bf16 MFMA 32x32x16 with M = tile rows (gathered through perm),
-//            N = (expert, rank), K = d_in split over the four waves and summed
-//            in a fixed order; each row keeps the fp32 v of its own two slots.
-//   expand   per (tile, 256 output columns, problem): y_rows += u B_U^T with
-//            u = s*g*v per (row, expert, rank).  u stays fp32-accurate by
+//   shrink   per (problem, 1024-wide K slice, tile): the slice's partial
+//            v = x_rows A_U^T for the tile's experts U, bf16 MFMA 32x32x16 with
+//            M = tile rows (gathered through perm, staged in LDS), N = (expert,
+//            rank); each row keeps the fp32 partial v of its own two slots.
+//   expand   per (problem, 1024 output columns, tile): v = the slices' sum
+//            in slice order, y_rows += u B_U^T with u = s*g*v per (row, expert,
+//            rank).  u stays fp32-accurate by
 //            entering the MFMA as two bf16 terms (hi + lo); B slices are
 //            k-contiguous and load straight into operand registers; lane l
 //            ends with 16 consecutive outputs of one row (two 128-bit y
@@ -32,7 +33,7 @@ namespace dlm {
 
 static size_t a256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-SgLayout sgmm_layout(int64_t T, int E, int r, int n_prob) {
+SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob) {
     SgLayout L;
     L.T = T;
     L.T_pad = ((T > 0 ? T : 1) + 31) / 32 * 32;
@@ -41,6 +42,7 @@ SgLayout sgmm_layout(int64_t T, int E, int r, int n_prob) {
     L.n_keys = (int64_t)(E + 1) * (E + 1);
     L.tiles_max = L.T_pad / 32;
     L.r_pad = (r + 15) / 16 * 16;
+    L.max_ks = (int)((d_in_max + kSgmmKSlice - 1) / kSgmmKSlice);
     size_t o = 0;
     L.hdr = o;   o += 256;
     L.perm = o;  o += a256((size_t)L.T_pad * 4);
@@ -48,7 +50,7 @@ SgLayout sgmm_layout(int64_t T, int E, int r, int n_prob) {
     L.key = o;   o += a256((size_t)(T > 0 ? T : 1) * 4);
     L.hist = o;  o += a256((size_t)L.n_chunks * L.n_keys * 4);
     L.tmask = o; o += a256((size_t)L.tiles_max * 4);
-    L.v = o;     o += a256((size_t)n_prob * L.T_pad * 2 * L.r_pad * 4);
+    L.v = o;     o += a256((size_t)n_prob * L.max_ks * L.T_pad * 2 * L.r_pad * 4);
     L.total = o;
     return L;
 }
@@ -176,37 +178,68 @@ __device__ __forceinline__ int mask_list(uint32_t m, int* out) {
     return n;
 }
 
+// Problem owning unit u of a prefix-summed per-problem count (last d with d.F <= u).
+template <int64_t SgDesc::*F>
 __device__ __forceinline__ int find_prob(const SgDesc* __restrict__ d, int n, int64_t u) {
     int lo = 0, hi = n - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (d[mid].unit0 <= u) lo = mid; else hi = mid - 1;
+        if (d[mid].*F <= u) lo = mid; else hi = mid - 1;
     }
     return lo;
 }
+__device__ __forceinline__ int find_prob_ks(const SgDesc* d, int n, int64_t u) { return find_prob<&SgDesc::ks0>(d, n, u); }
+__device__ __forceinline__ int find_prob_cb(const SgDesc* d, int n, int64_t u) { return find_prob<&SgDesc::unit0>(d, n, u); }
 
 // ---- shrink (bf16, MFMA) -----------------------------------------------------
 
-// N blocks (32 columns of (expert, rank)) accumulated per pass over K.
-constexpr int kNBG = 2;
+// 64-wide K chunks of one slice, and 16-byte chunks of one x row of a slice
+constexpr int kKC = kSgmmKSlice / 64;
+constexpr int kXC = kSgmmKSlice / 8;
+static_assert(kKC % 4 == 0, "slice is a whole number of 256-wide steps");
+// x slice in LDS: 32 rows of kSgmmKSlice bf16; the 16-byte chunk c of row m is
+// stored at chunk c ^ (m & 15), so the MFMA-layout reads (16 rows, one chunk)
+// and the row-contiguous writes both touch 16 distinct bank groups.
+__device__ __forceinline__ int x_off(int row, int c) { return row * kSgmmKSlice + ((c ^ (row & 15)) << 3); }
+// per-wave 32x64 bf16 scratch of the expand: rows of eight 16-byte chunks, chunk XOR (row & 7)
+__device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 
-template <int R16>
-__global__ __launch_bounds__(256) void sgmm_shrink_bf16(SgmmArgs a) {
+// One work item = (problem, K slice, tile), the tile fastest so the work items
+// that share a slice of A run next to each other on one XCD.  The four waves
+// first read the tile's 32 x rows of the slice, row-contiguous (each x byte is
+// read once), into LDS.  The N blocks (32 columns of (expert, rank) each) are
+// then spread over the waves: with four or more blocks each wave takes whole
+// blocks; with fewer, the waves of one block split the slice's 16 chunks and
+// their sums are added in a fixed order.  The A rows of a block stream from
+// L2 four chunks ahead of the MFMAs.  Each row's two slots get the slice's
+// partial v; the expand adds the slices up.  Loads are never guarded: a
+// padding row or (expert, rank) column reads an in-bounds dummy row whose
+// products reach only accumulator entries that are never stored, and k past
+// d_in reads a clamped address whose value is replaced by zero.
+template <int R16, bool PK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     constexpr int RPAD = R16 * 16;
     const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
     if (gld(hdr + SG_ERR)) return;
-    const int tile = blockIdx.x;
+    const int64_t bid = blockIdx.x;
+    const int64_t t = (bid & 7) * per_xcd + (bid >> 3);
+    if (t >= n_units) return;
+    const int64_t nt = a.L.tiles_max;
+    const int64_t gks = t / nt;  // slice index over all problems
+    const int tile = (int)(t - gks * nt);
     if (tile >= gld(hdr + SG_NTILES)) return;
-    const int prob = blockIdx.y;
+    const int prob = a.descs ? find_prob_ks(a.descs, a.n_prob, gks) : 0;
     const SgDesc D = a.descs ? a.descs[prob] : a.single;
+    const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
     const uint32_t* tmask = (const uint32_t*)(a.ws + a.L.tmask);
-    float* v = (float*)(a.ws + a.L.v) + (int64_t)prob * a.L.T_pad * 2 * RPAD;
+    float* v = (float*)(a.ws + a.L.v) + gks * a.L.T_pad * 2 * RPAD;
 
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[32 * kSgmmKSlice];
     __shared__ int s_U[32];
     __shared__ int s_nU;
     __shared__ int s_row[32], s_e0[32], s_e1[32];
-    __shared__ float s_red[3][kWave][16];
     const int tid = threadIdx.x;
     if (tid < 32) {
         const int row = gld(perm + tile * 32 + tid);
@@ -217,84 +250,155 @@ __global__ __launch_bounds__(256) void sgmm_shrink_bf16(SgmmArgs a) {
     if (tid == 0) s_nU = mask_list(gld(tmask + tile), s_U);
     __syncthreads();
 
-    const int nU = s_nU;
-    const int NB = (nU * RPAD + 31) / 32;
-    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
-    const int d_in = D.d_in, r = a.r;
+    const int d_in = uniform(D.d_in), r = a.r;
     const uint16_t* __restrict__ x = (const uint16_t*)D.x;
-    const uint16_t* __restrict__ A = (const uint16_t*)D.A;
-    const int xrow = s_row[n];
-    const uint16_t* xr = xrow >= 0 ? x + (int64_t)xrow * d_in : nullptr;
-    const int n_kc = (d_in + 63) / 64;
+    const uint16_t* __restrict__ A = (const uint16_t*)(PK ? D.Ap : D.A);
 
-    for (int g0 = 0; g0 < NB; g0 += kNBG) {
-        const int nbg = NB - g0 < kNBG ? NB - g0 : kNBG;
-        // lane's column of each N block: (expert U[u], rank rho)
-        const uint16_t* arow[kNBG];
+    // 1) x slice: thread tid reads chunk tid % kXC of rows tid / kXC + 2j
+    constexpr int kXR = 256 / kXC;           // rows per load instruction
+    constexpr int kXL = 32 / kXR;            // load instructions per thread
+    const int xc = tid % kXC, xr0 = tid / kXC;
+    const int xk = k0 + 8 * xc;
+    const bool xok = xk < d_in;
+    u32x4 xv[kXL];
 #pragma unroll
-        for (int j = 0; j < kNBG; ++j) {
-            const int nn = (g0 + j) * 32 + n;
-            const int u = nn / RPAD, rho = nn % RPAD;
-            arow[j] = (j < nbg && u < nU && rho < r) ? A + ((int64_t)s_U[u] * r + rho) * d_in : nullptr;
+    for (int j = 0; j < kXL; ++j) {
+        const int rr = s_row[xr0 + kXR * j];
+        xv[j] = ld128(x + (int64_t)(rr >= 0 ? rr : 0) * d_in + (xok ? xk : 0));
+    }
+
+    const int nU = uniform(s_nU);
+    const int NB = (nU * RPAD + 31) / 32;
+    const int G = NB < 4 ? NB : 4;  // blocks in flight
+    const int P = 4 / G;            // waves per block (1 when G == 3)
+    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
+    const int gw = w % G, kp = w / G;
+    const int nmy = kKC / P;        // chunks per wave: chunk kp + P i
+
+    // MFMA step s2 of chunk kc takes, in half-wave h, the 8-wide k group
+    // kq = (k0 + 64 kc) / 8 + 2 s2 + h: the two halves read adjacent groups, so
+    // in the packed A layout one load covers contiguous runs of 32 bytes x rank.
+    const int nq = d_in / 8;
+    const int64_t qstride = PK ? 8 * r : 8;  // elements from group kq to kq + 1
+    auto load_a = [&](u32x4 (&dst)[4], const uint16_t* abase, int kc) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int kq = k0 / 8 + 8 * kc + 2 * s2 + h;
+            const u32x4 val = ld128(abase + (kq < nq ? kq : nq - 1) * qstride);
+            dst[s2] = kq < nq ? val : u32x4{0u, 0u, 0u, 0u};
         }
-        f32x16 acc[kNBG];
+    };
+    // first element of this lane's (expert, rank) row in A (row start) or in
+    // the packed A (its 8 values of group 0)
+    auto a_row = [&](int blk, int& u, int& rho) {
+        const int nn = blk * 32 + n;
+        u = nn / RPAD;
+        rho = nn % RPAD;
+        const bool ok = u < nU && rho < r;
+        const int64_t e = ok ? s_U[u] : 0, rr = ok ? rho : 0;
+        return PK ? A + e * r * d_in + rr * 8 : A + (e * r + rr) * d_in;
+    };
+    auto mma = [&](const u32x4 (&ab)[4], int kc, f32x16& acc) {
 #pragma unroll
-        for (int j = 0; j < kNBG; ++j) acc[j] = f32x16{};
-        // K: 64-wide chunks, wave w takes chunks w, w+4, ...; inside a chunk the
-        // half-wave h covers k in [32h, 32h+32) as four 8-wide MFMA k-steps, so
-        // each lane reads 64 contiguous bytes of x and of each A row.
-        for (int kc = w; kc < n_kc; kc += 4) {
-            const int k0 = kc * 64 + 32 * h;
-            u32x4 xo[4];
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const u32x4 xo = *(const u32x4*)(s_x + x_off(n, 8 * kc + 2 * s2 + h));
+            acc = mfma32(xo, ab[s2], acc);
+        }
+    };
+    auto store_v = [&](const f32x16& acc, int u, int rho) {
+        if (u >= nU || rho >= r) return;
+        const int e = s_U[u];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int col = k0 + 8 * s;
-                xo[s] = (xr && col < d_in) ? ld128(xr + col) : u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int m = 8 * (i >> 2) + 4 * h + (i & 3);
+            if (s_row[m] < 0) continue;
+            float* vp = v + ((int64_t)(tile * 32 + m) * 2) * RPAD + rho;
+            if (s_e0[m] == e) gst(vp, acc[i]);
+            if (s_e1[m] == e) gst(vp + RPAD, acc[i]);
+        }
+    };
+
+    // first block's A: the first four chunks are in flight while x lands in LDS
+    u32x4 ab[4][4];
+    int u, rho;
+    const uint16_t* arow = a_row(gw, u, rho);
+    const bool act = kp < P;
 #pragma unroll
-            for (int j = 0; j < kNBG; ++j) {
-                if (j >= nbg) break;
+    for (int j = 0; j < 4; ++j)
+        if (act) load_a(ab[j], arow, kp + P * j);
+
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int col = k0 + 8 * s;
-                    const u32x4 ao = (arow[j] && col < d_in) ? ld128(arow[j] + col) : u32x4{0u, 0u, 0u, 0u};
-                    acc[j] = mfma32(xo[s], ao, acc[j]);
-                }
+    for (int j = 0; j < kXL; ++j) {
+        const u32x4 val = xok ? xv[j] : u32x4{0u, 0u, 0u, 0u};
+        *(u32x4*)(s_x + x_off(xr0 + kXR * j, xc)) = val;
+    }
+    __syncthreads();
+
+    // K loop of one block over this wave's chunks, A four chunks ahead
+    auto run_block = [&](f32x16& acc) {
+#pragma unroll 1
+        for (int i = 0; i < nmy; i += 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mma(ab[j], kp + P * (i + j), acc);
+                if (i + 4 < nmy) load_a(ab[j], arow, kp + P * (i + 4 + j));
             }
         }
-        // fixed-order sum of the four waves' partial products, one block at a time
+    };
+
+    if (P == 1) {
+        if (!act) return;
+        for (int blk = gw; blk < NB; blk += G) {
+            if (blk != gw) {
+                arow = a_row(blk, u, rho);
 #pragma unroll
-        for (int j = 0; j < kNBG; ++j) {
-            if (j >= nbg) break;
-            if (w > 0) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s_red[w - 1][lane][i] = acc[j][i];
+                for (int j = 0; j < 4; ++j) load_a(ab[j], arow, j);
             }
-            __syncthreads();
-            if (w == 0) {
-                const int nn = (g0 + j) * 32 + n;
-                const int u = nn / RPAD, rho = nn % RPAD;
-                if (u < nU && rho < r) {
-                    const int e = s_U[u];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float val = ((acc[j][i] + s_red[0][lane][i]) + s_red[1][lane][i]) + s_red[2][lane][i];
-                        const int m = 8 * (i >> 2) + 4 * h + (i & 3);
-                        if (s_row[m] < 0) continue;
-                        float* vp = v + ((int64_t)(tile * 32 + m) * 2) * RPAD + rho;
-                        if (s_e0[m] == e) gst(vp, val);
-                        if (s_e1[m] == e) gst(vp + RPAD, val);
-                    }
-                }
-            }
-            __syncthreads();
+            f32x16 acc = f32x16{};
+            run_block(acc);
+            store_v(acc, u, rho);
         }
+        return;
+    }
+    // one block per group of P waves: parts 1..P-1 go through LDS (the x
+    // slice is no longer read) and the part-0 wave adds them in order
+    f32x16 acc = f32x16{};
+    run_block(acc);
+    __syncthreads();
+    f32x4* red = (f32x4*)s_x;  // [wave][4][lane]
+    if (kp > 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            red[(w * 4 + q) * kWave + lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    }
+    __syncthreads();
+    if (kp == 0) {
+        for (int p = 1; p < P; ++p) {
+            const int wp = gw + p * G;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 o = red[(wp * 4 + q) * kWave + lane];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[4 * q + c] += o[c];
+            }
+        }
+        store_v(acc, u, rho);
     }
 }
 
 // ---- expand (bf16, MFMA) -----------------------------------------------------
 
 __device__ __forceinline__ int perm_col(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+// Columns of one expand work item: 4 waves x kEB blocks x 64 columns.
+constexpr int kEB = 4;
+constexpr int kECols = 4 * kEB * 64;
+static_assert(kECols == kSgmmExpandCols, "expand column group");
+// The row-side MFMA operands (u = s*g*v as hi + lo bf16, per (expert, 16-rank
+// chunk) pair q and lane) are the same for the four waves of a work item: they
+// are built once into LDS when the tile's union has at most kQLds pairs; larger
+// unions rebuild them per column block in registers.
+constexpr int kQLds = 16;
 
 template <int R16>
 __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_xcd) {
@@ -304,30 +408,51 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     const int64_t bid = blockIdx.x;
     const int64_t t = (bid & 7) * per_xcd + (bid >> 3);
     if (t >= a.n_expand_units) return;
-    // work item = (tile, problem, 256-column block), tile-major
-    const int tile = (int)(t / a.total_cb);
-    if (tile >= gld(hdr + SG_NTILES)) return;
-    const int64_t rem = t - (int64_t)tile * a.total_cb;
-    const int prob = a.descs ? find_prob(a.descs, a.n_prob, rem) : 0;
+    // work item = (problem, kECols-column group, tile) with the tile fastest:
+    // neighbouring work items (same XCD) reuse the same B column slices
+    const int64_t nt = a.L.tiles_max;
+    const int prob = a.descs ? find_prob_cb(a.descs, a.n_prob, t / nt) : 0;
     const SgDesc D = a.descs ? a.descs[prob] : a.single;
-    const int cb = (int)(rem - D.unit0);
+    const int64_t local = t - D.unit0 * nt;
+    const int cg = (int)(local / nt);
+    const int tile = (int)(local - (int64_t)cg * nt);
+    if (tile >= gld(hdr + SG_NTILES)) return;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
     const uint32_t* tmask = (const uint32_t*)(a.ws + a.L.tmask);
-    const float* v = (const float*)(a.ws + a.L.v) + (int64_t)prob * a.L.T_pad * 2 * RPAD;
+    const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * a.L.T_pad * 2 * RPAD;
 
     __shared__ int s_U[32];
     __shared__ int s_nU;
+    __shared__ __attribute__((aligned(16))) uint16_t s_y[4][32 * 64];
+    __shared__ __attribute__((aligned(16))) u32x4 s_u[kQLds][2][kWave];
     const int tid = threadIdx.x;
     if (tid == 0) s_nU = mask_list(gld(tmask + tile), s_U);
     __syncthreads();
 
     const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
-    const int d_out = D.d_out, r = a.r;
-    const int cw = cb * 256 + w * 64;  // this wave's 64 output columns
-    if (cw >= d_out) return;
-    const int nU = s_nU;
+    const int d_out = uniform(D.d_out), r = a.r;
+    const int cw = cg * kECols + w * (kEB * 64);  // this wave's first column
+    const int nblk = cw >= d_out ? 0 : ((d_out - cw + 63) / 64 < kEB ? (d_out - cw + 63) / 64 : kEB);
+    const int nU = uniform(s_nU);
     const uint16_t* __restrict__ B = (const uint16_t*)D.B;
     uint16_t* __restrict__ y = (uint16_t*)D.y;
+    uint16_t* ys = s_y[w];
+    const int lr = lane >> 3, lc = lane & 7;
+
+    // rows of the tile, row-major lane map (instruction i: row 8i + lr, chunk lc)
+    int yrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yrow[i] = gld(perm + tile * 32 + 8 * i + lr);
+    auto load_y = [&](u32x4 (&yv)[4], int blk) {
+        const int col = cw + blk * 64 + 8 * lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = yrow[i] >= 0 && col < d_out;
+            yv[i] = ld128(y + (ok ? (int64_t)yrow[i] * d_out + col : 0));
+        }
+    };
+    u32x4 ycur[4], ynxt[4];
+    if (nblk > 0) load_y(ycur, 0);
 
     // this lane's row (MFMA N index = tile row n) and its two slots
     const int row = gld(perm + tile * 32 + n);
@@ -341,82 +466,126 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     }
     const float* v0 = v + ((int64_t)(tile * 32 + n) * 2) * RPAD;
     const float* v1 = v0 + RPAD;
-
-    // the lane's two output-column rows of B for each 32-column block
-    int ocol[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) ocol[b] = cw + 32 * b + perm_col(n);
-
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
-    for (int u = 0; u < nU; ++u) {
-        const int e = s_U[u];
+    // row-side operand of (expert U[q / R16], ranks 16(q % R16) + 8h + [0,8)):
+    // u = s*g*v as hi + lo bf16 (v = the K slices' sum, kept in slice 0).  v of a slot that is not this expert, or of a
+    // padding rank, is never written: it is selected away, not multiplied by 0.
+    auto make_u = [&](int q, u32x4& bhi, u32x4& blo) {
+        const int e = s_U[q / R16];
+        const int rho0 = (q % R16) * 16 + 8 * h;
         const bool m0 = (e0 == e), m1 = (e1 == e);
+        const u32x4 p0 = ld128(v0 + rho0), p1 = ld128(v0 + rho0 + 4);
+        const u32x4 q0 = ld128(v1 + rho0), q1 = ld128(v1 + rho0 + 4);
+        float va[8], vb[8];
 #pragma unroll
-        for (int rc = 0; rc < R16; ++rc) {
-            const int rho0 = rc * 16 + 8 * h;
-            // u = s*g*v for this row, expert e, ranks rho0..rho0+7, as hi + lo bf16
-            // ranks beyond r are padding: v there was never written, keep u at 0
-            float uv[8];
+        for (int c = 0; c < 4; ++c) {
+            va[c] = __uint_as_float(p0[c]);
+            va[c + 4] = __uint_as_float(p1[c]);
+            vb[c] = __uint_as_float(q0[c]);
+            vb[c + 4] = __uint_as_float(q1[c]);
+        }
+        uint32_t hw[4], lw[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) uv[j] = 0.f;
-            if (m0) {
-                const u32x4 p0 = ld128(v0 + rho0), p1 = ld128(v0 + rho0 + 4);
+        for (int j = 0; j < 4; ++j) {
+            float uv[2];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (rho0 + j < r) uv[j] = c0 * __uint_as_float(j < 4 ? p0[j] : p1[j - 4]);
+            for (int k = 0; k < 2; ++k) {
+                const int jj = 2 * j + k;
+                const bool okr = rho0 + jj < r;
+                const float a0 = (m0 && okr) ? va[jj] : 0.f;
+                const float a1 = (m1 && okr) ? vb[jj] : 0.f;
+                uv[k] = fmaf(c1, a1, c0 * a0);
             }
-            if (m1) {
-                const u32x4 p0 = ld128(v1 + rho0), p1 = ld128(v1 + rho0 + 4);
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (rho0 + j < r) uv[j] = fmaf(c1, __uint_as_float(j < 4 ? p0[j] : p1[j - 4]), uv[j]);
-            }
-            uint32_t hw[4], lw[4];
+            hw[j] = pack2_bf16(uv[0], uv[1]);
+            lw[j] = pack2_bf16(uv[0] - bf_lo(hw[j]), uv[1] - bf_hi(hw[j]));
+        }
+        bhi = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        blo = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    };
+    // column-side operand: B[e][col][16(q % R16) + 8h .. +8]; padding columns
+    // read column 0 and are never stored
+    const bool r_vec = (r & 7) == 0;
+    auto load_bop = [&](int q, int col) {
+        const int e = s_U[q / R16];
+        const int rho0 = (q % R16) * 16 + 8 * h;
+        const uint16_t* bp = B + ((int64_t)e * d_out + (col < d_out ? col : 0)) * r + rho0;
+        u32x4 ao = {0u, 0u, 0u, 0u};
+        if (r_vec) {
+            if (rho0 < r) ao = ld128(bp);
+        } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float a0 = uv[2 * j], a1 = uv[2 * j + 1];
-                hw[j] = pack2_bf16(a0, a1);
-                lw[j] = pack2_bf16(a0 - bf_lo(hw[j]), a1 - bf_hi(hw[j]));
-            }
-            const u32x4 bhi = {hw[0], hw[1], hw[2], hw[3]};
-            const u32x4 blo = {lw[0], lw[1], lw[2], lw[3]};
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                u32x4 ao = {0u, 0u, 0u, 0u};
-                if (ocol[b] < d_out && rho0 < r) {
-                    const uint16_t* bp = B + ((int64_t)e * d_out + ocol[b]) * r + rho0;
-                    if ((r & 7) == 0) {
-                        ao = ld128(bp);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t lo = (rho0 + 2 * j < r) ? gld(bp + 2 * j) : 0u;
-                            const uint32_t hi = (rho0 + 2 * j + 1 < r) ? gld(bp + 2 * j + 1) : 0u;
-                            ao[j] = lo | (hi << 16);
-                        }
-                    }
-                }
-                acc[b] = mfma32(ao, bhi, acc[b]);
-                acc[b] = mfma32(ao, blo, acc[b]);
+                const uint32_t lo = (rho0 + 2 * j < r) ? gld(bp + 2 * j) : 0u;
+                const uint32_t hi = (rho0 + 2 * j + 1 < r) ? gld(bp + 2 * j + 1) : 0u;
+                ao[j] = lo | (hi << 16);
             }
         }
+        return ao;
+    };
+
+    const int nq = nU * R16;
+    const bool shared_u = nq <= kQLds;
+    if (shared_u) {
+        for (int q = w; q < nq; q += 4) make_u(q, s_u[q][0][lane], s_u[q][1][lane]);
     }
-    if (row < 0) return;
-    uint16_t* yr = y + (int64_t)row * d_out;
+    __syncthreads();
+    if (nblk == 0) return;
+
+#pragma unroll 1
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk + 1 < nblk) load_y(ynxt, blk + 1);
+        const int c0b = cw + blk * 64;
+        int ocol[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < 2; ++b) ocol[b] = c0b + 32 * b + perm_col(n);
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
+        if (shared_u) {
+            for (int q = 0; q < nq; ++q) {
+                const u32x4 uh = s_u[q][0][lane], ul = s_u[q][1][lane];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int col = cw + 32 * b + 16 * h + 8 * q;
-            if (col >= d_out) continue;
-            const u32x4 yv = ld128(yr + col);
-            uint32_t ow[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int i = 8 * q + 2 * p;
-                ow[p] = pack2_bf16(bf_lo(yv[p]) + acc[b][i], bf_hi(yv[p]) + acc[b][i + 1]);
+                for (int b = 0; b < 2; ++b) {
+                    const u32x4 ao = load_bop(q, ocol[b]);
+                    acc[b] = mfma32(ao, uh, acc[b]);
+                    acc[b] = mfma32(ao, ul, acc[b]);
+                }
             }
-            st128(yr + col, u32x4{ow[0], ow[1], ow[2], ow[3]});
+        } else {
+            for (int q = 0; q < nq; ++q) {
+                u32x4 bh, bl;
+                make_u(q, bh, bl);
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const u32x4 ao = load_bop(q, ocol[b]);
+                    acc[b] = mfma32(ao, bh, acc[b]);
+                    acc[b] = mfma32(ao, bl, acc[b]);
+                }
+            }
+        }
+        // y: row-major registers -> scratch -> MFMA layout (row n, columns
+        // 32b + 16h + [0,16)); add, round once; back through the scratch -> global
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4*)(ys + y_off(8 * i + lr, lc)) = ycur[i];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const u32x4 ym = *(const u32x4*)(ys + y_off(n, 4 * b + 2 * h + q));
+                uint32_t ow[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int i = 8 * q + 2 * p;
+                    ow[p] = pack2_bf16(bf_lo(ym[p]) + acc[b][i], bf_hi(ym[p]) + acc[b][i + 1]);
+                }
+                *(u32x4*)(ys + y_off(n, 4 * b + 2 * h + q)) = u32x4{ow[0], ow[1], ow[2], ow[3]};
+            }
+        const int col = c0b + 8 * lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 o = *(const u32x4*)(ys + y_off(8 * i + lr, lc));
+            if (yrow[i] >= 0 && col < d_out) st128(y + (int64_t)yrow[i] * d_out + col, o);
+        }
+        if (blk + 1 < nblk) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ycur[i] = ynxt[i];
         }
     }
 }
@@ -449,7 +618,7 @@ __global__ __launch_bounds__(256) void sgmm_shrink_generic(SgmmArgs a) {
         const T* A = (const T*)D.A + ((int64_t)e * a.r + rho) * D.d_in;
         for (int j = 0; j < D.d_in; ++j) acc = fmaf(ldf(x, j), ldf(A, j), acc);
     }
-    float* v = (float*)(a.ws + a.L.v) + (int64_t)prob * a.L.T_pad * 2 * RPAD;
+    float* v = (float*)(a.ws + a.L.v) + D.ks0 * a.L.T_pad * 2 * RPAD;
     v[(pos * 2 + slot) * RPAD + rho] = acc;
 }
 
@@ -467,7 +636,7 @@ __global__ __launch_bounds__(256) void sgmm_expand_generic(SgmmArgs a) {
     const int64_t pos = q / D.d_out;
     const int o = (int)(q % D.d_out);
     const int row = ((const int32_t*)(a.ws + a.L.perm))[pos];
-    const float* v = (const float*)(a.ws + a.L.v) + (int64_t)prob * a.L.T_pad * 2 * RPAD;
+    const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * a.L.T_pad * 2 * RPAD;
     const T* B = (const T*)D.B;
     float part[2];
 #pragma unroll
@@ -484,12 +653,73 @@ __global__ __launch_bounds__(256) void sgmm_expand_generic(SgmmArgs a) {
     stf(y, i, ldf(y, i) + (part[0] + part[1]));
 }
 
+// ---- K-slice sum ---------------------------------------------------------------
+
+// v of every problem with several K slices: slice 0 <- slice 0 + slice 1 + ...,
+// added in slice order (the sum is the same on every run).  One thread per
+// four floats of the rows in use.
+__global__ __launch_bounds__(256) void sgmm_vsum_kernel(SgmmArgs a) {
+    const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
+    if (gld(hdr + SG_ERR)) return;
+    const int prob = blockIdx.y;
+    const SgDesc D = a.descs ? a.descs[prob] : a.single;
+    const int nks = D.n_ks;
+    if (nks <= 1) return;
+    const int64_t n4 = (int64_t)gld(hdr + SG_NPOS) * 2 * a.L.r_pad / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const int64_t stride = a.L.T_pad * 2 * a.L.r_pad;  // floats per slice
+    float* v = (float*)(a.ws + a.L.v) + D.ks0 * stride + 4 * i;
+    u32x4 acc = ld128(v);
+    int ks = 1;
+    for (; ks + 4 <= nks; ks += 4) {
+        u32x4 p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = ld128(v + (ks + j) * stride);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                acc[c] = __float_as_uint(__uint_as_float(acc[c]) + __uint_as_float(p[j][c]));
+    }
+    for (; ks < nks; ++ks) {
+        const u32x4 p = ld128(v + ks * stride);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = __float_as_uint(__uint_as_float(acc[c]) + __uint_as_float(p[c]));
+    }
+    st128(v, acc);
+}
+
+// ---- A packing -------------------------------------------------------------------
+
+// One thread per 16-byte group: Ap[e][kq][rho] = A[e][rho][8kq .. 8kq+8).
+__global__ __launch_bounds__(256) void sgmm_pack_a_kernel(const uint16_t* __restrict__ A,
+                                                          uint16_t* __restrict__ Ap, int r,
+                                                          int64_t nq, int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int64_t rho = i % r, kq = (i / r) % nq, e = i / (r * nq);
+    st128(Ap + 8 * i, ld128(A + ((e * r + rho) * nq + kq) * 8));
+}
+
 template <int R16>
 hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((sgmm_shrink_bf16<R16>), dim3((unsigned)a.L.tiles_max, (unsigned)a.n_prob),
-                       dim3(256), 0, s, a);
+    const int64_t n_units = a.total_ks * a.L.tiles_max;
+    const int64_t sh_per_xcd = (n_units + 7) / 8;
+    if (a.packed)
+        hipLaunchKernelGGL((sgmm_shrink_bf16<R16, true>), dim3((unsigned)(8 * sh_per_xcd)), dim3(256), 0, s,
+                           a, n_units, sh_per_xcd);
+    else
+        hipLaunchKernelGGL((sgmm_shrink_bf16<R16, false>), dim3((unsigned)(8 * sh_per_xcd)), dim3(256), 0, s,
+                           a, n_units, sh_per_xcd);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.total_ks > a.n_prob) {  // some problem has more than one K slice
+        const dim3 gs((unsigned)((a.L.T_pad * 2 * a.L.r_pad / 4 + 255) / 256), (unsigned)a.n_prob);
+        hipLaunchKernelGGL(sgmm_vsum_kernel, gs, dim3(256), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int64_t per_xcd = (a.n_expand_units + 7) / 8;
     hipLaunchKernelGGL((sgmm_expand_bf16<R16>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, a,
                        per_xcd);
@@ -497,6 +727,13 @@ hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_sgmm_pack_a(const void* A, void* Ap, int E, int r, int64_t d_in, hipStream_t s) {
+    const int64_t nq = d_in / 8, total = (int64_t)E * r * nq;
+    hipLaunchKernelGGL(sgmm_pack_a_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)A, (uint16_t*)Ap, r, nq, total);
+    return hipGetLastError();
+}
 
 hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
     hipLaunchKernelGGL(sgmm_segment_kernel, dim3(1), dim3(kSegThreads), 0, s, a.idx, a.g, a.T, a.E,

@@ -155,13 +155,14 @@ int dlm_layers_status(dlm_layers* h, int32_t* code, void* stream);
 /* ------------------------------------------------------------------- SGMM */
 
 /*
- * Workspace bytes dlm_sgmm / dlm_sgmm_grouped need for T rows, E experts,
- * rank r and n_problems problems sharing one set of rows (row segmentation,
- * per-problem shrink results v [T][2][r] fp32, device status word).
- * *bytes is host memory.
+ * Workspace bytes dlm_sgmm / dlm_sgmm_group_run need for T rows, problems with
+ * d_in up to d_in_max, E experts, rank r and n_problems problems sharing one
+ * set of rows: row segmentation, the shrink's per-K-slice partial results
+ * (fp32, [n_problems][ceil(d_in_max / 1024)][T][2][r]) and the device status
+ * word.  *bytes is host memory.
  */
-int dlm_sgmm_workspace_size(int64_t T, int32_t E, int32_t r, int32_t n_problems,
-                            size_t* bytes);
+int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r,
+                            int32_t n_problems, size_t* bytes);
 
 /*
  * Batched unmerged adapters for rows with different expert sets:
@@ -169,16 +170,18 @@ int dlm_sgmm_workspace_size(int64_t T, int32_t E, int32_t r, int32_t n_problems,
  *   x [T][d_in], y [T][d_out] (in place, must not overlap x),
  *   idx [T][2] int32 (-1 = empty slot), g [T][2] fp32,
  *   A [E][r][d_in], B [E][d_out][r].
- * Three launches: segment (rows sorted by their unordered expert pair,
- * 32-row tiles, the experts each tile uses), shrink (v = x A^T on the tile's
- * experts, bf16 MFMA, fp32 result kept in the workspace) and expand
- * (y += (s g v) B^T, MFMA with v*s*g split into two bf16 terms, fp32 accumulate,
- * one bf16 rounding of y).  Rows whose two slots are empty are not touched.
+ * Launches: segment (rows sorted by their unordered expert pair, 32-row
+ * tiles, the experts each tile uses), shrink (v = x A^T on the tile's experts
+ * over 1024-wide K slices, bf16 MFMA, fp32 partial results kept in the
+ * workspace), a K-slice sum in a fixed order (only when d_in > 1024) and
+ * expand (y += (s g v) B^T, MFMA with v*s*g split into two bf16 terms, fp32
+ * accumulate, one bf16 rounding of y).  Results are bitwise reproducible run to run.
+ * Rows whose two slots are empty are not touched.
  * A row with an index outside [-1, E) or a non-finite gate on a used slot makes
  * the whole call a no-op on y and sets the workspace status word (read it with
  * dlm_sgmm_status).
  * bf16: x, y, A, B 16-byte aligned; d_in and d_out multiples of 8.
- * workspace: >= dlm_sgmm_workspace_size(T, E, r, 1) bytes, 256-byte aligned.
+ * workspace: >= dlm_sgmm_workspace_size(T, d_in, E, r, 1) bytes, 256-byte aligned.
  */
 int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A,
              const void* B, void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E,
@@ -201,16 +204,28 @@ typedef struct dlm_sgmm_group dlm_sgmm_group;
  * Register n problems (e.g. every adapted projection of every layer) that are
  * run together on the same rows' expert sets: the decide-once routing means
  * one segmentation serves all of them.  Copies the descriptors (host) to a
- * small device table; buffers stay owned by the caller.
+ * small device table; x, B and y stay owned by the caller and are used in place.
+ * bf16: the handle also keeps a packed copy of every distinct A bank
+ * (Ap[e][k/8][rho][8] = A[e][rho][k..k+8), the same size as A, allocated and
+ * filled here; the device is synchronised before returning), so that the shrink
+ * reads A in contiguous runs.  The copy is taken at create time: after
+ * changing an A bank in place call dlm_sgmm_group_repack.
  */
 int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, int32_t r,
                           float scale, int32_t dtype, dlm_sgmm_group** out);
 int dlm_sgmm_group_destroy(dlm_sgmm_group* h);
 
 /*
+ * Refresh the handle's packed A copies from the caller's A banks: one launch
+ * per distinct bank on `stream`, no allocation (no-op for fp32 groups).
+ */
+int dlm_sgmm_group_repack(dlm_sgmm_group* h, void* stream);
+
+/*
  * Run every problem of the group for T rows: one segment launch shared by all
- * problems, then one shrink and one expand launch covering all problems.
- * workspace: >= dlm_sgmm_workspace_size(T, E, r, n_problems) bytes.
+ * problems, then one shrink, one K-slice sum (only when some d_in > 1024) and
+ * one expand launch covering all problems.
+ * workspace: >= dlm_sgmm_workspace_size(T, max d_in, E, r, n_problems) bytes.
  */
 int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, int64_t T,
                        void* workspace, size_t ws_bytes, void* stream);

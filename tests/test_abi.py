@@ -96,24 +96,29 @@ def test_switch_and_status_validation(lib):
 
 def test_sgmm_workspace_size(lib):
     b = C.c_size_t(0)
-    assert lib.dlm_sgmm_workspace_size(4096, 8, 16, 7, C.byref(b)) == dlm.DLM_OK
-    # the per-problem shrink results dominate: 7 problems x 4096 rows x 2 slots x 16 x 4 bytes
-    assert b.value >= 7 * 4096 * 2 * 16 * 4
+    assert lib.dlm_sgmm_workspace_size(4096, 11008, 8, 16, 7, C.byref(b)) == dlm.DLM_OK
+    # the shrink's partial results dominate: 7 problems x 11 K slices of 1024 x
+    # 4096 rows x 2 slots x 16 x 4 bytes
+    assert b.value >= 7 * 11 * 4096 * 2 * 16 * 4
     assert b.value % 256 == 0
+    one = C.c_size_t(0)
+    assert lib.dlm_sgmm_workspace_size(4096, 1024, 8, 16, 7, C.byref(one)) == dlm.DLM_OK
+    assert one.value < b.value
     small = C.c_size_t(0)
-    assert lib.dlm_sgmm_workspace_size(64, 8, 16, 1, C.byref(small)) == dlm.DLM_OK
-    assert small.value < b.value
-    assert lib.dlm_sgmm_workspace_size(-1, 8, 16, 1, C.byref(b)) == dlm.DLM_ESHAPE
-    assert lib.dlm_sgmm_workspace_size(64, 0, 16, 1, C.byref(b)) == dlm.DLM_ESHAPE
-    assert lib.dlm_sgmm_workspace_size(64, 8, 0, 1, C.byref(b)) == dlm.DLM_ESHAPE
-    assert lib.dlm_sgmm_workspace_size(64, 8, 16, 0, C.byref(b)) == dlm.DLM_EINVAL
-    assert lib.dlm_sgmm_workspace_size(64, 8, 16, 1, None) == dlm.DLM_EINVAL
+    assert lib.dlm_sgmm_workspace_size(64, 1024, 8, 16, 1, C.byref(small)) == dlm.DLM_OK
+    assert small.value < one.value
+    assert lib.dlm_sgmm_workspace_size(-1, 64, 8, 16, 1, C.byref(b)) == dlm.DLM_ESHAPE
+    assert lib.dlm_sgmm_workspace_size(64, 0, 8, 16, 1, C.byref(b)) == dlm.DLM_ESHAPE
+    assert lib.dlm_sgmm_workspace_size(64, 64, 0, 16, 1, C.byref(b)) == dlm.DLM_ESHAPE
+    assert lib.dlm_sgmm_workspace_size(64, 64, 8, 0, 1, C.byref(b)) == dlm.DLM_ESHAPE
+    assert lib.dlm_sgmm_workspace_size(64, 64, 8, 16, 0, C.byref(b)) == dlm.DLM_EINVAL
+    assert lib.dlm_sgmm_workspace_size(64, 64, 8, 16, 1, None) == dlm.DLM_EINVAL
 
 
 def test_sgmm_validation(lib):
     P = C.c_void_p
     ws = C.c_size_t(0)
-    lib.dlm_sgmm_workspace_size(16, 4, 16, 1, C.byref(ws))
+    lib.dlm_sgmm_workspace_size(16, 64, 4, 16, 1, C.byref(ws))
     X, Y = FAKE, FAKE + (1 << 20)
 
     def call(x=X, idx=FAKE, g=FAKE, A=FAKE, B=FAKE, y=Y, T=16, d_in=64, d_out=64, E=4, r=16,

@@ -62,6 +62,10 @@ CASES = [
     (40, 64, 64, 32, 16, 1.0, torch.bfloat16),       # most experts
     (20, 64, 96, 4, 128, 0.5, torch.bfloat16),       # largest rank
     (300, 256, 264, 8, 16, 1.0, torch.bfloat16),
+    (40, 2056, 72, 8, 16, 1.0, torch.bfloat16),      # three K slices, the last 8 wide
+    (70, 1096, 136, 16, 64, 0.5, torch.bfloat16),    # two K slices, many N blocks per tile
+    (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # exactly one slice, largest rank
+    (9, 1500, 24, 4, 8, 1.0, torch.float32),         # fp32 past one slice width
 ]
 
 
@@ -73,7 +77,7 @@ def test_sgmm_parity(ci):
     idx, g = _sets(T, E, np.random.default_rng(ci))
     y0 = y.cpu().clone()
     idx_d, g_d = idx.cuda(), g.cuda()
-    ws = dlm.sgmm_workspace(T, E, r)
+    ws = dlm.sgmm_workspace(T, d_in, E, r)
     dlm.sgmm(x, idx_d, g_d, A, B, y, scale, ws)
     assert dlm.sgmm_status(ws) == dlm.DLM_OK
     st = _check(x, idx, g, A, B, y0, y, scale, f"sgmm case {ci}")
@@ -88,7 +92,7 @@ def test_sgmm_zero_gates_and_slot_swap():
     x, A, B, y = _problem(T, d_in, d_out, E, r, torch.bfloat16, 3100)
     idx, g = _sets(T, E, np.random.default_rng(5), 0, 0, 0)
     y0 = y.clone()
-    ws = dlm.sgmm_workspace(T, E, r)
+    ws = dlm.sgmm_workspace(T, d_in, E, r)
     dlm.sgmm(x, idx.cuda(), torch.zeros_like(g).cuda(), A, B, y, 1.0, ws)
     torch.cuda.synchronize()
     assert torch.equal(y, y0)
@@ -121,7 +125,7 @@ def test_sgmm_bad_set_is_a_noop_with_status():
     x, A, B, y = _problem(T, d_in, d_out, E, r, torch.bfloat16, 3102)
     y0 = y.clone()
     idx, g = _sets(T, E, np.random.default_rng(9), 0, 0, 0)
-    ws = dlm.sgmm_workspace(T, E, r)
+    ws = dlm.sgmm_workspace(T, d_in, E, r)
     for bad_i, bad_g in [((7, 0), 4), ((3, 1), -2), ((20, 0), None)]:
         ii, gg = idx.clone(), g.clone()
         if bad_g is None:
@@ -152,3 +156,27 @@ def test_sgmm_group_matches_single_calls():
         torch.cuda.synchronize()
         assert torch.equal(y1, y), k
         _check(x, idx, g, A, B, y0s[k].cpu(), y, 2.0, f"group problem {k}")
+
+
+def test_sgmm_group_shared_bank_and_repack():
+    """Two problems on one A bank (one packed copy), three K slices; after A is
+    changed in place, repack makes the next run use the new values."""
+    T, E, r = 70, 8, 16
+    x1, A, B1, y1 = _problem(T, 2056, 64, E, r, torch.bfloat16, 3300)
+    x2, _, B2, y2 = _problem(T, 2056, 136, E, r, torch.bfloat16, 3301)
+    idx, g = _sets(T, E, np.random.default_rng(12))
+    y10, y20 = y1.cpu().clone(), y2.cpu().clone()
+    grp = dlm.SgmmGroup([(x1, A, B1, y1), (x2, A, B2, y2)], E, r, 1.0)
+    grp.run(idx.cuda(), g.cuda())
+    torch.cuda.synchronize()
+    _check(x1, idx, g, A, B1, y10, y1, 1.0, "shared bank, problem 0")
+    _check(x2, idx, g, A, B2, y20, y2, 1.0, "shared bank, problem 1")
+    A.mul_(-0.5)  # exact in bf16
+    y1.copy_(y10)
+    y2.copy_(y20)
+    grp.repack()
+    grp.run(idx.cuda(), g.cuda())
+    torch.cuda.synchronize()
+    _check(x1, idx, g, A, B1, y10, y1, 1.0, "repacked, problem 0")
+    _check(x2, idx, g, A, B2, y20, y2, 1.0, "repacked, problem 1")
+    grp.close()
