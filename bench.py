@@ -141,7 +141,6 @@ def bench_sgmm(torch, dlm, synth, name, reps, log):
     sec = e0.elapsed_time(e1) / 1e3 / reps
     tokens = wl.T * len(sets)
     # algorithmic bytes: x once, y read + write, A/B of the experts used, idx/g
-    used = torch.zeros(wl.E, dtype=torch.bool)
     nbytes = 0
     for i, _ in sets:
         u = torch.unique(i.cpu())
@@ -151,7 +150,6 @@ def bench_sgmm(torch, dlm, synth, name, reps, log):
             d_in, d_out = x.shape[1], y.shape[1]
             per_step += wl.T * d_in * 2 + 2 * wl.T * d_out * 2 + len(u) * wl.r * (d_in + d_out) * 2
         nbytes += per_step + wl.T * 16
-        used[u.long()] = True
     res = {"tokens_per_s": tokens / sec, "ms_per_pass": sec * 1e3, "GBps": nbytes / sec / 1e9,
            "frac_of_hbm_peak": nbytes / sec / HBM_PEAK, "algo_bytes_per_pass": nbytes}
     grp.close()

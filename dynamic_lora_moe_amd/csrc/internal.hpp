@@ -60,15 +60,18 @@ struct SgDesc {
     void* y;
     int32_t d_in, d_out;
     int32_t n_cb;       // column groups of the expand (kSgmmExpandCols each)
-    int32_t n_ks;       // 1024-wide K slices of the shrink
+    int32_t n_ks;       // kSgmmKSlice-wide K slices of the shrink
     int64_t ks0;        // first K slice of this problem (prefix sum of n_ks)
     int64_t unit0;      // first column block of this problem (prefix sum of n_cb)
 };
 
 // Workspace sections (byte offsets, each 256-aligned).
 struct SgLayout {
-    size_t hdr, perm, rank, key, hist, tmask, v, total;
-    int64_t T, T_pad, n_chunks, n_keys, tiles_max;
+    // perm: row at each sorted position (-1 = padding); epk: its expert pair
+    // (slot 0 in the low 16 bits, slot 1 in the high, -1 = empty); gpk: its two
+    // gates; tmask: the experts each 32-row tile uses; v: the shrink's results
+    size_t hdr, perm, epk, gpk, tmask, v, total;
+    int64_t T, T_pad, tiles_max;
     int r_pad;
     int max_ks;  // K slices of the widest problem
 };

@@ -3,21 +3,23 @@
 // The AdaFuse digest (section 2-na) names its core kernel SGMM, "segmented
 // gather matrix multiplication"; this is the batched form of the same adapters.
 //
-// Three launches:
+// Launches:
 //   segment  (one workgroup) every row gets the key of its unordered expert
-//            pair; a stable counting sort lists the rows by key (perm), so
-//            rows sharing experts sit next to each other.  The sorted list is
-//            cut into 32-row tiles and each tile records the union of the
-//            experts its rows use (a bitmask).  Rows with two empty slots are
-//            left out.  The same segmentation serves every problem of a
-//            grouped call (one routing decision per token for all layers).
+//            pair; a stable counting sort lists the rows by key (perm, with
+//            each position's pair and gates beside it), so rows sharing
+//            experts sit next to each other.  The sorted list is cut into
+//            32-row tiles and each tile records the union of the experts its
+//            rows use (a bitmask).  Rows with two empty slots are left out.
+//            The same segmentation serves every problem of a grouped call
+//            (one routing decision per token for all layers).
 //   shrink   per (problem, 1024-wide K slice, tile): the slice's partial
 //            v = x_rows A_U^T for the tile's experts U, bf16 MFMA 32x32x16 with
 //            M = tile rows (gathered through perm, staged in LDS), N = (expert,
 //            rank); each row keeps the fp32 partial v of its own two slots.
-//   expand   per (problem, 1024 output columns, tile): v = the slices' sum
-//            in slice order, y_rows += u B_U^T with u = s*g*v per (row, expert,
-//            rank).  u stays fp32-accurate by
+//   sum      (problems with d_in > 1024) the slices' partials added in slice
+//            order.
+//   expand   per (problem, 1024 output columns, tile): y_rows += u B_U^T with
+//            u = s*g*v per (row, expert, rank).  u stays fp32-accurate by
 //            entering the MFMA as two bf16 terms (hi + lo); B slices are
 //            k-contiguous and load straight into operand registers; lane l
 //            ends with 16 consecutive outputs of one row (two 128-bit y
@@ -37,18 +39,15 @@ SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob) {
     SgLayout L;
     L.T = T;
     L.T_pad = ((T > 0 ? T : 1) + 31) / 32 * 32;
-    L.n_chunks = (T + 63) / 64;
-    if (L.n_chunks < 1) L.n_chunks = 1;
-    L.n_keys = (int64_t)(E + 1) * (E + 1);
     L.tiles_max = L.T_pad / 32;
     L.r_pad = (r + 15) / 16 * 16;
     L.max_ks = (int)((d_in_max + kSgmmKSlice - 1) / kSgmmKSlice);
+    (void)E;
     size_t o = 0;
     L.hdr = o;   o += 256;
     L.perm = o;  o += a256((size_t)L.T_pad * 4);
-    L.rank = o;  o += a256((size_t)(T > 0 ? T : 1) * 4);
-    L.key = o;   o += a256((size_t)(T > 0 ? T : 1) * 4);
-    L.hist = o;  o += a256((size_t)L.n_chunks * L.n_keys * 4);
+    L.epk = o;   o += a256((size_t)L.T_pad * 4);
+    L.gpk = o;   o += a256((size_t)L.T_pad * 8);
     L.tmask = o; o += a256((size_t)L.tiles_max * 4);
     L.v = o;     o += a256((size_t)n_prob * L.max_ks * L.T_pad * 2 * L.r_pad * 4);
     L.total = o;
@@ -58,109 +57,225 @@ SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob) {
 namespace {
 
 constexpr int kSegThreads = 1024;
+constexpr int kSegWaves = kSegThreads / kWave;
+constexpr int kMaxKeys = (32 + 1) * (32 + 1);
 
 // ---- segment ---------------------------------------------------------------
 
+// A row's set as loaded once: slots, gates and key.  key = the unordered pair
+// (a <= b, -1 = empty slot) as (a + 1) (E + 1) + (b + 1); -1 for a row with
+// two empty slots, a bad set or t >= T.
+struct SegRow {
+    int e0, e1, key;
+    float g0, g1;
+    bool bad;
+};
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Raw set of row t.  The loads are not guarded (t past the end reads row
+// T - 1, T >= 1, and is marked empty later), so several rows' loads can be in
+// flight at once.
+struct SegRaw {
+    i32x2 e;
+    f32x2 g;
+};
+__device__ __forceinline__ SegRaw seg_load(const int32_t* idx, const float* g, int64_t t, int64_t T) {
+    const int64_t tc = t < T ? t : T - 1;
+    return SegRaw{gld((const i32x2*)idx + tc), gld((const f32x2*)g + tc)};
+}
+__device__ __forceinline__ SegRow seg_row(const SegRaw& r, bool in, int E) {
+    SegRow q;
+    q.e0 = in ? r.e.x : -1;
+    q.e1 = in ? r.e.y : -1;
+    q.g0 = r.g.x;
+    q.g1 = r.g.y;
+    q.bad = q.e0 < -1 || q.e0 >= E || q.e1 < -1 || q.e1 >= E;
+    if (q.e0 >= 0 && !__builtin_isfinite(q.g0)) q.bad = true;
+    if (q.e1 >= 0 && !__builtin_isfinite(q.g1)) q.bad = true;
+    const int a = q.e0 < q.e1 ? q.e0 : q.e1, b = q.e0 < q.e1 ? q.e1 : q.e0;
+    q.key = (!q.bad && b >= 0) ? (a + 1) * (E + 1) + (b + 1) : -1;
+    return q;
+}
+
+// Exclusive scan over the workgroup (one value per thread, thread order).
+__device__ __forceinline__ int block_exscan(int v, int* s_tot, int& total) {
+    const int lane = lane_id(), w = wave_id();
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += y;
+    }
+    if (lane == kWave - 1) s_tot[w] = inc;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int i = 0; i < kSegWaves; ++i) {
+        const int x = s_tot[i];
+        before += i < w ? x : 0;
+        total += x;
+    }
+    __syncthreads();
+    return before + inc - v;
+}
+
+// One workgroup: a stable counting sort of the rows by key, all bookkeeping in
+// LDS.  Pass 1 counts the keys (and keeps the keys of the first kKeyCache rows
+// in LDS); their exclusive scan gives each key's first position.  Pass 2 takes
+// the rows in batches of kSegThreads, in order: a row's position = its key's
+// first position + rows of that key in earlier batches + in earlier waves of
+// this batch + earlier lanes of its wave (ballots).  A batch's sets are loaded
+// at its start and first needed when the rows are written out.
+constexpr int kKeyCache = 8192;
+constexpr int kTileCache = kKeyCache / 32;
 __global__ __launch_bounds__(kSegThreads) void sgmm_segment_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ g, int64_t T, int E, char* ws,
     SgLayout L) {
     int32_t* hdr = (int32_t*)(ws + L.hdr);
     int32_t* perm = (int32_t*)(ws + L.perm);
-    int32_t* rank = (int32_t*)(ws + L.rank);
-    int32_t* key = (int32_t*)(ws + L.key);
-    int32_t* hist = (int32_t*)(ws + L.hist);
+    uint32_t* epk = (uint32_t*)(ws + L.epk);
+    float* gpk = (float*)(ws + L.gpk);
     uint32_t* tmask = (uint32_t*)(ws + L.tmask);
     __shared__ int s_err;
-    __shared__ int s_sum[kSegThreads];
+    __shared__ int s_next[kMaxKeys];   // counts, then the next free position of each key
+    __shared__ int s_base[kMaxKeys];   // first position of each key in the current batch
+    __shared__ uint16_t s_wc[kSegWaves][kMaxKeys];  // per-wave counts of a batch, then
+                                                    // their exclusive prefix over waves
+    __shared__ int16_t s_key[kKeyCache];
+    __shared__ uint32_t s_tm[kTileCache];
+    __shared__ int s_tot[kSegWaves];
     const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-    const int nw = kSegThreads / kWave;
-    const int64_t nk = L.n_keys, nc = L.n_chunks;
+    const int nk = (E + 1) * (E + 1);
     if (tid == 0) s_err = 0;
-    for (int64_t q = tid; q < nc * nk; q += kSegThreads) hist[q] = 0;
-    __threadfence_block();
+    for (int k = tid; k < nk; k += kSegThreads) s_next[k] = 0;
+    for (int q = tid; q < kTileCache; q += kSegThreads) s_tm[q] = 0;
     __syncthreads();
 
-    // 1) keys, per-chunk counts and the rank of each row among the earlier rows
-    //    of its 64-row chunk with the same key (wave ballots: stable).
-    for (int64_t c = w; c < nc; c += nw) {
-        const int64_t t = c * kWave + lane;
-        int k = -1;
-        if (t < T) {
-            const int e0 = idx[2 * t], e1 = idx[2 * t + 1];
-            bool bad = e0 < -1 || e0 >= E || e1 < -1 || e1 >= E;
-            if (e0 >= 0 && !__builtin_isfinite(g[2 * t])) bad = true;
-            if (e1 >= 0 && !__builtin_isfinite(g[2 * t + 1])) bad = true;
-            if (bad) s_err = 1;
-            const int a = e0 < e1 ? e0 : e1, b = e0 < e1 ? e1 : e0;
-            if (!bad && b >= 0) k = (a + 1) * (E + 1) + (b + 1);
-            key[t] = k;
+    // pass 1: key counts (LDS atomics)
+    for (int64_t b0 = 0; b0 < T; b0 += 4 * kSegThreads) {
+        SegRaw raw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[j] = seg_load(idx, g, b0 + j * kSegThreads + tid, T);
+        __builtin_amdgcn_sched_barrier(0);  // all four rows' loads are issued first
+        SegRow q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = seg_row(raw[j], b0 + j * kSegThreads + tid < T, E);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t t = b0 + j * kSegThreads + tid;
+            if (q[j].bad) s_err = 1;
+            if (t < kKeyCache) s_key[t] = (int16_t)q[j].key;
+            if (q[j].key >= 0) atomicAdd(&s_next[q[j].key], 1);
         }
+    }
+    __syncthreads();
+    const int err = s_err;
+
+    // exclusive scan of the counts in key order (each thread owns a run of keys)
+    constexpr int kPer = (kMaxKeys + kSegThreads - 1) / kSegThreads;
+    int cnt[kPer], run = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int k = tid * kPer + j;
+        cnt[j] = k < nk ? s_next[k] : 0;
+        run += cnt[j];
+    }
+    int n_pos;
+    int base = block_exscan(run, s_tot, n_pos);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int k = tid * kPer + j;
+        if (k < nk) s_next[k] = base;
+        base += cnt[j];
+    }
+    if (err) n_pos = 0;
+    const int n_tiles = (n_pos + 31) / 32;
+    const bool lds_masks = n_tiles <= kTileCache;
+    __syncthreads();
+
+    // pass 2: place the rows batch by batch
+    for (int64_t b0 = 0; !err && b0 < T; b0 += kSegThreads) {
+        const int64_t t = b0 + tid;
+        const SegRaw raw = seg_load(idx, g, t, T);  // first needed when the row is written
+        static_assert((kSegWaves * kMaxKeys) % 2 == 0 && kKeyCache % kSegThreads == 0, "LDS table shapes");
+        for (int q = tid; q < kSegWaves * kMaxKeys / 2; q += kSegThreads) ((uint32_t*)&s_wc[0][0])[q] = 0;
+        __syncthreads();
+        int k;
+        if (b0 + kSegThreads <= kKeyCache)  // batch-uniform: keys from LDS, the loads stay in flight
+            k = t < T ? (int)s_key[t] : -1;
+        else
+            k = seg_row(raw, t < T, E).key;
+        // stable rank within the wave and the wave's count of each key (ballots)
         uint64_t todo = __ballot(k >= 0);
         int rk = 0;
         while (todo) {
             const int leader = __ffsll((unsigned long long)todo) - 1;
-            const int lk = __shfl(k, leader, kWave);
+            const int lk = __builtin_amdgcn_readlane(k, leader);
             const uint64_t same = __ballot(k == lk) & todo;
             if (k == lk) rk = __popcll(same & ((1ull << lane) - 1ull));
-            if (lane == leader) hist[c * nk + lk] = __popcll(same);
+            if (lane == leader) s_wc[w][lk] = (uint16_t)__popcll(same);
             todo &= ~same;
         }
-        if (t < T) rank[t] = rk;
-    }
-    __threadfence_block();
-    __syncthreads();
-
-    // 2) exclusive scan of the counts in (key, chunk) order: the start of each
-    //    key's segment, and within it of each chunk's rows.
-    const int64_t N = nk * nc;
-    const int64_t per = (N + kSegThreads - 1) / kSegThreads;
-    const int64_t q0 = tid * per, q1 = (q0 + per < N) ? q0 + per : N;
-    int run = 0;
-    for (int64_t q = q0; q < q1; ++q) run += hist[(q % nc) * nk + q / nc];
-    s_sum[tid] = run;
-    __syncthreads();
-    for (int off = 1; off < kSegThreads; off <<= 1) {
-        const int v = tid >= off ? s_sum[tid - off] : 0;
         __syncthreads();
-        s_sum[tid] += v;
-        __syncthreads();
-    }
-    int base = s_sum[tid] - run;
-    for (int64_t q = q0; q < q1; ++q) {
-        int32_t* p = &hist[(q % nc) * nk + q / nc];
-        const int cnt = *p;
-        *p = base;
-        base += cnt;
-    }
-    const int n_pos = s_sum[kSegThreads - 1];
-    __threadfence_block();
-    __syncthreads();
-
-    // 3) scatter rows to their sorted positions.
-    for (int64_t t = tid; t < T; t += kSegThreads) {
-        const int k = key[t];
-        if (k >= 0) perm[hist[(t / kWave) * nk + k] + rank[t]] = (int32_t)t;
-    }
-    for (int64_t p = n_pos + tid; p < L.T_pad; p += kSegThreads) perm[p] = -1;
-    __threadfence_block();
-    __syncthreads();
-
-    // 4) 32-row tiles and the experts each one uses.
-    const int n_tiles = s_err ? 0 : (n_pos + 31) / 32;
-    for (int64_t tl = tid; tl < n_tiles; tl += kSegThreads) {
-        uint32_t m = 0;
-        for (int j = 0; j < 32; ++j) {
-            const int t = perm[tl * 32 + j];
-            if (t < 0) continue;
-            const int e0 = idx[2 * (int64_t)t], e1 = idx[2 * (int64_t)t + 1];
-            if (e0 >= 0) m |= 1u << e0;
-            if (e1 >= 0) m |= 1u << e1;
+        // rows of each key in earlier waves of the batch, in wave order
+        for (int kk = tid; kk < nk; kk += kSegThreads) {
+            int acc = 0;
+            for (int i = 0; i < kSegWaves; ++i) {
+                const int c = s_wc[i][kk];
+                s_wc[i][kk] = (uint16_t)acc;
+                acc += c;
+            }
+            s_base[kk] = s_next[kk];
+            s_next[kk] += acc;
         }
-        tmask[tl] = m;
+        __syncthreads();
+        if (k >= 0) {
+            const SegRow cur = seg_row(raw, true, E);
+            const int64_t p = (int64_t)s_base[k] + s_wc[w][k] + rk;
+            perm[p] = (int32_t)t;
+            epk[p] = ((uint32_t)cur.e0 & 0xffffu) | ((uint32_t)cur.e1 << 16);
+            gpk[2 * p] = cur.e0 >= 0 ? cur.g0 : 0.f;
+            gpk[2 * p + 1] = cur.e1 >= 0 ? cur.g1 : 0.f;
+            if (lds_masks) {
+                const uint32_t m = (cur.e0 >= 0 ? 1u << cur.e0 : 0u) | (cur.e1 >= 0 ? 1u << cur.e1 : 0u);
+                atomicOr(&s_tm[p >> 5], m);
+            }
+        }
+    }
+    for (int64_t p = n_pos + tid; p < L.T_pad; p += kSegThreads) {
+        perm[p] = -1;
+        epk[p] = 0xffffffffu;
+        gpk[2 * p] = 0.f;
+        gpk[2 * p + 1] = 0.f;
+    }
+    __syncthreads();
+
+    // tile masks: from LDS, or (more tiles than LDS keeps) each half-wave ORs
+    // the expert bits of one tile's 32 positions read back from epk
+    if (lds_masks) {
+        for (int q = tid; q < n_tiles; q += kSegThreads) tmask[q] = s_tm[q];
+    } else {
+        for (int64_t q0 = 2 * w; q0 < n_tiles; q0 += 8 * kSegWaves) {
+            uint32_t m[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t q = q0 + 2 * kSegWaves * j + (lane >> 5);
+                const uint32_t ep = q < n_tiles ? epk[q * 32 + (lane & 31)] : 0xffffffffu;
+                const int e0 = (int16_t)(ep & 0xffffu), e1 = (int16_t)(ep >> 16);
+                m[j] = (e0 >= 0 ? 1u << e0 : 0u) | (e1 >= 0 ? 1u << e1 : 0u);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) m[j] |= __shfl_xor(m[j], o, kWave);
+                const int64_t q = q0 + 2 * kSegWaves * j + (lane >> 5);
+                if ((lane & 31) == 0 && q < n_tiles) tmask[q] = m[j];
+            }
+        }
     }
     if (tid == 0) {
-        hdr[SG_ERR] = s_err;
-        hdr[SG_NPOS] = s_err ? 0 : n_pos;
+        hdr[SG_ERR] = err;
+        hdr[SG_NPOS] = n_pos;
         hdr[SG_NTILES] = n_tiles;
     }
 }
@@ -193,29 +308,34 @@ __device__ __forceinline__ int find_prob_cb(const SgDesc* d, int n, int64_t u) {
 
 // ---- shrink (bf16, MFMA) -----------------------------------------------------
 
+// Tiles per shrink work item: every A operand feeds one MFMA per tile.
+constexpr int kTM = 1;
+constexpr int kXRows = 32 * kTM;
 // 64-wide K chunks of one slice, and 16-byte chunks of one x row of a slice
 constexpr int kKC = kSgmmKSlice / 64;
 constexpr int kXC = kSgmmKSlice / 8;
-static_assert(kKC % 4 == 0, "slice is a whole number of 256-wide steps");
-// x slice in LDS: 32 rows of kSgmmKSlice bf16; the 16-byte chunk c of row m is
-// stored at chunk c ^ (m & 15), so the MFMA-layout reads (16 rows, one chunk)
+static_assert(kKC >= 4 && kKC % 4 == 0, "slice is a whole number of 256-wide steps");
+static_assert(256 % kXC == 0 && kXRows % (256 / kXC) == 0, "x slice load shape");
+// x slice in LDS: kXRows rows of kSgmmKSlice bf16; the 16-byte chunk c of row m
+// is stored at chunk c ^ (m & 15), so the MFMA-layout reads (16 rows, one chunk)
 // and the row-contiguous writes both touch 16 distinct bank groups.
 __device__ __forceinline__ int x_off(int row, int c) { return row * kSgmmKSlice + ((c ^ (row & 15)) << 3); }
 // per-wave 32x64 bf16 scratch of the expand: rows of eight 16-byte chunks, chunk XOR (row & 7)
 __device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 
-// One work item = (problem, K slice, tile), the tile fastest so the work items
-// that share a slice of A run next to each other on one XCD.  The four waves
-// first read the tile's 32 x rows of the slice, row-contiguous (each x byte is
-// read once), into LDS.  The N blocks (32 columns of (expert, rank) each) are
-// then spread over the waves: with four or more blocks each wave takes whole
-// blocks; with fewer, the waves of one block split the slice's 16 chunks and
-// their sums are added in a fixed order.  The A rows of a block stream from
-// L2 four chunks ahead of the MFMAs.  Each row's two slots get the slice's
-// partial v; the expand adds the slices up.  Loads are never guarded: a
-// padding row or (expert, rank) column reads an in-bounds dummy row whose
-// products reach only accumulator entries that are never stored, and k past
-// d_in reads a clamped address whose value is replaced by zero.
+// One work item = (problem, K slice, kTM consecutive tiles), the tiles fastest
+// so the work items that share a slice of A run next to each other on one XCD.
+// The four waves first read the tiles' x rows of the slice, row-contiguous
+// (each x byte is read once), into LDS.  The N blocks (32 columns of (expert,
+// rank) each, over the union of the tiles' experts) are then spread over the
+// waves: with four or more blocks each wave takes whole blocks; with fewer, the
+// waves of one block split the slice's chunks and their sums are added in a
+// fixed order.  The A rows of a block stream from L2 up to four chunks ahead
+// of the MFMAs, and each A operand serves the kTM tiles.  Each row's two
+// slots get the slice's partial v; a later pass adds the slices up.  Loads are
+// never guarded: a padding row or (expert, rank) column reads an in-bounds
+// dummy row whose products reach only accumulator entries that are never
+// stored, and k past d_in reads a clamped address whose value is replaced by 0.
 template <int R16, bool PK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
@@ -225,38 +345,48 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     const int64_t bid = blockIdx.x;
     const int64_t t = (bid & 7) * per_xcd + (bid >> 3);
     if (t >= n_units) return;
-    const int64_t nt = a.L.tiles_max;
-    const int64_t gks = t / nt;  // slice index over all problems
-    const int tile = (int)(t - gks * nt);
-    if (tile >= gld(hdr + SG_NTILES)) return;
+    const int64_t ntp = (a.L.tiles_max + kTM - 1) / kTM;
+    const int64_t gks = t / ntp;  // slice index over all problems
+    const int tile0 = (int)(t - gks * ntp) * kTM;
+    const int n_tiles = gld(hdr + SG_NTILES);
+    if (tile0 >= n_tiles) return;
     const int prob = a.descs ? find_prob_ks(a.descs, a.n_prob, gks) : 0;
     const SgDesc D = a.descs ? a.descs[prob] : a.single;
     const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
+    const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
     const uint32_t* tmask = (const uint32_t*)(a.ws + a.L.tmask);
     float* v = (float*)(a.ws + a.L.v) + gks * a.L.T_pad * 2 * RPAD;
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[32 * kSgmmKSlice];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kXRows * kSgmmKSlice];
     __shared__ int s_U[32];
     __shared__ int s_nU;
-    __shared__ int s_row[32], s_e0[32], s_e1[32];
+    __shared__ int s_row[kXRows], s_e0[kXRows], s_e1[kXRows];
     const int tid = threadIdx.x;
-    if (tid < 32) {
-        const int row = gld(perm + tile * 32 + tid);
+    if (tid < kXRows) {
+        const bool in = tile0 + tid / 32 < n_tiles;
+        const int p = tile0 * 32 + tid;
+        const int row = in ? gld(perm + p) : -1;
+        const uint32_t ep = in ? gld(epk + p) : 0xffffffffu;
         s_row[tid] = row;
-        s_e0[tid] = row >= 0 ? gld(a.idx + 2 * (int64_t)row) : -1;
-        s_e1[tid] = row >= 0 ? gld(a.idx + 2 * (int64_t)row + 1) : -1;
+        s_e0[tid] = (int16_t)(ep & 0xffffu);
+        s_e1[tid] = (int16_t)(ep >> 16);
     }
-    if (tid == 0) s_nU = mask_list(gld(tmask + tile), s_U);
+    if (tid == 0) {
+        uint32_t m = 0;
+        for (int j = 0; j < kTM; ++j)
+            if (tile0 + j < n_tiles) m |= gld(tmask + tile0 + j);
+        s_nU = mask_list(m, s_U);
+    }
     __syncthreads();
 
     const int d_in = uniform(D.d_in), r = a.r;
     const uint16_t* __restrict__ x = (const uint16_t*)D.x;
     const uint16_t* __restrict__ A = (const uint16_t*)(PK ? D.Ap : D.A);
 
-    // 1) x slice: thread tid reads chunk tid % kXC of rows tid / kXC + 2j
+    // 1) x slice: thread tid reads chunk tid % kXC of rows tid / kXC + kXR j
     constexpr int kXR = 256 / kXC;           // rows per load instruction
-    constexpr int kXL = 32 / kXR;            // load instructions per thread
+    constexpr int kXL = kXRows / kXR;        // load instructions per thread
     const int xc = tid % kXC, xr0 = tid / kXC;
     const int xk = k0 + 8 * xc;
     const bool xok = xk < d_in;
@@ -298,34 +428,38 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
         const int64_t e = ok ? s_U[u] : 0, rr = ok ? rho : 0;
         return PK ? A + e * r * d_in + rr * 8 : A + (e * r + rr) * d_in;
     };
-    auto mma = [&](const u32x4 (&ab)[4], int kc, f32x16& acc) {
+    auto mma = [&](const u32x4 (&ab)[4], int kc, f32x16 (&acc)[kTM]) {
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-            const u32x4 xo = *(const u32x4*)(s_x + x_off(n, 8 * kc + 2 * s2 + h));
-            acc = mfma32(xo, ab[s2], acc);
-        }
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+            for (int j = 0; j < kTM; ++j) {
+                const u32x4 xo = *(const u32x4*)(s_x + x_off(32 * j + n, 8 * kc + 2 * s2 + h));
+                acc[j] = mfma32(xo, ab[s2], acc[j]);
+            }
     };
-    auto store_v = [&](const f32x16& acc, int u, int rho) {
+    auto store_v = [&](const f32x16 (&acc)[kTM], int u, int rho) {
         if (u >= nU || rho >= r) return;
         const int e = s_U[u];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = 8 * (i >> 2) + 4 * h + (i & 3);
-            if (s_row[m] < 0) continue;
-            float* vp = v + ((int64_t)(tile * 32 + m) * 2) * RPAD + rho;
-            if (s_e0[m] == e) gst(vp, acc[i]);
-            if (s_e1[m] == e) gst(vp + RPAD, acc[i]);
-        }
+        for (int j = 0; j < kTM; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = 32 * j + 8 * (i >> 2) + 4 * h + (i & 3);
+                if (s_row[m] < 0) continue;
+                float* vp = v + ((int64_t)(tile0 * 32 + m) * 2) * RPAD + rho;
+                if (s_e0[m] == e) gst(vp, acc[j][i]);
+                if (s_e1[m] == e) gst(vp + RPAD, acc[j][i]);
+            }
     };
 
-    // first block's A: the first four chunks are in flight while x lands in LDS
+    // first block's A: its first chunks are in flight while x lands in LDS
     u32x4 ab[4][4];
     int u, rho;
     const uint16_t* arow = a_row(gw, u, rho);
     const bool act = kp < P;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        if (act) load_a(ab[j], arow, kp + P * j);
+        if (act && j < nmy) load_a(ab[j], arow, kp + P * j);
 
 #pragma unroll
     for (int j = 0; j < kXL; ++j) {
@@ -334,14 +468,16 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     }
     __syncthreads();
 
-    // K loop of one block over this wave's chunks, A four chunks ahead
-    auto run_block = [&](f32x16& acc) {
+    // K loop of one block over this wave's chunks, A up to four chunks ahead
+    auto run_block = [&](f32x16 (&acc)[kTM]) {
 #pragma unroll 1
         for (int i = 0; i < nmy; i += 4) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                mma(ab[j], kp + P * (i + j), acc);
-                if (i + 4 < nmy) load_a(ab[j], arow, kp + P * (i + 4 + j));
+                if (i + j < nmy) {
+                    mma(ab[j], kp + P * (i + j), acc);
+                    if (i + j + 4 < nmy) load_a(ab[j], arow, kp + P * (i + j + 4));
+                }
             }
         }
     };
@@ -352,9 +488,12 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
             if (blk != gw) {
                 arow = a_row(blk, u, rho);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) load_a(ab[j], arow, j);
+                for (int j = 0; j < 4; ++j)
+                    if (j < nmy) load_a(ab[j], arow, j);
             }
-            f32x16 acc = f32x16{};
+            f32x16 acc[kTM];
+#pragma unroll
+            for (int j = 0; j < kTM; ++j) acc[j] = f32x16{};
             run_block(acc);
             store_v(acc, u, rho);
         }
@@ -362,25 +501,33 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     }
     // one block per group of P waves: parts 1..P-1 go through LDS (the x
     // slice is no longer read) and the part-0 wave adds them in order
-    f32x16 acc = f32x16{};
+    f32x16 acc[kTM];
+#pragma unroll
+    for (int j = 0; j < kTM; ++j) acc[j] = f32x16{};
     run_block(acc);
     __syncthreads();
-    f32x4* red = (f32x4*)s_x;  // [wave][4][lane]
+    f32x4* red = (f32x4*)s_x;  // [wave][tile][4][lane]
+    static_assert(4 * kTM * 4 * kWave * 16 <= kXRows * kSgmmKSlice * 2, "reduction fits the x slice");
     if (kp > 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            red[(w * 4 + q) * kWave + lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        for (int j = 0; j < kTM; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                red[((w * kTM + j) * 4 + q) * kWave + lane] =
+                    f32x4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
     }
     __syncthreads();
     if (kp == 0) {
         for (int p = 1; p < P; ++p) {
             const int wp = gw + p * G;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 o = red[(wp * 4 + q) * kWave + lane];
+            for (int j = 0; j < kTM; ++j)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[4 * q + c] += o[c];
-            }
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 o = red[((wp * kTM + j) * 4 + q) * kWave + lane];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[j][4 * q + c] += o[c];
+                }
         }
         store_v(acc, u, rho);
     }
@@ -418,6 +565,8 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     const int tile = (int)(local - (int64_t)cg * nt);
     if (tile >= gld(hdr + SG_NTILES)) return;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
+    const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
+    const float* gpk = (const float*)(a.ws + a.L.gpk);
     const uint32_t* tmask = (const uint32_t*)(a.ws + a.L.tmask);
     const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * a.L.T_pad * 2 * RPAD;
 
@@ -454,16 +603,12 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     u32x4 ycur[4], ynxt[4];
     if (nblk > 0) load_y(ycur, 0);
 
-    // this lane's row (MFMA N index = tile row n) and its two slots
-    const int row = gld(perm + tile * 32 + n);
-    int e0 = -1, e1 = -1;
-    float c0 = 0.f, c1 = 0.f;
-    if (row >= 0) {
-        e0 = gld(a.idx + 2 * (int64_t)row);
-        e1 = gld(a.idx + 2 * (int64_t)row + 1);
-        c0 = e0 >= 0 ? a.scale * gld(a.g + 2 * (int64_t)row) : 0.f;
-        c1 = e1 >= 0 ? a.scale * gld(a.g + 2 * (int64_t)row + 1) : 0.f;
-    }
+    // this lane's tile row (MFMA N index n): its two slots and gates (a padding
+    // position has two empty slots)
+    const uint32_t ep = gld(epk + tile * 32 + n);
+    const int e0 = (int16_t)(ep & 0xffffu), e1 = (int16_t)(ep >> 16);
+    const float c0 = a.scale * gld(gpk + 2 * (tile * 32 + n));
+    const float c1 = a.scale * gld(gpk + 2 * (tile * 32 + n) + 1);
     const float* v0 = v + ((int64_t)(tile * 32 + n) * 2) * RPAD;
     const float* v1 = v0 + RPAD;
     // row-side operand of (expert U[q / R16], ranks 16(q % R16) + 8h + [0,8)):
@@ -704,7 +849,7 @@ __global__ __launch_bounds__(256) void sgmm_pack_a_kernel(const uint16_t* __rest
 
 template <int R16>
 hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
-    const int64_t n_units = a.total_ks * a.L.tiles_max;
+    const int64_t n_units = a.total_ks * ((a.L.tiles_max + kTM - 1) / kTM);
     const int64_t sh_per_xcd = (n_units + 7) / 8;
     if (a.packed)
         hipLaunchKernelGGL((sgmm_shrink_bf16<R16, true>), dim3((unsigned)(8 * sh_per_xcd)), dim3(256), 0, s,

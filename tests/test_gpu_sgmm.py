@@ -66,6 +66,7 @@ CASES = [
     (70, 1096, 136, 16, 64, 0.5, torch.bfloat16),    # two K slices, many N blocks per tile
     (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # exactly one slice, largest rank
     (9, 1500, 24, 4, 8, 1.0, torch.float32),         # fp32 past one slice width
+    (9000, 64, 72, 8, 16, 1.0, torch.bfloat16),      # more rows than the segment's LDS caches
 ]
 
 
