@@ -91,7 +91,7 @@ const char* dlm_version(void) { return "dlm 0.1.0 (gfx950)"; }
 
 int dlm_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int32_t E, int32_t dtype,
                 int32_t* idx, float* g, void* stream) {
-    if (T < 0 || T > ((int64_t)1 << 31)) return fail(DLM_ESHAPE, "pregate: T=%lld out of range", (long long)T);
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(DLM_ESHAPE, "pregate: T=%lld out of range", (long long)T);
     if (d < 1 || d > kMaxDim) return fail(DLM_ESHAPE, "pregate: d=%lld out of range", (long long)d);
     if (E < 2 || E > DLM_MAX_EXPERTS) return fail(DLM_ESHAPE, "pregate: E=%d not in [2, %d]", E, DLM_MAX_EXPERTS);
     if (!valid_dtype(dtype)) return fail(DLM_EDTYPE, "pregate: unknown dtype %d", dtype);

@@ -2,8 +2,8 @@
 // top-2 router at the first layer fixes each token's expert set, which every
 // later layer reuses).
 //
-// One wave64 per token.  Lane j accumulates the E logits over the columns
-// j, j+64, ... in binary64 (the products of fp32 or bf16 operands are exact in
+// One wave64 per token.  Each lane accumulates the E logits over its share of
+// the columns in binary64 (the products of fp32 or bf16 operands are exact in
 // binary64), a fixed butterfly sums the 64 partials, and lane 0 takes the
 // top two (ties -> lower index) and the renormalised pair of weights
 // g0 = 1/(1+exp(l1-l0)), g1 = exp(l1-l0)/(1+exp(l1-l0)).
@@ -23,6 +23,37 @@ template <> __device__ __forceinline__ double ldv<uint16_t>(const uint16_t* p, i
 
 constexpr int kTokPerBlock = 4;
 
+// Lane 0 takes the top two of the summed logits l by strict '>' scans (equal
+// logits keep the lower index; a NaN logit never compares greater, so the
+// indices stay in range and distinct) and the renormalised pair of weights.
+template <int EMAX>
+__device__ __forceinline__ void top2_store(const double (&l)[EMAX], int E, int64_t t, int32_t* idx, float* g) {
+    int i0 = 0;
+    double l0 = l[0];
+#pragma unroll
+    for (int e = 1; e < EMAX; ++e)
+        if (e < E && l[e] > l0) { l0 = l[e]; i0 = e; }
+    int i1 = (i0 == 0) ? 1 : 0;
+    double l1 = (i0 == 0) ? l[1] : l[0];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+        if (e < E && e != i0 && l[e] > l1) { l1 = l[e]; i1 = e; }
+    const double q = exp(l1 - l0);  // <= 1
+    idx[2 * t] = i0;
+    idx[2 * t + 1] = i1;
+    g[2 * t] = (float)(1.0 / (1.0 + q));
+    g[2 * t + 1] = (float)(q / (1.0 + q));
+}
+
+// Sum each logit over the wave (fixed butterfly); lane 0 stores the result.
+template <int EMAX>
+__device__ __forceinline__ void top2(double (&acc)[EMAX], int E, int64_t t, int32_t* idx, float* g) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+        if (e < E) acc[e] = wave_sum(acc[e]);
+    if (lane_id() == 0) top2_store<EMAX>(acc, E, t, idx, g);
+}
+
 template <typename T, int EMAX>
 __global__ __launch_bounds__(kTokPerBlock* kWave) void pregate_kernel(
     const T* __restrict__ x, const T* __restrict__ Wr, int64_t n_tok, int64_t d, int E,
@@ -41,27 +72,85 @@ __global__ __launch_bounds__(kTokPerBlock* kWave) void pregate_kernel(
         for (int e = 0; e < EMAX; ++e)
             if (e < E) acc[e] = fma(xv, ldv(w, e), acc[e]);
     }
+    top2<EMAX>(acc, E, t, idx, g);
+}
+
+// bf16 with d and E multiples of 8 (16-byte aligned rows): one workgroup of
+// kVecWaves waves per token.  Lane j of wave w takes the 8 consecutive columns
+// of chunks c = j + 64 (w + kVecWaves i); x comes in one 16-byte load and each
+// Wr row in E/8 (two chunks' loads in flight at a time for E <= 16).  The
+// waves' sums are added in wave order.
+constexpr int kVecWaves = 4;
+template <int EMAX>
+__global__ __launch_bounds__(kVecWaves* kWave) void pregate_bf16_vec(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wr, int64_t n_tok, int64_t d, int E,
+    int32_t* __restrict__ idx, float* __restrict__ g) {
+    const int64_t t = blockIdx.x;
+    const int lane = lane_id(), w = wave_id();
+    __shared__ double s_part[kVecWaves][EMAX];
+    double acc[EMAX];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[e] = 0.0;
+    const uint16_t* xr = x + t * d;
+    const int64_t nc = d / 8;
+    auto chunk = [&](const u32x4& xv, const u32x4 (&wv)[8][EMAX / 8]) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const double xj = (double)(jj & 1 ? bf_hi(xv[jj >> 1]) : bf_lo(xv[jj >> 1]));
+#pragma unroll
+            for (int e = 0; e < EMAX; ++e) {
+                if (e >= E) continue;
+                const uint32_t wp = wv[jj][e >> 3][(e & 7) >> 1];
+                acc[e] = fma(xj, (double)(e & 1 ? bf_hi(wp) : bf_lo(wp)), acc[e]);
+            }
+        }
+    };
+    auto load = [&](int64_t c, u32x4& xv, u32x4 (&wv)[8][EMAX / 8]) {
+        xv = ld128(xr + 8 * c);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+            for (int e8 = 0; e8 < EMAX / 8; ++e8) {
+                // experts past E (E < EMAX) re-read the row's first 8, unused
+                const u32x4 v = ld128(Wr + (8 * c + jj) * E + (8 * e8 < E ? 8 * e8 : 0));
+                wv[jj][e8] = 8 * e8 < E ? v : u32x4{0u, 0u, 0u, 0u};
+            }
+    };
+    constexpr int64_t kStep = (int64_t)kVecWaves * kWave;
+    int64_t c = lane + (int64_t)kWave * w;
+    if constexpr (EMAX <= 16) {  // two chunks in flight (registers allow it)
+        for (; c + kStep < nc; c += 2 * kStep) {
+            u32x4 xa, xb, wa[8][EMAX / 8], wb[8][EMAX / 8];
+            load(c, xa, wa);
+            load(c + kStep, xb, wb);
+            __builtin_amdgcn_sched_barrier(0);  // both chunks' loads issue before any use
+            chunk(xa, wa);
+            chunk(xb, wb);
+        }
+    }
+    for (; c < nc; c += kStep) {
+        u32x4 xa, wa[8][EMAX / 8];
+        load(c, xa, wa);
+        __builtin_amdgcn_sched_barrier(0);
+        chunk(xa, wa);
+    }
 #pragma unroll
     for (int e = 0; e < EMAX; ++e)
         if (e < E) acc[e] = wave_sum(acc[e]);
-    if (lane != 0) return;
-    // Top two by strict '>' scans: equal logits keep the lower index.  A NaN
-    // logit never compares greater, so the indices stay in range and distinct.
-    int i0 = 0;
-    double l0 = acc[0];
+    if (lane == 0) {
 #pragma unroll
-    for (int e = 1; e < EMAX; ++e)
-        if (e < E && acc[e] > l0) { l0 = acc[e]; i0 = e; }
-    int i1 = (i0 == 0) ? 1 : 0;
-    double l1 = (i0 == 0) ? acc[1] : acc[0];
+        for (int e = 0; e < EMAX; ++e) s_part[w][e] = acc[e];
+    }
+    __syncthreads();
+    if (w != 0 || lane != 0) return;
+    double l[EMAX];
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e)
-        if (e < E && e != i0 && acc[e] > l1) { l1 = acc[e]; i1 = e; }
-    const double q = exp(l1 - l0);  // <= 1
-    idx[2 * t] = i0;
-    idx[2 * t + 1] = i1;
-    g[2 * t] = (float)(1.0 / (1.0 + q));
-    g[2 * t + 1] = (float)(q / (1.0 + q));
+    for (int e = 0; e < EMAX; ++e) {
+        l[e] = s_part[0][e];
+#pragma unroll
+        for (int q = 1; q < kVecWaves; ++q) l[e] += s_part[q][e];
+    }
+    top2_store<EMAX>(l, E, t, idx, g);
 }
 
 template <typename T>
@@ -85,7 +174,19 @@ hipError_t launch_t(const void* x, const void* Wr, int64_t T_, int64_t d, int E,
 hipError_t launch_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int E, int dtype,
                           int32_t* idx, float* g, hipStream_t s) {
     if (dtype == 0) return launch_t<float>(x, Wr, T, d, E, idx, g, s);
-    return launch_t<uint16_t>(x, Wr, T, d, E, idx, g, s);
+    const bool vec = d % 8 == 0 && E % 8 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)Wr & 15) == 0;
+    if (!vec) return launch_t<uint16_t>(x, Wr, T, d, E, idx, g, s);
+    const dim3 grid((unsigned)T);
+    const dim3 block(kVecWaves * kWave);
+    const uint16_t* xp = (const uint16_t*)x;
+    const uint16_t* wp = (const uint16_t*)Wr;
+    if (E <= 8)
+        hipLaunchKernelGGL((pregate_bf16_vec<8>), grid, block, 0, s, xp, wp, T, d, E, idx, g);
+    else if (E <= 16)
+        hipLaunchKernelGGL((pregate_bf16_vec<16>), grid, block, 0, s, xp, wp, T, d, E, idx, g);
+    else
+        hipLaunchKernelGGL((pregate_bf16_vec<32>), grid, block, 0, s, xp, wp, T, d, E, idx, g);
+    return hipGetLastError();
 }
 
 }  // namespace dlm

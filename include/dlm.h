@@ -90,7 +90,8 @@ const char* dlm_version(void);
  * Logits accumulate in binary64 (the products of fp32/bf16 inputs are exact),
  * so the decision is exact up to the summation order.  idx is always in
  * [0, E) and idx[t][0] != idx[t][1], also for non-finite inputs.
- * Requires 2 <= E <= DLM_MAX_EXPERTS, d >= 1, T >= 0 (T = 0 enqueues nothing).
+ * Requires 2 <= E <= DLM_MAX_EXPERTS, d >= 1, 0 <= T < 2^31 (T = 0 enqueues
+ * nothing).
  */
 int dlm_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int32_t E,
                 int32_t dtype, int32_t* idx, float* g, void* stream);

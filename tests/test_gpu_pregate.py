@@ -62,7 +62,8 @@ def test_router_on_batched_workload_shapes(name):
 
 @pytest.mark.parametrize("T,d,E,dt", [(1, 4096, 8, torch.bfloat16), (3, 100, 2, torch.bfloat16),
                                       (65, 130, 32, torch.float32), (7, 64, 17, torch.bfloat16),
-                                      (200, 1, 5, torch.float32)])
+                                      (200, 1, 5, torch.float32), (5, 1000, 16, torch.bfloat16),
+                                      (9, 520, 32, torch.bfloat16), (33, 8192, 24, torch.bfloat16)])
 def test_router_shapes(T, d, E, dt):
     x, Wr = _xw(T, d, E, dt, 99, T, d, E)
     _check(x, Wr, f"shape {T}x{d}x{E}")
