@@ -11,8 +11,10 @@ value = weight bytes read + written per second (GB/s).
 Beside it, in the same JSON line: SGMM tokens/s on the prefill workload (4096
 tokens x 7 projections, Zipf(1.1) pairs) and on the mixed decode workload
 (64 rows x 32 layers x 7 projections, 128 Markov steps); the switch kernel's
-roofline (HIP-event timing of each launch on its stream, against 8 TB/s); and
-the CPU oracle timed on a bounded sample of the headline workload.
+roofline (HIP-event timing of each launch on its stream, against 8 TB/s); the
+same switch on the 70B-shaped workload; the router's latency at T = 1 and at
+the full token counts; and the CPU oracle timed on a bounded sample of the
+headline workload.
 """
 from __future__ import annotations
 
@@ -101,6 +103,7 @@ def bench_switch(torch, dlm, synth, steps, warmup, log):
         "algo_GBps": algo_bytes * n_switch / wall / 1e9,
         "switch_ms": avg_launch_s * 1e3,
         "switch_ms_p50": sorted(launch_ms)[len(launch_ms) // 2],
+        "switch_ms_p90": sorted(launch_ms)[int(len(launch_ms) * 0.9)],
         "algo_bytes_per_launch": algo_bytes,
         "weight_bytes_per_launch": w_bytes,
         "launches_per_switch": L.launches_per_switch(),
@@ -110,6 +113,71 @@ def bench_switch(torch, dlm, synth, steps, warmup, log):
     del model
     torch.cuda.empty_cache()
     return res
+
+
+def bench_switch_70b(torch, dlm, synth, n_timed, log):
+    """The 70B-shaped decode workload (80 layers x q,o 8192x8192, k,v 8192->1024,
+    gate,up 8192->28672, down 28672->8192; E=16, r=64): router on its 128 tokens,
+    then fused switches token t-1 -> t, each launch timed with HIP events on its
+    stream (2 untimed, then `n_timed`)."""
+    wl = synth.WORKLOADS["70b-decode"]
+    free, _ = torch.cuda.mem_get_info()
+    need = wl.switch_w_elems() * 2 * 1.25
+    if free < need:
+        log(f"70b-decode skipped: needs {need / 2**30:.0f} GiB free, have {free / 2**30:.0f}")
+        return None
+    log(f"building {wl.name}: {wl.n_mats} weights, {wl.switch_w_elems() * 2 / 1e9:.2f} GB bf16")
+    model = synth.switch_model(wl)
+    x, Wr = synth.router_inputs(wl)
+    L = dlm.Layers([(W, A, B) for _, _, W, A, B in model], wl.E, wl.r, wl.scale)
+    stream = torch.cuda.current_stream()
+    idx, g = dlm.pregate(x, Wr)
+    L.switch(None, (idx[0], g[0]))
+    n = min(n_timed + 2, wl.T - 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for t in range(1, n + 1):
+        ev[t - 1][0].record(stream)
+        L.switch((idx[t - 1], g[t - 1]), (idx[t], g[t]))
+        ev[t - 1][1].record(stream)
+    torch.cuda.synchronize()
+    assert L.status() == dlm.DLM_OK
+    ms = sorted(a.elapsed_time(b) for a, b in ev[2:])
+    w_bytes = wl.switch_w_elems() * 2 * 2
+    slice_bytes_per_expert = wl.layers * sum((o + i) * wl.r * 2 for _, o, i in wl.projs)
+    algo = w_bytes + 4 * slice_bytes_per_expert
+    avg = sum(ms) / len(ms) / 1e3
+    res = {"launches_timed": len(ms), "switch_ms": avg * 1e3, "switch_ms_p50": ms[len(ms) // 2],
+           "switch_ms_p90": ms[int(len(ms) * 0.9)], "algo_bytes_per_launch": algo,
+           "achieved_launch_GBps": algo / avg / 1e9, "frac_of_hbm_peak": algo / avg / HBM_PEAK}
+    L.close()
+    del model
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_router(torch, dlm, synth, log):
+    """Router latency per call (HIP events, 20 calls after 3 warm-up) at T = 1
+    and at the full token count of the 7B- and 70B-shaped workloads."""
+    out = {}
+    for name in ("7b-decode", "70b-decode"):
+        wl = synth.WORKLOADS[name]
+        x, Wr = synth.router_inputs(wl)
+        for T in (1, wl.T):
+            xt = x[:T].contiguous()
+            idx = torch.empty(T, 2, dtype=torch.int32, device="cuda")
+            g = torch.empty(T, 2, dtype=torch.float32, device="cuda")
+            for _ in range(3):
+                dlm.pregate(xt, Wr, idx, g)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                dlm.pregate(xt, Wr, idx, g)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 20 * 1e3
+            nbytes = (xt.numel() + Wr.numel()) * xt.element_size()
+            out[f"{name}_T{T}"] = {"us_per_call": us, "GBps_x_Wr": nbytes / us / 1e3}
+    return out
 
 
 def bench_sgmm(torch, dlm, synth, name, reps, log):
@@ -260,6 +328,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sgmm", action="store_true")
+    ap.add_argument("--no-70b", action="store_true", help="skip the 70B-shaped switch measurement")
+    ap.add_argument("--switch-70b-launches", type=int, default=32)
     ap.add_argument("--profile-kernels", type=int, nargs="?", const=4, default=0,
                     help="short run for rocprofv3 counter collection (N switches + 1 GiB copy)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -287,6 +357,12 @@ def main():
         return
     sw = bench_switch(torch, dlm, synth, args.steps, args.warmup, log)
     log(f"switch: {sw}")
+    router = bench_router(torch, dlm, synth, log)
+    log(f"router: {router}")
+    sw70 = None
+    if not args.no_70b:
+        sw70 = bench_switch_70b(torch, dlm, synth, args.switch_70b_launches, log)
+        log(f"switch 70b: {sw70}")
     sg = {}
     if not args.no_sgmm:
         sg["prefill"] = bench_sgmm(torch, dlm, synth, "sgmm-prefill", args.sgmm_reps, log)
@@ -322,6 +398,9 @@ def main():
                      "algo_bytes_per_launch": sw["algo_bytes_per_launch"]},
         "cpu_baseline": cpu,
         "switch": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in sw.items()},
+        "switch_70b": None if sw70 is None else {k: (round(v, 4) if isinstance(v, float) else v)
+                                                 for k, v in sw70.items()},
+        "router": {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in router.items()},
         "sgmm": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                  for k, v in sg.items()},
     }

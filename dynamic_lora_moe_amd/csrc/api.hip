@@ -12,6 +12,7 @@
 
 #include "dlm.h"
 #include "internal.hpp"
+#include "sgmm.hpp"
 
 using namespace dlm;
 

@@ -30,6 +30,7 @@
 // expert's A and B once per tile instead of once per pair.
 #include "gfx950.hpp"
 #include "internal.hpp"
+#include "sgmm.hpp"
 
 namespace dlm {
 
