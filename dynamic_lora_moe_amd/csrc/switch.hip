@@ -10,7 +10,8 @@
 // gfx950 design (bf16 path):
 //   * The switch is a stream over W (read once, written once, 4 bytes per
 //     element) with 4r MACs per element: HBM-bound, with the delta on MFMA.
-//   * Work unit = a 256-row x CT-column tile of one weight.  Tiles of all L*P
+//   * Work unit = a 256-row x CT-column tile of one weight (ranks 17..64 use
+//     the wide tiles below instead).  Tiles of all L*P
 //     weights form one launch; a workgroup finds its weight by binary search in
 //     the device descriptor table.  Consecutive tiles go to the same XCD so each
 //     XCD streams a contiguous band of W and its L2 keeps the band's slices.
@@ -35,11 +36,19 @@
 
 namespace dlm {
 
+// Wide tiles (ranks 17..64): 64-column sub-bands per tile (4096 columns:
+// measured 74.6 / 72.2 / 70.5 ms per 70B-shaped switch for 16 / 32 / 64),
+// waves = 32-row groups per workgroup, row bands per tile group.
+constexpr int kWideSB = 64;
+constexpr int kWW = 8;
+constexpr int kWRT = kWW * 32;
+constexpr int kWGroup = 8;
+
 SwTile switch_tile_for_rank(int r) {
     SwTile t;
     t.r16 = (r + 15) / 16;
-    t.ct = t.r16 <= 1 ? 256 : (t.r16 <= 2 ? 128 : 64);
-    t.rt = 256;
+    t.ct = t.r16 <= 1 ? 256 : (t.r16 <= 4 ? 64 * kWideSB : 64);
+    t.rt = (t.r16 >= 2 && t.r16 <= 4) ? kWRT : 256;
     return t;
 }
 
@@ -325,6 +334,218 @@ void switch_bf16_kernel(SwitchArgs a) {
         switch_tile<R16, CT, false>(a, sc, D, row_base, col_base, As, Ws);
 }
 
+// ---- wide tiles for ranks 17..64 -------------------------------------------
+//
+// At these ranks the A/B slices of a tile are as large as its W, so the
+// 256 x CT tiles above spend most of their time waiting for operands.  Here a
+// workgroup of 8 waves takes a 256-row x (64 * NSB)-column tile: each wave owns
+// one 32-row group and loads its B rows once per tile; the A slices pass through
+// a double-buffered LDS stage one 64-column sub-band at a time (the next
+// sub-band's slices load during the current one); each wave's W is read two
+// sub-bands ahead.  Tiles of a weight run in groups of kWGroup row bands,
+// column band by column band, so the A slices of a column band and the B rows
+// of the group's row bands are reused from L2 instead of re-read from HBM.
+// The per-slot fp32 products and the epilogue are those of switch_tile.
+
+template <int R16, int NSB, bool FULL>
+__device__ __forceinline__ void switch_wide_tile(const SwitchArgs& a, const Sets& sc, const SwDesc& D,
+                                                 int row_base, int col_base, uint16_t* As, uint16_t* Ws) {
+    constexpr int RPAD = R16 * 16;
+    constexpr int SLOT_ELEMS = 2 * 32 * RPAD;  // one slot's slice of one 64-column sub-band
+    constexpr int BUF_ELEMS = 4 * SLOT_ELEMS;
+    constexpr int NQ = RPAD * 8;               // 16-byte chunks of one slot's sub-band slice
+    constexpr int NSTAGE = (NQ + kWW * kWave - 1) / (kWW * kWave);
+    const int d_out = D.d_out, d_in = D.d_in, r = a.r;
+    const uint16_t* __restrict__ Ab = (const uint16_t*)D.A;
+    const uint16_t* __restrict__ Bb = (const uint16_t*)D.B;
+    uint16_t* __restrict__ W = (uint16_t*)D.W;
+    const int tid = threadIdx.x, w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
+    const bool act[4] = {sc.e[0] >= 0, sc.e[1] >= 0, sc.e[2] >= 0, sc.e[3] >= 0};
+    const bool r_vec = (r & 7) == 0;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    uint16_t* ws = Ws + w * (32 * 64);
+    const int lr = lane >> 3, lc = lane & 7;
+    const int row0 = row_base + w * 32;
+    const int nsb = FULL ? NSB : uniform((d_in - col_base + 63) / 64 < NSB ? (d_in - col_base + 63) / 64 : NSB);
+
+    // A slices of sub-band sb: loads into registers, then the transposed LDS write
+    auto load_a = [&](u32x4 (&av)[4][NSTAGE], int sb) {
+#pragma unroll
+        for (int slot = 0; slot < 4; ++slot)
+#pragma unroll
+            for (int i = 0; i < NSTAGE; ++i) {
+                const int q = tid + i * kWW * kWave;
+                const int rho = q / 8, col = col_base + sb * 64 + (q % 8) * 8;
+                bool ok = act[slot] && (NQ % (kWW * kWave) == 0 || q < NQ);
+                if (!FULL) ok = ok && rho < r && col < d_in;
+                av[slot][i] = ok ? ld128(Ab + ((int64_t)sc.e[slot] * r + rho) * d_in + col) : zero;
+            }
+    };
+    auto store_a = [&](const u32x4 (&av)[4][NSTAGE], uint16_t* buf) {
+#pragma unroll
+        for (int slot = 0; slot < 4; ++slot) {
+            if (!act[slot]) continue;
+#pragma unroll
+            for (int i = 0; i < NSTAGE; ++i) {
+                const int q = tid + i * kWW * kWave;
+                if (NQ % (kWW * kWave) != 0 && q >= NQ) continue;
+                const int rho = q / 8, ch = q % 8;
+                uint16_t* dst = buf + slot * SLOT_ELEMS + (ch >> 2) * 32 * RPAD + (rho & 7);
+                const int cc0 = (ch & 3) * 8;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int m = perm_row(cc0 + j);
+                    const uint32_t word = av[slot][i][j >> 1];
+                    dst[m * RPAD + (a_chunk_swz<R16>(m, rho >> 3) << 3)] =
+                        (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
+                }
+            }
+        }
+    };
+    u32x4 bcur[4][R16];
+    {
+        const int row = row0 + n;
+#pragma unroll
+        for (int slot = 0; slot < 4; ++slot)
+#pragma unroll
+            for (int ks = 0; ks < R16; ++ks) {
+                const int rho0 = ks * 16 + 8 * h;
+                const uint16_t* bp = Bb + ((int64_t)sc.e[slot] * d_out + row) * r + rho0;
+                u32x4 v = zero;
+                if (FULL) {
+                    if (act[slot]) v = ld128(bp);
+                } else if (act[slot] && row < d_out && rho0 < r) {
+                    if (r_vec) {
+                        v = ld128(bp);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t lo = (rho0 + 2 * j < r) ? gld(bp + 2 * j) : 0u;
+                            const uint32_t hi = (rho0 + 2 * j + 1 < r) ? gld(bp + 2 * j + 1) : 0u;
+                            v[j] = lo | (hi << 16);
+                        }
+                    }
+                }
+                bcur[slot][ks] = v;
+            }
+    }
+    // W of sub-band sb, row-major: instruction i reads row 8i + lr, columns 8lc .. +8
+    auto load_w = [&](u32x4 (&wv)[4], int sb) {
+        const int col = col_base + sb * 64 + 8 * lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 8 * i + lr;
+            const uint16_t* p = W + (int64_t)row * d_in + col;
+            if (FULL) wv[i] = ld128(p);
+            else wv[i] = (row < d_out && col < d_in) ? ld128(p) : zero;
+        }
+    };
+    // one 32 x 64 unit; its W registers are refilled with sub-band sb + 2 as
+    // soon as they are in the scratch
+    auto unit = [&](u32x4 (&wv)[4], int sb) {
+        const uint16_t* Acur = As + (sb & 1) * BUF_ELEMS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4*)(ws + w_off(8 * i + lr, lc)) = wv[i];
+        if (sb + 2 < nsb) load_w(wv, sb + 2);
+#pragma unroll 1
+        for (int b = 0; b < 2; ++b) {
+            u32x4 wm[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) wm[q] = *(const u32x4*)(ws + w_off(n, 4 * b + 2 * h + q));
+            f32x16 P[4];
+#pragma unroll
+            for (int slot = 0; slot < 4; ++slot) {
+                P[slot] = f32x16{};
+                if (!act[slot]) continue;
+                const uint16_t* ap = Acur + slot * SLOT_ELEMS + b * 32 * RPAD + n * RPAD;
+#pragma unroll
+                for (int ks = 0; ks < R16; ++ks)
+                    P[slot] = mfma32(*(const u32x4*)(ap + (a_chunk_swz<R16>(n, 2 * ks + h) << 3)),
+                                     bcur[slot][ks], P[slot]);
+            }
+            uint32_t ow[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t word = wm[p >> 2][p & 3];
+                float o2[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int i = 2 * p + j;
+                    const float sn = fmaf(sc.c[1], P[1][i], sc.c[0] * P[0][i]);
+                    const float so = fmaf(sc.c[3], P[3][i], sc.c[2] * P[2][i]);
+                    const float wf = j ? bf_hi(word) : bf_lo(word);
+                    o2[j] = wf - (so - sn);
+                }
+                ow[p] = pack2_bf16(o2[0], o2[1]);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                *(u32x4*)(ws + w_off(n, 4 * b + 2 * h + q)) =
+                    u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
+        }
+        const int col = col_base + sb * 64 + 8 * lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 8 * i + lr;
+            const u32x4 v = *(const u32x4*)(ws + w_off(8 * i + lr, lc));
+            if (FULL || (row < d_out && col < d_in)) st128(W + (int64_t)row * d_in + col, v);
+        }
+    };
+
+    u32x4 av[4][NSTAGE];
+    u32x4 wA[4], wB[4];
+    load_a(av, 0);
+    load_w(wA, 0);
+    if (nsb > 1) load_w(wB, 1);
+    store_a(av, As);
+    __syncthreads();
+    // sub-bands in pairs so each W buffer keeps its role (no register copies)
+#pragma unroll 1
+    for (int sb = 0; sb < nsb; sb += 2) {
+        if (sb + 1 < nsb) load_a(av, sb + 1);
+        unit(wA, sb);
+        if (sb + 1 < nsb) store_a(av, As + ((sb + 1) & 1) * BUF_ELEMS);
+        __syncthreads();
+        if (sb + 1 < nsb) {
+            if (sb + 2 < nsb) load_a(av, sb + 2);
+            unit(wB, sb + 1);
+            if (sb + 2 < nsb) store_a(av, As + ((sb + 2) & 1) * BUF_ELEMS);
+            __syncthreads();
+        }
+    }
+}
+
+template <int R16, int NSB>
+__global__ __launch_bounds__(kWW* kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void switch_wide_kernel(SwitchArgs a) {
+    // 2 x [4 slots][2][32][R16*16] A slices, then 8 x [32][64] W scratch
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint16_t* As = smem;
+    uint16_t* Ws = smem + 2 * 4 * 2 * 32 * (R16 * 16);
+    const int64_t bid = blockIdx.x;
+    const int64_t t = (bid & 7) * a.per_xcd + (bid >> 3);
+    if (t >= a.n_units) return;
+    const Sets sc = read_sets(a);
+    if (!sc.ok) {
+        if (t == 0 && threadIdx.x == 0) *a.err = 1;
+        return;
+    }
+    const SwDesc D = a.descs[find_desc<true>(a.descs, a.n_desc, t)];
+    // groups of kWGroup row bands; inside a group, column band by column band
+    const int64_t local = t - D.tile0;
+    const int64_t per_group = (int64_t)kWGroup * D.n_ct;
+    const int grp = (int)(local / per_group);
+    const int in_grp = D.n_rt - grp * kWGroup < kWGroup ? D.n_rt - grp * kWGroup : kWGroup;
+    const int64_t lg = local - grp * per_group;
+    const int rt = grp * kWGroup + (int)(lg % in_grp), ct = (int)(lg / in_grp);
+    const int row_base = rt * kWRT, col_base = ct * (64 * NSB);
+    const bool full = row_base + kWRT <= D.d_out && col_base + 64 * NSB <= D.d_in && a.r == R16 * 16;
+    if (full)
+        switch_wide_tile<R16, NSB, true>(a, sc, D, row_base, col_base, As, Ws);
+    else
+        switch_wide_tile<R16, NSB, false>(a, sc, D, row_base, col_base, As, Ws);
+}
+
 // ---- element-wise path: fp32 weights (and any shape) ----------------------
 
 template <typename T> __device__ __forceinline__ float ldf(const T* p, int64_t i);
@@ -386,12 +607,25 @@ hipError_t launch_r(const SwitchArgs& a, hipStream_t s) {
 
 }  // namespace
 
+template <int R16>
+hipError_t launch_wide(const SwitchArgs& a, hipStream_t s) {
+    const size_t lds = ((size_t)2 * 4 * 2 * 32 * (R16 * 16) + (size_t)kWW * 32 * 64) * sizeof(uint16_t);
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)switch_wide_kernel<R16, kWideSB>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t grid = 8 * a.per_xcd;
+    hipLaunchKernelGGL((switch_wide_kernel<R16, kWideSB>), dim3((unsigned)grid), dim3(kWW * kWave), lds, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_switch_bf16(const SwitchArgs& a, const SwTile& t, hipStream_t s) {
     switch (t.r16) {
         case 1: return launch_r<1, 256>(a, s);
-        case 2: return launch_r<2, 128>(a, s);
-        case 3: return launch_r<3, 64>(a, s);
-        case 4: return launch_r<4, 64>(a, s);
+        case 2: return launch_wide<2>(a, s);
+        case 3: return launch_wide<3>(a, s);
+        case 4: return launch_wide<4>(a, s);
         case 5: return launch_r<5, 64>(a, s);
         case 6: return launch_r<6, 64>(a, s);
         case 7: return launch_r<7, 64>(a, s);

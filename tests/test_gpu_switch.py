@@ -47,6 +47,10 @@ CASES = [
     ([(130, 96)], 8, 8, 1.5, torch.bfloat16),
     ([(96, 200), (520, 128)], 8, 24, 1.0, torch.bfloat16),             # r not a multiple of 16
     ([(200, 136), (64, 64)], 16, 64, 1.0, torch.bfloat16),             # 70B rank
+    ([(512, 1024), (300, 1000), (256, 520)], 16, 64, 1.0, torch.bfloat16),  # wide tiles: full, ragged
+    ([(520, 1536), (64, 576)], 8, 32, 2.0, torch.bfloat16),            # rank 32: odd sub-band count
+    ([(257, 640), (768, 512)], 8, 48, 1.0, torch.bfloat16),            # rank 48
+    ([(300, 1096), (16, 1032)], 4, 40, 1.0, torch.bfloat16),           # rank 40: padded ranks, d_in % 64
     ([(40, 64)], 2, 128, 0.5, torch.bfloat16),                         # largest rank
     ([(33, 64)], 32, 16, 1.0, torch.bfloat16),                         # most experts
 ]
