@@ -259,24 +259,33 @@ def cpu_baseline(torch, synth, target_s, log):
 
 def profile_kernels(torch, dlm, synth, n_switch, log):
     """A short run for hardware-counter collection: the router on the 256 tokens,
-    `n_switch` fused switches of the 7B-shaped workload, then one 1 GiB device
-    copy (torch) whose byte count calibrates the FETCH_SIZE/WRITE_SIZE counters."""
-    wl = synth.WORKLOADS["7b-decode"]
-    model = synth.switch_model(wl)
-    x, Wr = synth.router_inputs(wl)
-    L = dlm.Layers([(W, A, B) for _, _, W, A, B in model], wl.E, wl.r, wl.scale)
-    idx, g = dlm.pregate(x, Wr)
-    L.switch(None, (idx[0], g[0]))
-    for t in range(1, n_switch):
-        L.switch((idx[t - 1], g[t - 1]), (idx[t], g[t]))
-    torch.cuda.synchronize()
+    `n_switch` fused switches of the 7B-shaped workload, `n_switch` of the
+    70B-shaped one (when it fits), then one 1 GiB device copy (torch) whose byte
+    count calibrates the FETCH_SIZE/WRITE_SIZE counters."""
+    for name in ("7b-decode", "70b-decode"):
+        wl = synth.WORKLOADS[name]
+        free, _ = torch.cuda.mem_get_info()
+        if free < wl.switch_w_elems() * 2 * 1.25:
+            log(f"{name} skipped (memory)")
+            continue
+        model = synth.switch_model(wl)
+        x, Wr = synth.router_inputs(wl)
+        L = dlm.Layers([(W, A, B) for _, _, W, A, B in model], wl.E, wl.r, wl.scale)
+        idx, g = dlm.pregate(x, Wr)
+        L.switch(None, (idx[0], g[0]))
+        for t in range(1, n_switch):
+            L.switch((idx[t - 1], g[t - 1]), (idx[t], g[t]))
+        torch.cuda.synchronize()
+        L.close()
+        del model
+        torch.cuda.empty_cache()
     src = torch.empty(2 ** 29, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1.0)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"profiled {n_switch} switches and one copy of {src.numel() * 2} bytes")
+    log(f"profiled {n_switch} switches per workload and one copy of {src.numel() * 2} bytes")
 
 
 def traffic_from(fetch_csv, write_csv, log):
@@ -286,7 +295,7 @@ def traffic_from(fetch_csv, write_csv, log):
     written to profiles/traffic.json with a hash of the kernel source."""
     import csv
 
-    def read(path, counter):
+    def read(path, counter, kernel):
         sw, cp = [], []
         with open(path) as f:
             for row in csv.DictReader(f):
@@ -294,25 +303,34 @@ def traffic_from(fetch_csv, write_csv, log):
                     continue
                 name = row.get("Kernel_Name", "")
                 v = float(row["Counter_Value"])
-                if "switch_bf16_kernel" in name:
+                if kernel in name:
                     sw.append(v)
                 elif "copy" in name.lower() and "dlm" not in name:
                     cp.append(v)
         return sw, cp
-    out = {}
-    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
-        sw, cp = read(path, counter)
-        copy_kib = max(cp)  # the 1 GiB copy is the largest copy dispatch
-        factor = (2 ** 30 / 1024) / copy_kib
-        out[key] = {"switch_kib_per_launch": sum(sw) / len(sw), "launches": len(sw),
-                    "copy_kib": copy_kib, "scale": factor,
-                    "bytes_per_launch": sum(sw) / len(sw) * 1024 * factor}
-    res = {"switch_bf16_7b": {
-        "source_hash": _src_hash(SWITCH_SOURCES),
-        "bytes_per_launch": out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"],
-        "fetch": out["fetch"], "write": out["write"],
-        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
-                   "python3 bench.py --profile-kernels"}}
+    res = {}
+    # the 7B-shaped switch (rank 16) runs switch_bf16_kernel, the 70B-shaped one
+    # (rank 64) the wide-tile kernel
+    for key, kernel, wl_name in (("switch_bf16_7b", "switch_bf16_kernel", "7b-decode"),
+                                 ("switch_bf16_70b", "switch_wide_kernel", "70b-decode")):
+        out = {}
+        for part, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+            sw, cp = read(path, counter, kernel)
+            if not sw:
+                break
+            copy_kib = max(cp)  # the 1 GiB copy is the largest copy dispatch
+            factor = (2 ** 30 / 1024) / copy_kib
+            out[part] = {"switch_kib_per_launch": sum(sw) / len(sw), "launches": len(sw),
+                         "copy_kib": copy_kib, "scale": factor,
+                         "bytes_per_launch": sum(sw) / len(sw) * 1024 * factor}
+        if len(out) < 2:
+            continue
+        res[key] = {
+            "source_hash": _src_hash(SWITCH_SOURCES), "workload": wl_name,
+            "bytes_per_launch": out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"],
+            "fetch": out["fetch"], "write": out["write"],
+            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                       "python3 bench.py --profile-kernels"}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
@@ -362,6 +380,8 @@ def main():
     sw70 = None
     if not args.no_70b:
         sw70 = bench_switch_70b(torch, dlm, synth, args.switch_70b_launches, log)
+        if sw70 is not None:
+            sw70["traffic"] = _traffic("switch_bf16_70b", sw70["algo_bytes_per_launch"])
         log(f"switch 70b: {sw70}")
     sg = {}
     if not args.no_sgmm:
