@@ -220,9 +220,10 @@ __device__ __forceinline__ void switch_tile(const SwitchArgs& a, const Sets& sc,
     load_w(wcur, 0);
 
     // 2) transpose the A slices into LDS: As[slot][cb][m][rho] = A[e][rho][col(cb, m)]
+    //    (an inactive slot's slice too: its loads gave zeros, so the MFMAs below
+    //    need no per-slot branch)
 #pragma unroll
     for (int slot = 0; slot < 4; ++slot) {
-        if (!act[slot]) continue;
         uint16_t* dst_slot = As + slot * SLOT_ELEMS;
 #pragma unroll
         for (int i = 0; i < NSTAGE; ++i) {
@@ -258,16 +259,19 @@ __device__ __forceinline__ void switch_tile(const SwitchArgs& a, const Sets& sc,
             u32x4 wm[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) wm[q] = *(const u32x4*)(ws + w_off(n, 4 * b + 2 * h + q));
-            f32x16 P[4];
+            // rank chunk outermost: the four slots' MFMAs of a chunk are
+            // independent and issue back to back; each slot sums its chunks in
+            // order (an inactive slot multiplies zeros)
+            f32x16 P[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+            const uint16_t* ap = As + (sub * 2 + b) * 32 * RPAD + n * RPAD;
 #pragma unroll
-            for (int slot = 0; slot < 4; ++slot) {
-                P[slot] = f32x16{};
-                if (!act[slot]) continue;
-                const uint16_t* ap = As + slot * SLOT_ELEMS + (sub * 2 + b) * 32 * RPAD + n * RPAD;
+            for (int ks = 0; ks < R16; ++ks) {
+                u32x4 ao[4];
 #pragma unroll
-                for (int ks = 0; ks < R16; ++ks)
-                    P[slot] = mfma32(*(const u32x4*)(ap + (a_chunk_swz<R16>(n, 2 * ks + h) << 3)),
-                                     bcur[slot][ks], P[slot]);
+                for (int slot = 0; slot < 4; ++slot)
+                    ao[slot] = *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, 2 * ks + h) << 3));
+#pragma unroll
+                for (int slot = 0; slot < 4; ++slot) P[slot] = mfma32(ao[slot], bcur[slot][ks], P[slot]);
             }
             if (b == 1 && u + 1 < U && (u + 1) % NSUB == 0) load_b(bcur, (u + 1) / NSUB);
             uint32_t ow[8];
@@ -381,23 +385,33 @@ __device__ __forceinline__ void switch_wide_tile(const SwitchArgs& a, const Sets
                 av[slot][i] = ok ? ld128(Ab + ((int64_t)sc.e[slot] * r + rho) * d_in + col) : zero;
             }
     };
+    // LDS element offsets of this thread's 8 transposed writes: the same for
+    // every sub-band, slot and buffer (those add constants)
+    int aoff[NSTAGE][8];
+#pragma unroll
+    for (int i = 0; i < NSTAGE; ++i) {
+        const int q = tid + i * kWW * kWave;
+        const int rho = q / 8, ch = q % 8, cc0 = (ch & 3) * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int m = perm_row(cc0 + j);
+            aoff[i][j] = (ch >> 2) * 32 * RPAD + (rho & 7) + m * RPAD + (a_chunk_swz<R16>(m, rho >> 3) << 3);
+        }
+    }
     auto store_a = [&](const u32x4 (&av)[4][NSTAGE], uint16_t* buf) {
 #pragma unroll
         for (int slot = 0; slot < 4; ++slot) {
-            if (!act[slot]) continue;
+            // an inactive slot's slice is written too (its loads gave zeros), so
+            // the MFMAs below need no per-slot branch
 #pragma unroll
             for (int i = 0; i < NSTAGE; ++i) {
                 const int q = tid + i * kWW * kWave;
                 if (NQ % (kWW * kWave) != 0 && q >= NQ) continue;
-                const int rho = q / 8, ch = q % 8;
-                uint16_t* dst = buf + slot * SLOT_ELEMS + (ch >> 2) * 32 * RPAD + (rho & 7);
-                const int cc0 = (ch & 3) * 8;
+                uint16_t* dst = buf + slot * SLOT_ELEMS;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int m = perm_row(cc0 + j);
                     const uint32_t word = av[slot][i][j >> 1];
-                    dst[m * RPAD + (a_chunk_swz<R16>(m, rho >> 3) << 3)] =
-                        (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
+                    dst[aoff[i][j]] = (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
                 }
             }
         }
@@ -452,16 +466,19 @@ __device__ __forceinline__ void switch_wide_tile(const SwitchArgs& a, const Sets
             u32x4 wm[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) wm[q] = *(const u32x4*)(ws + w_off(n, 4 * b + 2 * h + q));
-            f32x16 P[4];
+            // rank chunk outermost: the four slots' MFMAs of a chunk are
+            // independent, so they issue back to back; each slot still sums its
+            // chunks in order (an inactive slot multiplies zeros)
+            f32x16 P[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+            const uint16_t* ap = Acur + b * 32 * RPAD + n * RPAD;
 #pragma unroll
-            for (int slot = 0; slot < 4; ++slot) {
-                P[slot] = f32x16{};
-                if (!act[slot]) continue;
-                const uint16_t* ap = Acur + slot * SLOT_ELEMS + b * 32 * RPAD + n * RPAD;
+            for (int ks = 0; ks < R16; ++ks) {
+                u32x4 ao[4];
 #pragma unroll
-                for (int ks = 0; ks < R16; ++ks)
-                    P[slot] = mfma32(*(const u32x4*)(ap + (a_chunk_swz<R16>(n, 2 * ks + h) << 3)),
-                                     bcur[slot][ks], P[slot]);
+                for (int slot = 0; slot < 4; ++slot)
+                    ao[slot] = *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, 2 * ks + h) << 3));
+#pragma unroll
+                for (int slot = 0; slot < 4; ++slot) P[slot] = mfma32(ao[slot], bcur[slot][ks], P[slot]);
             }
             uint32_t ow[8];
 #pragma unroll
