@@ -548,7 +548,7 @@ static_assert(kECols == kSgmmExpandCols, "expand column group");
 // unions rebuild them per column block in registers.
 constexpr int kQLds = 16;
 
-template <int R16>
+template <int R16, bool RVEC>
 __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_xcd) {
     constexpr int RPAD = R16 * 16;
     const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
@@ -648,15 +648,17 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
         blo = u32x4{lw[0], lw[1], lw[2], lw[3]};
     };
     // column-side operand: B[e][col][16(q % R16) + 8h .. +8]; padding columns
-    // read column 0 and are never stored
-    const bool r_vec = (r & 7) == 0;
+    // read column 0 and are never stored.  With r % 8 == 0 (RVEC) the load is
+    // one unguarded 16-byte access (a rank chunk past r reads rank 0 and is
+    // replaced by zero), so the loads of consecutive q stay in flight together.
     auto load_bop = [&](int q, int col) {
         const int e = s_U[q / R16];
         const int rho0 = (q % R16) * 16 + 8 * h;
         const uint16_t* bp = B + ((int64_t)e * d_out + (col < d_out ? col : 0)) * r + rho0;
         u32x4 ao = {0u, 0u, 0u, 0u};
-        if (r_vec) {
-            if (rho0 < r) ao = ld128(bp);
+        if constexpr (RVEC) {
+            const u32x4 t = ld128(bp - (rho0 < r ? 0 : rho0));
+            ao = rho0 < r ? t : ao;
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -685,13 +687,27 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
         for (int b = 0; b < 2; ++b) ocol[b] = c0b + 32 * b + perm_col(n);
         f32x16 acc[2] = {f32x16{}, f32x16{}};
         if (shared_u) {
-            for (int q = 0; q < nq; ++q) {
-                const u32x4 uh = s_u[q][0][lane], ul = s_u[q][1][lane];
+            // q in groups of four: the group's B operands are all loaded before
+            // its MFMAs (q past nq re-reads q = nq - 1 and is skipped); each acc
+            // still sums q in order
+            for (int q0 = 0; q0 < nq; q0 += 4) {
+                u32x4 bo[4][2];
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    const u32x4 ao = load_bop(q, ocol[b]);
-                    acc[b] = mfma32(ao, uh, acc[b]);
-                    acc[b] = mfma32(ao, ul, acc[b]);
+                for (int j = 0; j < 4; ++j) {
+                    const int qj = q0 + j < nq ? q0 + j : nq - 1;
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) bo[j][b] = load_bop(qj, ocol[b]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (q0 + j >= nq) break;
+                    const u32x4 uh = s_u[q0 + j][0][lane], ul = s_u[q0 + j][1][lane];
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        acc[b] = mfma32(bo[j][b], uh, acc[b]);
+                        acc[b] = mfma32(bo[j][b], ul, acc[b]);
+                    }
                 }
             }
         } else {
@@ -867,8 +883,12 @@ hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     const int64_t per_xcd = (a.n_expand_units + 7) / 8;
-    hipLaunchKernelGGL((sgmm_expand_bf16<R16>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, a,
-                       per_xcd);
+    if (a.r % 8 == 0)
+        hipLaunchKernelGGL((sgmm_expand_bf16<R16, true>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, a,
+                           per_xcd);
+    else
+        hipLaunchKernelGGL((sgmm_expand_bf16<R16, false>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, a,
+                           per_xcd);
     return hipGetLastError();
 }
 
