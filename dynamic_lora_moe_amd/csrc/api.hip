@@ -66,7 +66,9 @@ struct dlm_layers {
 };
 
 struct dlm_sgmm_group {
-    SgDesc* d_descs = nullptr;
+    SgDesc* d_descs = nullptr;          // device block: descriptors, then the owner tables
+    const int32_t* d_ks_owner = nullptr;
+    const int32_t* d_cb_owner = nullptr;
     std::vector<SgDesc> h_descs;
     int32_t n = 0;
     int32_t E = 0, r = 0;
@@ -260,11 +262,14 @@ int check_ws(void* ws, size_t ws_bytes, const SgLayout& L) {
     return DLM_OK;
 }
 
-int run_sgmm(const SgDesc* d_descs, const SgDesc& single, int n_prob, int64_t total_cb,
+int run_sgmm(const SgDesc* d_descs, const int32_t* ks_owner, const int32_t* cb_owner,
+             const SgDesc& single, int n_prob, int64_t total_cb,
              int64_t total_ks, int64_t d_out_max, const int32_t* idx, const float* g, int64_t T, int E, int r,
              float scale, int dtype, int packed, void* ws, const SgLayout& L, hipStream_t s) {
     SgmmArgs a;
     a.descs = d_descs;
+    a.ks_owner = ks_owner;
+    a.cb_owner = cb_owner;
     a.packed = packed;
     a.single = single;
     a.n_prob = n_prob;
@@ -317,7 +322,7 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, c
     d.unit0 = 0;
     d.n_ks = (int32_t)((d_in + kSgmmKSlice - 1) / kSgmmKSlice);
     d.ks0 = 0;
-    return run_sgmm(nullptr, d, 1, d.n_cb, d.n_ks, d_out, idx, g, T, E, r, scale, dtype, 0, workspace, L,
+    return run_sgmm(nullptr, nullptr, nullptr, d, 1, d.n_cb, d.n_ks, d_out, idx, g, T, E, r, scale, dtype, 0, workspace, L,
                     (hipStream_t)stream);
 }
 
@@ -386,14 +391,29 @@ int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, i
         }
         if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
     }
-    if (e == hipSuccess) e = hipMalloc((void**)&h->d_descs, sizeof(SgDesc) * n);
-    if (e == hipSuccess) e = hipMemcpy(h->d_descs, h->h_descs.data(), sizeof(SgDesc) * n, hipMemcpyHostToDevice);
+    // one device block: the descriptors, then the owner of every K slice and of
+    // every expand column group (work items find their problem with one load)
+    const size_t desc_bytes = (sizeof(SgDesc) * n + 255) & ~(size_t)255;
+    const size_t ks_bytes = ((size_t)ks * 4 + 255) & ~(size_t)255;
+    std::vector<char> blob(desc_bytes + ks_bytes + (size_t)cb * 4);
+    std::memcpy(blob.data(), h->h_descs.data(), sizeof(SgDesc) * n);
+    int32_t* ks_owner = (int32_t*)(blob.data() + desc_bytes);
+    int32_t* cb_owner = (int32_t*)(blob.data() + desc_bytes + ks_bytes);
+    for (int i = 0; i < n; ++i) {
+        const SgDesc& d = h->h_descs[i];
+        for (int k = 0; k < d.n_ks; ++k) ks_owner[d.ks0 + k] = i;
+        for (int k = 0; k < d.n_cb; ++k) cb_owner[d.unit0 + k] = i;
+    }
+    if (e == hipSuccess) e = hipMalloc((void**)&h->d_descs, blob.size());
+    if (e == hipSuccess) e = hipMemcpy(h->d_descs, blob.data(), blob.size(), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         if (h->d_descs) (void)hipFree(h->d_descs);
         for (auto& pk : h->packs) (void)hipFree(pk.Ap);
         delete h;
         return hip_fail(e, "sgmm_group_create");
     }
+    h->d_ks_owner = (const int32_t*)((const char*)h->d_descs + desc_bytes);
+    h->d_cb_owner = (const int32_t*)((const char*)h->d_descs + desc_bytes + ks_bytes);
     *out = h;
     return ok();
 }
@@ -432,7 +452,7 @@ int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, in
     const SgLayout L = sgmm_layout(T, h->d_in_max, h->E, h->r, h->n);
     const int rc = check_ws(workspace, ws_bytes, L);
     if (rc != DLM_OK) return rc;
-    return run_sgmm(h->d_descs, h->h_descs[0], h->n, h->total_cb, h->total_ks, h->d_out_max, idx, g, T, h->E,
+    return run_sgmm(h->d_descs, h->d_ks_owner, h->d_cb_owner, h->h_descs[0], h->n, h->total_cb, h->total_ks, h->d_out_max, idx, g, T, h->E,
                     h->r, h->scale, h->dtype, h->packs.empty() ? 0 : 1, workspace, L, (hipStream_t)stream);
 }
 

@@ -294,19 +294,6 @@ __device__ __forceinline__ int mask_list(uint32_t m, int* out) {
     return n;
 }
 
-// Problem owning unit u of a prefix-summed per-problem count (last d with d.F <= u).
-template <int64_t SgDesc::*F>
-__device__ __forceinline__ int find_prob(const SgDesc* __restrict__ d, int n, int64_t u) {
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (d[mid].*F <= u) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-__device__ __forceinline__ int find_prob_ks(const SgDesc* d, int n, int64_t u) { return find_prob<&SgDesc::ks0>(d, n, u); }
-__device__ __forceinline__ int find_prob_cb(const SgDesc* d, int n, int64_t u) { return find_prob<&SgDesc::unit0>(d, n, u); }
-
 // ---- shrink (bf16, MFMA) -----------------------------------------------------
 
 // Tiles per shrink work item: every A operand feeds one MFMA per tile.
@@ -351,7 +338,7 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     const int tile0 = (int)(t - gks * ntp) * kTM;
     const int n_tiles = gld(hdr + SG_NTILES);
     if (tile0 >= n_tiles) return;
-    const int prob = a.descs ? find_prob_ks(a.descs, a.n_prob, gks) : 0;
+    const int prob = a.descs ? gld(a.ks_owner + gks) : 0;
     const SgDesc D = a.descs ? a.descs[prob] : a.single;
     const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
@@ -559,7 +546,7 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     // work item = (problem, kECols-column group, tile) with the tile fastest:
     // neighbouring work items (same XCD) reuse the same B column slices
     const int64_t nt = a.L.tiles_max;
-    const int prob = a.descs ? find_prob_cb(a.descs, a.n_prob, t / nt) : 0;
+    const int prob = a.descs ? gld(a.cb_owner + t / nt) : 0;
     const SgDesc D = a.descs ? a.descs[prob] : a.single;
     const int64_t local = t - D.unit0 * nt;
     const int cg = (int)(local / nt);

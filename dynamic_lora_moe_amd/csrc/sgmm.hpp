@@ -44,6 +44,8 @@ enum { SG_ERR = 0, SG_NPOS = 1, SG_NTILES = 2 };
 
 struct SgmmArgs {
     const SgDesc* descs;   // device table, or nullptr to use `single`
+    const int32_t* ks_owner;  // problem of each K slice (device; with descs)
+    const int32_t* cb_owner;  // problem of each expand column group (device; with descs)
     SgDesc single;
     int32_t n_prob;
     int64_t n_expand_units;  // tiles_max * total_cb
