@@ -220,10 +220,66 @@ def bench_sgmm(torch, dlm, synth, name, reps, log):
         nbytes += per_step + wl.T * 16
     res = {"tokens_per_s": tokens / sec, "ms_per_pass": sec * 1e3, "GBps": nbytes / sec / 1e9,
            "frac_of_hbm_peak": nbytes / sec / HBM_PEAK, "algo_bytes_per_pass": nbytes}
+    if name == "mixed-decode":
+        res.update(_per_layer_variant(torch, dlm, wl, probs, sets, reps, sec, log))
     grp.close()
     del probs
     torch.cuda.empty_cache()
     return res
+
+
+def _per_layer_variant(torch, dlm, wl, probs, sets, reps, sec_grouped, log):
+    """The mixed decode step as one group per layer (7 projections each): one
+    segmentation per layer, 4 launches per layer, run eagerly and replayed from a
+    HIP graph captured once (the step's sets are copied into the graph's static
+    input buffers before each replay).  Beside the grouped call, whose single
+    segmentation serves all layers (4 launches per step)."""
+    layers = sorted({l for l, *_ in probs})
+    per = [dlm.SgmmGroup([(x, A, B, y) for l2, _, x, A, B, y in probs if l2 == l], wl.E, wl.r, wl.scale)
+           for l in layers]
+    wsl = [gp.workspace(wl.T) for gp in per]
+
+    def step(i, gg, stream=None):
+        for gp, w in zip(per, wsl):
+            gp.run(i, gg, workspace=w, stream=stream)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps / len(sets)
+
+    eager = timed(lambda: [step(i, gg) for i, gg in sets])
+    idx_s = torch.zeros_like(sets[0][0])
+    g_s = torch.zeros_like(sets[0][1])
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(idx_s, g_s, stream=side)
+    torch.cuda.synchronize()
+
+    def replay_all():
+        for i, gg in sets:
+            idx_s.copy_(i)
+            g_s.copy_(gg)
+            graph.replay()
+
+    graphed = timed(replay_all)
+    for w in wsl:
+        assert dlm.sgmm_status(w) == dlm.DLM_OK
+    for gp in per:
+        gp.close()
+    log(f"mixed decode per layer: eager {eager * 1e3:.3f} ms/step, graph {graphed * 1e3:.3f} ms/step")
+    return {"launches_per_step_grouped": 4, "launches_per_step_per_layer": 4 * len(layers),
+            "per_layer_eager_ms_per_step": eager * 1e3, "per_layer_graph_ms_per_step": graphed * 1e3,
+            "grouped_ms_per_step": sec_grouped * 1e3 / len(sets)}
 
 
 def cpu_baseline(torch, synth, target_s, log):

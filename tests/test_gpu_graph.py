@@ -1,0 +1,128 @@
+"""The hot path captured in a HIP graph (torch.cuda.CUDAGraph over the library's
+launches on the capturing stream): every replay must give the same bits as the
+same calls made eagerly.  Replays run several times in a row, with eager work,
+synchronisations and new input sets between them (the sets live in static
+device buffers the graph reads)."""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_lora_moe_amd as dlm
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _sets(T, E, rng):
+    idx = np.full((T, 2), -1, np.int32)
+    g = np.zeros((T, 2), np.float32)
+    for t in range(T):
+        k = rng.integers(1, 3)
+        e = rng.choice(E, size=k, replace=False)
+        idx[t, :k] = e
+        w = rng.random(k).astype(np.float32)
+        g[t, :k] = w / w.sum()
+    return torch.from_numpy(idx), torch.from_numpy(g)
+
+
+def test_switch_graph_replays_match_eager():
+    shapes = [(256, 512), (300, 264), (1024, 1024)]
+    E, r, scale = 8, 16, 2.0
+    model = []
+    for i, (o, n) in enumerate(shapes):
+        model.append((synth.normal_device((o, n), 0.02, torch.bfloat16, "cuda", 5000, "W", i),
+                      synth.normal_device((E, r, n), 0.02, torch.bfloat16, "cuda", 5000, "A", i),
+                      synth.normal_device((E, o, r), 0.02, torch.bfloat16, "cuda", 5000, "B", i)))
+    W0 = [W.clone() for W, _, _ in model]
+    L = dlm.Layers(model, E, r, scale)
+    old_i = torch.zeros(2, dtype=torch.int32, device="cuda")
+    old_g = torch.zeros(2, dtype=torch.float32, device="cuda")
+    new_i = torch.zeros(2, dtype=torch.int32, device="cuda")
+    new_g = torch.zeros(2, dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(3)
+
+    def draw():
+        e = rng.choice(E, size=4, replace=False)
+        w = rng.random(4).astype(np.float32)
+        return ((e[:2].tolist(), (w[:2] / w[:2].sum()).tolist()), (e[2:].tolist(), (w[2:] / w[2:].sum()).tolist()))
+
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            L.switch((old_i, old_g), (new_i, new_g), stream=s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        old, new = draw()
+        for (W, _, _), w0 in zip(model, W0):
+            W.copy_(w0)
+        old_i.copy_(torch.tensor(old[0], dtype=torch.int32))
+        old_g.copy_(torch.tensor(old[1], dtype=torch.float32))
+        new_i.copy_(torch.tensor(new[0], dtype=torch.int32))
+        new_g.copy_(torch.tensor(new[1], dtype=torch.float32))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [W.clone() for W, _, _ in model]
+        for (W, _, _), w0 in zip(model, W0):
+            W.copy_(w0)
+        L.switch((old_i, old_g), (new_i, new_g))
+        torch.cuda.synchronize()
+        for k, ((W, _, _), gw) in enumerate(zip(model, got)):
+            assert torch.equal(W, gw), (rep, k)
+    assert L.status() == dlm.DLM_OK
+    L.close()
+
+
+def test_sgmm_per_layer_groups_in_graph_match_grouped_eager():
+    """Per-layer groups (one segmentation per layer) captured in one graph give
+    the same bits as one group over all layers run eagerly: the rows and their
+    sets, hence tiles and unions, are the same for every layer."""
+    T, E, r, layers = 64, 8, 16, 4
+    shapes = [(256, 256), (512, 256), (256, 512)]
+    probs = []
+    for l in range(layers):
+        for p, (n, o) in enumerate(shapes):
+            key = (6000, l, p)
+            probs.append((synth.normal_device((T, n), 1.0, torch.bfloat16, "cuda", *key, "x"),
+                          synth.normal_device((E, r, n), 0.02, torch.bfloat16, "cuda", *key, "A"),
+                          synth.normal_device((E, o, r), 0.02, torch.bfloat16, "cuda", *key, "B"),
+                          synth.normal_device((T, o), 0.3, torch.bfloat16, "cuda", *key, "y")))
+    y0 = [p[3].clone() for p in probs]
+    per_layer = [dlm.SgmmGroup(probs[l * len(shapes):(l + 1) * len(shapes)], E, r, 1.0)
+                 for l in range(layers)]
+    ws = [grp.workspace(T) for grp in per_layer]
+    whole = dlm.SgmmGroup(probs, E, r, 1.0)
+    ws_whole = whole.workspace(T)
+    idx_s = torch.zeros(T, 2, dtype=torch.int32, device="cuda")
+    g_s = torch.zeros(T, 2, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for grp, w in zip(per_layer, ws):
+                grp.run(idx_s, g_s, T, workspace=w, stream=s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    for rep in range(4):
+        idx, g = _sets(T, E, rng)
+        idx_s.copy_(idx)
+        g_s.copy_(g)
+        for (_, _, _, y), y00 in zip(probs, y0):
+            y.copy_(y00)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [p[3].clone() for p in probs]
+        for (_, _, _, y), y00 in zip(probs, y0):
+            y.copy_(y00)
+        whole.run(idx_s, g_s, T, workspace=ws_whole)
+        torch.cuda.synchronize()
+        for k, (p, gy) in enumerate(zip(probs, got)):
+            assert torch.equal(p[3], gy), (rep, k)
+        assert all(dlm.sgmm_status(w) == dlm.DLM_OK for w in ws)
+    for grp in per_layer:
+        grp.close()
+    whole.close()
