@@ -12,11 +12,11 @@
 //            rows use (a bitmask).  Rows with two empty slots are left out.
 //            The same segmentation serves every problem of a grouped call
 //            (one routing decision per token for all layers).
-//   shrink   per (problem, 1024-wide K slice, tile): the slice's partial
+//   shrink   per (problem, 512-wide K slice, tile): the slice's partial
 //            v = x_rows A_U^T for the tile's experts U, bf16 MFMA 32x32x16 with
 //            M = tile rows (gathered through perm, staged in LDS), N = (expert,
 //            rank); each row keeps the fp32 partial v of its own two slots.
-//   sum      (problems with d_in > 1024) the slices' partials added in slice
+//   sum      (problems with d_in > 512) the slices' partials added in slice
 //            order.
 //   expand   per (problem, 1024 output columns, tile): y_rows += u B_U^T with
 //            u = s*g*v per (row, expert, rank).  u stays fp32-accurate by
@@ -302,7 +302,12 @@ constexpr int kXRows = 32 * kTM;
 // 64-wide K chunks of one slice, and 16-byte chunks of one x row of a slice
 constexpr int kKC = kSgmmKSlice / 64;
 constexpr int kXC = kSgmmKSlice / 8;
-static_assert(kKC >= 4 && kKC % 4 == 0, "slice is a whole number of 256-wide steps");
+// A chunks in flight per wave in the shrink's K loop.  The shrink runs at 3
+// waves per SIMD (three workgroups per CU, each with a 32 KB x slice):
+// measured on the 4096-token prefill 114 us with 1024-wide slices, a 4-chunk
+// ring and 2 waves per SIMD, 100 us like this.
+constexpr int kShrinkRing = 2;
+static_assert(kKC >= kShrinkRing && kKC % kShrinkRing == 0, "slice is a whole number of ring steps");
 static_assert(256 % kXC == 0 && kXRows % (256 / kXC) == 0, "x slice load shape");
 // x slice in LDS: kXRows rows of kSgmmKSlice bf16; the 16-byte chunk c of row m
 // is stored at chunk c ^ (m & 15), so the MFMA-layout reads (16 rows, one chunk)
@@ -325,7 +330,7 @@ __device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((c
 // dummy row whose products reach only accumulator entries that are never
 // stored, and k past d_in reads a clamped address whose value is replaced by 0.
 template <int R16, bool PK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     constexpr int RPAD = R16 * 16;
     const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
@@ -441,12 +446,12 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     };
 
     // first block's A: its first chunks are in flight while x lands in LDS
-    u32x4 ab[4][4];
+    u32x4 ab[kShrinkRing][4];
     int u, rho;
     const uint16_t* arow = a_row(gw, u, rho);
     const bool act = kp < P;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kShrinkRing; ++j)
         if (act && j < nmy) load_a(ab[j], arow, kp + P * j);
 
 #pragma unroll
@@ -459,12 +464,12 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     // K loop of one block over this wave's chunks, A up to four chunks ahead
     auto run_block = [&](f32x16 (&acc)[kTM]) {
 #pragma unroll 1
-        for (int i = 0; i < nmy; i += 4) {
+        for (int i = 0; i < nmy; i += kShrinkRing) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kShrinkRing; ++j) {
                 if (i + j < nmy) {
                     mma(ab[j], kp + P * (i + j), acc);
-                    if (i + j + 4 < nmy) load_a(ab[j], arow, kp + P * (i + j + 4));
+                    if (i + j + kShrinkRing < nmy) load_a(ab[j], arow, kp + P * (i + j + kShrinkRing));
                 }
             }
         }
@@ -476,7 +481,7 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
             if (blk != gw) {
                 arow = a_row(blk, u, rho);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < kShrinkRing; ++j)
                     if (j < nmy) load_a(ab[j], arow, j);
             }
             f32x16 acc[kTM];

@@ -33,7 +33,7 @@ struct SgLayout {
     int max_ks;  // K slices of the widest problem
 };
 // Width of one shrink K slice.
-constexpr int kSgmmKSlice = 1024;
+constexpr int kSgmmKSlice = 512;
 SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob);
 
 // Output columns one SGMM expand work item covers (4 waves x 4 x 64).

@@ -97,9 +97,9 @@ def test_switch_and_status_validation(lib):
 def test_sgmm_workspace_size(lib):
     b = C.c_size_t(0)
     assert lib.dlm_sgmm_workspace_size(4096, 11008, 8, 16, 7, C.byref(b)) == dlm.DLM_OK
-    # the shrink's partial results dominate: 7 problems x 11 K slices of 1024 x
+    # the shrink's partial results dominate: 7 problems x 22 K slices of 512 x
     # 4096 rows x 2 slots x 16 x 4 bytes
-    assert b.value >= 7 * 11 * 4096 * 2 * 16 * 4
+    assert b.value >= 7 * 22 * 4096 * 2 * 16 * 4
     assert b.value % 256 == 0
     one = C.c_size_t(0)
     assert lib.dlm_sgmm_workspace_size(4096, 1024, 8, 16, 7, C.byref(one)) == dlm.DLM_OK

@@ -62,9 +62,9 @@ CASES = [
     (40, 64, 64, 32, 16, 1.0, torch.bfloat16),       # most experts
     (20, 64, 96, 4, 128, 0.5, torch.bfloat16),       # largest rank
     (300, 256, 264, 8, 16, 1.0, torch.bfloat16),
-    (40, 2056, 72, 8, 16, 1.0, torch.bfloat16),      # three K slices, the last 8 wide
-    (70, 1096, 136, 16, 64, 0.5, torch.bfloat16),    # two K slices, many N blocks per tile
-    (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # exactly one slice, largest rank
+    (40, 2056, 72, 8, 16, 1.0, torch.bfloat16),      # five K slices of 512, the last 8 wide
+    (70, 1096, 136, 16, 64, 0.5, torch.bfloat16),    # three K slices, many N blocks per tile
+    (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # two whole slices, largest rank
     (9, 1500, 24, 4, 8, 1.0, torch.float32),         # fp32 past one slice width
     (9000, 64, 72, 8, 16, 1.0, torch.bfloat16),      # more rows than the segment's LDS caches
 ]
