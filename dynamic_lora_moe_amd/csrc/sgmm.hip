@@ -302,10 +302,11 @@ constexpr int kXRows = 32 * kTM;
 // 64-wide K chunks of one slice, and 16-byte chunks of one x row of a slice
 constexpr int kKC = kSgmmKSlice / 64;
 constexpr int kXC = kSgmmKSlice / 8;
-// A chunks in flight per wave in the shrink's K loop.  The shrink runs at 3
-// waves per SIMD (three workgroups per CU, each with a 32 KB x slice):
-// measured on the 4096-token prefill 114 us with 1024-wide slices, a 4-chunk
-// ring and 2 waves per SIMD, 100 us like this.
+// A chunks in flight per wave in the shrink's K loop.  The shrink runs at 4
+// waves per SIMD (3 for ranks 17..32, which would spill at 4): several
+// workgroups per CU, each with a 32 KB x slice.  Measured on the 4096-token
+// prefill: 114 us with 1024-wide slices, a 4-chunk ring and 2 waves per SIMD;
+// 102 us like this at 3 waves per SIMD, 98 us at 4.
 constexpr int kShrinkRing = 2;
 static_assert(kKC >= kShrinkRing && kKC % kShrinkRing == 0, "slice is a whole number of ring steps");
 static_assert(256 % kXC == 0 && kXRows % (256 / kXC) == 0, "x slice load shape");
@@ -330,7 +331,7 @@ __device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((c
 // dummy row whose products reach only accumulator entries that are never
 // stored, and k past d_in reads a clamped address whose value is replaced by 0.
 template <int R16, bool PK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R16 == 2 ? 3 : 4)))
 void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     constexpr int RPAD = R16 * 16;
     const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
