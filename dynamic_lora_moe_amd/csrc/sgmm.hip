@@ -324,7 +324,7 @@ __device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((c
 // rank) each, over the union of the tiles' experts) are then spread over the
 // waves: with four or more blocks each wave takes whole blocks; with fewer, the
 // waves of one block split the slice's chunks and their sums are added in a
-// fixed order.  The A rows of a block stream from L2 up to four chunks ahead
+// fixed order.  The A rows of a block stream from L2 kShrinkRing chunks ahead
 // of the MFMAs, and each A operand serves the kTM tiles.  Each row's two
 // slots get the slice's partial v; a later pass adds the slices up.  Loads are
 // never guarded: a padding row or (expert, rank) column reads an in-bounds
@@ -462,7 +462,7 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     }
     __syncthreads();
 
-    // K loop of one block over this wave's chunks, A up to four chunks ahead
+    // K loop of one block over this wave's chunks, A kShrinkRing chunks ahead
     auto run_block = [&](f32x16 (&acc)[kTM]) {
 #pragma unroll 1
         for (int i = 0; i < nmy; i += kShrinkRing) {
