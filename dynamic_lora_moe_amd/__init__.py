@@ -71,6 +71,7 @@ def load(path: str = LIB_PATH):
         "dlm_sgmm": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, F, I32, P, C.c_size_t, P], C.c_int),
         "dlm_sgmm_group_create": ([P, I32, I32, I32, F, I32, P], C.c_int),
         "dlm_sgmm_group_destroy": ([P], C.c_int),
+        "dlm_layers_repack": ([P, P], C.c_int),
         "dlm_sgmm_group_repack": ([P, P], C.c_int),
         "dlm_sgmm_group_run": ([P, P, P, I64, P, C.c_size_t, P], C.c_int),
         "dlm_sgmm_status": ([P, P, P], C.c_int),
@@ -183,6 +184,10 @@ class Layers:
 
     def launches_per_switch(self) -> int:
         return load().dlm_switch_launches(self._h)
+
+    def repack(self, stream=None):
+        """Refresh the packed A copy (ranks 17..64, bf16) after changing an A bank in place."""
+        _check(load().dlm_layers_repack(self._h, _stream(stream)), "dlm_layers_repack")
 
     def close(self):
         if getattr(self, "_h", None):

@@ -8,6 +8,7 @@
 #include <cstring>
 #include <map>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "dlm.h"
@@ -57,6 +58,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 struct dlm_layers {
     SwDesc* d_descs = nullptr;
     int32_t* d_err = nullptr;
+    void* d_pack = nullptr;       // packed A images of every weight, then the zero image (wide tiles)
+    void* d_zimg = nullptr;
+    std::vector<SwDesc> h_descs;
     int32_t n = 0;
     int32_t E = 0, r = 0;
     float scale = 1.f;
@@ -142,6 +146,7 @@ int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, fl
         d.n_ct = (int32_t)((p.d_in + tile.ct - 1) / tile.ct);
         d.tile0 = tiles;
         d.elem0 = elems;
+        d.Ap = nullptr;
         tiles += (int64_t)d.n_rt * d.n_ct;
         elems += p.d_out * p.d_in;
     }
@@ -156,17 +161,52 @@ int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, fl
     hd->n_tiles = tiles;
     hd->n_elems = elems;
     hd->per_xcd = (tiles + 7) / 8;
-    hipError_t e = hipMalloc((void**)&hd->d_descs, sizeof(SwDesc) * n);
+    hipError_t e = hipSuccess;
+    if (dtype == DLM_BF16 && switch_packs_a(tile)) {
+        // ranks 17..64: packed A images for the copy-staged tiles, one block
+        size_t elems_total = 0;
+        std::vector<size_t> off(n);
+        for (int i = 0; i < n; ++i) {
+            off[i] = elems_total;
+            elems_total += switch_packed_a_elems(h[i].d_in, E, tile);
+        }
+        const size_t zero_off = elems_total;
+        elems_total += switch_zero_image_elems(tile);
+        e = hipMalloc(&hd->d_pack, elems_total * 2);
+        if (e == hipSuccess) {
+            uint16_t* base = (uint16_t*)hd->d_pack;
+            hd->d_zimg = base + zero_off;
+            e = hipMemset(hd->d_zimg, 0, switch_zero_image_elems(tile) * 2);
+            for (int i = 0; i < n && e == hipSuccess; ++i) {
+                h[i].Ap = base + off[i];
+                e = launch_switch_pack_a(h[i].A, base + off[i], h[i].d_in, E, r, tile, nullptr);
+            }
+            if (e == hipSuccess) e = hipDeviceSynchronize();
+        }
+    }
+    if (e == hipSuccess) e = hipMalloc((void**)&hd->d_descs, sizeof(SwDesc) * n);
     if (e == hipSuccess) e = hipMalloc((void**)&hd->d_err, 256);
     if (e == hipSuccess) e = hipMemcpy(hd->d_descs, h.data(), sizeof(SwDesc) * n, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(hd->d_err, 0, 256);
     if (e != hipSuccess) {
         if (hd->d_descs) (void)hipFree(hd->d_descs);
         if (hd->d_err) (void)hipFree(hd->d_err);
+        if (hd->d_pack) (void)hipFree(hd->d_pack);
         delete hd;
         return hip_fail(e, "layers_create");
     }
+    hd->h_descs = std::move(h);
     *out = hd;
+    return ok();
+}
+
+int dlm_layers_repack(dlm_layers* h, void* stream) {
+    if (!h) return fail(DLM_EINVAL, "layers_repack: null handle");
+    if (!h->d_pack) return ok();
+    for (const SwDesc& d : h->h_descs) {
+        hipError_t e = launch_switch_pack_a(d.A, (void*)d.Ap, d.d_in, h->E, h->r, h->tile, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "layers_repack launch");
+    }
     return ok();
 }
 
@@ -175,6 +215,7 @@ int dlm_layers_destroy(dlm_layers* h) {
     hipError_t e = hipDeviceSynchronize();
     if (h->d_descs) (void)hipFree(h->d_descs);
     if (h->d_err) (void)hipFree(h->d_err);
+    if (h->d_pack) (void)hipFree(h->d_pack);
     delete h;
     if (e != hipSuccess) return hip_fail(e, "layers_destroy");
     return ok();
@@ -196,6 +237,7 @@ int dlm_switch(dlm_layers* h, const int32_t* old_idx, const float* old_g, const 
     a.new_idx = new_idx;
     a.new_g = new_g;
     a.err = h->d_err;
+    a.zimg = h->d_zimg;
     hipError_t e;
     if (h->dtype == DLM_BF16) {
         a.n_units = h->n_tiles;

@@ -60,6 +60,32 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Direct global -> LDS copy, 16 bytes per lane (global_load_lds_dwordx4): lane
+// L's 16 bytes land at lds + 16 L, so one wave instruction fills 1 KB of LDS.
+// `lds` must be the same for every lane.  The copy is a vector-memory
+// instruction: its data is in LDS once the wave's vmcnt has passed it.
+__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds((gcptr<void>)g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory instructions of this wave are in flight.
+// gfx9 s_waitcnt immediate: vmcnt in bits [3:0] and [15:14], expcnt [6:4] and
+// lgkmcnt [11:8] left at their maxima (not waited for).  Vector-memory loads,
+// stores and LDS copies retire from vmcnt in issue order.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// The same for a wave-uniform count known only at run time, n <= NMAX.
+template <int NMAX> __device__ __forceinline__ void wait_vmcnt_le(int n) {
+    if constexpr (NMAX == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (n >= NMAX) wait_vmcnt<NMAX>();
+        else wait_vmcnt_le<NMAX - 1>(n);
+    }
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 // Wave index within the workgroup, marked wave-uniform (an SGPR): control flow
 // that depends on it stays scalar instead of running under exec masks.

@@ -19,6 +19,7 @@ struct SwDesc {
     int32_t n_rt, n_ct; // row tiles x column tiles of this weight
     int64_t tile0;      // index of its first tile in the launch (prefix sum)
     int64_t elem0;      // index of its first element (generic path)
+    const void* Ap;     // packed A images of the wide tiles (ranks 17..64), else null
 };
 
 struct SwitchArgs {
@@ -33,6 +34,7 @@ struct SwitchArgs {
     const int32_t* new_idx;
     const float* new_g;
     int32_t* err;
+    const void* zimg;   // one all-zero A image (inactive slots of the wide tiles)
 };
 
 // Tile geometry of the bf16 MFMA switch for a padded rank.
@@ -44,6 +46,16 @@ struct SwTile {
 SwTile switch_tile_for_rank(int r);
 
 hipError_t launch_switch_bf16(const SwitchArgs& a, const SwTile& t, hipStream_t s);
+
+// Packed A images used by the wide tiles (ranks 17..64, bf16): for expert e and
+// 64-column block cb of a weight, one contiguous image of the block's A slice
+// in the LDS layout the MFMAs read ([half][MFMA row][rank], chunk-swizzled), so
+// a tile stages it with direct global->LDS copies.  Zero past d_in.
+bool switch_packs_a(const SwTile& t);
+size_t switch_packed_a_elems(int64_t d_in, int E, const SwTile& t);  // per weight
+size_t switch_zero_image_elems(const SwTile& t);
+hipError_t launch_switch_pack_a(const void* A, void* Ap, int64_t d_in, int E, int r, const SwTile& t,
+                                hipStream_t s);
 hipError_t launch_switch_generic(const SwitchArgs& a, int dtype, hipStream_t s);
 
 // ---- router ---------------------------------------------------------------

@@ -532,10 +532,177 @@ __device__ __forceinline__ void switch_wide_tile(const SwitchArgs& a, const Sets
     }
 }
 
+// Wide tiles entirely inside their weight (every tile of the model shapes)
+// stage both operands with direct global -> LDS copies instead of through
+// registers, so the copies can run further ahead of the MFMAs:
+//   * A: the handle keeps every (expert, 64-column block) slice as a packed
+//     image already in the LDS layout above, so a sub-band's four slot slices
+//     are four contiguous copies (an inactive slot copies the zero image).  Two
+//     buffers; the next sub-band's copy is issued right after the barrier that
+//     frees its buffer.
+//   * W: each wave copies its own 32 x 64 block, row-major and chunk-swizzled
+//     (lane L fetches the chunk that belongs at LDS position L), into one of
+//     three per-wave buffers, two sub-bands ahead; the result goes back out
+//     through the same buffer as above.
+// Each wait names the exact number of vector-memory instructions (copies and W
+// stores, the only ones issued in the loop) that follow the copy it waits for;
+// scheduling barriers keep the compiler from moving any of them across.
+constexpr int kWideWBufs = 3;
+
+template <typename T>
+__device__ __forceinline__ T pick4(int i, T v0, T v1, T v2, T v3) {
+    return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
+}
+
+template <int R16, int NSB>
+__device__ __forceinline__ void switch_wide_tile_copy(const SwitchArgs& a, const Sets& sc, const SwDesc& D,
+                                                      int row_base, int col_base, uint16_t* smem) {
+    constexpr int RPAD = R16 * 16;
+    constexpr int SLOT_ELEMS = 2 * 32 * RPAD;        // one slot's image of one sub-band
+    constexpr int BUF_ELEMS = 4 * SLOT_ELEMS;
+    constexpr int KB = 512;                          // bf16 elements per 1 KB copy instruction
+    constexpr int NAI = 4 * SLOT_ELEMS / KB / kWW;   // A copies per wave per sub-band (= R16)
+    constexpr int WBLK = 32 * 64;                    // one wave's W block
+    constexpr int WBUF = kWW * WBLK;
+    static_assert((4 * SLOT_ELEMS / KB) % kWW == 0, "A copies split evenly over the waves");
+    static_assert(NSB >= 3, "the copy schedule assumes at least three sub-bands");
+    uint16_t* As = smem;                              // [2][BUF_ELEMS]
+    uint16_t* Wb = smem + 2 * BUF_ELEMS;              // [kWideWBufs][kWW][WBLK]
+    const int d_in = D.d_in, d_out = D.d_out, r = a.r;
+    const uint16_t* __restrict__ Bb = (const uint16_t*)D.B;
+    uint16_t* __restrict__ W = (uint16_t*)D.W;
+    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
+    const int lr = lane >> 3, lc = lane & 7;
+    const int row0 = row_base + w * 32;
+
+    // first-sub-band image of each slot; the zero image does not advance
+    const int64_t n_cb = (d_in + 63) / 64;
+    const uint16_t* img[4];
+    int step[4];
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+        const bool on = sc.e[slot] >= 0;
+        img[slot] = on ? (const uint16_t*)D.Ap + ((int64_t)sc.e[slot] * n_cb + col_base / 64) * SLOT_ELEMS
+                       : (const uint16_t*)a.zimg;
+        step[slot] = on ? SLOT_ELEMS : 0;
+    }
+    auto copy_a = [&](int sb) {
+        uint16_t* dst = As + (sb & 1) * BUF_ELEMS;
+#pragma unroll
+        for (int j = 0; j < NAI; ++j) {
+            const int q = j * kWW + w;  // 1 KB piece q of the sub-band's four images
+            const int slot = q / (SLOT_ELEMS / KB), piece = q % (SLOT_ELEMS / KB);
+            const uint16_t* src = pick4(slot, img[0], img[1], img[2], img[3]) +
+                                  (int64_t)sb * pick4(slot, step[0], step[1], step[2], step[3]) + piece * KB;
+            copy16_to_lds(src + lane * 8, dst + q * KB);
+        }
+    };
+    auto copy_w = [&](int sb) {
+        uint16_t* dst = Wb + (sb % kWideWBufs) * WBUF + w * WBLK;
+        const int col = col_base + sb * 64 + 8 * (lc ^ lr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) copy16_to_lds(W + (int64_t)(row0 + 8 * i + lr) * d_in + col, dst + i * KB);
+    };
+
+    // B rows of the wave's 32 rows; an inactive slot reads zeros from the zero
+    // image (rows of RPAD there), so every load issues unconditionally.  (The
+    // compiler drains the copies of the prologue before entering the loop, as
+    // the loop uses registers loaded outside it: one latency per tile.)
+    u32x4 bcur[4][R16];
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+        const uint16_t* bp = sc.e[slot] >= 0 ? Bb + ((int64_t)sc.e[slot] * d_out + row0 + n) * r + 8 * h
+                                             : (const uint16_t*)a.zimg + n * RPAD + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < R16; ++ks) bcur[slot][ks] = ld128(bp + ks * 16);
+    }
+
+    auto unit = [&](int sb) {
+        const uint16_t* Acur = As + (sb & 1) * BUF_ELEMS;
+        uint16_t* ws = Wb + (sb % kWideWBufs) * WBUF + w * WBLK;
+#pragma unroll 1
+        for (int b = 0; b < 2; ++b) {
+            u32x4 wm[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) wm[q] = *(const u32x4*)(ws + w_off(n, 4 * b + 2 * h + q));
+            f32x16 P[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+            const uint16_t* ap = Acur + b * 32 * RPAD + n * RPAD;
+#pragma unroll
+            for (int ks = 0; ks < R16; ++ks) {
+                u32x4 ao[4];
+#pragma unroll
+                for (int slot = 0; slot < 4; ++slot)
+                    ao[slot] = *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, 2 * ks + h) << 3));
+#pragma unroll
+                for (int slot = 0; slot < 4; ++slot) P[slot] = mfma32(ao[slot], bcur[slot][ks], P[slot]);
+            }
+            uint32_t ow[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t word = wm[p >> 2][p & 3];
+                float o2[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int i = 2 * p + j;
+                    const float sn = fmaf(sc.c[1], P[1][i], sc.c[0] * P[0][i]);
+                    const float so = fmaf(sc.c[3], P[3][i], sc.c[2] * P[2][i]);
+                    const float wf = j ? bf_hi(word) : bf_lo(word);
+                    o2[j] = wf - (so - sn);
+                }
+                ow[p] = pack2_bf16(o2[0], o2[1]);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                *(u32x4*)(ws + w_off(n, 4 * b + 2 * h + q)) =
+                    u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
+        }
+        const int col = col_base + sb * 64 + 8 * lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st128(W + (int64_t)(row0 + 8 * i + lr) * d_in + col, *(const u32x4*)(ws + w_off(8 * i + lr, lc)));
+    };
+
+    // issue order: B loads, A(0), W(0), W(1); then per sub-band sb: A(sb+1),
+    // W(sb+2), the 4 stores of sb
+    copy_a(0);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_w(0);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_w(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+    for (int sb = 0; sb < NSB; ++sb) {
+        const bool more1 = sb + 1 < NSB, more2 = sb + 2 < NSB;
+        // A(sb): followed by W(sb+1) (if any) and the stores of sb-1 (W(0), W(1) for sb = 0)
+        wait_vmcnt_le<8>(4 + (more1 ? 4 : 0));
+        __builtin_amdgcn_s_barrier();  // A(sb) is in LDS for every wave; A buffer (sb+1)&1 is free
+        __builtin_amdgcn_sched_barrier(0);
+        if (more1) copy_a(sb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more2) copy_w(sb + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        // W(sb): issued after it were the stores of sb-2; A(sb), W(sb+1) and
+        // the stores of sb-1; A(sb+1) and W(sb+2) (fewer for sb < 2 and at the end)
+        if (sb >= 2 && more2) {
+            wait_vmcnt<16 + 2 * NAI>();
+        } else {
+            int after;
+            if (sb == 0) after = 4 + NAI + 4;  // W(1), A(1), W(2)
+            else if (sb == 1) after = NAI + 4 + 4 + NAI + (more2 ? 4 : 0);
+            else after = 4 + NAI + (more1 ? 4 : 0) + 4 + (more1 ? NAI : 0);
+            wait_vmcnt_le<16 + 2 * NAI>(after);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        unit(sb);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int R16, int NSB>
 __global__ __launch_bounds__(kWW* kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void switch_wide_kernel(SwitchArgs a) {
-    // 2 x [4 slots][2][32][R16*16] A slices, then 8 x [32][64] W scratch
+    // 2 x [4 slots][2][32][R16*16] A slices, then 8 x [32][64] W scratch (the
+    // copy-staged tiles: then kWideWBufs x 8 x [32][64] W buffers)
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* As = smem;
     uint16_t* Ws = smem + 2 * 4 * 2 * 32 * (R16 * 16);
@@ -557,7 +724,9 @@ void switch_wide_kernel(SwitchArgs a) {
     const int rt = grp * kWGroup + (int)(lg % in_grp), ct = (int)(lg / in_grp);
     const int row_base = rt * kWRT, col_base = ct * (64 * NSB);
     const bool full = row_base + kWRT <= D.d_out && col_base + 64 * NSB <= D.d_in && a.r == R16 * 16;
-    if (full)
+    if (full && D.Ap != nullptr)
+        switch_wide_tile_copy<R16, NSB>(a, sc, D, row_base, col_base, smem);
+    else if (full)
         switch_wide_tile<R16, NSB, true>(a, sc, D, row_base, col_base, As, Ws);
     else
         switch_wide_tile<R16, NSB, false>(a, sc, D, row_base, col_base, As, Ws);
@@ -608,6 +777,33 @@ __global__ __launch_bounds__(256) void switch_generic_kernel(SwitchArgs a) {
     stf(W, i, ldf(W, i) - (so - sn));
 }
 
+// Packed A images of the copy-staged wide tiles: thread (e, cb, rank chunk
+// ch, column c) writes the 16 bytes holding ranks 8ch..8ch+7 of column
+// 64cb + c at the position the MFMA reads them from (zero past r and d_in).
+// Consecutive threads take consecutive columns, so the A reads coalesce.
+template <int R16>
+__global__ __launch_bounds__(256) void switch_pack_a_kernel(const uint16_t* __restrict__ A, uint16_t* __restrict__ Ap,
+                                                            int64_t d_in, int E, int r, int64_t n_cb) {
+    constexpr int RPAD = R16 * 16, SLOT_ELEMS = 2 * 32 * RPAD, NCH = RPAD / 8;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)E * n_cb * NCH * 64) return;
+    const int c = (int)(t % 64), ch = (int)((t / 64) % NCH);
+    const int64_t blk = t / (64 * NCH);  // e * n_cb + cb
+    const int e = (int)(blk / n_cb);
+    const int64_t col = (blk % n_cb) * 64 + c;
+    uint32_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r0 = ch * 8 + 2 * j;
+        const uint32_t lo = (r0 < r && col < d_in) ? gld(A + ((int64_t)e * r + r0) * d_in + col) : 0u;
+        const uint32_t hi = (r0 + 1 < r && col < d_in) ? gld(A + ((int64_t)e * r + r0 + 1) * d_in + col) : 0u;
+        v[j] = lo | (hi << 16);
+    }
+    const int m = perm_row(c & 31);
+    st128(Ap + blk * SLOT_ELEMS + (c >> 5) * 32 * RPAD + m * RPAD + (a_chunk_swz<R16>(m, ch) << 3),
+          u32x4{v[0], v[1], v[2], v[3]});
+}
+
 template <int R16, int CT>
 hipError_t launch_r(const SwitchArgs& a, hipStream_t s) {
     const size_t lds = ((size_t)4 * (CT / 32) * 32 * (R16 * 16) + (size_t)kWaves * 32 * 64) * sizeof(uint16_t);
@@ -626,7 +822,7 @@ hipError_t launch_r(const SwitchArgs& a, hipStream_t s) {
 
 template <int R16>
 hipError_t launch_wide(const SwitchArgs& a, hipStream_t s) {
-    const size_t lds = ((size_t)2 * 4 * 2 * 32 * (R16 * 16) + (size_t)kWW * 32 * 64) * sizeof(uint16_t);
+    const size_t lds = ((size_t)2 * 4 * 2 * 32 * (R16 * 16) + (size_t)kWideWBufs * kWW * 32 * 64) * sizeof(uint16_t);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)switch_wide_kernel<R16, kWideSB>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -649,6 +845,30 @@ hipError_t launch_switch_bf16(const SwitchArgs& a, const SwTile& t, hipStream_t 
         case 8: return launch_r<8, 64>(a, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+bool switch_packs_a(const SwTile& t) { return t.r16 >= 2 && t.r16 <= 4; }
+
+size_t switch_packed_a_elems(int64_t d_in, int E, const SwTile& t) {
+    return (size_t)E * (size_t)((d_in + 63) / 64) * 2 * 32 * (t.r16 * 16);
+}
+
+size_t switch_zero_image_elems(const SwTile& t) { return (size_t)2 * 32 * (t.r16 * 16); }
+
+hipError_t launch_switch_pack_a(const void* A, void* Ap, int64_t d_in, int E, int r, const SwTile& t,
+                                hipStream_t s) {
+    const int64_t n_cb = (d_in + 63) / 64;
+    const int64_t threads = (int64_t)E * n_cb * (t.r16 * 2) * 64;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    const uint16_t* a = (const uint16_t*)A;
+    uint16_t* ap = (uint16_t*)Ap;
+    switch (t.r16) {
+        case 2: hipLaunchKernelGGL(switch_pack_a_kernel<2>, grid, dim3(256), 0, s, a, ap, d_in, E, r, n_cb); break;
+        case 3: hipLaunchKernelGGL(switch_pack_a_kernel<3>, grid, dim3(256), 0, s, a, ap, d_in, E, r, n_cb); break;
+        case 4: hipLaunchKernelGGL(switch_pack_a_kernel<4>, grid, dim3(256), 0, s, a, ap, d_in, E, r, n_cb); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_switch_generic(const SwitchArgs& a, int dtype, hipStream_t s) {

@@ -112,19 +112,29 @@ typedef struct dlm_layers dlm_layers;
 /*
  * Build the table of every adapted weight of every layer (L*P entries) that
  * one dlm_switch call updates.  Copies the host descriptors to a small device
- * table (the only allocation of the switch path, freed by destroy) plus a
- * device error word.  The buffers themselves stay owned by the caller and must
- * outlive the handle.
+ * table plus a device error word.  The buffers themselves stay owned by the
+ * caller and must outlive the handle.
  *   projs (host) [n]; E in [1, DLM_MAX_EXPERTS]; r in [1, DLM_MAX_RANK];
  *   scale = the LoRA scale s multiplying every delta.
  * bf16: every W/A/B pointer 16-byte aligned and every d_in a multiple of 8.
- * Does not synchronise.  *out (host) receives the handle.
+ * bf16 with r in 17..64: the handle also allocates and fills a packed copy of
+ * every A bank (E * ceil(d_in/64) * 64 * 16*ceil(r/16) bf16 per weight, about
+ * the size of A) that the switch stages into LDS with direct copies; the
+ * device is synchronised before returning.  The copy is taken here: after
+ * changing an A bank in place call dlm_layers_repack.  Otherwise does not
+ * synchronise.  All of it is freed by destroy.  *out (host) receives the handle.
  */
 int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r,
                       float scale, int32_t dtype, dlm_layers** out);
 
-/* Free the handle's device table (synchronises the device first). */
+/* Free the handle's device memory (synchronises the device first). */
 int dlm_layers_destroy(dlm_layers* h);
+
+/*
+ * Refresh the handle's packed A copies from the caller's A banks: one launch
+ * per weight on `stream`, no allocation (no-op when the handle keeps none).
+ */
+int dlm_layers_repack(dlm_layers* h, void* stream);
 
 /*
  * One fused switch over every weight of the handle, one kernel launch:
@@ -139,7 +149,8 @@ int dlm_layers_destroy(dlm_layers* h);
  * A set with an index outside [-1, E) or a non-finite gate on a used slot is
  * rejected on the device: no weight is written and the handle's error word is
  * set (read it with dlm_layers_status).
- * No allocation; one launch on `stream`.
+ * No allocation; one launch on `stream`.  Reads the packed A copy where the
+ * handle keeps one, so A banks changed after create need dlm_layers_repack.
  */
 int dlm_switch(dlm_layers* h, const int32_t* old_idx, const float* old_g,
                const int32_t* new_idx, const float* new_g, void* stream);

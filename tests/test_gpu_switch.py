@@ -50,6 +50,10 @@ CASES = [
     ([(512, 1024), (300, 1000), (256, 520)], 16, 64, 1.0, torch.bfloat16),  # wide tiles: full, ragged
     ([(520, 1536), (64, 576)], 8, 32, 2.0, torch.bfloat16),            # rank 32: odd sub-band count
     ([(257, 640), (768, 512)], 8, 48, 1.0, torch.bfloat16),            # rank 48
+    # wide tiles (256 x 4096) entirely inside the weight: copy-staged from the packed A
+    ([(256, 4096), (512, 8256)], 16, 64, 1.0, torch.bfloat16),         # full tiles + a ragged column band
+    ([(256, 4096)], 8, 32, 2.0, torch.bfloat16),                       # rank 32 full tile
+    ([(768, 4096), (300, 4096)], 8, 48, 1.0, torch.bfloat16),          # rank 48 full tiles + ragged rows
     ([(300, 1096), (16, 1032)], 4, 40, 1.0, torch.bfloat16),           # rank 40: padded ranks, d_in % 64
     ([(40, 64)], 2, 128, 0.5, torch.bfloat16),                         # largest rank
     ([(33, 64)], 32, 16, 1.0, torch.bfloat16),                         # most experts
@@ -165,3 +169,21 @@ def test_switch_uses_router_output_without_host_sync():
     assert torch.equal(ri, idx.cpu())
     _compare(model, W0s, 2.0, host_set(ri[0], rg[0]), host_set(ri[1], rg[1]), "router->switch",
              torch.bfloat16)
+
+
+def test_repack_after_changing_a_in_place():
+    """Full wide tiles read the handle's packed A copy: after A changes in place,
+    repack refreshes it (checked against the oracle on the new A)."""
+    E, r, scale = 8, 64, 1.0
+    model = _model([(256, 4096)], E, r, torch.bfloat16, 2005)
+    L = dlm.Layers(model, E, r, scale)
+    W, A, B = model[0]
+    A.copy_(synth.normal_device(tuple(A.shape), 0.02, torch.bfloat16, "cuda", 2005, "A2", 0))
+    L.repack()
+    W0 = W.cpu().clone()
+    s = ([2, 6], [0.6, 0.4])
+    L.switch(None, dev_set(s))
+    torch.cuda.synchronize()
+    _compare(model, [W0], scale, None, s, "repacked A", torch.bfloat16)
+    assert L.status() == dlm.DLM_OK
+    L.close()
