@@ -342,143 +342,155 @@ void switch_bf16_kernel(SwitchArgs a) {
 //
 // At these ranks the A/B slices of a tile are as large as its W, so the
 // 256 x CT tiles above spend most of their time waiting for operands.  Here a
-// workgroup of 8 waves takes a 256-row x (64 * NSB)-column tile: each wave owns
-// one 32-row group and loads its B rows once per tile; the A slices pass through
-// a double-buffered LDS stage one 64-column sub-band at a time (the next
-// sub-band's slices load during the current one); each wave's W is read two
-// sub-bands ahead.  Tiles of a weight run in groups of kWGroup row bands,
-// column band by column band, so the A slices of a column band and the B rows
-// of the group's row bands are reused from L2 instead of re-read from HBM.
-// The per-slot fp32 products and the epilogue are those of switch_tile.
+// workgroup of 8 waves takes a 256-row x (64 * NSB)-column tile; each wave owns
+// one 32-row group and keeps its B rows in registers for the whole tile.  Tiles
+// of a weight run in groups of kWGroup row bands, column band by column band,
+// so the A slices of a column band and the B rows of the group's row bands are
+// reused from L2 instead of re-read from HBM.  The per-slot fp32 products and
+// the epilogue are those of switch_tile.
+//
+// Both operands are staged with direct global -> LDS copies instead of
+// through registers, so the copies run well ahead of the MFMAs:
+//   * A: the handle keeps every (expert, 64-column block) slice as a packed
+//     image already in the LDS layout of switch_tile (zero past r and d_in),
+//     so a 64-column sub-band's four slot slices are four contiguous copies (an
+//     inactive slot copies the zero image).  Two buffers; the next sub-band's
+//     copy is issued right after the barrier that frees its buffer.
+//   * W: each wave copies its own 32 x 64 block, row-major and chunk-swizzled
+//     (lane L fetches the chunk that belongs at LDS position L), into one of
+//     three per-wave buffers, two sub-bands ahead; the result goes back out
+//     through the same buffer.  Edge tiles copy from clamped addresses (rows
+//     past d_out and columns past d_in are never stored).
+// Each wait names the exact number of vector-memory instructions (copies and W
+// stores, the only ones issued in the loop) that follow the copy it waits for;
+// scheduling barriers keep the compiler from moving any of them across.
+constexpr int kWideWBufs = 3;
+
+template <typename T>
+__device__ __forceinline__ T pick4(int i, T v0, T v1, T v2, T v3) {
+    return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
+}
 
 template <int R16, int NSB, bool FULL>
 __device__ __forceinline__ void switch_wide_tile(const SwitchArgs& a, const Sets& sc, const SwDesc& D,
-                                                 int row_base, int col_base, uint16_t* As, uint16_t* Ws) {
+                                                 int row_base, int col_base, uint16_t* smem) {
     constexpr int RPAD = R16 * 16;
-    constexpr int SLOT_ELEMS = 2 * 32 * RPAD;  // one slot's slice of one 64-column sub-band
+    constexpr int SLOT_ELEMS = 2 * 32 * RPAD;        // one slot's image of one sub-band
     constexpr int BUF_ELEMS = 4 * SLOT_ELEMS;
-    constexpr int NQ = RPAD * 8;               // 16-byte chunks of one slot's sub-band slice
-    constexpr int NSTAGE = (NQ + kWW * kWave - 1) / (kWW * kWave);
-    const int d_out = D.d_out, d_in = D.d_in, r = a.r;
-    const uint16_t* __restrict__ Ab = (const uint16_t*)D.A;
+    constexpr int KB = 512;                          // bf16 elements per 1 KB copy instruction
+    constexpr int NAI = 4 * SLOT_ELEMS / KB / kWW;   // A copies per wave per sub-band (= R16)
+    constexpr int WBLK = 32 * 64;                    // one wave's W block
+    constexpr int WBUF = kWW * WBLK;
+    static_assert((4 * SLOT_ELEMS / KB) % kWW == 0, "A copies split evenly over the waves");
+    uint16_t* As = smem;                              // [2][BUF_ELEMS]
+    uint16_t* Wb = smem + 2 * BUF_ELEMS;              // [kWideWBufs][kWW][WBLK]
+    const int d_in = D.d_in, d_out = D.d_out, r = a.r;
     const uint16_t* __restrict__ Bb = (const uint16_t*)D.B;
     uint16_t* __restrict__ W = (uint16_t*)D.W;
-    const int tid = threadIdx.x, w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
-    const bool act[4] = {sc.e[0] >= 0, sc.e[1] >= 0, sc.e[2] >= 0, sc.e[3] >= 0};
-    const bool r_vec = (r & 7) == 0;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    uint16_t* ws = Ws + w * (32 * 64);
+    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
     const int lr = lane >> 3, lc = lane & 7;
     const int row0 = row_base + w * 32;
     const int nsb = FULL ? NSB : uniform((d_in - col_base + 63) / 64 < NSB ? (d_in - col_base + 63) / 64 : NSB);
 
-    // A slices of sub-band sb: loads into registers, then the transposed LDS write
-    auto load_a = [&](u32x4 (&av)[4][NSTAGE], int sb) {
+    // first-sub-band image of each slot; the zero image does not advance
+    const int64_t n_cb = (d_in + 63) / 64;
+    const uint16_t* img[4];
+    int step[4];
 #pragma unroll
-        for (int slot = 0; slot < 4; ++slot)
-#pragma unroll
-            for (int i = 0; i < NSTAGE; ++i) {
-                const int q = tid + i * kWW * kWave;
-                const int rho = q / 8, col = col_base + sb * 64 + (q % 8) * 8;
-                bool ok = act[slot] && (NQ % (kWW * kWave) == 0 || q < NQ);
-                if (!FULL) ok = ok && rho < r && col < d_in;
-                av[slot][i] = ok ? ld128(Ab + ((int64_t)sc.e[slot] * r + rho) * d_in + col) : zero;
-            }
-    };
-    // LDS element offsets of this thread's 8 transposed writes: the same for
-    // every sub-band, slot and buffer (those add constants)
-    int aoff[NSTAGE][8];
-#pragma unroll
-    for (int i = 0; i < NSTAGE; ++i) {
-        const int q = tid + i * kWW * kWave;
-        const int rho = q / 8, ch = q % 8, cc0 = (ch & 3) * 8;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int m = perm_row(cc0 + j);
-            aoff[i][j] = (ch >> 2) * 32 * RPAD + (rho & 7) + m * RPAD + (a_chunk_swz<R16>(m, rho >> 3) << 3);
-        }
+    for (int slot = 0; slot < 4; ++slot) {
+        const bool on = sc.e[slot] >= 0;
+        img[slot] = on ? (const uint16_t*)D.Ap + ((int64_t)sc.e[slot] * n_cb + col_base / 64) * SLOT_ELEMS
+                       : (const uint16_t*)a.zimg;
+        step[slot] = on ? SLOT_ELEMS : 0;
     }
-    auto store_a = [&](const u32x4 (&av)[4][NSTAGE], uint16_t* buf) {
+    auto copy_a = [&](int sb) {
+        uint16_t* dst = As + (sb & 1) * BUF_ELEMS;
 #pragma unroll
-        for (int slot = 0; slot < 4; ++slot) {
-            // an inactive slot's slice is written too (its loads gave zeros), so
-            // the MFMAs below need no per-slot branch
-#pragma unroll
-            for (int i = 0; i < NSTAGE; ++i) {
-                const int q = tid + i * kWW * kWave;
-                if (NQ % (kWW * kWave) != 0 && q >= NQ) continue;
-                uint16_t* dst = buf + slot * SLOT_ELEMS;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t word = av[slot][i][j >> 1];
-                    dst[aoff[i][j]] = (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
-                }
-            }
+        for (int j = 0; j < NAI; ++j) {
+            const int q = j * kWW + w;  // 1 KB piece q of the sub-band's four images
+            const int slot = q / (SLOT_ELEMS / KB), piece = q % (SLOT_ELEMS / KB);
+            const uint16_t* src = pick4(slot, img[0], img[1], img[2], img[3]) +
+                                  (int64_t)sb * pick4(slot, step[0], step[1], step[2], step[3]) + piece * KB;
+            copy16_to_lds(src + lane * 8, dst + q * KB);
         }
     };
+    auto copy_w = [&](int sb) {
+        uint16_t* dst = Wb + (sb % kWideWBufs) * WBUF + w * WBLK;
+        int col = col_base + sb * 64 + 8 * (lc ^ lr);
+        if (!FULL) col = col < d_in ? col : d_in - 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int row = row0 + 8 * i + lr;
+            if (!FULL) row = row < d_out ? row : d_out - 1;
+            copy16_to_lds(W + (int64_t)row * d_in + col, dst + i * KB);
+        }
+    };
+
+    // B rows of the wave's 32 rows.  An inactive slot, and a full-rank tile's
+    // every slot, load unconditionally (an inactive slot from the zero image,
+    // rows of RPAD there).  The compiler drains the prologue's copies before
+    // entering the loop, which uses registers loaded outside it: one latency
+    // per tile.
     u32x4 bcur[4][R16];
     {
-        const int row = row0 + n;
+        const int row = FULL ? row0 + n : (row0 + n < d_out ? row0 + n : d_out - 1);
+        const bool r_full = FULL || r == RPAD;
+        const bool r_vec = (r & 7) == 0;
 #pragma unroll
-        for (int slot = 0; slot < 4; ++slot)
+        for (int slot = 0; slot < 4; ++slot) {
+            const bool on = sc.e[slot] >= 0;
+            const uint16_t* bp = on ? Bb + ((int64_t)sc.e[slot] * d_out + row) * r + 8 * h
+                                    : (const uint16_t*)a.zimg + n * RPAD + 8 * h;
 #pragma unroll
             for (int ks = 0; ks < R16; ++ks) {
                 const int rho0 = ks * 16 + 8 * h;
-                const uint16_t* bp = Bb + ((int64_t)sc.e[slot] * d_out + row) * r + rho0;
-                u32x4 v = zero;
-                if (FULL) {
-                    if (act[slot]) v = ld128(bp);
-                } else if (act[slot] && row < d_out && rho0 < r) {
-                    if (r_vec) {
-                        v = ld128(bp);
-                    } else {
+                if (r_full || !on) {
+                    bcur[slot][ks] = ld128(bp + ks * 16);
+                } else if (r_vec) {
+                    bcur[slot][ks] = rho0 < r ? ld128(bp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+                } else {
+                    u32x4 v;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t lo = (rho0 + 2 * j < r) ? gld(bp + 2 * j) : 0u;
-                            const uint32_t hi = (rho0 + 2 * j + 1 < r) ? gld(bp + 2 * j + 1) : 0u;
-                            v[j] = lo | (hi << 16);
-                        }
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t lo = (rho0 + 2 * j < r) ? gld(bp + ks * 16 + 2 * j) : 0u;
+                        const uint32_t hi = (rho0 + 2 * j + 1 < r) ? gld(bp + ks * 16 + 2 * j + 1) : 0u;
+                        v[j] = lo | (hi << 16);
                     }
+                    bcur[slot][ks] = v;
                 }
-                bcur[slot][ks] = v;
             }
-    }
-    // W of sub-band sb, row-major: instruction i reads row 8i + lr, columns 8lc .. +8
-    auto load_w = [&](u32x4 (&wv)[4], int sb) {
-        const int col = col_base + sb * 64 + 8 * lc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = row0 + 8 * i + lr;
-            const uint16_t* p = W + (int64_t)row * d_in + col;
-            if (FULL) wv[i] = ld128(p);
-            else wv[i] = (row < d_out && col < d_in) ? ld128(p) : zero;
         }
-    };
-    // one 32 x 64 unit; its W registers are refilled with sub-band sb + 2 as
-    // soon as they are in the scratch
-    auto unit = [&](u32x4 (&wv)[4], int sb) {
+    }
+
+    auto unit = [&](int sb) {
         const uint16_t* Acur = As + (sb & 1) * BUF_ELEMS;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)(ws + w_off(8 * i + lr, lc)) = wv[i];
-        if (sb + 2 < nsb) load_w(wv, sb + 2);
+        uint16_t* ws = Wb + (sb % kWideWBufs) * WBUF + w * WBLK;
 #pragma unroll 1
         for (int b = 0; b < 2; ++b) {
             u32x4 wm[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) wm[q] = *(const u32x4*)(ws + w_off(n, 4 * b + 2 * h + q));
             // rank chunk outermost: the four slots' MFMAs of a chunk are
-            // independent, so they issue back to back; each slot still sums its
-            // chunks in order (an inactive slot multiplies zeros)
+            // independent and issue back to back; each slot sums its chunks in
+            // order (an inactive slot multiplies zeros)
             f32x16 P[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
             const uint16_t* ap = Acur + b * 32 * RPAD + n * RPAD;
+            // the next chunk's four A operands are read while this chunk's MFMAs run
+            u32x4 ao[2][4];
+#pragma unroll
+            for (int slot = 0; slot < 4; ++slot)
+                ao[0][slot] = *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, h) << 3));
 #pragma unroll
             for (int ks = 0; ks < R16; ++ks) {
-                u32x4 ao[4];
+                if (ks + 1 < R16) {
 #pragma unroll
-                for (int slot = 0; slot < 4; ++slot)
-                    ao[slot] = *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, 2 * ks + h) << 3));
+                    for (int slot = 0; slot < 4; ++slot)
+                        ao[(ks + 1) & 1][slot] =
+                            *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, 2 * ks + 2 + h) << 3));
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int slot = 0; slot < 4; ++slot) P[slot] = mfma32(ao[slot], bcur[slot][ks], P[slot]);
+                for (int slot = 0; slot < 4; ++slot) P[slot] = mfma32(ao[ks & 1][slot], bcur[slot][ks], P[slot]);
             }
             uint32_t ow[8];
 #pragma unroll
@@ -509,171 +521,20 @@ __device__ __forceinline__ void switch_wide_tile(const SwitchArgs& a, const Sets
         }
     };
 
-    u32x4 av[4][NSTAGE];
-    u32x4 wA[4], wB[4];
-    load_a(av, 0);
-    load_w(wA, 0);
-    if (nsb > 1) load_w(wB, 1);
-    store_a(av, As);
-    __syncthreads();
-    // sub-bands in pairs so each W buffer keeps its role (no register copies)
-#pragma unroll 1
-    for (int sb = 0; sb < nsb; sb += 2) {
-        if (sb + 1 < nsb) load_a(av, sb + 1);
-        unit(wA, sb);
-        if (sb + 1 < nsb) store_a(av, As + ((sb + 1) & 1) * BUF_ELEMS);
-        __syncthreads();
-        if (sb + 1 < nsb) {
-            if (sb + 2 < nsb) load_a(av, sb + 2);
-            unit(wB, sb + 1);
-            if (sb + 2 < nsb) store_a(av, As + ((sb + 2) & 1) * BUF_ELEMS);
-            __syncthreads();
-        }
-    }
-}
-
-// Wide tiles entirely inside their weight (every tile of the model shapes)
-// stage both operands with direct global -> LDS copies instead of through
-// registers, so the copies can run further ahead of the MFMAs:
-//   * A: the handle keeps every (expert, 64-column block) slice as a packed
-//     image already in the LDS layout above, so a sub-band's four slot slices
-//     are four contiguous copies (an inactive slot copies the zero image).  Two
-//     buffers; the next sub-band's copy is issued right after the barrier that
-//     frees its buffer.
-//   * W: each wave copies its own 32 x 64 block, row-major and chunk-swizzled
-//     (lane L fetches the chunk that belongs at LDS position L), into one of
-//     three per-wave buffers, two sub-bands ahead; the result goes back out
-//     through the same buffer as above.
-// Each wait names the exact number of vector-memory instructions (copies and W
-// stores, the only ones issued in the loop) that follow the copy it waits for;
-// scheduling barriers keep the compiler from moving any of them across.
-constexpr int kWideWBufs = 3;
-
-template <typename T>
-__device__ __forceinline__ T pick4(int i, T v0, T v1, T v2, T v3) {
-    return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
-}
-
-template <int R16, int NSB>
-__device__ __forceinline__ void switch_wide_tile_copy(const SwitchArgs& a, const Sets& sc, const SwDesc& D,
-                                                      int row_base, int col_base, uint16_t* smem) {
-    constexpr int RPAD = R16 * 16;
-    constexpr int SLOT_ELEMS = 2 * 32 * RPAD;        // one slot's image of one sub-band
-    constexpr int BUF_ELEMS = 4 * SLOT_ELEMS;
-    constexpr int KB = 512;                          // bf16 elements per 1 KB copy instruction
-    constexpr int NAI = 4 * SLOT_ELEMS / KB / kWW;   // A copies per wave per sub-band (= R16)
-    constexpr int WBLK = 32 * 64;                    // one wave's W block
-    constexpr int WBUF = kWW * WBLK;
-    static_assert((4 * SLOT_ELEMS / KB) % kWW == 0, "A copies split evenly over the waves");
-    static_assert(NSB >= 3, "the copy schedule assumes at least three sub-bands");
-    uint16_t* As = smem;                              // [2][BUF_ELEMS]
-    uint16_t* Wb = smem + 2 * BUF_ELEMS;              // [kWideWBufs][kWW][WBLK]
-    const int d_in = D.d_in, d_out = D.d_out, r = a.r;
-    const uint16_t* __restrict__ Bb = (const uint16_t*)D.B;
-    uint16_t* __restrict__ W = (uint16_t*)D.W;
-    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
-    const int lr = lane >> 3, lc = lane & 7;
-    const int row0 = row_base + w * 32;
-
-    // first-sub-band image of each slot; the zero image does not advance
-    const int64_t n_cb = (d_in + 63) / 64;
-    const uint16_t* img[4];
-    int step[4];
-#pragma unroll
-    for (int slot = 0; slot < 4; ++slot) {
-        const bool on = sc.e[slot] >= 0;
-        img[slot] = on ? (const uint16_t*)D.Ap + ((int64_t)sc.e[slot] * n_cb + col_base / 64) * SLOT_ELEMS
-                       : (const uint16_t*)a.zimg;
-        step[slot] = on ? SLOT_ELEMS : 0;
-    }
-    auto copy_a = [&](int sb) {
-        uint16_t* dst = As + (sb & 1) * BUF_ELEMS;
-#pragma unroll
-        for (int j = 0; j < NAI; ++j) {
-            const int q = j * kWW + w;  // 1 KB piece q of the sub-band's four images
-            const int slot = q / (SLOT_ELEMS / KB), piece = q % (SLOT_ELEMS / KB);
-            const uint16_t* src = pick4(slot, img[0], img[1], img[2], img[3]) +
-                                  (int64_t)sb * pick4(slot, step[0], step[1], step[2], step[3]) + piece * KB;
-            copy16_to_lds(src + lane * 8, dst + q * KB);
-        }
-    };
-    auto copy_w = [&](int sb) {
-        uint16_t* dst = Wb + (sb % kWideWBufs) * WBUF + w * WBLK;
-        const int col = col_base + sb * 64 + 8 * (lc ^ lr);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) copy16_to_lds(W + (int64_t)(row0 + 8 * i + lr) * d_in + col, dst + i * KB);
-    };
-
-    // B rows of the wave's 32 rows; an inactive slot reads zeros from the zero
-    // image (rows of RPAD there), so every load issues unconditionally.  (The
-    // compiler drains the copies of the prologue before entering the loop, as
-    // the loop uses registers loaded outside it: one latency per tile.)
-    u32x4 bcur[4][R16];
-#pragma unroll
-    for (int slot = 0; slot < 4; ++slot) {
-        const uint16_t* bp = sc.e[slot] >= 0 ? Bb + ((int64_t)sc.e[slot] * d_out + row0 + n) * r + 8 * h
-                                             : (const uint16_t*)a.zimg + n * RPAD + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < R16; ++ks) bcur[slot][ks] = ld128(bp + ks * 16);
-    }
-
-    auto unit = [&](int sb) {
-        const uint16_t* Acur = As + (sb & 1) * BUF_ELEMS;
-        uint16_t* ws = Wb + (sb % kWideWBufs) * WBUF + w * WBLK;
-#pragma unroll 1
-        for (int b = 0; b < 2; ++b) {
-            u32x4 wm[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) wm[q] = *(const u32x4*)(ws + w_off(n, 4 * b + 2 * h + q));
-            f32x16 P[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-            const uint16_t* ap = Acur + b * 32 * RPAD + n * RPAD;
-#pragma unroll
-            for (int ks = 0; ks < R16; ++ks) {
-                u32x4 ao[4];
-#pragma unroll
-                for (int slot = 0; slot < 4; ++slot)
-                    ao[slot] = *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, 2 * ks + h) << 3));
-#pragma unroll
-                for (int slot = 0; slot < 4; ++slot) P[slot] = mfma32(ao[slot], bcur[slot][ks], P[slot]);
-            }
-            uint32_t ow[8];
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const uint32_t word = wm[p >> 2][p & 3];
-                float o2[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int i = 2 * p + j;
-                    const float sn = fmaf(sc.c[1], P[1][i], sc.c[0] * P[0][i]);
-                    const float so = fmaf(sc.c[3], P[3][i], sc.c[2] * P[2][i]);
-                    const float wf = j ? bf_hi(word) : bf_lo(word);
-                    o2[j] = wf - (so - sn);
-                }
-                ow[p] = pack2_bf16(o2[0], o2[1]);
-            }
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                *(u32x4*)(ws + w_off(n, 4 * b + 2 * h + q)) =
-                    u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
-        }
-        const int col = col_base + sb * 64 + 8 * lc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            st128(W + (int64_t)(row0 + 8 * i + lr) * d_in + col, *(const u32x4*)(ws + w_off(8 * i + lr, lc)));
-    };
-
     // issue order: B loads, A(0), W(0), W(1); then per sub-band sb: A(sb+1),
-    // W(sb+2), the 4 stores of sb
+    // W(sb+2), the stores of sb (4 per wave in full tiles; an edge tile's
+    // guarded stores are drained before the next sub-band so the counts hold)
     copy_a(0);
     __builtin_amdgcn_sched_barrier(0);
     copy_w(0);
     __builtin_amdgcn_sched_barrier(0);
-    copy_w(1);
+    if (nsb > 1) copy_w(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
-    for (int sb = 0; sb < NSB; ++sb) {
-        const bool more1 = sb + 1 < NSB, more2 = sb + 2 < NSB;
-        // A(sb): followed by W(sb+1) (if any) and the stores of sb-1 (W(0), W(1) for sb = 0)
+    for (int sb = 0; sb < nsb; ++sb) {
+        const bool more1 = sb + 1 < nsb, more2 = sb + 2 < nsb;
+        // A(sb) is followed by W(sb+1) (if any) and the stores of sb-1 (W(0)
+        // for sb = 0: the same count)
         wait_vmcnt_le<8>(4 + (more1 ? 4 : 0));
         __builtin_amdgcn_s_barrier();  // A(sb) is in LDS for every wave; A buffer (sb+1)&1 is free
         __builtin_amdgcn_sched_barrier(0);
@@ -681,19 +542,18 @@ __device__ __forceinline__ void switch_wide_tile_copy(const SwitchArgs& a, const
         __builtin_amdgcn_sched_barrier(0);
         if (more2) copy_w(sb + 2);
         __builtin_amdgcn_sched_barrier(0);
-        // W(sb): issued after it were the stores of sb-2; A(sb), W(sb+1) and
-        // the stores of sb-1; A(sb+1) and W(sb+2) (fewer for sb < 2 and at the end)
-        if (sb >= 2 && more2) {
+        // W(sb) is followed, in issue order, by: the stores of sb-2 (sb >= 2);
+        // A(sb) (sb >= 1); W(sb+1) (if any); the stores of sb-1 (sb >= 1);
+        // A(sb+1) and W(sb+2) (if any)
+        if (FULL && sb >= 2 && more2) {
             wait_vmcnt<16 + 2 * NAI>();
         } else {
-            int after;
-            if (sb == 0) after = 4 + NAI + 4;  // W(1), A(1), W(2)
-            else if (sb == 1) after = NAI + 4 + 4 + NAI + (more2 ? 4 : 0);
-            else after = 4 + NAI + (more1 ? 4 : 0) + 4 + (more1 ? NAI : 0);
+            const int after = (sb >= 1 ? 4 + NAI : 0) + (sb >= 2 ? 4 : 0) + (more1 ? 4 + NAI : 0) + (more2 ? 4 : 0);
             wait_vmcnt_le<16 + 2 * NAI>(after);
         }
         __builtin_amdgcn_sched_barrier(0);
         unit(sb);
+        if (!FULL) wait_vmcnt<0>();
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -701,11 +561,8 @@ __device__ __forceinline__ void switch_wide_tile_copy(const SwitchArgs& a, const
 template <int R16, int NSB>
 __global__ __launch_bounds__(kWW* kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void switch_wide_kernel(SwitchArgs a) {
-    // 2 x [4 slots][2][32][R16*16] A slices, then 8 x [32][64] W scratch (the
-    // copy-staged tiles: then kWideWBufs x 8 x [32][64] W buffers)
+    // 2 x [4 slots][2][32][R16*16] A images, then kWideWBufs x 8 x [32][64] W buffers
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    uint16_t* As = smem;
-    uint16_t* Ws = smem + 2 * 4 * 2 * 32 * (R16 * 16);
     const int64_t bid = blockIdx.x;
     const int64_t t = (bid & 7) * a.per_xcd + (bid >> 3);
     if (t >= a.n_units) return;
@@ -724,12 +581,10 @@ void switch_wide_kernel(SwitchArgs a) {
     const int rt = grp * kWGroup + (int)(lg % in_grp), ct = (int)(lg / in_grp);
     const int row_base = rt * kWRT, col_base = ct * (64 * NSB);
     const bool full = row_base + kWRT <= D.d_out && col_base + 64 * NSB <= D.d_in && a.r == R16 * 16;
-    if (full && D.Ap != nullptr)
-        switch_wide_tile_copy<R16, NSB>(a, sc, D, row_base, col_base, smem);
-    else if (full)
-        switch_wide_tile<R16, NSB, true>(a, sc, D, row_base, col_base, As, Ws);
+    if (full)
+        switch_wide_tile<R16, NSB, true>(a, sc, D, row_base, col_base, smem);
     else
-        switch_wide_tile<R16, NSB, false>(a, sc, D, row_base, col_base, As, Ws);
+        switch_wide_tile<R16, NSB, false>(a, sc, D, row_base, col_base, smem);
 }
 
 // ---- element-wise path: fp32 weights (and any shape) ----------------------
