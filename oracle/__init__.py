@@ -54,6 +54,8 @@ def _bind(lib):
     lib.dlmref_switch_rows.argtypes = [P, P, I64, P, P, I64, I64, I32, I32, D, I32,
                                        P, P, P, P, P, P]
     lib.dlmref_sgmm_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, I32, D, I32, P, P]
+    lib.dlmref_gemv.argtypes = [P, P, I64, I64, I32, P, P, P]
+    lib.dlmref_gemv.restype = C.c_int
     lib.dlmref_round.argtypes = [P, I64, I32, P]
     lib.dlmref_threads.restype = C.c_int
     lib.dlmref_set_threads.argtypes = [C.c_int]
@@ -187,6 +189,27 @@ def sgmm(x, idx, g, A, B, y, scale, with_stats=False, lib=None):
     if rc != 0:
         raise ValueError(f"dlmref_sgmm_rows failed ({rc})")
     out = _to_torch(ya, dt)
+    if with_stats:
+        return out, torch.from_numpy(ex), torch.from_numpy(ab)
+    return out
+
+
+def gemv(W, x, with_stats=False, lib=None):
+    """y = round_fp32(W @ x) for W [d_out][d_in], x [d_in] (fp32 torch out);
+    with_stats also returns (exact f64 [d_out], absum f64 [d_out])."""
+    lib = lib or load()
+    wa, dt = _np(W)
+    xa, dtx = _np(x)
+    assert dt == dtx and dt is not None
+    d_out, d_in = wa.shape
+    assert xa.shape == (d_in,)
+    y = np.empty((d_out,), np.float32)
+    ex = np.empty((d_out,), np.float64) if with_stats else None
+    ab = np.empty((d_out,), np.float64) if with_stats else None
+    rc = lib.dlmref_gemv(_ptr(wa), _ptr(xa), d_out, d_in, dt, _ptr(y), _ptr(ex), _ptr(ab))
+    if rc != 0:
+        raise ValueError(f"dlmref_gemv failed ({rc})")
+    out = torch.from_numpy(y)
     if with_stats:
         return out, torch.from_numpy(ex), torch.from_numpy(ab)
     return out

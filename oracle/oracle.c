@@ -289,6 +289,36 @@ int dlmref_sgmm_rows(const void* x, const int32_t* idx, const float* g,
     return 0;
 }
 
+/* ---- merged-weight matrix-vector product ---------------------------------- */
+
+/*
+ * The decode step that follows a switch: with the token's adapters merged into
+ * the backbone, each adapted projection is the plain product of the merged
+ * weight with the layer input (Chinese digest, "technical framework": the fused
+ * kernel merges the selected adapter parameters into the backbone and carries
+ * out the computation in a single kernel).
+ *   y[i] = round_fp32( sum_j W[i][j] * x[j] ),  W [d_out][d_in], x [d_in] (dt)
+ * Optional exact [d_out] gets the unrounded binary64 sum and absum [d_out] the
+ * sum of |W[i][j] * x[j]|.
+ */
+int dlmref_gemv(const void* W, const void* x, int64_t d_out, int64_t d_in, int32_t dt,
+                float* y, double* exact, double* absum) {
+    if (!W || !x || !y || d_out < 1 || d_in < 1) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < d_out; ++i) {
+        double acc = 0.0, acc_abs = 0.0;
+        for (int64_t j = 0; j < d_in; ++j) {
+            double p = ld(W, i * d_in + j, dt) * ld(x, j, dt);
+            acc += p;
+            acc_abs += fabs(p);
+        }
+        if (exact) exact[i] = acc;
+        if (absum) absum[i] = acc_abs;
+        y[i] = (float)acc;  /* C conversion: RNE */
+    }
+    return 0;
+}
+
 /* Threads OpenMP will use (1 when built without OpenMP). */
 #ifdef _OPENMP
 #include <omp.h>

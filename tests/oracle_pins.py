@@ -12,6 +12,8 @@ must fail).  What each pin holds the oracle to:
   roundtrip A -> B -> A returns the starting weights within the rounding bound
   merged    merged weights applied to x = base output + unmerged adapters
   gemm      SGMM with one set for every row = a dense textbook GEMM
+  gemv      merged-weight product against NumPy's binary64 matmul; merged
+            product = base product + unmerged adapters + the rounding of W
   rounding  one nearest-even rounding to bf16 / fp32
 """
 from __future__ import annotations
@@ -269,6 +271,48 @@ def pin_merged_equals_unmerged(lib):
     assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ gemv ----
+
+def pin_gemv_golden(lib):
+    for c in _golden("gemv_tiny.json")["cases"]:
+        dt = torch.float32 if c["dtype"] == "fp32" else torch.bfloat16
+        y = oracle.gemv(_t(c["W"], dt), _t(c["x"], dt), lib=lib)
+        assert torch.equal(y, torch.tensor(c["y"], dtype=torch.float32)), (c, y)
+
+
+def pin_gemv_numpy(lib):
+    rng = _rng(41)
+    for dt in (torch.float32, torch.bfloat16):
+        for d_out, d_in in ((1, 1), (7, 13), (33, 257)):
+            W = torch.from_numpy(rng.standard_normal((d_out, d_in))).to(dt)
+            x = torch.from_numpy(rng.standard_normal(d_in)).to(dt)
+            y, ex, ab = oracle.gemv(W, x, with_stats=True, lib=lib)
+            ref = W.double().numpy() @ x.double().numpy()
+            assert np.allclose(ex.numpy(), ref, rtol=1e-12, atol=1e-12 * ab.numpy().max())
+            assert np.allclose(ab.numpy(), np.abs(W.double().numpy()) @ np.abs(x.double().numpy()), rtol=1e-12)
+            assert (_fp32_ulps(y.numpy(), ref.astype(np.float32)) <= 1).all()
+
+
+def pin_gemv_merged(lib):
+    """Product with the merged (rounded) weight = base product + unmerged
+    adapters + x applied to the rounding of the merged weight."""
+    rng = _rng(42)
+    E, r, d_out, d_in = 4, 3, 9, 21
+    for dt in (torch.float32, torch.bfloat16):
+        A, B = _rand_bank(rng, E, r, d_in, d_out, dt)
+        W0 = torch.from_numpy(rng.standard_normal((d_out, d_in))).to(dt)
+        x = torch.from_numpy(rng.standard_normal(d_in)).to(dt)
+        S = ([3, 1], [0.625, 0.375])
+        Wm, Wm_ex, _ = oracle.switch(W0, A, B, 1.5, None, S, with_stats=True, lib=lib)
+        _, lhs, ab = oracle.gemv(Wm, x, with_stats=True, lib=lib)
+        _, base, _ = oracle.gemv(W0, x, with_stats=True, lib=lib)
+        _, ys, _ = oracle.sgmm(x.reshape(1, d_in), [S[0]], [S[1]], A, B, torch.zeros(1, d_out, dtype=dt), 1.5,
+                               with_stats=True, lib=lib)
+        rnd = (Wm.double() - Wm_ex).numpy() @ x.double().numpy()
+        rhs = base.numpy() + ys.numpy()[0] + rnd
+        assert np.allclose(lhs.numpy(), rhs, rtol=0, atol=1e-12 * (ab.numpy().max() + 1))
+
+
 # ------------------------------------------------------------------ sgmm ----
 
 def pin_sgmm_golden(lib):
@@ -361,6 +405,7 @@ ALL_PINS = [
     pin_router_golden, pin_router_brute, pin_router_closed_form, pin_router_permutation,
     pin_switch_golden, pin_switch_premerge, pin_switch_general, pin_switch_noop,
     pin_switch_roundtrip, pin_merged_equals_unmerged,
+    pin_gemv_golden, pin_gemv_numpy, pin_gemv_merged,
     pin_sgmm_golden, pin_sgmm_gemm, pin_sgmm_brute, pin_sgmm_properties,
     pin_rounding,
 ]

@@ -36,6 +36,11 @@ MUTANTS = [
      "double b = ld(B, ((int64_t)idx[2 * t] * d_out + o) * r + rho, dt);"),
     ("sgmm_x_row", "double p = ld(x, t * d_in + j, dt) * ld(A,", "double p = ld(x, 0 * d_in + j, dt) * ld(A,"),
     ("sgmm_v_slot", "acc += v[k * r + rho] * b;", "acc += v[rho] * b;"),
+    ("gemv_x_reversed", "* ld(x, j, dt);", "* ld(x, d_in - 1 - j, dt);"),
+    ("gemv_W_transposed", "double p = ld(W, i * d_in + j, dt)", "double p = ld(W, j * d_out + i, dt)"),
+    ("gemv_drop_last", "for (int64_t j = 0; j < d_in; ++j) {\n            double p = ld(W,",
+     "for (int64_t j = 0; j + 1 < d_in; ++j) {\n            double p = ld(W,"),
+    ("gemv_truncate", "y[i] = (float)acc;  /* C conversion: RNE */", "y[i] = (float)trunc(acc * 1048576.0) / 1048576.0f;"),
     # an empty slot (-1) read as expert 0 everywhere it is tested
     ("empty_slot_as_expert0", "if (e < 0) continue;", "if (e < 0) e = 0;", 3),
 ]
