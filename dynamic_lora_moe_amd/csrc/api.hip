@@ -60,6 +60,9 @@ struct dlm_layers {
     int32_t* d_err = nullptr;
     void* d_pack = nullptr;       // packed A images of every weight, then the zero image (wide tiles)
     void* d_zimg = nullptr;
+    float* d_part = nullptr;      // partial products of the fused switch + product (bound vectors)
+    bool bound = false;           // dlm_layers_bind_vectors has been called
+    int64_t n_blocks = 0, n_bands = 0;  // 16-row blocks and 256-row bands over all weights
     std::vector<SwDesc> h_descs;
     int32_t n = 0;
     int32_t E = 0, r = 0;
@@ -123,7 +126,7 @@ int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, fl
     if (!std::isfinite(scale)) return fail(DLM_EINVAL, "layers_create: scale is not finite");
     const SwTile tile = switch_tile_for_rank(r);
     std::vector<SwDesc> h(n);
-    int64_t tiles = 0, elems = 0;
+    int64_t tiles = 0, elems = 0, blocks = 0, bands = 0;
     for (int i = 0; i < n; ++i) {
         const dlm_proj& p = projs[i];
         if (!p.W || !p.A || !p.B) return fail(DLM_EINVAL, "layers_create: proj %d has a null pointer", i);
@@ -147,6 +150,13 @@ int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, fl
         d.tile0 = tiles;
         d.elem0 = elems;
         d.Ap = nullptr;
+        d.xv = nullptr;
+        d.yv = nullptr;
+        d.part = nullptr;
+        d.rb0 = blocks;
+        d.rt0 = bands;
+        blocks += (p.d_out + 15) / 16;
+        bands += (p.d_out + 255) / 256;
         tiles += (int64_t)d.n_rt * d.n_ct;
         elems += p.d_out * p.d_in;
     }
@@ -161,6 +171,8 @@ int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, fl
     hd->n_tiles = tiles;
     hd->n_elems = elems;
     hd->per_xcd = (tiles + 7) / 8;
+    hd->n_blocks = blocks;
+    hd->n_bands = bands;
     hipError_t e = hipSuccess;
     if (dtype == DLM_BF16 && switch_packs_a(tile)) {
         // ranks 17..64: packed A images for the copy-staged tiles, one block
@@ -216,9 +228,34 @@ int dlm_layers_destroy(dlm_layers* h) {
     if (h->d_descs) (void)hipFree(h->d_descs);
     if (h->d_err) (void)hipFree(h->d_err);
     if (h->d_pack) (void)hipFree(h->d_pack);
+    if (h->d_part) (void)hipFree(h->d_part);
     delete h;
     if (e != hipSuccess) return hip_fail(e, "layers_destroy");
     return ok();
+}
+
+static SwitchArgs switch_args(const dlm_layers* h, const int32_t* old_idx, const float* old_g,
+                              const int32_t* new_idx, const float* new_g) {
+    SwitchArgs a;
+    a.descs = h->d_descs;
+    a.n_desc = h->n;
+    a.E = h->E;
+    a.r = h->r;
+    a.scale = h->scale;
+    a.old_idx = old_idx;
+    a.old_g = old_g;
+    a.new_idx = new_idx;
+    a.new_g = new_g;
+    a.err = h->d_err;
+    a.zimg = h->d_zimg;
+    if (h->dtype == DLM_BF16) {
+        a.n_units = h->n_tiles;
+        a.per_xcd = h->per_xcd;
+    } else {
+        a.n_units = h->n_elems;
+        a.per_xcd = 0;
+    }
+    return a;
 }
 
 int dlm_switch(dlm_layers* h, const int32_t* old_idx, const float* old_g, const int32_t* new_idx,
@@ -253,6 +290,77 @@ int dlm_switch(dlm_layers* h, const int32_t* old_idx, const float* old_g, const 
 }
 
 int dlm_switch_launches(const dlm_layers* h) { return h ? 1 : 0; }
+
+// ------------------------------------------------- merged-weight products ----
+
+int dlm_layers_bind_vectors(dlm_layers* h, const void* const* x, float* const* y) {
+    if (!h || !x || !y) return fail(DLM_EINVAL, "bind_vectors: null argument");
+    std::vector<SwDesc> d = h->h_descs;
+    for (int i = 0; i < h->n; ++i) {
+        if (!x[i] || !y[i]) return fail(DLM_EINVAL, "bind_vectors: vector %d is null", i);
+        if (h->dtype == DLM_BF16 && !aligned16(x[i]))
+            return fail(DLM_EALIGN, "bind_vectors: x %d not 16-byte aligned", i);
+        if (((uintptr_t)y[i] & 3u) != 0) return fail(DLM_EALIGN, "bind_vectors: y %d not 4-byte aligned", i);
+        if (overlap(x[i], (size_t)d[i].d_in * esize(h->dtype), y[i], (size_t)d[i].d_out * 4) ||
+            overlap(d[i].W, (size_t)d[i].d_out * d[i].d_in * esize(h->dtype), y[i], (size_t)d[i].d_out * 4))
+            return fail(DLM_EINVAL, "bind_vectors: y %d overlaps its x or W", i);
+        d[i].xv = x[i];
+        d[i].yv = y[i];
+    }
+    float* part = nullptr;
+    hipError_t e = hipSuccess;
+    if (switch_gemv_fused(h->tile, h->dtype)) {
+        size_t total = 0;
+        for (const SwDesc& q : d) total += (size_t)q.n_ct * q.d_out;
+        e = hipMalloc((void**)&part, total * sizeof(float));
+        size_t off = 0;
+        for (int i = 0; i < h->n && e == hipSuccess; ++i) {
+            d[i].part = part + off;
+            off += (size_t)d[i].n_ct * d[i].d_out;
+        }
+    }
+    if (e == hipSuccess) e = hipMemcpy(h->d_descs, d.data(), sizeof(SwDesc) * h->n, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (part) (void)hipFree(part);
+        return hip_fail(e, "bind_vectors");
+    }
+    if (h->d_part) (void)hipFree(h->d_part);
+    h->d_part = part;
+    h->h_descs = std::move(d);
+    h->bound = true;
+    return ok();
+}
+
+int dlm_gemv(dlm_layers* h, void* stream) {
+    if (!h) return fail(DLM_EINVAL, "gemv: null handle");
+    if (!h->bound) return fail(DLM_EINVAL, "gemv: no vectors bound (dlm_layers_bind_vectors)");
+    const SwitchArgs a = switch_args(h, nullptr, nullptr, nullptr, nullptr);
+    hipError_t e = launch_gemv(a, h->n_blocks, h->dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gemv launch");
+    return ok();
+}
+
+int dlm_switch_gemv(dlm_layers* h, const int32_t* old_idx, const float* old_g, const int32_t* new_idx,
+                    const float* new_g, void* stream) {
+    if (!h) return fail(DLM_EINVAL, "switch_gemv: null handle");
+    if (!h->bound) return fail(DLM_EINVAL, "switch_gemv: no vectors bound (dlm_layers_bind_vectors)");
+    if ((old_idx && !old_g) || (new_idx && !new_g))
+        return fail(DLM_EINVAL, "switch_gemv: a set has indices but no gates");
+    const SwitchArgs a = switch_args(h, old_idx, old_g, new_idx, new_g);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (switch_gemv_fused(h->tile, h->dtype)) {
+        e = launch_switch_gemv_bf16(a, s);
+        if (e == hipSuccess) e = launch_gemv_reduce(a, h->n_bands, s);
+    } else {
+        e = h->dtype == DLM_BF16 ? launch_switch_bf16(a, h->tile, s) : launch_switch_generic(a, h->dtype, s);
+        if (e == hipSuccess) e = launch_gemv(a, h->n_blocks, h->dtype, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "switch_gemv launch");
+    return ok();
+}
+
+int dlm_switch_gemv_launches(const dlm_layers* h) { return h ? 2 : 0; }
 
 int dlm_layers_status(dlm_layers* h, int32_t* code, void* stream) {
     if (!h || !code) return fail(DLM_EINVAL, "layers_status: null argument");

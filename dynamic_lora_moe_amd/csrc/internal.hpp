@@ -20,6 +20,12 @@ struct SwDesc {
     int64_t tile0;      // index of its first tile in the launch (prefix sum)
     int64_t elem0;      // index of its first element (generic path)
     const void* Ap;     // packed A images of the wide tiles (ranks 17..64), else null
+    // merged-weight products (dlm_gemv / dlm_switch_gemv), once vectors are bound
+    const void* xv;     // [d_in], the weight's input
+    float* yv;          // [d_out] fp32, its output
+    float* part;        // [n_ct][d_out] fp32 per-column-tile partial products (fused path)
+    int64_t rb0;        // index of its first 16-row block in a product launch
+    int64_t rt0;        // index of its first 256-row band in a partial-sum launch
 };
 
 struct SwitchArgs {
@@ -46,6 +52,18 @@ struct SwTile {
 SwTile switch_tile_for_rank(int r);
 
 hipError_t launch_switch_bf16(const SwitchArgs& a, const SwTile& t, hipStream_t s);
+
+// y = W x for every weight of a.descs (bound vectors), one launch: n_blocks
+// 16-row blocks over all weights.  With sets in a (after a switch), sets the
+// switch rejects leave y alone.
+hipError_t launch_gemv(const SwitchArgs& a, int64_t n_blocks, int dtype, hipStream_t s);
+// Whether the fused switch + product kernel serves this configuration (bf16,
+// ranks up to 16); it writes per-column-tile partial products, which
+// launch_gemv_reduce then adds up in a fixed order (n_bands 256-row bands;
+// it writes nothing for sets the switch rejects).
+bool switch_gemv_fused(const SwTile& t, int dtype);
+hipError_t launch_switch_gemv_bf16(const SwitchArgs& a, hipStream_t s);
+hipError_t launch_gemv_reduce(const SwitchArgs& a, int64_t n_bands, hipStream_t s);
 
 // Packed A images used by the wide tiles (ranks 17..64, bf16): for expert e and
 // 64-column block cb of a weight, one contiguous image of the block's A slice

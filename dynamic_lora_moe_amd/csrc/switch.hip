@@ -98,13 +98,20 @@ __device__ __forceinline__ Sets read_sets(const SwitchArgs& a) {
     return s;
 }
 
-template <bool kByTile>
+// Which prefix a launch's work units are numbered by.
+enum { kKeyElem = 0, kKeyTile = 1, kKeyRowBlock = 2, kKeyBand = 3 };
+
+template <int K>
+__device__ __forceinline__ int64_t desc_key(const SwDesc& d) {
+    return K == kKeyElem ? d.elem0 : (K == kKeyTile ? d.tile0 : (K == kKeyRowBlock ? d.rb0 : d.rt0));
+}
+
+template <int K>
 __device__ __forceinline__ int find_desc(const SwDesc* __restrict__ d, int n, int64_t u) {
     int lo = 0, hi = n - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        const int64_t start = kByTile ? d[mid].tile0 : d[mid].elem0;
-        if (start <= u) lo = mid; else hi = mid - 1;
+        if (desc_key<K>(d[mid]) <= u) lo = mid; else hi = mid - 1;
     }
     return lo;
 }
@@ -135,9 +142,17 @@ __device__ __forceinline__ int w_off(int row, int chunk) {  // bf16 element offs
 // is in range (all tiles of model-sized weights): then no load or store carries
 // a guard, so the compiler issues them back to back instead of branching
 // around each one.  Edge tiles run the guarded instance.
-template <int R16, int CT, bool FULL>
+//
+// GEMV = also form the tile's share of y = W' x (the fused switch + product):
+// every lane multiplies its 16 new (rounded) weights of a 32-column block with
+// the matching x values, in column order, and adds them to a running sum over
+// the tile's columns; the two half-waves' sums of a row are then added (lower
+// half first) and stored as the tile's partial product of that row.  Xs holds
+// the tile's CT x values (zero past d_in).
+template <int R16, int CT, bool FULL, bool GEMV = false>
 __device__ __forceinline__ void switch_tile(const SwitchArgs& a, const Sets& sc, const SwDesc& D,
-                                            int row_base, int col_base, uint16_t* As, uint16_t* Ws) {
+                                            int row_base, int col_base, uint16_t* As, uint16_t* Ws,
+                                            const uint16_t* Xs = nullptr) {
     constexpr int RPAD = R16 * 16;
     constexpr int NCB = CT / 32;   // 32-column MFMA blocks per tile
     constexpr int NSUB = CT / 64;  // 64-column steps per row group
@@ -218,6 +233,7 @@ __device__ __forceinline__ void switch_tile(const SwitchArgs& a, const Sets& sc,
     u32x4 wcur[4], wnxt[4];
     load_b(bcur, 0);
     load_w(wcur, 0);
+    float ysum = 0.f;  // GEMV: this lane's running share of its row's product
 
     // 2) transpose the A slices into LDS: As[slot][cb][m][rho] = A[e][rho][col(cb, m)]
     //    (an inactive slot's slice too: its loads gave zeros, so the MFMAs below
@@ -293,6 +309,25 @@ __device__ __forceinline__ void switch_tile(const SwitchArgs& a, const Sets& sc,
             for (int q = 0; q < 2; ++q)
                 *(u32x4*)(ws + w_off(n, 4 * b + 2 * h + q)) =
                     u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
+            if constexpr (GEMV) {
+                // columns 32b + 16h + 2p (+1) of this 64-column step hold ow[p]
+                const uint16_t* xp = Xs + sub * 64 + 32 * b + 16 * h;
+                const u32x4 x0 = *(const u32x4*)xp, x1 = *(const u32x4*)(xp + 8);
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const uint32_t xw = p < 4 ? x0[p] : x1[p - 4];
+                    ysum = fmaf(bf_lo(ow[p]), bf_lo(xw), ysum);
+                    ysum = fmaf(bf_hi(ow[p]), bf_hi(xw), ysum);
+                }
+            }
+        }
+        if constexpr (GEMV) {
+            if (sub == NSUB - 1) {
+                const float other = __shfl_xor(ysum, 32, kWave);
+                const int row = row_base + (w * kRowGroups + g) * 32 + n;
+                if (h == 0 && (FULL || row < d_out)) gst(D.part + (int64_t)(col_base / CT) * d_out + row, ysum + other);
+                ysum = 0.f;
+            }
         }
         // scratch -> row-major registers -> global
         const int row0 = row_base + (w * kRowGroups + g) * 32;
@@ -327,7 +362,7 @@ void switch_bf16_kernel(SwitchArgs a) {
         if (t == 0 && threadIdx.x == 0) *a.err = 1;
         return;
     }
-    const SwDesc D = a.descs[find_desc<true>(a.descs, a.n_desc, t)];
+    const SwDesc D = a.descs[find_desc<kKeyTile>(a.descs, a.n_desc, t)];
     const int64_t local = t - D.tile0;
     const int row_base = (int)(local / D.n_ct) * kRT;
     const int col_base = (int)(local % D.n_ct) * CT;
@@ -571,7 +606,7 @@ void switch_wide_kernel(SwitchArgs a) {
         if (t == 0 && threadIdx.x == 0) *a.err = 1;
         return;
     }
-    const SwDesc D = a.descs[find_desc<true>(a.descs, a.n_desc, t)];
+    const SwDesc D = a.descs[find_desc<kKeyTile>(a.descs, a.n_desc, t)];
     // groups of kWGroup row bands; inside a group, column band by column band
     const int64_t local = t - D.tile0;
     const int64_t per_group = (int64_t)kWGroup * D.n_ct;
@@ -585,6 +620,118 @@ void switch_wide_kernel(SwitchArgs a) {
         switch_wide_tile<R16, NSB, true>(a, sc, D, row_base, col_base, smem);
     else
         switch_wide_tile<R16, NSB, false>(a, sc, D, row_base, col_base, smem);
+}
+
+// ---- merged-weight products -------------------------------------------------
+//
+// After a switch the adapted projection of a decode step is the plain product
+// of the merged weight with the layer input (the pages' fused kernel merges
+// the selected adapters into the backbone and carries out the computation in a
+// single kernel).  Two forms:
+//   * switch_gemv_kernel: the rank-16 switch tile above with GEMV = true, so
+//     every weight is read once, written once and multiplied by x in the same
+//     pass; each 256 x 256 tile stores its partial products, and
+//     gemv_reduce_kernel adds a row's n_ct partials in column-tile order (a
+//     kernel boundary in between, so no cross-workgroup synchronisation).
+//   * gemv_kernel: the product alone (the unfused baseline, or after a switch
+//     the fused kernel does not serve): 16-row blocks, each wave 4 rows, lanes
+//     striding over 16-byte chunks of a row with fp32 sums, then a fixed-order
+//     butterfly across the wave.  Every result is bitwise reproducible.
+
+__global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(3)))
+void switch_gemv_kernel(SwitchArgs a) {
+    constexpr int R16 = 1, CT = 256;
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint16_t* As = smem;
+    uint16_t* Ws = smem + 4 * (CT / 32) * 32 * (R16 * 16);
+    uint16_t* Xs = Ws + kWaves * 32 * 64;
+    const int64_t bid = blockIdx.x;
+    const int64_t t = (bid & 7) * a.per_xcd + (bid >> 3);
+    if (t >= a.n_units) return;
+    const Sets sc = read_sets(a);
+    if (!sc.ok) {
+        if (t == 0 && threadIdx.x == 0) *a.err = 1;
+        return;
+    }
+    const SwDesc D = a.descs[find_desc<kKeyTile>(a.descs, a.n_desc, t)];
+    const int64_t local = t - D.tile0;
+    const int row_base = (int)(local / D.n_ct) * kRT;
+    const int col_base = (int)(local % D.n_ct) * CT;
+    const int tid = threadIdx.x;
+    if (tid < CT / 8) {
+        const int col = col_base + 8 * tid;
+        *(u32x4*)(Xs + 8 * tid) = col < D.d_in ? ld128((const uint16_t*)D.xv + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    const bool full = row_base + kRT <= D.d_out && col_base + CT <= D.d_in && a.r == R16 * 16;
+    if (full)
+        switch_tile<R16, CT, true, true>(a, sc, D, row_base, col_base, As, Ws, Xs);
+    else
+        switch_tile<R16, CT, false, true>(a, sc, D, row_base, col_base, As, Ws, Xs);
+}
+
+// y[row] = sum over column tiles c = 0, 1, ... of part[c][row]; one thread per
+// row of a 256-row band.  Sets the switch rejects (same check) leave y alone.
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(SwitchArgs a, int64_t n_bands) {
+    const int64_t t = blockIdx.x;
+    if (t >= n_bands || !read_sets(a).ok) return;
+    const SwDesc D = a.descs[find_desc<kKeyBand>(a.descs, a.n_desc, t)];
+    const int row = (int)(t - D.rt0) * kRT + threadIdx.x;
+    if (row >= D.d_out) return;
+    float sum = 0.f;
+    for (int c = 0; c < D.n_ct; ++c) sum += gld(D.part + (int64_t)c * D.d_out + row);
+    gst(D.yv + row, sum);
+}
+
+constexpr int kGemvRowsPerWave = 4;
+constexpr int kGemvRows = kWaves * kGemvRowsPerWave;  // rows per block
+
+// After a switch in the same call, sets the switch rejects (same check) leave
+// y alone; without sets (plain product) the check always passes.
+template <typename T>
+__global__ __launch_bounds__(kWaves* kWave) void gemv_kernel(SwitchArgs a, int64_t n_blocks) {
+    const int64_t t = blockIdx.x;
+    if (t >= n_blocks || !read_sets(a).ok) return;
+    const SwDesc D = a.descs[find_desc<kKeyRowBlock>(a.descs, a.n_desc, t)];
+    const int d_in = D.d_in, d_out = D.d_out;
+    const int lane = lane_id();
+    const int row0 = (int)(t - D.rb0) * kGemvRows + wave_id() * kGemvRowsPerWave;
+    const T* __restrict__ W = (const T*)D.W;
+    const T* __restrict__ x = (const T*)D.xv;
+    int rows[kGemvRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kGemvRowsPerWave; ++i) rows[i] = row0 + i < d_out ? row0 + i : d_out - 1;
+    float acc[kGemvRowsPerWave] = {};
+    if constexpr (sizeof(T) == 2) {
+        // 8 bf16 per 16-byte chunk; d_in is a multiple of 8
+        const int nch = d_in / 8;
+        for (int c = lane; c < nch; c += kWave) {
+            const u32x4 xv = ld128(x + 8 * c);
+            u32x4 wv[kGemvRowsPerWave];
+#pragma unroll
+            for (int i = 0; i < kGemvRowsPerWave; ++i) wv[i] = ld128(W + (int64_t)rows[i] * d_in + 8 * c);
+#pragma unroll
+            for (int i = 0; i < kGemvRowsPerWave; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[i] = fmaf(bf_lo(wv[i][q]), bf_lo(xv[q]), acc[i]);
+                    acc[i] = fmaf(bf_hi(wv[i][q]), bf_hi(xv[q]), acc[i]);
+                }
+        }
+    } else {
+        for (int j = lane; j < d_in; j += kWave) {
+            const float xj = gld(x + j);
+#pragma unroll
+            for (int i = 0; i < kGemvRowsPerWave; ++i) acc[i] = fmaf(gld(W + (int64_t)rows[i] * d_in + j), xj, acc[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kGemvRowsPerWave; ++i) {
+        float v = acc[i];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+        if (lane == 0 && row0 + i < d_out) gst(D.yv + row0 + i, v);
+    }
 }
 
 // ---- element-wise path: fp32 weights (and any shape) ----------------------
@@ -609,7 +756,7 @@ __global__ __launch_bounds__(256) void switch_generic_kernel(SwitchArgs a) {
         if (u == 0) *a.err = 1;
         return;
     }
-    const SwDesc D = a.descs[find_desc<false>(a.descs, a.n_desc, u)];
+    const SwDesc D = a.descs[find_desc<kKeyElem>(a.descs, a.n_desc, u)];
     const int64_t local = u - D.elem0;
     const int64_t row = local / D.d_in, col = local % D.d_in;
     const T* A = (const T*)D.A;
@@ -723,6 +870,29 @@ hipError_t launch_switch_pack_a(const void* A, void* Ap, int64_t d_in, int E, in
         case 4: hipLaunchKernelGGL(switch_pack_a_kernel<4>, grid, dim3(256), 0, s, a, ap, d_in, E, r, n_cb); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+bool switch_gemv_fused(const SwTile& t, int dtype) { return dtype == 1 && t.r16 == 1 && t.ct == 256; }
+
+hipError_t launch_switch_gemv_bf16(const SwitchArgs& a, hipStream_t s) {
+    const size_t lds = ((size_t)4 * 8 * 32 * 16 + (size_t)kWaves * 32 * 64 + 256) * sizeof(uint16_t);
+    hipLaunchKernelGGL(switch_gemv_kernel, dim3((unsigned)(8 * a.per_xcd)), dim3(kWaves * kWave), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_reduce(const SwitchArgs& a, int64_t n_bands, hipStream_t s) {
+    if (n_bands == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)n_bands), dim3(256), 0, s, a, n_bands);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(const SwitchArgs& a, int64_t n_blocks, int dtype, hipStream_t s) {
+    if (n_blocks == 0) return hipSuccess;
+    if (dtype == 0)
+        hipLaunchKernelGGL(gemv_kernel<float>, dim3((unsigned)n_blocks), dim3(kWaves * kWave), 0, s, a, n_blocks);
+    else
+        hipLaunchKernelGGL(gemv_kernel<uint16_t>, dim3((unsigned)n_blocks), dim3(kWaves * kWave), 0, s, a, n_blocks);
     return hipGetLastError();
 }
 

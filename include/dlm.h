@@ -158,6 +158,45 @@ int dlm_switch(dlm_layers* h, const int32_t* old_idx, const float* old_g,
 /* Number of kernel launches one dlm_switch call makes (always 1). */
 int dlm_switch_launches(const dlm_layers* h);
 
+/* -------------------------------------------- merged-weight products */
+
+/*
+ * The decode step after a switch: each adapted projection is the product of
+ * its merged weight with the layer input, y_i = W_i x_i (Chinese digest,
+ * "technical framework": the fused kernel merges the selected adapters into
+ * the backbone and carries out the computation in a single kernel).
+ *
+ * Bind one input and one output vector to every weight of the handle:
+ *   x (host) [n] device pointers, x_i [d_in_i] in the handle's dtype (bf16:
+ *   16-byte aligned); y (host) [n] device pointers, y_i [d_out_i] fp32, not
+ *   overlapping x_i or W_i.  The pointers are copied into the device table
+ *   (synchronous); the buffers stay owned by the caller.  bf16 handles with
+ *   r <= 16 also get a partial-product buffer (sum of ceil(d_in_i/256) *
+ *   d_out_i floats), freed by destroy.  Binding again replaces the vectors.
+ */
+int dlm_layers_bind_vectors(dlm_layers* h, const void* const* x, float* const* y);
+
+/*
+ * y_i = W_i x_i for every weight (fp32 accumulation, one rounding to fp32 per
+ * lane sum, then a fixed-order reduction: bitwise reproducible).  One launch,
+ * no allocation.  DLM_EINVAL if no vectors are bound.
+ */
+int dlm_gemv(dlm_layers* h, void* stream);
+
+/*
+ * dlm_switch followed by y_i = W'_i x_i with the new (rounded) weights.  bf16
+ * with r <= 16: one fused kernel reads each W once, writes W' and forms
+ * per-256-column partial products, and a second launch adds each row's
+ * partials in column order.  Otherwise the switch and dlm_gemv's kernel run
+ * back to back.  Two launches either way, no allocation.  A set the switch
+ * rejects leaves W and y unchanged (the error word is set as for dlm_switch).
+ */
+int dlm_switch_gemv(dlm_layers* h, const int32_t* old_idx, const float* old_g,
+                    const int32_t* new_idx, const float* new_g, void* stream);
+
+/* Number of kernel launches one dlm_switch_gemv call makes (always 2). */
+int dlm_switch_gemv_launches(const dlm_layers* h);
+
 /*
  * Synchronise `stream`, then read and clear the handle's device error word:
  * *code (host) = DLM_OK or DLM_EDEVICE.
