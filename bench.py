@@ -115,6 +115,106 @@ def bench_switch(torch, dlm, synth, steps, warmup, log):
     return res
 
 
+def bench_decode_loop(torch, dlm, synth, n_tokens, log):
+    """Per-token decode steps on the 7B-shaped workload: router (T = 1) -> switch ->
+    the merged-weight product of every adapted projection, layer by layer, on one
+    stream with the expert sets kept on the device.
+      unfused: router, one switch over all 224 weights, then one product launch per
+               layer (W read twice, written once: 3 x 12.95 GB per token);
+      fused:   router, then per layer the switch fused with the product (2 launches:
+               W read once, written once, plus partial sums).
+    Each is timed eagerly and replayed from HIP graphs (one per set-buffer parity);
+    inputs are synthetic per (layer, projection), tokens come from the router's
+    x.  W returns to its starting sets between the two variants (unmerge)."""
+    wl = synth.WORKLOADS["7b-decode"]
+    log(f"decode loop: building {wl.name}")
+    model = synth.switch_model(wl)
+    x, Wr = synth.router_inputs(wl)
+    P = len(wl.projs)
+    whole = dlm.Layers([(W, A, B) for _, _, W, A, B in model], wl.E, wl.r, wl.scale)
+    layers, ys = [], []
+    for l in range(wl.layers):
+        grp = model[l * P:(l + 1) * P]
+        h = dlm.Layers([(W, A, B) for _, _, W, A, B in grp], wl.E, wl.r, wl.scale)
+        xs = [synth.normal_device((W.shape[1],), 1.0, wl.dtype, "cuda", wl.cfg_id, "xin", l, k)
+              for k, (_, _, W, _, _) in enumerate(grp)]
+        yv = [torch.empty(W.shape[0], dtype=torch.float32, device="cuda") for _, _, W, _, _ in grp]
+        h.bind_vectors(xs, yv)
+        layers.append(h)
+        ys.append((xs, yv))
+    x_tok = torch.empty((1, wl.d_model), dtype=wl.dtype, device="cuda")
+    idx = [torch.zeros((1, 2), dtype=torch.int32, device="cuda") for _ in range(2)]
+    g = [torch.zeros((1, 2), dtype=torch.float32, device="cuda") for _ in range(2)]
+    s = torch.cuda.Stream()
+
+    def step(kind, cur, first, stream):
+        dlm.pregate(x_tok, Wr, idx=idx[cur], g=g[cur], stream=stream)
+        new = (idx[cur][0], g[cur][0])
+        old = None if first else (idx[1 - cur][0], g[1 - cur][0])
+        if kind == "unfused":
+            whole.switch(old, new, stream=stream)
+            for h in layers:
+                h.gemv(stream=stream)
+        else:
+            for h in layers:
+                h.switch_gemv(old, new, stream=stream)
+
+    res = {"tokens": n_tokens}
+    w_bytes = wl.switch_w_elems() * 2
+    for kind in ("unfused", "fused"):
+        out = {}
+        with torch.cuda.stream(s):
+            # eager: token 0 from the merged-in-nothing state, then n-1 switches
+            x_tok.copy_(x[0:1])
+            step(kind, 0, True, s)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for t in range(1, n_tokens):
+                x_tok.copy_(x[t:t + 1])
+                step(kind, t % 2, False, s)
+            b.record(s)
+        torch.cuda.synchronize()
+        out["ms_per_token_eager"] = a.elapsed_time(b) / (n_tokens - 1)
+        # graphs: one per parity of the current set buffer
+        graphs = []
+        for cur in (0, 1):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(gr, stream=s):
+                    step(kind, cur, False, s)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        last = (n_tokens - 1) % 2
+        with torch.cuda.stream(s):
+            a.record(s)
+            for t in range(n_tokens):
+                cur = 1 - last if t == 0 else 1 - cur
+                x_tok.copy_(x[t:t + 1])
+                graphs[cur].replay()
+            b.record(s)
+        torch.cuda.synchronize()
+        out["ms_per_token_graph"] = a.elapsed_time(b) / n_tokens
+        lpt = 1 + (whole.launches_per_switch() + wl.layers if kind == "unfused"
+                   else wl.layers * layers[0].launches_per_switch_gemv())
+        out["launches_per_token"] = lpt
+        out["weight_bytes_per_token"] = (3 if kind == "unfused" else 2) * w_bytes
+        out["GBps_graph"] = out["weight_bytes_per_token"] / out["ms_per_token_graph"] / 1e6
+        # back to the starting weights: remove the last token's set
+        cur_last = cur
+        whole.switch((idx[cur_last][0], g[cur_last][0]), None)
+        torch.cuda.synchronize()
+        assert whole.status() == dlm.DLM_OK and all(h.status() == dlm.DLM_OK for h in layers)
+        res[kind] = out
+        log(f"decode loop {kind}: {out}")
+        del graphs
+    for h in layers:
+        h.close()
+    whole.close()
+    del model, ys
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_switch_70b(torch, dlm, synth, n_timed, log):
     """The 70B-shaped decode workload (80 layers x q,o 8192x8192, k,v 8192->1024,
     gate,up 8192->28672, down 28672->8192; E=16, r=64): router on its 128 tokens,
@@ -404,6 +504,8 @@ def main():
     ap.add_argument("--no-sgmm", action="store_true")
     ap.add_argument("--no-70b", action="store_true", help="skip the 70B-shaped switch measurement")
     ap.add_argument("--switch-70b-launches", type=int, default=32)
+    ap.add_argument("--no-decode-loop", action="store_true", help="skip the per-token decode loop")
+    ap.add_argument("--decode-tokens", type=int, default=64)
     ap.add_argument("--profile-kernels", type=int, nargs="?", const=4, default=0,
                     help="short run for rocprofv3 counter collection (N switches + 1 GiB copy)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -431,6 +533,9 @@ def main():
         return
     sw = bench_switch(torch, dlm, synth, args.steps, args.warmup, log)
     log(f"switch: {sw}")
+    dec = None
+    if not args.no_decode_loop:
+        dec = bench_decode_loop(torch, dlm, synth, args.decode_tokens, log)
     router = bench_router(torch, dlm, synth, log)
     log(f"router: {router}")
     sw70 = None
@@ -477,6 +582,9 @@ def main():
         "switch_70b": None if sw70 is None else {k: (round(v, 4) if isinstance(v, float) else v)
                                                  for k, v in sw70.items()},
         "router": {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in router.items()},
+        "decode_loop": None if dec is None else {k: ({kk: round(vv, 4) if isinstance(vv, float) else vv
+                                                      for kk, vv in v.items()} if isinstance(v, dict) else v)
+                                                 for k, v in dec.items()},
         "sgmm": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                  for k, v in sg.items()},
     }

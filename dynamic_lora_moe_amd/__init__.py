@@ -213,6 +213,9 @@ class Layers:
         ni, ng = _set_ptrs(new)
         _check(load().dlm_switch_gemv(self._h, oi, og, ni, ng, _stream(stream)), "dlm_switch_gemv")
 
+    def launches_per_switch_gemv(self) -> int:
+        return load().dlm_switch_gemv_launches(self._h)
+
     def repack(self, stream=None):
         """Refresh the packed A copy (ranks 17..64, bf16) after changing an A bank in place."""
         _check(load().dlm_layers_repack(self._h, _stream(stream)), "dlm_layers_repack")
@@ -311,6 +314,9 @@ class SgmmGroup:
         oi, og = _set_ptrs(old)
         ni, ng = _set_ptrs(new)
         _check(load().dlm_switch_gemv(self._h, oi, og, ni, ng, _stream(stream)), "dlm_switch_gemv")
+
+    def launches_per_switch_gemv(self) -> int:
+        return load().dlm_switch_gemv_launches(self._h)
 
     def repack(self, stream=None):
         """Refresh the packed A copies after the A banks were changed in place."""

@@ -126,3 +126,66 @@ def test_sgmm_per_layer_groups_in_graph_match_grouped_eager():
     for grp in per_layer:
         grp.close()
     whole.close()
+
+
+def test_switch_gemv_per_layer_graph_replays_match_eager():
+    """Two 'layers', each switched and multiplied by its bound inputs with
+    dlm_switch_gemv, captured in one graph: every replay gives the weights and
+    products of the same calls made eagerly."""
+    E, r = 8, 16
+    shapes = [(256, 512), (300, 264)]
+    layers, W0, vecs = [], [], []
+    for l in range(2):
+        m = [(synth.normal_device((o, n), 0.02, torch.bfloat16, "cuda", 7000, "W", l, i),
+              synth.normal_device((E, r, n), 0.02, torch.bfloat16, "cuda", 7000, "A", l, i),
+              synth.normal_device((E, o, r), 0.02, torch.bfloat16, "cuda", 7000, "B", l, i))
+             for i, (o, n) in enumerate(shapes)]
+        xs = [synth.normal_device((n,), 1.0, torch.bfloat16, "cuda", 7000, "x", l, i) for i, (_, n) in enumerate(shapes)]
+        ys = [torch.zeros(o, dtype=torch.float32, device="cuda") for o, _ in shapes]
+        h = dlm.Layers(m, E, r, 2.0)
+        h.bind_vectors(xs, ys)
+        layers.append((h, m, ys))
+        W0.append([W.clone() for W, _, _ in m])
+    old_i = torch.zeros(2, dtype=torch.int32, device="cuda")
+    old_g = torch.zeros(2, dtype=torch.float32, device="cuda")
+    new_i = torch.zeros(2, dtype=torch.int32, device="cuda")
+    new_g = torch.zeros(2, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for h, _, _ in layers:
+                h.switch_gemv((old_i, old_g), (new_i, new_g), stream=s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+
+    def reset():
+        for (_, m, ys), w0 in zip(layers, W0):
+            for (W, _, _), w in zip(m, w0):
+                W.copy_(w)
+            for y in ys:
+                y.zero_()
+
+    for rep in range(4):
+        e = rng.choice(E, size=4, replace=False)
+        w = rng.random(4).astype(np.float32)
+        old_i.copy_(torch.tensor(e[:2].tolist(), dtype=torch.int32))
+        old_g.copy_(torch.tensor((w[:2] / w[:2].sum()).tolist(), dtype=torch.float32))
+        new_i.copy_(torch.tensor(e[2:].tolist(), dtype=torch.int32))
+        new_g.copy_(torch.tensor((w[2:] / w[2:].sum()).tolist(), dtype=torch.float32))
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [([W.clone() for W, _, _ in m], [y.clone() for y in ys]) for _, m, ys in layers]
+        reset()
+        for h, _, _ in layers:
+            h.switch_gemv((old_i, old_g), (new_i, new_g))
+        torch.cuda.synchronize()
+        for (h, m, ys), (gw, gy) in zip(layers, got):
+            assert all(torch.equal(W, a) for (W, _, _), a in zip(m, gw)), rep
+            assert all(torch.equal(y, a) for y, a in zip(ys, gy)), rep
+    for h, _, _ in layers:
+        assert h.status() == dlm.DLM_OK
+        h.close()
