@@ -678,8 +678,19 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(SwitchArgs a, int64_t 
     const SwDesc D = a.descs[find_desc<kKeyBand>(a.descs, a.n_desc, t)];
     const int row = (int)(t - D.rt0) * kRT + threadIdx.x;
     if (row >= D.d_out) return;
+    // eight independent loads in flight per step; the additions stay in c order
+    const float* pp = D.part + row;
+    const int64_t st = D.d_out;
     float sum = 0.f;
-    for (int c = 0; c < D.n_ct; ++c) sum += gld(D.part + (int64_t)c * D.d_out + row);
+    int c = 0;
+    for (; c + 8 <= D.n_ct; c += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = gld(pp + (c + j) * st);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += v[j];
+    }
+    for (; c < D.n_ct; ++c) sum += gld(pp + c * st);
     gst(D.yv + row, sum);
 }
 
