@@ -54,6 +54,8 @@ def _bind(lib):
     lib.dlmref_switch_rows.argtypes = [P, P, I64, P, P, I64, I64, I32, I32, D, I32,
                                        P, P, P, P, P, P]
     lib.dlmref_sgmm_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, I32, D, I32, P, P]
+    lib.dlmref_pregate_centroid.argtypes = [P, P, I64, I64, I32, I32, I32, P, P, P, P]
+    lib.dlmref_pregate_centroid.restype = C.c_int
     lib.dlmref_gemv.argtypes = [P, P, I64, I64, I32, P, P, P]
     lib.dlmref_gemv.restype = C.c_int
     lib.dlmref_round.argtypes = [P, I64, I32, P]
@@ -127,6 +129,30 @@ def pregate(x, Wr, with_stats: bool = False, lib=None):
     out = (torch.from_numpy(idx), torch.from_numpy(g))
     if with_stats:
         return out + (torch.from_numpy(lg), torch.from_numpy(mg), torch.from_numpy(bd))
+    return out
+
+
+def pregate_centroid(x, C, with_stats: bool = False, lib=None):
+    """Nearest-centroid router: x [T][d], C [E][J][d] -> idx [T][2] int32 (slot 1
+    empty), g [T][2] fp32 = (1, 0).  with_stats also returns (dist [T][E] f64,
+    margin [T] f64)."""
+    lib = lib or load()
+    xa, dt = _np(x)
+    ca, dtc = _np(C)
+    assert dt is not None and dt == dtc
+    T, d = xa.shape
+    E, J, d2 = ca.shape
+    assert d2 == d
+    idx = np.empty((T, 2), np.int32)
+    g = np.empty((T, 2), np.float32)
+    ds = np.empty((T, E), np.float64) if with_stats else None
+    mg = np.empty((T,), np.float64) if with_stats else None
+    rc = lib.dlmref_pregate_centroid(_ptr(xa), _ptr(ca), T, d, E, J, dt, _ptr(idx), _ptr(g), _ptr(ds), _ptr(mg))
+    if rc != 0:
+        raise ValueError(f"dlmref_pregate_centroid failed ({rc})")
+    out = (torch.from_numpy(idx), torch.from_numpy(g))
+    if with_stats:
+        return out + (torch.from_numpy(ds), torch.from_numpy(mg))
     return out
 
 

@@ -23,6 +23,8 @@
  *     remove the previous token's adapters and merge the current token's into
  *     the backbone of every layer, on concatenated adapter matrices, in place.
  *     English abstract: merging the selected LoRA adapters into the backbone.
+ *   - nearest-centroid pre-gate: the ARIADNE page (training-free routing by
+ *     proximity of the input embedding to each adapter's centroids).
  *   - sgmm: the batched unmerged form y += sum_k g_k (x A_k^T) B_k^T of the
  *     same adapters (the pages only name the SGMM kernel; the formula is the
  *     standard LoRA product with per-row gates).
@@ -146,6 +148,54 @@ int dlmref_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int32_t 
         }
         free(l);
         free(a);
+    }
+    return 0;
+}
+
+/* ---- nearest-centroid pre-gate ------------------------------------------- */
+
+/*
+ * Training-free routing (ARIADNE page: each adapter is represented by a set of
+ * centroids of its training data's embeddings; at inference the input's
+ * embedding is compared with every adapter's centroids and the closest adapter
+ * is chosen).  Here: x [T][d], centroids C [E][J][d] (dtype dt); the distance
+ * of token t to adapter e is min over its J centroids of the squared Euclidean
+ * distance; the nearest adapter (ties -> lower index) goes to slot 0 with
+ * weight 1, slot 1 is empty (-1, 0), the set format of the top-2 router.
+ * Optional: dist [T][E] (binary64 adapter distances) and margin [T] (second
+ * smallest minus smallest adapter distance; +inf when E == 1).
+ */
+int dlmref_pregate_centroid(const void* x, const void* C, int64_t T, int64_t d, int32_t E, int32_t J,
+                            int32_t dt, int32_t* idx, float* g, double* dist, double* margin) {
+    if (T < 0 || d < 1 || E < 1 || J < 1 || !x || !C || !idx || !g) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double* de = (double*)malloc(sizeof(double) * (size_t)E);
+        for (int32_t e = 0; e < E; ++e) {
+            double best = INFINITY;
+            for (int32_t j = 0; j < J; ++j) {
+                double s = 0.0;
+                for (int64_t k = 0; k < d; ++k) {
+                    double diff = ld(x, t * d + k, dt) - ld(C, ((int64_t)e * J + j) * d + k, dt);
+                    s += diff * diff;
+                }
+                if (s < best) best = s;
+            }
+            de[e] = best;
+        }
+        int32_t eb = 0;
+        for (int32_t e = 1; e < E; ++e) if (de[e] < de[eb]) eb = e;
+        idx[2 * t] = eb;
+        idx[2 * t + 1] = -1;
+        g[2 * t] = 1.0f;
+        g[2 * t + 1] = 0.0f;
+        if (dist) for (int32_t e = 0; e < E; ++e) dist[t * E + e] = de[e];
+        if (margin) {
+            double m = INFINITY;
+            for (int32_t e = 0; e < E; ++e) if (e != eb && de[e] - de[eb] < m) m = de[e] - de[eb];
+            margin[t] = m;
+        }
+        free(de);
     }
     return 0;
 }

@@ -12,6 +12,8 @@ must fail).  What each pin holds the oracle to:
   roundtrip A -> B -> A returns the starting weights within the rounding bound
   merged    merged weights applied to x = base output + unmerged adapters
   gemm      SGMM with one set for every row = a dense textbook GEMM
+  centroid  nearest-centroid router: hand-worked fixture, NumPy brute force,
+            permutation / translation / duplicate invariants
   gemv      merged-weight product against NumPy's binary64 matmul; merged
             product = base product + unmerged adapters + the rounding of W
   rounding  one nearest-even rounding to bf16 / fp32
@@ -150,6 +152,67 @@ def pin_router_permutation(lib):
     Wt[0, 1] = Wt[0, 4] = 3.0
     Wt[0, 0] = 1.0
     assert oracle.pregate(x2, Wt, lib=lib)[0].tolist() == [[1, 4]]
+
+
+# ------------------------------------------------------ centroid router ----
+
+def pin_centroid_golden(lib):
+    c = _golden("centroid_tiny.json")
+    for dt in (torch.float32, torch.bfloat16):
+        idx, g, dist, _ = oracle.pregate_centroid(_t(c["x"], dt), _t(c["C"], dt), with_stats=True, lib=lib)
+        assert idx.tolist() == c["idx"] and g.tolist() == c["g"], (idx, g)
+        assert dist.tolist() == c["dist"], dist
+
+
+def _centroid_brute(x, C):
+    X, Cd = x.double().numpy(), C.double().numpy()
+    d2 = ((X[:, None, None, :] - Cd[None]) ** 2).sum(-1)    # [T][E][J]
+    de = d2.min(-1)
+    return de, de.argmin(-1)                                  # first minimum: lower index on ties
+
+
+def pin_centroid_brute(lib):
+    rng = _rng(51)
+    for dt in (torch.float32, torch.bfloat16):
+        for T, d, E, J in ((1, 1, 1, 1), (9, 5, 3, 2), (17, 33, 8, 4), (5, 64, 16, 1)):
+            x = torch.from_numpy(rng.standard_normal((T, d))).to(dt)
+            C = torch.from_numpy(rng.standard_normal((E, J, d))).to(dt)
+            idx, g, dist, mg = oracle.pregate_centroid(x, C, with_stats=True, lib=lib)
+            de, eb = _centroid_brute(x, C)
+            assert np.allclose(dist.numpy(), de, rtol=1e-13, atol=0)
+            assert (idx[:, 0].numpy() == eb).all() and (idx[:, 1] == -1).all()
+            assert (g[:, 0] == 1).all() and (g[:, 1] == 0).all()
+            srt = np.sort(de, axis=1)
+            ref_m = srt[:, 1] - srt[:, 0] if E > 1 else np.full(T, np.inf)
+            assert np.allclose(mg.numpy(), ref_m, rtol=1e-12, atol=1e-12)
+
+
+def pin_centroid_invariants(lib):
+    rng = _rng(52)
+    T, d, E, J = 12, 16, 6, 3
+    x = torch.from_numpy(_dyadic(rng, (T, d))).float()
+    C = torch.from_numpy(_dyadic(rng, (E, J, d))).float()
+    idx, _, dist, _ = oracle.pregate_centroid(x, C, with_stats=True, lib=lib)
+    # permuting adapters permutes the choice (ties aside: none at these seeds)
+    perm = rng.permutation(E)
+    idx_p, _, dist_p, _ = oracle.pregate_centroid(x, C[perm], with_stats=True, lib=lib)
+    assert torch.equal(dist_p, dist[:, perm])
+    assert (perm[idx_p[:, 0].numpy()] == idx[:, 0].numpy()).all()
+    # permuting an adapter's own centroids changes nothing
+    idx_j, _, dist_j, _ = oracle.pregate_centroid(x, C[:, rng.permutation(J)], with_stats=True, lib=lib)
+    assert torch.equal(idx_j, idx) and torch.equal(dist_j, dist)
+    # translating x and every centroid by the same (dyadic) vector changes nothing
+    sh = torch.from_numpy(_dyadic(rng, (d,))).float()
+    idx_t, _, dist_t, _ = oracle.pregate_centroid(x + sh, C + sh, with_stats=True, lib=lib)
+    assert torch.equal(idx_t, idx) and torch.equal(dist_t, dist)
+    # a token sitting on a centroid of adapter e picks e (distance 0) unless a lower adapter also has 0
+    x0 = C[4, 1].reshape(1, d).clone()
+    i0, _, d0, _ = oracle.pregate_centroid(x0, C, with_stats=True, lib=lib)
+    assert d0[0, 4] == 0 and i0[0, 0] == 4
+    # an adapter duplicated at a higher index never wins over its original
+    C2 = torch.cat([C, C[2:3]], 0)
+    i2, _, _, _ = oracle.pregate_centroid(x, C2, with_stats=True, lib=lib)
+    assert (i2[:, 0] != E).all()
 
 
 # ---------------------------------------------------------------- switch ----
@@ -406,6 +469,7 @@ ALL_PINS = [
     pin_switch_golden, pin_switch_premerge, pin_switch_general, pin_switch_noop,
     pin_switch_roundtrip, pin_merged_equals_unmerged,
     pin_gemv_golden, pin_gemv_numpy, pin_gemv_merged,
+    pin_centroid_golden, pin_centroid_brute, pin_centroid_invariants,
     pin_sgmm_golden, pin_sgmm_gemm, pin_sgmm_brute, pin_sgmm_properties,
     pin_rounding,
 ]

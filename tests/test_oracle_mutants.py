@@ -41,6 +41,12 @@ MUTANTS = [
     ("gemv_drop_last", "for (int64_t j = 0; j < d_in; ++j) {\n            double p = ld(W,",
      "for (int64_t j = 0; j + 1 < d_in; ++j) {\n            double p = ld(W,"),
     ("gemv_truncate", "y[i] = (float)acc;  /* C conversion: RNE */", "y[i] = (float)trunc(acc * 1048576.0) / 1048576.0f;"),
+    ("centroid_tie_to_higher", "if (de[e] < de[eb]) eb = e;", "if (de[e] <= de[eb]) eb = e;"),
+    ("centroid_max_over_centroids", "if (s < best) best = s;", "if (s > best || best == INFINITY) best = s;"),
+    ("centroid_wrong_centroid", "ld(C, ((int64_t)e * J + j) * d + k, dt)", "ld(C, ((int64_t)j * E + e) * d + k, dt)"),
+    ("centroid_abs_not_square", "s += diff * diff;", "s += fabs(diff);"),
+    ("centroid_drop_last_dim", "for (int64_t k = 0; k < d; ++k) {\n                    double diff",
+     "for (int64_t k = 0; k + 1 < d; ++k) {\n                    double diff"),
     # an empty slot (-1) read as expert 0 everywhere it is tested
     ("empty_slot_as_expert0", "if (e < 0) continue;", "if (e < 0) e = 0;", 3),
 ]
