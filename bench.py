@@ -277,6 +277,25 @@ def bench_router(torch, dlm, synth, log):
             us = e0.elapsed_time(e1) / 20 * 1e3
             nbytes = (xt.numel() + Wr.numel()) * xt.element_size()
             out[f"{name}_T{T}"] = {"us_per_call": us, "GBps_x_Wr": nbytes / us / 1e3}
+        # the nearest-centroid pre-gate on the same tokens: J = 4 synthetic
+        # centroids per adapter, N(0, 1) like the tokens
+        J = 4
+        C = synth.normal_device((wl.E, J, wl.d_model), 1.0, wl.dtype, "cuda", wl.cfg_id, "centroids")
+        for T in (1, wl.T):
+            xt = x[:T].contiguous()
+            idx = torch.empty(T, 2, dtype=torch.int32, device="cuda")
+            g = torch.empty(T, 2, dtype=torch.float32, device="cuda")
+            for _ in range(3):
+                dlm.pregate_centroid(xt, C, idx, g)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                dlm.pregate_centroid(xt, C, idx, g)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 20 * 1e3
+            out[f"{name}_centroid_J{J}_T{T}"] = {"us_per_call": us,
+                                                 "GBps_x_C": (xt.numel() + C.numel()) * xt.element_size() / us / 1e3}
     return out
 
 

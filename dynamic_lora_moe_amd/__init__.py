@@ -62,6 +62,7 @@ def load(path: str = LIB_PATH):
         "dlm_last_error": ([], C.c_char_p),
         "dlm_version": ([], C.c_char_p),
         "dlm_pregate": ([P, P, I64, I64, I32, I32, P, P, P], C.c_int),
+        "dlm_pregate_centroid": ([P, P, I64, I64, I32, I32, I32, P, P, P], C.c_int),
         "dlm_layers_create": ([P, I32, I32, I32, F, I32, P], C.c_int),
         "dlm_layers_destroy": ([P], C.c_int),
         "dlm_switch": ([P, P, P, P, P, P], C.c_int),
@@ -141,6 +142,24 @@ def pregate(x: torch.Tensor, Wr: torch.Tensor, idx=None, g=None, stream=None):
         g = torch.empty((T, 2), dtype=torch.float32, device=x.device)
     _check(load().dlm_pregate(_p(x), _p(Wr), T, d, E, _dt(x), _p(idx), _p(g), _stream(stream)),
            "dlm_pregate")
+    return idx, g
+
+
+def pregate_centroid(x: torch.Tensor, C: torch.Tensor, idx=None, g=None, stream=None):
+    """Nearest-centroid pre-gate: x [T][d], C [E][J][d] -> idx [T][2] int32 (slot 1
+    empty), g [T][2] fp32 = (1, 0) (device)."""
+    _need(x, "x")
+    _need(C, "C")
+    T, d = x.shape
+    E, J, d2 = C.shape
+    if d2 != d or C.dtype != x.dtype:
+        raise ValueError("C must be [E][J][d] with x's dtype")
+    if idx is None:
+        idx = torch.empty((T, 2), dtype=torch.int32, device=x.device)
+    if g is None:
+        g = torch.empty((T, 2), dtype=torch.float32, device=x.device)
+    _check(load().dlm_pregate_centroid(_p(x), _p(C), T, d, E, J, _dt(x), _p(idx), _p(g), _stream(stream)),
+           "dlm_pregate_centroid")
     return idx, g
 
 

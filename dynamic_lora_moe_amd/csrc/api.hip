@@ -112,6 +112,22 @@ int dlm_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int32_t E, 
     return ok();
 }
 
+int dlm_pregate_centroid(const void* x, const void* C, int64_t T, int64_t d, int32_t E, int32_t J, int32_t dtype,
+                         int32_t* idx, float* g, void* stream) {
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(DLM_ESHAPE, "pregate_centroid: T=%lld out of range", (long long)T);
+    if (d < 1 || d > kMaxDim) return fail(DLM_ESHAPE, "pregate_centroid: d=%lld out of range", (long long)d);
+    if (E < 1 || E > DLM_MAX_EXPERTS)
+        return fail(DLM_ESHAPE, "pregate_centroid: E=%d not in [1, %d]", E, DLM_MAX_EXPERTS);
+    if (J < 1 || J > DLM_MAX_CENTROIDS)
+        return fail(DLM_ESHAPE, "pregate_centroid: J=%d not in [1, %d]", J, DLM_MAX_CENTROIDS);
+    if (!valid_dtype(dtype)) return fail(DLM_EDTYPE, "pregate_centroid: unknown dtype %d", dtype);
+    if (T == 0) return ok();
+    if (!x || !C || !idx || !g) return fail(DLM_EINVAL, "pregate_centroid: null pointer");
+    hipError_t e = launch_pregate_centroid(x, C, T, d, E, J, dtype, idx, g, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "pregate_centroid launch");
+    return ok();
+}
+
 // ---------------------------------------------------------------- switch ----
 
 int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, float scale,

@@ -80,5 +80,7 @@ hipError_t launch_switch_generic(const SwitchArgs& a, int dtype, hipStream_t s);
 
 hipError_t launch_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int E,
                           int dtype, int32_t* idx, float* g, hipStream_t s);
+hipError_t launch_pregate_centroid(const void* x, const void* C, int64_t T, int64_t d, int E, int J, int dtype,
+                                   int32_t* idx, float* g, hipStream_t s);
 
 }  // namespace dlm

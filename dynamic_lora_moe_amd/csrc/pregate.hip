@@ -7,6 +7,7 @@
 // binary64), a fixed butterfly sums the 64 partials, and lane 0 takes the
 // top two (ties -> lower index) and the renormalised pair of weights
 // g0 = 1/(1+exp(l1-l0)), g1 = exp(l1-l0)/(1+exp(l1-l0)).
+#include "dlm.h"
 #include "gfx950.hpp"
 #include "internal.hpp"
 
@@ -153,6 +154,70 @@ __global__ __launch_bounds__(kVecWaves* kWave) void pregate_bf16_vec(
     top2_store<EMAX>(l, E, t, idx, g);
 }
 
+// Nearest-centroid pre-gate (the ARIADNE page: training-free routing by the
+// proximity of the input embedding to centroids of each adapter's training
+// data; the closest adapter is chosen).  One workgroup of kVecWaves waves per
+// token.  The E*J centroids (C [E][J][d], adapter-major) are taken kCGroup at a
+// time: each lane sums (x_k - c_k)^2 in binary64 over the columns
+// k = lane + 64 (w + kVecWaves i) (fp32 or bf16 inputs: the differences and
+// their squares are exact in binary64), the wave sums are added in wave order,
+// and each adapter keeps the smallest of its centroids' distances.  Thread 0
+// then takes the nearest adapter (strict '<': ties keep the lower index) for
+// slot 0 with weight 1; slot 1 is empty (-1, 0).  A NaN distance never
+// compares smaller, so the index stays in range.
+constexpr int kCGroup = 8;
+
+template <typename T>
+__global__ __launch_bounds__(kVecWaves* kWave) void pregate_centroid_kernel(
+    const T* __restrict__ x, const T* __restrict__ C, int64_t d, int E, int J, int32_t* __restrict__ idx,
+    float* __restrict__ g) {
+    const int64_t t = blockIdx.x;
+    const int lane = lane_id(), w = wave_id();
+    __shared__ double s_part[kVecWaves][kCGroup];
+    __shared__ double s_de[DLM_MAX_EXPERTS];
+    const int EJ = E * J;
+    const T* xr = x + t * d;
+    for (int c0 = 0; c0 < EJ; c0 += kCGroup) {
+        double acc[kCGroup];
+#pragma unroll
+        for (int q = 0; q < kCGroup; ++q) acc[q] = 0.0;
+        for (int64_t k = lane + (int64_t)kWave * w; k < d; k += (int64_t)kVecWaves * kWave) {
+            const double xv = ldv(xr, k);
+#pragma unroll
+            for (int q = 0; q < kCGroup; ++q) {
+                if (c0 + q >= EJ) break;
+                const double df = xv - ldv(C + (int64_t)(c0 + q) * d, k);
+                acc[q] = fma(df, df, acc[q]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kCGroup; ++q) acc[q] = wave_sum(acc[q]);
+        if (lane == 0) {
+#pragma unroll
+            for (int q = 0; q < kCGroup; ++q) s_part[w][q] = acc[q];
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int q = 0; q < kCGroup && c0 + q < EJ; ++q) {
+                double s = s_part[0][q];
+#pragma unroll
+                for (int p = 1; p < kVecWaves; ++p) s += s_part[p][q];
+                const int e = (c0 + q) / J;
+                if ((c0 + q) % J == 0 || s < s_de[e]) s_de[e] = s;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x != 0) return;
+    int eb = 0;
+    for (int e = 1; e < E; ++e)
+        if (s_de[e] < s_de[eb]) eb = e;
+    idx[2 * t] = eb;
+    idx[2 * t + 1] = -1;
+    g[2 * t] = 1.0f;
+    g[2 * t + 1] = 0.0f;
+}
+
 template <typename T>
 hipError_t launch_t(const void* x, const void* Wr, int64_t T_, int64_t d, int E, int32_t* idx,
                     float* g, hipStream_t s) {
@@ -170,6 +235,19 @@ hipError_t launch_t(const void* x, const void* Wr, int64_t T_, int64_t d, int E,
 }
 
 }  // namespace
+
+hipError_t launch_pregate_centroid(const void* x, const void* C, int64_t T, int64_t d, int E, int J, int dtype,
+                                   int32_t* idx, float* g, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid((unsigned)T), block(kVecWaves * kWave);
+    if (dtype == 0)
+        hipLaunchKernelGGL(pregate_centroid_kernel<float>, grid, block, 0, s, (const float*)x, (const float*)C, d, E, J,
+                           idx, g);
+    else
+        hipLaunchKernelGGL(pregate_centroid_kernel<uint16_t>, grid, block, 0, s, (const uint16_t*)x,
+                           (const uint16_t*)C, d, E, J, idx, g);
+    return hipGetLastError();
+}
 
 hipError_t launch_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int E, int dtype,
                           int32_t* idx, float* g, hipStream_t s) {

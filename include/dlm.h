@@ -67,6 +67,7 @@ typedef enum { DLM_F32 = 0, DLM_BF16 = 1 } dlm_dtype;
 /* Limits of this build. */
 #define DLM_MAX_EXPERTS 32
 #define DLM_MAX_RANK 128
+#define DLM_MAX_CENTROIDS 1024   /* per adapter, dlm_pregate_centroid */
 
 /* Text of the calling thread's last non-OK status (static storage). */
 const char* dlm_last_error(void);
@@ -95,6 +96,22 @@ const char* dlm_version(void);
  */
 int dlm_pregate(const void* x, const void* Wr, int64_t T, int64_t d, int32_t E,
                 int32_t dtype, int32_t* idx, float* g, void* stream);
+
+/*
+ * Training-free nearest-centroid pre-gate (the ARIADNE page: each adapter is
+ * represented by centroids of its training data's embeddings; the input's
+ * embedding is compared with them and the closest adapter is chosen), with the
+ * same output format as dlm_pregate so it feeds dlm_switch / dlm_sgmm as is:
+ *   x [T][d], C [E][J][d] (row-major, dtype; C adapter-major: J centroids of
+ *   adapter 0, then adapter 1, ...).  Adapter distance = min over its J
+ *   centroids of sum_k (x_k - c_k)^2, accumulated in binary64 with a fixed
+ *   reduction order.  idx[t] = {nearest adapter (ties -> lower index), -1},
+ *   g[t] = {1, 0}.
+ * Requires 1 <= E <= DLM_MAX_EXPERTS, 1 <= J <= DLM_MAX_CENTROIDS, d >= 1,
+ * 0 <= T < 2^31.  One launch on `stream`, no allocation.
+ */
+int dlm_pregate_centroid(const void* x, const void* C, int64_t T, int64_t d, int32_t E,
+                         int32_t J, int32_t dtype, int32_t* idx, float* g, void* stream);
 
 /* ------------------------------------------------------------ fused switch */
 

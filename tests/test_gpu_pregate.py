@@ -99,3 +99,85 @@ def test_router_empty_batch_is_noop():
     Wr = torch.zeros(64, 8, dtype=torch.bfloat16, device="cuda")
     idx, g = dlm.pregate(x, Wr)
     assert idx.shape == (0, 2)
+
+
+# ---- nearest-centroid pre-gate ------------------------------------------------
+
+def _check_centroid(x, C, what):
+    """Slot 0 bit-exact wherever the nearest adapter is farther from a tie than
+    twice the binary64 summation bound of its distance; near ties the GPU's pick
+    must be within that bound of the oracle's.  Slot 1 empty, g = (1, 0)."""
+    print(f"[centroid] {what} T={x.shape[0]} d={x.shape[1]} E={C.shape[0]} J={C.shape[1]} {x.dtype}", flush=True)
+    idx, g = dlm.pregate_centroid(x, C)
+    torch.cuda.synchronize()
+    idx, g = idx.cpu(), g.cpu()
+    ri, rg, dist, mg = oracle.pregate_centroid(x.cpu(), C.cpu(), with_stats=True)
+    E = C.shape[0]
+    assert (idx[:, 1] == -1).all() and (g[:, 0] == 1).all() and (g[:, 1] == 0).all()
+    assert ((idx[:, 0] >= 0) & (idx[:, 0] < E)).all()
+    d = x.shape[1]
+    u = 2.0 ** -53
+    bd = (d + 2) * u / (1 - (d + 2) * u) * dist.max(1).values.numpy()
+    safe = mg.numpy() > 2 * bd
+    assert (idx[:, 0].numpy()[safe] == ri[:, 0].numpy()[safe]).all(), f"{what}: centroid index mismatch"
+    dd = dist.numpy()
+    for t in np.nonzero(~safe)[0]:
+        assert dd[t, idx[t, 0]] - dd[t, ri[t, 0]] <= 2 * bd[t], (what, t)
+    return int((~safe).sum())
+
+
+def _xc(T, d, E, J, dt, *keys):
+    x = synth.normal_device((T, d), 1.0, dt, "cuda", *keys, "x")
+    C = synth.normal_device((E, J, d), 1.0, dt, "cuda", *keys, "C")
+    return x, C
+
+
+@pytest.mark.parametrize("T,d,E,J,dt", [(16, 64, 4, 2, torch.float32), (256, 4096, 8, 4, torch.bfloat16),
+                                        (128, 8192, 16, 2, torch.bfloat16), (37, 100, 3, 5, torch.bfloat16),
+                                        (5, 1, 1, 1, torch.float32), (64, 256, 32, 3, torch.bfloat16),
+                                        (1, 4096, 8, 1, torch.bfloat16), (9, 520, 7, 9, torch.float32)])
+def test_centroid_router_shapes(T, d, E, J, dt):
+    x, C = _xc(T, d, E, J, dt, 4000, T, d, E, J)
+    assert _check_centroid(x, C, f"shape {T}x{d} E={E} J={J}") == 0
+
+
+def test_centroid_router_ties_and_exact_hits():
+    d, E, J = 96, 6, 3
+    x, C = _xc(5, d, E, J, torch.bfloat16, 4100)
+    C[4] = C[1]                 # a duplicated adapter never beats its lower-indexed twin
+    x[0] = C[3, 2]              # a token on a centroid picks its adapter (distance 0)
+    x[1] = C[1, 0]              # ... and on a duplicated one, the lower index
+    idx, g = dlm.pregate_centroid(x, C)
+    torch.cuda.synchronize()
+    assert idx[0, 0].item() == 3 and idx[1, 0].item() == 1
+    assert (idx[:, 0] != 4).all()
+    _check_centroid(x, C, "ties")
+
+
+def test_centroid_router_feeds_the_switch():
+    """The centroid router's one-slot sets drive the fused switch directly."""
+    E, r, d = 6, 16, 256
+    x, C = _xc(2, d, E, 2, torch.bfloat16, 4200)
+    W = synth.normal_device((128, d), 0.02, torch.bfloat16, "cuda", 4200, "W")
+    A = synth.normal_device((E, r, d), 0.02, torch.bfloat16, "cuda", 4200, "A")
+    B = synth.normal_device((E, 128, r), 0.02, torch.bfloat16, "cuda", 4200, "B")
+    W0 = W.cpu().clone()
+    idx, g = dlm.pregate_centroid(x, C)
+    L = dlm.Layers([(W, A, B)], E, r, 1.0)
+    L.switch((idx[0], g[0]), (idx[1], g[1]))
+    torch.cuda.synchronize()
+    ri, rg = oracle.pregate_centroid(x.cpu(), C.cpu())
+    assert torch.equal(ri, idx.cpu())
+    from gpu_util import check_bf16, host_set
+    ref, ex, ab = oracle.switch(W0, A.cpu(), B.cpu(), 1.0, host_set(ri[0], rg[0]), host_set(ri[1], rg[1]),
+                                with_stats=True)
+    check_bf16(W.cpu(), ref, ex, ab, 4 * r + 2, what="centroid->switch")
+    assert L.status() == dlm.DLM_OK
+    L.close()
+
+
+def test_centroid_router_empty_batch_is_noop():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros(4, 2, 64, dtype=torch.bfloat16, device="cuda")
+    idx, g = dlm.pregate_centroid(x, C)
+    assert idx.shape == (0, 2)
