@@ -341,6 +341,27 @@ def bench_sgmm(torch, dlm, synth, name, reps, log):
            "frac_of_hbm_peak": nbytes / sec / HBM_PEAK, "algo_bytes_per_pass": nbytes}
     if name == "mixed-decode":
         res.update(_per_layer_variant(torch, dlm, wl, probs, sets, reps, sec, log))
+        # rows that release their adapters (both slots empty) are left out by the
+        # segmentation: the same steps with the upper half of the rows released
+        rel = []
+        for i, gg in sets:
+            i2, g2 = i.clone(), gg.clone()
+            i2[wl.T // 2:] = -1
+            g2[wl.T // 2:] = 0
+            rel.append((i2, g2))
+        for i, gg in rel:
+            grp.run(i, gg, workspace=ws)
+        e0.record(stream)
+        for _ in range(reps):
+            for i, gg in rel:
+                grp.run(i, gg, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert dlm.sgmm_status(ws) == dlm.DLM_OK
+        sec_rel = e0.elapsed_time(e1) / 1e3 / reps
+        res["half_released_ms_per_step"] = sec_rel * 1e3 / len(sets)
+        res["half_released_time_ratio"] = sec_rel / sec
+        res["grouped_ms_per_step"] = sec * 1e3 / len(sets)
     grp.close()
     del probs
     torch.cuda.empty_cache()
