@@ -167,7 +167,10 @@ __global__ __launch_bounds__(kVecWaves* kWave) void pregate_bf16_vec(
 // compares smaller, so the index stays in range.
 constexpr int kCGroup = 8;
 
-template <typename T>
+// VEC (bf16, d a multiple of 8, 16-byte aligned rows): a lane takes 8
+// consecutive columns per step, one 16-byte load of x and of each centroid of
+// the group, all issued before any arithmetic.
+template <typename T, bool VEC>
 __global__ __launch_bounds__(kVecWaves* kWave) void pregate_centroid_kernel(
     const T* __restrict__ x, const T* __restrict__ C, int64_t d, int E, int J, int32_t* __restrict__ idx,
     float* __restrict__ g) {
@@ -181,13 +184,35 @@ __global__ __launch_bounds__(kVecWaves* kWave) void pregate_centroid_kernel(
         double acc[kCGroup];
 #pragma unroll
         for (int q = 0; q < kCGroup; ++q) acc[q] = 0.0;
-        for (int64_t k = lane + (int64_t)kWave * w; k < d; k += (int64_t)kVecWaves * kWave) {
-            const double xv = ldv(xr, k);
+        if constexpr (VEC) {
+            const int64_t nc = d / 8;
+            for (int64_t c = lane + (int64_t)kWave * w; c < nc; c += (int64_t)kVecWaves * kWave) {
+                const u32x4 xv = ld128((const uint16_t*)xr + 8 * c);
+                u32x4 cv[kCGroup];
 #pragma unroll
-            for (int q = 0; q < kCGroup; ++q) {
-                if (c0 + q >= EJ) break;
-                const double df = xv - ldv(C + (int64_t)(c0 + q) * d, k);
-                acc[q] = fma(df, df, acc[q]);
+                for (int q = 0; q < kCGroup; ++q)  // centroids past E*J re-read the group's first, unused
+                    cv[q] = ld128((const uint16_t*)C + (int64_t)(c0 + q < EJ ? c0 + q : c0) * d + 8 * c);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const double xj = (double)(jj & 1 ? bf_hi(xv[jj >> 1]) : bf_lo(xv[jj >> 1]));
+#pragma unroll
+                    for (int q = 0; q < kCGroup; ++q) {
+                        const uint32_t cw = cv[q][jj >> 1];
+                        const double df = xj - (double)(jj & 1 ? bf_hi(cw) : bf_lo(cw));
+                        acc[q] = fma(df, df, acc[q]);
+                    }
+                }
+            }
+        } else {
+            for (int64_t k = lane + (int64_t)kWave * w; k < d; k += (int64_t)kVecWaves * kWave) {
+                const double xv = ldv(xr, k);
+#pragma unroll
+                for (int q = 0; q < kCGroup; ++q) {
+                    if (c0 + q >= EJ) break;
+                    const double df = xv - ldv(C + (int64_t)(c0 + q) * d, k);
+                    acc[q] = fma(df, df, acc[q]);
+                }
             }
         }
 #pragma unroll
@@ -240,11 +265,15 @@ hipError_t launch_pregate_centroid(const void* x, const void* C, int64_t T, int6
                                    int32_t* idx, float* g, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const dim3 grid((unsigned)T), block(kVecWaves * kWave);
+    const bool vec = dtype == 1 && d % 8 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)C & 15) == 0;
     if (dtype == 0)
-        hipLaunchKernelGGL(pregate_centroid_kernel<float>, grid, block, 0, s, (const float*)x, (const float*)C, d, E, J,
-                           idx, g);
+        hipLaunchKernelGGL((pregate_centroid_kernel<float, false>), grid, block, 0, s, (const float*)x,
+                           (const float*)C, d, E, J, idx, g);
+    else if (vec)
+        hipLaunchKernelGGL((pregate_centroid_kernel<uint16_t, true>), grid, block, 0, s, (const uint16_t*)x,
+                           (const uint16_t*)C, d, E, J, idx, g);
     else
-        hipLaunchKernelGGL(pregate_centroid_kernel<uint16_t>, grid, block, 0, s, (const uint16_t*)x,
+        hipLaunchKernelGGL((pregate_centroid_kernel<uint16_t, false>), grid, block, 0, s, (const uint16_t*)x,
                            (const uint16_t*)C, d, E, J, idx, g);
     return hipGetLastError();
 }
