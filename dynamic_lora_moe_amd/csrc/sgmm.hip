@@ -296,8 +296,11 @@ __device__ __forceinline__ int mask_list(uint32_t m, int* out) {
 
 // ---- shrink (bf16, MFMA) -----------------------------------------------------
 
-// Tiles per shrink work item: every A operand feeds one MFMA per tile.
+// Tiles per shrink work item: every A operand feeds one MFMA per tile.  Only
+// one tile per item is built and tested (two measured slower on both
+// workloads); the loops over kTM keep the shape of the multi-tile form.
 constexpr int kTM = 1;
+static_assert(kTM == 1, "only single-tile shrink work items are tested");
 constexpr int kXRows = 32 * kTM;
 // 64-wide K chunks of one slice, and 16-byte chunks of one x row of a slice
 constexpr int kKC = kSgmmKSlice / 64;
