@@ -94,6 +94,31 @@ def test_switch_and_status_validation(lib):
     assert lib.dlm_sgmm_group_run(None, P(FAKE), P(FAKE), 4, P(FAKE), 1 << 20, None) == dlm.DLM_EINVAL
 
 
+def test_centroid_pregate_validation(lib):
+    P = C.c_void_p
+    f = lib.dlm_pregate_centroid
+    assert f(P(FAKE), P(FAKE), 4, 64, 0, 2, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert "E=0" in _err(lib)
+    assert f(P(FAKE), P(FAKE), 4, 64, 33, 2, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert f(P(FAKE), P(FAKE), 4, 64, 8, 0, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert f(P(FAKE), P(FAKE), 4, 64, 8, 1025, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert f(P(FAKE), P(FAKE), 4, 0, 8, 2, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert f(P(FAKE), P(FAKE), -1, 64, 8, 2, 1, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+    assert f(P(FAKE), P(FAKE), 4, 64, 8, 2, 5, P(FAKE), P(FAKE), None) == dlm.DLM_EDTYPE
+    assert f(P(FAKE), None, 4, 64, 8, 2, 1, P(FAKE), P(FAKE), None) == dlm.DLM_EINVAL
+    # E = 1 is valid here (a single adapter always wins); T = 0 touches nothing
+    assert f(None, None, 0, 64, 1, 1, 1, None, None, None) == dlm.DLM_OK
+
+
+def test_product_entry_points_validation(lib):
+    P = C.c_void_p
+    assert lib.dlm_layers_bind_vectors(None, P(FAKE), P(FAKE)) == dlm.DLM_EINVAL
+    assert lib.dlm_gemv(None, None) == dlm.DLM_EINVAL
+    assert lib.dlm_switch_gemv(None, None, None, None, None, None) == dlm.DLM_EINVAL
+    assert lib.dlm_switch_gemv_launches(None) == 0
+    assert lib.dlm_layers_repack(None, None) == dlm.DLM_EINVAL
+
+
 def test_sgmm_workspace_size(lib):
     b = C.c_size_t(0)
     assert lib.dlm_sgmm_workspace_size(4096, 11008, 8, 16, 7, C.byref(b)) == dlm.DLM_OK
