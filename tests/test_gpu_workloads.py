@@ -154,3 +154,44 @@ def test_mixed_decode_grouped_sampled():
         rows = np.sort(rng.choice(wl.T, 8, replace=False))
         _sgmm_check_rows(wl, probs, ys, idx[step], g[step], rows, f"mixed step {step}")
     grp.close()
+
+
+def test_7b_decode_fused_switch_and_product_per_layer_sampled():
+    """The decode loop's fused form at its full size: one layer handle of the
+    7B-shaped workload (7 projections), dlm_switch_gemv with the router's device
+    sets.  Sampled rows of W' against the oracle's switch of those rows; the same
+    rows of y against the oracle's product of those switched rows with x."""
+    from test_gpu_gemv import _bf16_ulp, _check_y
+    from gpu_util import gamma
+    wl = synth.WORKLOADS["7b-decode"]
+    print("[workload] 7b-decode fused switch + product: building one layer", flush=True)
+    model = synth.switch_model(wl, layers=[5])
+    x, Wr = synth.router_inputs(wl)
+    ri, rg = oracle.pregate(x.cpu(), Wr.cpu())
+    idx, g = dlm.pregate(x, Wr)
+    xs = [synth.normal_device((W.shape[1],), 1.0, wl.dtype, "cuda", wl.cfg_id, "xin", 5, k)
+          for k, (_, _, W, _, _) in enumerate(model)]
+    ys = [torch.full((W.shape[0],), float("nan"), dtype=torch.float32, device="cuda") for _, _, W, _, _ in model]
+    L = dlm.Layers([(W, A, B) for _, _, W, A, B in model], wl.E, wl.r, wl.scale)
+    L.bind_vectors(xs, ys)
+    W0 = [W.clone() for _, _, W, _, _ in model]
+    for t in (0, 41):
+        for (_, _, W, _, _), w0 in zip(model, W0):
+            W.copy_(w0)
+        old = None if t == 0 else host_set(ri[t - 1], rg[t - 1])
+        new = host_set(ri[t], rg[t])
+        pre = _switch_sampled(wl, model, 4, old, new, "7b fused")
+        L.switch_gemv(None if t == 0 else (idx[t - 1], g[t - 1]), (idx[t], g[t]))
+        torch.cuda.synchronize()
+        print(f"[workload] 7b-decode fused step {t}", flush=True)
+        _check_sampled(wl, model, pre, old, new, f"7b fused step {t}")
+        for (l, name, W, A, B), (rows, W0r), xv, y in zip(model, pre, xs, ys):
+            ref, ex, ab = oracle.switch_rows(W0r, rows, A.cpu(), B.cpu(), W.shape[0], wl.scale, old, new,
+                                             with_stats=True)
+            wtol = np.maximum(2 * _bf16_ulp(ref.double().numpy()), gamma(4 * wl.r + 2) * ab.numpy())
+            _check_y(y[torch.from_numpy(rows).cuda()], ref, wtol, xv, f"7b fused step {t} {name}")
+    assert L.status() == dlm.DLM_OK
+    L.close()
+    del model, W0
+    gc.collect()
+    torch.cuda.empty_cache()
