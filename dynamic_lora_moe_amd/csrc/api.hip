@@ -466,10 +466,14 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, c
     if (r < 1 || r > DLM_MAX_RANK) return fail(DLM_ESHAPE, "sgmm: r=%d not in [1, %d]", r, DLM_MAX_RANK);
     if (!valid_dtype(dtype)) return fail(DLM_EDTYPE, "sgmm: unknown dtype %d", dtype);
     if (!std::isfinite(scale)) return fail(DLM_EINVAL, "sgmm: scale is not finite");
+    if (T == 0) {  // nothing to do; the (possibly empty) buffers are not looked at
+        if (d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim)
+            return fail(DLM_ESHAPE, "sgmm: shape d_in=%lld d_out=%lld", (long long)d_in, (long long)d_out);
+        return ok();
+    }
     dlm_sgmm_problem p{x, A, B, y, d_in, d_out};
     int rc = check_problem(p, dtype, 0);
     if (rc != DLM_OK) return rc;
-    if (T == 0) return ok();
     if (!idx || !g) return fail(DLM_EINVAL, "sgmm: idx or g is null");
     const size_t es = esize(dtype);
     if (overlap(x, (size_t)T * d_in * es, y, (size_t)T * d_out * es))

@@ -250,6 +250,7 @@ int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r,
  * dlm_sgmm_status).
  * bf16: x, y, A, B 16-byte aligned; d_in and d_out multiples of 8.
  * workspace: >= dlm_sgmm_workspace_size(T, d_in, E, r, 1) bytes, 256-byte aligned.
+ * T = 0 enqueues nothing and looks at no buffer (they may be null).
  */
 int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A,
              const void* B, void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E,

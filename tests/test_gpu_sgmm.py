@@ -67,6 +67,9 @@ CASES = [
     (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # two whole slices, largest rank
     (9, 1500, 24, 4, 8, 1.0, torch.float32),         # fp32 past one slice width
     (9000, 64, 72, 8, 16, 1.0, torch.bfloat16),      # more rows than the segment's LDS caches
+    (12, 64, 64, 1, 16, 1.0, torch.bfloat16),         # one expert: every used slot is expert 0
+    (7, 8, 8, 2, 1, 1.0, torch.bfloat16),             # rank 1, one 8-wide chunk of d_in
+    (3, 16, 8, 1, 1, 3.0, torch.float32),
 ]
 
 
@@ -181,3 +184,27 @@ def test_sgmm_group_shared_bank_and_repack():
     _check(x1, idx, g, A, B1, y10, y1, 1.0, "repacked, problem 0")
     _check(x2, idx, g, A, B2, y20, y2, 1.0, "repacked, problem 1")
     grp.close()
+
+
+def test_sgmm_all_rows_released_leaves_y_bitwise():
+    T, d_in, d_out, E, r = 64, 256, 136, 8, 16
+    x, A, B, y = _problem(T, d_in, d_out, E, r, torch.bfloat16, 3300)
+    y0 = y.clone()
+    idx = torch.full((T, 2), -1, dtype=torch.int32, device="cuda")
+    g = torch.zeros((T, 2), dtype=torch.float32, device="cuda")
+    ws = dlm.sgmm_workspace(T, d_in, E, r)
+    dlm.sgmm(x, idx, g, A, B, y, 1.0, ws)
+    torch.cuda.synchronize()
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    assert torch.equal(y, y0)
+
+
+def test_sgmm_empty_batch_is_noop():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros(4, 16, 64, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(4, 64, 16, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty(0, 2, dtype=torch.int32, device="cuda")
+    g = torch.empty(0, 2, dtype=torch.float32, device="cuda")
+    dlm.sgmm(x, idx, g, A, B, y, 1.0)
+    torch.cuda.synchronize()

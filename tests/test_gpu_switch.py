@@ -57,6 +57,8 @@ CASES = [
     ([(300, 1096), (16, 1032)], 4, 40, 1.0, torch.bfloat16),           # rank 40: padded ranks, d_in % 64
     ([(40, 64)], 2, 128, 0.5, torch.bfloat16),                         # largest rank
     ([(33, 64)], 32, 16, 1.0, torch.bfloat16),                         # most experts
+    ([(40, 24), (8, 8)], 1, 1, 1.0, torch.bfloat16),                    # one expert of rank 1
+    ([(5, 7)], 1, 1, 2.0, torch.float32),
 ]
 
 
@@ -71,7 +73,7 @@ def test_switch_parity(ci):
     # sequence: first token from the empty set, then changes of one / both / no expert
     sets = [None]
     for _ in range(4):
-        e = rng.choice(E, size=2, replace=False).tolist()
+        e = rng.choice(E, size=2, replace=E < 2).tolist()
         g = rng.random(2).astype(np.float32)
         g = (g / g.sum()).astype(np.float32).tolist()
         sets.append((e, g))
