@@ -548,47 +548,50 @@ template <int R16, bool RVEC>
 __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_xcd) {
     constexpr int RPAD = R16 * 16;
     const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
-    if (gld(hdr + SG_ERR)) return;
     const int64_t bid = blockIdx.x;
     const int64_t t = (bid & 7) * per_xcd + (bid >> 3);
     if (t >= a.n_expand_units) return;
     // work item = (problem, kECols-column group, tile) with the tile fastest:
-    // neighbouring work items (same XCD) reuse the same B column slices
+    // neighbouring work items (same XCD) reuse the same B column slices.  A
+    // problem's first item is a multiple of the tile count, so the tile is
+    // known before the problem's descriptor.
     const int64_t nt = a.L.tiles_max;
-    const int prob = a.descs ? gld(a.cb_owner + t / nt) : 0;
-    const SgDesc D = a.descs ? a.descs[prob] : a.single;
-    const int64_t local = t - D.unit0 * nt;
-    const int cg = (int)(local / nt);
-    const int tile = (int)(local - (int64_t)cg * nt);
-    if (tile >= gld(hdr + SG_NTILES)) return;
+    const int tile = (int)(t % nt);
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
     const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
     const float* gpk = (const float*)(a.ws + a.L.gpk);
     const uint32_t* tmask = (const uint32_t*)(a.ws + a.L.tmask);
+    const int tid = threadIdx.x;
+    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
+    const int lr = lane >> 3, lc = lane & 7;
+    // every load whose address does not depend on another load goes out
+    // first: the header words, the owner of the column group, the tile's rows
+    // (row-major lane map: instruction i holds row 8i + lr, chunk lc), slots,
+    // gates and expert mask
+    int yrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yrow[i] = gld(perm + tile * 32 + 8 * i + lr);
+    const uint32_t ep = gld(epk + tile * 32 + n);
+    const float g0 = gld(gpk + 2 * (tile * 32 + n)), g1 = gld(gpk + 2 * (tile * 32 + n) + 1);
+    const uint32_t tm = tid == 0 ? gld(tmask + tile) : 0u;
+    const int err = gld(hdr + SG_ERR), n_tiles = gld(hdr + SG_NTILES);
+    const int prob = a.descs ? gld(a.cb_owner + t / nt) : 0;
+    if (err || tile >= n_tiles) return;
+    const SgDesc D = a.descs ? a.descs[prob] : a.single;
+    const int cg = (int)(t / nt - D.unit0);
     const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * a.L.T_pad * 2 * RPAD;
 
     __shared__ int s_U[32];
     __shared__ int s_nU;
     __shared__ __attribute__((aligned(16))) uint16_t s_y[4][32 * 64];
     __shared__ __attribute__((aligned(16))) u32x4 s_u[kQLds][2][kWave];
-    const int tid = threadIdx.x;
-    if (tid == 0) s_nU = mask_list(gld(tmask + tile), s_U);
-    __syncthreads();
 
-    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
     const int d_out = uniform(D.d_out), r = a.r;
     const int cw = cg * kECols + w * (kEB * 64);  // this wave's first column
     const int nblk = cw >= d_out ? 0 : ((d_out - cw + 63) / 64 < kEB ? (d_out - cw + 63) / 64 : kEB);
-    const int nU = uniform(s_nU);
     const uint16_t* __restrict__ B = (const uint16_t*)D.B;
     uint16_t* __restrict__ y = (uint16_t*)D.y;
     uint16_t* ys = s_y[w];
-    const int lr = lane >> 3, lc = lane & 7;
-
-    // rows of the tile, row-major lane map (instruction i: row 8i + lr, chunk lc)
-    int yrow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) yrow[i] = gld(perm + tile * 32 + 8 * i + lr);
     auto load_y = [&](u32x4 (&yv)[4], int blk) {
         const int col = cw + blk * 64 + 8 * lc;
 #pragma unroll
@@ -599,13 +602,15 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     };
     u32x4 ycur[4], ynxt[4];
     if (nblk > 0) load_y(ycur, 0);
+    if (tid == 0) s_nU = mask_list(tm, s_U);
+    __syncthreads();
+    const int nU = uniform(s_nU);
 
     // this lane's tile row (MFMA N index n): its two slots and gates (a padding
     // position has two empty slots)
-    const uint32_t ep = gld(epk + tile * 32 + n);
     const int e0 = (int16_t)(ep & 0xffffu), e1 = (int16_t)(ep >> 16);
-    const float c0 = a.scale * gld(gpk + 2 * (tile * 32 + n));
-    const float c1 = a.scale * gld(gpk + 2 * (tile * 32 + n) + 1);
+    const float c0 = a.scale * g0;
+    const float c1 = a.scale * g1;
     const float* v0 = v + ((int64_t)(tile * 32 + n) * 2) * RPAD;
     const float* v1 = v0 + RPAD;
     // row-side operand of (expert U[q / R16], ranks 16(q % R16) + 8h + [0,8)):
