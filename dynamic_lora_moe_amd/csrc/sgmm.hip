@@ -407,12 +407,13 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     // in the packed A layout one load covers contiguous runs of 32 bytes x rank.
     const int nq = d_in / 8;
     const int64_t qstride = PK ? 8 * r : 8;  // elements from group kq to kq + 1
+    // A group past d_in loads a clamped address and is replaced by zeros where
+    // the MFMA takes it: a select right after the load would wait for it.
     auto load_a = [&](u32x4 (&dst)[4], const uint16_t* abase, int kc) {
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
             const int kq = k0 / 8 + 8 * kc + 2 * s2 + h;
-            const u32x4 val = ld128(abase + (kq < nq ? kq : nq - 1) * qstride);
-            dst[s2] = kq < nq ? val : u32x4{0u, 0u, 0u, 0u};
+            dst[s2] = ld128(abase + (kq < nq ? kq : nq - 1) * qstride);
         }
     };
     // first element of this lane's (expert, rank) row in A (row start) or in
@@ -427,12 +428,15 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     };
     auto mma = [&](const u32x4 (&ab)[4], int kc, f32x16 (&acc)[kTM]) {
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2)
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const bool in = k0 / 8 + 8 * kc + 2 * s2 + h < nq;
+            const u32x4 av = in ? ab[s2] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int j = 0; j < kTM; ++j) {
                 const u32x4 xo = *(const u32x4*)(s_x + x_off(32 * j + n, 8 * kc + 2 * s2 + h));
-                acc[j] = mfma32(xo, ab[s2], acc[j]);
+                acc[j] = mfma32(xo, av, acc[j]);
             }
+        }
     };
     auto store_v = [&](const f32x16 (&acc)[kTM], int u, int rho) {
         if (u >= nU || rho >= r) return;
