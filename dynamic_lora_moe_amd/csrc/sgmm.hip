@@ -98,6 +98,17 @@ __device__ __forceinline__ SegRow seg_row(const SegRaw& r, bool in, int E) {
     return q;
 }
 
+// Lanes of the wave whose key equals this lane's (keys in [0, 2^nbits); a
+// negative key matches nothing): one ballot per key bit.
+__device__ __forceinline__ uint64_t wave_match(int k, int nbits) {
+    uint64_t same = __ballot(k >= 0);
+    for (int b = 0; b < nbits; ++b) {
+        const uint64_t set = __ballot((k >> b) & 1);
+        same &= ((k >> b) & 1) ? set : ~set;
+    }
+    return k >= 0 ? same : 0ull;
+}
+
 // Exclusive scan over the workgroup (one value per thread, thread order).
 __device__ __forceinline__ int block_exscan(int v, int* s_tot, int& total) {
     const int lane = lane_id(), w = wave_id();
@@ -125,8 +136,10 @@ __device__ __forceinline__ int block_exscan(int v, int* s_tot, int& total) {
 // in LDS); their exclusive scan gives each key's first position.  Pass 2 takes
 // the rows in batches of kSegThreads, in order: a row's position = its key's
 // first position + rows of that key in earlier batches + in earlier waves of
-// this batch + earlier lanes of its wave (ballots).  A batch's sets are loaded
-// at its start and first needed when the rows are written out.
+// this batch + earlier lanes of its wave with the same key (a lane's
+// same-key mask comes from one ballot per key bit, so the cost does not grow
+// with the number of distinct keys in the wave).  A batch's sets are loaded at
+// its start and first needed when the rows are written out.
 constexpr int kKeyCache = 8192;
 constexpr int kTileCache = kKeyCache / 32;
 __global__ __launch_bounds__(kSegThreads) void sgmm_segment_kernel(
@@ -147,6 +160,8 @@ __global__ __launch_bounds__(kSegThreads) void sgmm_segment_kernel(
     __shared__ int s_tot[kSegWaves];
     const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
     const int nk = (E + 1) * (E + 1);
+    const int nbits = 32 - __builtin_clz((unsigned)(nk - 1));
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
     if (tid == 0) s_err = 0;
     for (int k = tid; k < nk; k += kSegThreads) s_next[k] = 0;
     for (int q = tid; q < kTileCache; q += kSegThreads) s_tm[q] = 0;
@@ -198,25 +213,18 @@ __global__ __launch_bounds__(kSegThreads) void sgmm_segment_kernel(
     for (int64_t b0 = 0; !err && b0 < T; b0 += kSegThreads) {
         const int64_t t = b0 + tid;
         const SegRaw raw = seg_load(idx, g, t, T);  // first needed when the row is written
-        static_assert((kSegWaves * kMaxKeys) % 2 == 0 && kKeyCache % kSegThreads == 0, "LDS table shapes");
-        for (int q = tid; q < kSegWaves * kMaxKeys / 2; q += kSegThreads) ((uint32_t*)&s_wc[0][0])[q] = 0;
+        static_assert(kKeyCache % kSegThreads == 0, "key cache holds whole batches");
+        for (int q = tid; q < kSegWaves * nk; q += kSegThreads) s_wc[q / nk][q % nk] = 0;
         __syncthreads();
         int k;
         if (b0 + kSegThreads <= kKeyCache)  // batch-uniform: keys from LDS, the loads stay in flight
             k = t < T ? (int)s_key[t] : -1;
         else
             k = seg_row(raw, t < T, E).key;
-        // stable rank within the wave and the wave's count of each key (ballots)
-        uint64_t todo = __ballot(k >= 0);
-        int rk = 0;
-        while (todo) {
-            const int leader = __ffsll((unsigned long long)todo) - 1;
-            const int lk = __builtin_amdgcn_readlane(k, leader);
-            const uint64_t same = __ballot(k == lk) & todo;
-            if (k == lk) rk = __popcll(same & ((1ull << lane) - 1ull));
-            if (lane == leader) s_wc[w][lk] = (uint16_t)__popcll(same);
-            todo &= ~same;
-        }
+        // stable rank within the wave and the wave's count of each key
+        const uint64_t same = wave_match(k, nbits);
+        const int rk = (int)__popcll(same & lt_mask);
+        if (same && rk == 0) s_wc[w][k] = (uint16_t)__popcll(same);
         __syncthreads();
         // rows of each key in earlier waves of the batch, in wave order
         for (int kk = tid; kk < nk; kk += kSegThreads) {
