@@ -60,6 +60,7 @@ CASES = [
     (64, 128, 256, 8, 24, 1.0, torch.bfloat16),
     (70, 72, 64, 16, 64, 1.0, torch.bfloat16),       # 70B rank, many experts
     (40, 64, 64, 32, 16, 1.0, torch.bfloat16),       # most experts
+    (2500, 64, 64, 32, 16, 1.0, torch.bfloat16),     # most experts, waves with many distinct pairs
     (20, 64, 96, 4, 128, 0.5, torch.bfloat16),       # largest rank
     (300, 256, 264, 8, 16, 1.0, torch.bfloat16),
     (40, 2056, 72, 8, 16, 1.0, torch.bfloat16),      # five K slices of 512, the last 8 wide
