@@ -159,3 +159,43 @@ def test_gemv_requires_bound_vectors():
     with pytest.raises(RuntimeError):
         L.gemv()
     L.close()
+
+
+def test_switch_gemv_multi_round_tail():
+    """A fused launch of more tiles than the GPU keeps resident at once: 6300 x
+    8264 is 25 x 33 = 825 tiles of 256 x 256, with a ragged last row band and a
+    72-column edge tile.  W' must equal a plain dlm_switch bit for bit; sampled
+    rows of W' and y (first band, middle, and the last two bands) are checked
+    against the oracle, and y is bitwise reproducible."""
+    o, n, E, r, scale = 6300, 8264, 8, 16, 2.0
+    print(f"[switch_gemv] multi-round tail: {o}x{n}", flush=True)
+    model = _model([(o, n)], E, r, torch.bfloat16, 3200)
+    W, A, B = model[0]
+    w0 = W.clone()
+    twin = [(W.clone(), A, B)]
+    xs, ys = _vectors([(o, n)], torch.bfloat16, 3200)
+    L = dlm.Layers(model, E, r, scale)
+    L.bind_vectors(xs, ys)
+    T = dlm.Layers(twin, E, r, scale)
+    old, new = ((1, 6), (0.625, 0.375)), ((3, 1), (0.5, 0.5))
+    for k in range(2):
+        W.copy_(w0)
+        twin[0][0].copy_(w0)
+        L.switch_gemv(dev_set(old), dev_set(new))
+        T.switch(dev_set(old), dev_set(new))
+        torch.cuda.synchronize()
+        assert torch.equal(W, twin[0][0]), "fused switch differs from dlm_switch"
+        if k == 0:
+            y1 = ys[0].clone()
+        else:
+            assert torch.equal(y1, ys[0]), "y not bitwise reproducible"
+    rows = np.array([0, 1, 255, 3000, 5887, 5888, 5900, 6143, 6144, 6200, 6299], dtype=np.int64)
+    w0r = w0[torch.from_numpy(rows).cuda()].cpu()
+    ref, ex, ab = oracle.switch_rows(w0r, rows, A.cpu(), B.cpu(), o, scale, old, new, with_stats=True)
+    got = W[torch.from_numpy(rows).cuda()].cpu()
+    check_bf16(got, ref, ex, ab, 4 * r + 2, what="multi-round tail W'")
+    wtol = np.maximum(2 * _bf16_ulp(ref.double().numpy()), gamma(4 * r + 2) * ab.numpy())
+    _check_y(ys[0][torch.from_numpy(rows).cuda()], ref, wtol, xs[0], "multi-round tail y")
+    assert L.status() == dlm.DLM_OK
+    L.close()
+    T.close()
