@@ -445,12 +445,18 @@ def cpu_baseline(torch, synth, target_s, log):
             elems += W.numel()
         layers += 1
         torch.cuda.empty_cache()
-    log(f"cpu oracle: {layers} layers, {elems} elements in {secs:.1f} s on {threads} threads")
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
+    log(f"cpu oracle: {layers} layers, {elems} elements in {secs:.1f} s on {threads} threads ({cpu})")
     return {"value": elems * 4 / secs / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"switch (old {old} -> new {new}) of all 7 adapted weights of the first "
                       f"{layers} of 32 layers of the 7B-shaped workload ({elems} elements, "
                       f"{secs:.1f} s of oracle time); weight bytes read+written per second, "
-                      f"binary64 oracle, OpenMP over rows"}
+                      f"binary64 oracle, OpenMP over rows, {threads} threads of {cpu}"}
 
 
 def profile_kernels(torch, dlm, synth, n_switch, log):
