@@ -310,33 +310,6 @@ class SgmmGroup:
     def workspace(self, T: int, device="cuda"):
         return sgmm_workspace(T, self.d_in_max, self.E, self.r, self.n, device)
 
-    def bind_vectors(self, xs, ys):
-        """Bind an input x_i [d_in] (the weights' dtype) and an output y_i [d_out]
-        (fp32) device tensor to every weight, for gemv() and switch_gemv()."""
-        assert len(xs) == len(ys) == len(self._keep)
-        for (W, _, _), x, y in zip(self._keep, xs, ys):
-            _need(x, "x")
-            _need(y, "y")
-            assert x.dtype == W.dtype and x.numel() == W.shape[1] and y.dtype == torch.float32 \
-                and y.numel() == W.shape[0]
-        xa = (C.c_void_p * len(xs))(*[x.data_ptr() for x in xs])
-        ya = (C.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
-        _check(load().dlm_layers_bind_vectors(self._h, xa, ya), "dlm_layers_bind_vectors")
-        self._vecs = (list(xs), list(ys))
-
-    def gemv(self, stream=None):
-        """y_i = W_i x_i for every weight (bound vectors)."""
-        _check(load().dlm_gemv(self._h, _stream(stream)), "dlm_gemv")
-
-    def switch_gemv(self, old=None, new=None, stream=None):
-        """switch(old, new), then y_i = W'_i x_i (bound vectors)."""
-        oi, og = _set_ptrs(old)
-        ni, ng = _set_ptrs(new)
-        _check(load().dlm_switch_gemv(self._h, oi, og, ni, ng, _stream(stream)), "dlm_switch_gemv")
-
-    def launches_per_switch_gemv(self) -> int:
-        return load().dlm_switch_gemv_launches(self._h)
-
     def repack(self, stream=None):
         """Refresh the packed A copies after the A banks were changed in place."""
         _check(load().dlm_sgmm_group_repack(self._h, _stream(stream)), "dlm_sgmm_group_repack")

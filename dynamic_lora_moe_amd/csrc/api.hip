@@ -279,28 +279,9 @@ int dlm_switch(dlm_layers* h, const int32_t* old_idx, const float* old_g, const 
     if (!h) return fail(DLM_EINVAL, "switch: null handle");
     if ((old_idx && !old_g) || (new_idx && !new_g))
         return fail(DLM_EINVAL, "switch: a set has indices but no gates");
-    SwitchArgs a;
-    a.descs = h->d_descs;
-    a.n_desc = h->n;
-    a.E = h->E;
-    a.r = h->r;
-    a.scale = h->scale;
-    a.old_idx = old_idx;
-    a.old_g = old_g;
-    a.new_idx = new_idx;
-    a.new_g = new_g;
-    a.err = h->d_err;
-    a.zimg = h->d_zimg;
-    hipError_t e;
-    if (h->dtype == DLM_BF16) {
-        a.n_units = h->n_tiles;
-        a.per_xcd = h->per_xcd;
-        e = launch_switch_bf16(a, h->tile, (hipStream_t)stream);
-    } else {
-        a.n_units = h->n_elems;
-        a.per_xcd = 0;
-        e = launch_switch_generic(a, h->dtype, (hipStream_t)stream);
-    }
+    const SwitchArgs a = switch_args(h, old_idx, old_g, new_idx, new_g);
+    const hipError_t e = h->dtype == DLM_BF16 ? launch_switch_bf16(a, h->tile, (hipStream_t)stream)
+                                              : launch_switch_generic(a, h->dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "switch launch");
     return ok();
 }
@@ -324,8 +305,10 @@ int dlm_layers_bind_vectors(dlm_layers* h, const void* const* x, float* const* y
         d[i].yv = y[i];
     }
     float* part = nullptr;
-    hipError_t e = hipSuccess;
-    if (switch_gemv_fused(h->tile, h->dtype)) {
+    // launches still in flight on any stream read the current table and
+    // partial buffer: let them finish before either is replaced
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess && switch_gemv_fused(h->tile, h->dtype)) {
         size_t total = 0;
         for (const SwDesc& q : d) total += (size_t)q.n_ct * q.d_out;
         e = hipMalloc((void**)&part, total * sizeof(float));

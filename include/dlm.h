@@ -186,8 +186,9 @@ int dlm_switch_launches(const dlm_layers* h);
  * Bind one input and one output vector to every weight of the handle:
  *   x (host) [n] device pointers, x_i [d_in_i] in the handle's dtype (bf16:
  *   16-byte aligned); y (host) [n] device pointers, y_i [d_out_i] fp32, not
- *   overlapping x_i or W_i.  The pointers are copied into the device table
- *   (synchronous); the buffers stay owned by the caller.  bf16 handles with
+ *   overlapping x_i or W_i.  The device is synchronised first (launches in
+ *   flight on any stream finish with the previous binding), then the pointers
+ *   are copied into the device table; the buffers stay owned by the caller.  bf16 handles with
  *   r <= 16 also get a partial-product buffer (sum of ceil(d_in_i/256) *
  *   d_out_i floats), freed by destroy.  Binding again replaces the vectors.
  */
