@@ -126,6 +126,29 @@ def _need(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _like(t: torch.Tensor, name: str, shape, dtype, device):
+    """The library takes bare pointers and cannot see a tensor's extent: every
+    buffer it reads or writes is checked here against the shape it will assume."""
+    _need(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _sets_out(idx, g, T: int, device, what: str):
+    """Per-row expert sets: idx [T][2] int32 and g [T][2] fp32 (allocated when None)."""
+    if idx is None:
+        idx = torch.empty((T, 2), dtype=torch.int32, device=device)
+    if g is None:
+        g = torch.empty((T, 2), dtype=torch.float32, device=device)
+    _like(idx, f"{what} idx", (T, 2), torch.int32, device)
+    _like(g, f"{what} g", (T, 2), torch.float32, device)
+    return idx, g
+
+
 # ---- router -------------------------------------------------------------------
 
 def pregate(x: torch.Tensor, Wr: torch.Tensor, idx=None, g=None, stream=None):
@@ -134,12 +157,8 @@ def pregate(x: torch.Tensor, Wr: torch.Tensor, idx=None, g=None, stream=None):
     _need(Wr, "Wr")
     T, d = x.shape
     E = Wr.shape[1]
-    if Wr.shape[0] != d or Wr.dtype != x.dtype:
-        raise ValueError("Wr must be [d][E] with x's dtype")
-    if idx is None:
-        idx = torch.empty((T, 2), dtype=torch.int32, device=x.device)
-    if g is None:
-        g = torch.empty((T, 2), dtype=torch.float32, device=x.device)
+    _like(Wr, "Wr", (d, E), x.dtype, x.device)
+    idx, g = _sets_out(idx, g, T, x.device, "pregate")
     _check(load().dlm_pregate(_p(x), _p(Wr), T, d, E, _dt(x), _p(idx), _p(g), _stream(stream)),
            "dlm_pregate")
     return idx, g
@@ -152,12 +171,8 @@ def pregate_centroid(x: torch.Tensor, C: torch.Tensor, idx=None, g=None, stream=
     _need(C, "C")
     T, d = x.shape
     E, J, d2 = C.shape
-    if d2 != d or C.dtype != x.dtype:
-        raise ValueError("C must be [E][J][d] with x's dtype")
-    if idx is None:
-        idx = torch.empty((T, 2), dtype=torch.int32, device=x.device)
-    if g is None:
-        g = torch.empty((T, 2), dtype=torch.float32, device=x.device)
+    _like(C, "C", (E, J, d), x.dtype, x.device)
+    idx, g = _sets_out(idx, g, T, x.device, "pregate_centroid")
     _check(load().dlm_pregate_centroid(_p(x), _p(C), T, d, E, J, _dt(x), _p(idx), _p(g), _stream(stream)),
            "dlm_pregate_centroid")
     return idx, g
@@ -184,8 +199,14 @@ class Layers:
         arr = (dlm_proj * len(self._keep))()
         dt = None
         for k, (W, A, B) in enumerate(self._keep):
-            for t, nm in ((W, "W"), (A, "A"), (B, "B")):
-                _need(t, nm)
+            _need(W, f"weight {k} W")
+            if W.dim() != 2:
+                raise ValueError(f"weight {k}: W must be [d_out][d_in]")
+            d_out, d_in = W.shape
+            W0 = self._keep[0][0]
+            _like(W, f"weight {k} W", (d_out, d_in), W0.dtype, W0.device)
+            _like(A, f"weight {k} A", (E, r, d_in), W.dtype, W.device)
+            _like(B, f"weight {k} B", (E, d_out, r), W.dtype, W.device)
             dt = _dt(W) if dt is None else dt
             arr[k] = dlm_proj(W.data_ptr(), A.data_ptr(), B.data_ptr(), W.shape[0], W.shape[1])
         h = C.c_void_p()
@@ -211,12 +232,11 @@ class Layers:
     def bind_vectors(self, xs, ys):
         """Bind an input x_i [d_in] (the weights' dtype) and an output y_i [d_out]
         (fp32) device tensor to every weight, for gemv() and switch_gemv()."""
-        assert len(xs) == len(ys) == len(self._keep)
-        for (W, _, _), x, y in zip(self._keep, xs, ys):
-            _need(x, "x")
-            _need(y, "y")
-            assert x.dtype == W.dtype and x.numel() == W.shape[1] and y.dtype == torch.float32 \
-                and y.numel() == W.shape[0]
+        if not len(xs) == len(ys) == len(self._keep):
+            raise ValueError("one x and one y per weight")
+        for k, ((W, _, _), x, y) in enumerate(zip(self._keep, xs, ys)):
+            _like(x, f"x {k}", (W.shape[1],), W.dtype, W.device)
+            _like(y, f"y {k}", (W.shape[0],), torch.float32, W.device)
         xa = (C.c_void_p * len(xs))(*[x.data_ptr() for x in xs])
         ya = (C.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
         _check(load().dlm_layers_bind_vectors(self._h, xa, ya), "dlm_layers_bind_vectors")
@@ -266,17 +286,28 @@ def sgmm_workspace(T: int, d_in_max: int, E: int, r: int, n_problems: int = 1,
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _ws_bytes(workspace) -> int:
+    _need(workspace, "workspace")
+    return workspace.numel() * workspace.element_size()
+
+
 def sgmm(x, idx, g, A, B, y, scale: float, workspace=None, stream=None):
     """y += sum_k s g_k (x A_k^T) B_k^T row by row, in place (returns y)."""
-    for t, nm in ((x, "x"), (idx, "idx"), (g, "g"), (A, "A"), (B, "B"), (y, "y")):
-        _need(t, nm)
+    _need(x, "x")
+    _need(A, "A")
+    _need(B, "B")
     T, d_in = x.shape
     E, r, _ = A.shape
     d_out = B.shape[1]
+    _like(A, "A", (E, r, d_in), x.dtype, x.device)
+    _like(B, "B", (E, d_out, r), x.dtype, x.device)
+    _like(y, "y", (T, d_out), x.dtype, x.device)
+    _like(idx, "idx", (T, 2), torch.int32, x.device)
+    _like(g, "g", (T, 2), torch.float32, x.device)
     if workspace is None:
         workspace = sgmm_workspace(T, d_in, E, r, 1, x.device)
     _check(load().dlm_sgmm(_p(x), _p(idx), _p(g), _p(A), _p(B), _p(y), T, d_in, d_out, E, r,
-                           float(scale), _dt(x), _p(workspace), workspace.numel(), _stream(stream)),
+                           float(scale), _dt(x), _p(workspace), _ws_bytes(workspace), _stream(stream)),
            "dlm_sgmm")
     return y
 
@@ -294,9 +325,19 @@ class SgmmGroup:
         self._keep = list(problems)
         arr = (dlm_sgmm_problem * len(self._keep))()
         dt = None
+        x0 = self._keep[0][0]
+        _need(x0, "problem 0 x")
         for k, (x, A, B, y) in enumerate(self._keep):
-            for t, nm in ((x, "x"), (A, "A"), (B, "B"), (y, "y")):
-                _need(t, nm)
+            _need(x, f"problem {k} x")
+            _need(B, f"problem {k} B")
+            if x.dim() != 2 or B.dim() != 3:
+                raise ValueError(f"problem {k}: x must be [T][d_in] and B [E][d_out][r]")
+            T_k, d_in = x.shape
+            d_out = B.shape[1]
+            _like(x, f"problem {k} x", (T_k, d_in), x0.dtype, x0.device)
+            _like(A, f"problem {k} A", (E, r, d_in), x.dtype, x.device)
+            _like(B, f"problem {k} B", (E, d_out, r), x.dtype, x.device)
+            _like(y, f"problem {k} y", (T_k, d_out), x.dtype, x.device)
             dt = _dt(x) if dt is None else dt
             arr[k] = dlm_sgmm_problem(x.data_ptr(), A.data_ptr(), B.data_ptr(), y.data_ptr(),
                                       x.shape[1], y.shape[1])
@@ -306,6 +347,8 @@ class SgmmGroup:
         self._h = h
         self.E, self.r, self.n = E, r, len(self._keep)
         self.d_in_max = max(x.shape[1] for x, _, _, _ in self._keep)
+        self.rows = min(x.shape[0] for x, _, _, _ in self._keep)  # rows every problem holds
+        self.device = x0.device
 
     def workspace(self, T: int, device="cuda"):
         return sgmm_workspace(T, self.d_in_max, self.E, self.r, self.n, device)
@@ -316,12 +359,15 @@ class SgmmGroup:
 
     def run(self, idx, g, T: int | None = None, workspace=None, stream=None):
         _need(idx, "idx")
-        _need(g, "g")
         T = idx.shape[0] if T is None else T
+        if not 0 <= T <= self.rows:
+            raise ValueError(f"T={T} rows, but the group's problems hold {self.rows}")
+        _like(idx[:T], "idx", (T, 2), torch.int32, self.device)
+        _like(g[:T], "g", (T, 2), torch.float32, self.device)
         if workspace is None:
             workspace = self.workspace(T, idx.device)
         _check(load().dlm_sgmm_group_run(self._h, _p(idx), _p(g), T, _p(workspace),
-                                         workspace.numel(), _stream(stream)), "dlm_sgmm_group_run")
+                                         _ws_bytes(workspace), _stream(stream)), "dlm_sgmm_group_run")
         return workspace
 
     def close(self):
