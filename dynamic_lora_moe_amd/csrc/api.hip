@@ -35,6 +35,8 @@ int ok() {
 }
 
 int hip_fail(hipError_t e, const char* what) {
+    if (e == hipErrorInvalidConfiguration)  // the launchers' own refusal (grid_fits)
+        return fail(DLM_ESHAPE, "%s: the sizes need a launch grid of more than 2^32 - 1 work-items", what);
     return fail(DLM_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 

@@ -8,6 +8,14 @@
 
 namespace dlm {
 
+// A launch covers at most 2^32 - 1 work-items along x (the dispatch packet's
+// grid size is 32 bits).  Launchers check their grid with this before they
+// launch anything and refuse one past it with hipErrorInvalidConfiguration,
+// rather than letting the block count wrap when it is narrowed.
+inline bool grid_fits(int64_t blocks, int64_t threads_per_block) {
+    return blocks >= 0 && blocks <= (int64_t)0xffffffffLL / threads_per_block;
+}
+
 // ---- fused switch ---------------------------------------------------------
 
 // One adapted weight in the device table of a dlm_layers handle.

@@ -246,6 +246,8 @@ __global__ __launch_bounds__(kVecWaves* kWave) void pregate_centroid_kernel(
 template <typename T>
 hipError_t launch_t(const void* x, const void* Wr, int64_t T_, int64_t d, int E, int32_t* idx,
                     float* g, hipStream_t s) {
+    if (!grid_fits((T_ + kTokPerBlock - 1) / kTokPerBlock, kTokPerBlock * kWave))
+        return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)((T_ + kTokPerBlock - 1) / kTokPerBlock));
     const dim3 block(kTokPerBlock * kWave);
     const T* xp = (const T*)x;
@@ -264,6 +266,7 @@ hipError_t launch_t(const void* x, const void* Wr, int64_t T_, int64_t d, int E,
 hipError_t launch_pregate_centroid(const void* x, const void* C, int64_t T, int64_t d, int E, int J, int dtype,
                                    int32_t* idx, float* g, hipStream_t s) {
     if (T == 0) return hipSuccess;
+    if (!grid_fits(T, kVecWaves * kWave)) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)T), block(kVecWaves * kWave);
     const bool vec = dtype == 1 && d % 8 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)C & 15) == 0;
     if (dtype == 0)
@@ -283,6 +286,7 @@ hipError_t launch_pregate(const void* x, const void* Wr, int64_t T, int64_t d, i
     if (dtype == 0) return launch_t<float>(x, Wr, T, d, E, idx, g, s);
     const bool vec = d % 8 == 0 && E % 8 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)Wr & 15) == 0;
     if (!vec) return launch_t<uint16_t>(x, Wr, T, d, E, idx, g, s);
+    if (!grid_fits(T, kVecWaves * kWave)) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)T);
     const dim3 block(kVecWaves * kWave);
     const uint16_t* xp = (const uint16_t*)x;

@@ -909,12 +909,27 @@ hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
 
 hipError_t launch_sgmm_pack_a(const void* A, void* Ap, int E, int r, int64_t d_in, hipStream_t s) {
     const int64_t nq = d_in / 8, total = (int64_t)E * r * nq;
+    if (!grid_fits((total + 255) / 256, 256)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(sgmm_pack_a_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        (const uint16_t*)A, (uint16_t*)Ap, r, nq, total);
     return hipGetLastError();
 }
 
+// Every grid of the call fits (checked before the first launch, so a refused
+// call leaves the workspace and y untouched).
+static bool sgmm_grids_fit(const SgmmArgs& a, int dtype) {
+    if (dtype == 1) {
+        const int64_t n_units = a.total_ks * ((a.L.tiles_max + kTM - 1) / kTM);
+        return grid_fits(8 * ((n_units + 7) / 8), 256) &&
+               grid_fits((a.L.T_pad * 2 * a.L.r_pad / 4 + 255) / 256, 256) &&
+               grid_fits(8 * ((a.n_expand_units + 7) / 8), 256);
+    }
+    return grid_fits((a.L.T_pad * 2 * a.r + 255) / 256, 256) &&
+           grid_fits((a.L.T_pad * a.d_out_max + 255) / 256, 256);
+}
+
 hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
+    if (!sgmm_grids_fit(a, dtype)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(sgmm_segment_kernel, dim3(1), dim3(kSegThreads), 0, s, a.idx, a.g, a.T, a.E,
                        a.ws, a.L);
     hipError_t e = hipGetLastError();

@@ -820,12 +820,14 @@ __global__ __launch_bounds__(256) void switch_pack_a_kernel(const uint16_t* __re
 template <int R16, int CT>
 hipError_t launch_r(const SwitchArgs& a, hipStream_t s) {
     const size_t lds = ((size_t)4 * (CT / 32) * 32 * (R16 * 16) + (size_t)kWaves * 32 * 64) * sizeof(uint16_t);
+    if (!grid_fits(8 * a.per_xcd, kWaves * kWave)) return hipErrorInvalidConfiguration;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)switch_bf16_kernel<R16, CT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int64_t grid = 8 * a.per_xcd;
+    if (!grid_fits(grid, kWaves * kWave)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((switch_bf16_kernel<R16, CT>), dim3((unsigned)grid), dim3(kWaves * kWave),
                        lds, s, a);
     return hipGetLastError();
@@ -836,6 +838,7 @@ hipError_t launch_r(const SwitchArgs& a, hipStream_t s) {
 template <int R16>
 hipError_t launch_wide(const SwitchArgs& a, hipStream_t s) {
     const size_t lds = ((size_t)2 * 4 * 2 * 32 * (R16 * 16) + (size_t)kWideWBufs * kWW * 32 * 64) * sizeof(uint16_t);
+    if (!grid_fits(8 * a.per_xcd, kWW * kWave)) return hipErrorInvalidConfiguration;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)switch_wide_kernel<R16, kWideSB>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -872,6 +875,7 @@ hipError_t launch_switch_pack_a(const void* A, void* Ap, int64_t d_in, int E, in
                                 hipStream_t s) {
     const int64_t n_cb = (d_in + 63) / 64;
     const int64_t threads = (int64_t)E * n_cb * (t.r16 * 2) * 64;
+    if (!grid_fits((threads + 255) / 256, 256)) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)((threads + 255) / 256));
     const uint16_t* a = (const uint16_t*)A;
     uint16_t* ap = (uint16_t*)Ap;
@@ -888,18 +892,21 @@ bool switch_gemv_fused(const SwTile& t, int dtype) { return dtype == 1 && t.r16 
 
 hipError_t launch_switch_gemv_bf16(const SwitchArgs& a, hipStream_t s) {
     const size_t lds = ((size_t)4 * 8 * 32 * 16 + (size_t)kWaves * 32 * 64 + 256) * sizeof(uint16_t);
+    if (!grid_fits(8 * a.per_xcd, kWaves * kWave)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(switch_gemv_kernel, dim3((unsigned)(8 * a.per_xcd)), dim3(kWaves * kWave), lds, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_reduce(const SwitchArgs& a, int64_t n_bands, hipStream_t s) {
     if (n_bands == 0) return hipSuccess;
+    if (!grid_fits(n_bands, 256)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)n_bands), dim3(256), 0, s, a, n_bands);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv(const SwitchArgs& a, int64_t n_blocks, int dtype, hipStream_t s) {
     if (n_blocks == 0) return hipSuccess;
+    if (!grid_fits(n_blocks, kWaves * kWave)) return hipErrorInvalidConfiguration;
     if (dtype == 0)
         hipLaunchKernelGGL(gemv_kernel<float>, dim3((unsigned)n_blocks), dim3(kWaves * kWave), 0, s, a, n_blocks);
     else
@@ -908,6 +915,7 @@ hipError_t launch_gemv(const SwitchArgs& a, int64_t n_blocks, int dtype, hipStre
 }
 
 hipError_t launch_switch_generic(const SwitchArgs& a, int dtype, hipStream_t s) {
+    if (!grid_fits((a.n_units + 255) / 256, 256)) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)((a.n_units + 255) / 256));
     if (dtype == 0)
         hipLaunchKernelGGL(switch_generic_kernel<float>, grid, dim3(256), 0, s, a);

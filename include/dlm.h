@@ -52,7 +52,9 @@ extern "C" {
 typedef enum {
     DLM_OK = 0,
     DLM_EINVAL = -1,     /* null pointer, bad count, bad value */
-    DLM_ESHAPE = -2,     /* a size out of the supported range */
+    DLM_ESHAPE = -2,     /* a size out of the supported range, or sizes whose
+                            launch grid would exceed 2^32 - 1 work-items (refused
+                            before anything is launched) */
     DLM_EDTYPE = -3,     /* unknown or unsupported dtype */
     DLM_EALIGN = -4,     /* a pointer or row pitch not 16-byte aligned (bf16 fast path) */
     DLM_EWORKSPACE = -5, /* workspace missing or too small */

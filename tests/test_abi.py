@@ -182,3 +182,20 @@ def test_sgmm_group_create_validation(lib):
     assert lib.dlm_sgmm_group_create(arr, 2, 4, 16, 1.0, 1, C.byref(h)) == dlm.DLM_EALIGN
     assert "problem 1" in _err(lib)
     assert h.value is None
+
+
+def test_grids_past_32_bits_are_refused_before_any_launch(lib):
+    """Sizes the API accepts but whose launch grid would exceed 2^32 - 1
+    work-items: every launcher refuses them (DLM_ESHAPE) before any HIP call,
+    so the fake pointers are never used."""
+    P = C.c_void_p
+    T = 1 << 30
+    for dt in (dlm.DLM_BF16, dlm.DLM_F32):
+        assert lib.dlm_pregate(P(FAKE), P(FAKE), T, 64, 8, dt, P(FAKE), P(FAKE), None) == dlm.DLM_ESHAPE
+        assert "2^32" in _err(lib)
+        assert lib.dlm_pregate_centroid(P(FAKE), P(FAKE), T, 64, 8, 4, dt, P(FAKE), P(FAKE),
+                                        None) == dlm.DLM_ESHAPE
+        x, y = FAKE, 1 << 44  # x's and y's extents do not overlap
+        assert lib.dlm_sgmm(P(x), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(y), T, 8, 8, 1, 1, 1.0, dt,
+                            P(FAKE), C.c_size_t(1 << 62), None) == dlm.DLM_ESHAPE
+        assert "2^32" in _err(lib)
