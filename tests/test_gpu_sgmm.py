@@ -62,6 +62,10 @@ CASES = [
     (40, 64, 64, 32, 16, 1.0, torch.bfloat16),       # most experts
     (2500, 64, 64, 32, 16, 1.0, torch.bfloat16),     # most experts, waves with many distinct pairs
     (20, 64, 96, 4, 128, 0.5, torch.bfloat16),       # largest rank
+    (50, 200, 96, 4, 40, 1.0, torch.bfloat16),       # rank 40 (3 rank chunks)
+    (40, 136, 72, 4, 80, 1.0, torch.bfloat16),       # rank 80 (5)
+    (33, 64, 64, 2, 96, 1.0, torch.bfloat16),        # rank 96 (6)
+    (20, 520, 40, 3, 100, 0.5, torch.bfloat16),      # rank 100 (7): r % 8 != 0, two K slices
     (300, 256, 264, 8, 16, 1.0, torch.bfloat16),
     (40, 2056, 72, 8, 16, 1.0, torch.bfloat16),      # five K slices of 512, the last 8 wide
     (70, 1096, 136, 16, 64, 0.5, torch.bfloat16),    # three K slices, many N blocks per tile

@@ -56,6 +56,9 @@ CASES = [
     ([(768, 4096), (300, 4096)], 8, 48, 1.0, torch.bfloat16),          # rank 48 full tiles + ragged rows
     ([(300, 1096), (16, 1032)], 4, 40, 1.0, torch.bfloat16),           # rank 40: padded ranks, d_in % 64
     ([(40, 64)], 2, 128, 0.5, torch.bfloat16),                         # largest rank
+    ([(96, 200), (64, 128)], 4, 80, 1.0, torch.bfloat16),             # rank 80 (5 rank chunks)
+    ([(130, 136)], 4, 96, 2.0, torch.bfloat16),                        # rank 96 (6)
+    ([(70, 64), (256, 192)], 2, 100, 1.0, torch.bfloat16),            # rank 100 (7): r % 8 != 0
     ([(33, 64)], 32, 16, 1.0, torch.bfloat16),                         # most experts
     ([(40, 24), (8, 8)], 1, 1, 1.0, torch.bfloat16),                    # one expert of rank 1
     ([(5, 7)], 1, 1, 2.0, torch.float32),
