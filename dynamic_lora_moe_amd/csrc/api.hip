@@ -64,7 +64,7 @@ struct dlm_layers {
     void* d_zimg = nullptr;
     float* d_part = nullptr;      // partial products of the fused switch + product (bound vectors)
     bool bound = false;           // dlm_layers_bind_vectors has been called
-    int64_t n_blocks = 0, n_bands = 0;  // 16-row blocks and 256-row bands over all weights
+    int64_t n_blocks = 0, n_bands = 0;  // product blocks (kGemvRows rows) and 256-row bands over all weights
     std::vector<SwDesc> h_descs;
     int32_t n = 0;
     int32_t E = 0, r = 0;
@@ -173,7 +173,7 @@ int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, fl
         d.part = nullptr;
         d.rb0 = blocks;
         d.rt0 = bands;
-        blocks += (p.d_out + 15) / 16;
+        blocks += (p.d_out + kGemvRows - 1) / kGemvRows;
         bands += (p.d_out + 255) / 256;
         tiles += (int64_t)d.n_rt * d.n_ct;
         elems += p.d_out * p.d_in;

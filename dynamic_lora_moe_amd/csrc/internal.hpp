@@ -32,7 +32,7 @@ struct SwDesc {
     const void* xv;     // [d_in], the weight's input
     float* yv;          // [d_out] fp32, its output
     float* part;        // [n_ct][d_out] fp32 per-column-tile partial products (fused path)
-    int64_t rb0;        // index of its first 16-row block in a product launch
+    int64_t rb0;        // index of its first kGemvRows-row block in a product launch
     int64_t rt0;        // index of its first 256-row band in a partial-sum launch
 };
 
@@ -61,8 +61,11 @@ SwTile switch_tile_for_rank(int r);
 
 hipError_t launch_switch_bf16(const SwitchArgs& a, const SwTile& t, hipStream_t s);
 
+// Rows per block of the product kernel (one row per wave).
+constexpr int kGemvRows = 4;
+
 // y = W x for every weight of a.descs (bound vectors), one launch: n_blocks
-// 16-row blocks over all weights.  With sets in a (after a switch), sets the
+// kGemvRows-row blocks over all weights.  With sets in a (after a switch), sets the
 // switch rejects leave y alone.
 hipError_t launch_gemv(const SwitchArgs& a, int64_t n_blocks, int dtype, hipStream_t s);
 // Whether the fused switch + product kernel serves this configuration (bf16,

@@ -634,9 +634,10 @@ void switch_wide_kernel(SwitchArgs a) {
 //     gemv_reduce_kernel adds a row's n_ct partials in column-tile order (a
 //     kernel boundary in between, so no cross-workgroup synchronisation).
 //   * gemv_kernel: the product alone (the unfused baseline, or after a switch
-//     the fused kernel does not serve): 16-row blocks, each wave 4 rows, lanes
-//     striding over 16-byte chunks of a row with fp32 sums, then a fixed-order
-//     butterfly across the wave.  Every result is bitwise reproducible.
+//     the fused kernel does not serve): one row per wave, lanes striding over
+//     16-byte chunks of the row (four in flight) with fp32 sums, then a
+//     fixed-order butterfly across the wave.  Every result is bitwise
+//     reproducible.
 
 __global__ __launch_bounds__(kWaves* kWave) __attribute__((amdgpu_waves_per_eu(3)))
 void switch_gemv_kernel(SwitchArgs a) {
@@ -694,55 +695,67 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(SwitchArgs a, int64_t 
     gst(D.yv + row, sum);
 }
 
-constexpr int kGemvRowsPerWave = 4;
-constexpr int kGemvRows = kWaves * kGemvRowsPerWave;  // rows per block
+static_assert(kGemvRows == kWaves, "one row per wave");
+constexpr int kGemvUnroll = 4;  // 16-byte chunks of the row in flight per lane
 
-// After a switch in the same call, sets the switch rejects (same check) leave
-// y alone; without sets (plain product) the check always passes.
+// Blocks run last-first: in a layer the longest rows (the MLP's down
+// projection) come last, so they start early instead of forming the tail.
+
 template <typename T>
 __global__ __launch_bounds__(kWaves* kWave) void gemv_kernel(SwitchArgs a, int64_t n_blocks) {
-    const int64_t t = blockIdx.x;
-    if (t >= n_blocks || !read_sets(a).ok) return;
+    const int64_t t = n_blocks - 1 - (int64_t)blockIdx.x;
+    if (t < 0 || !read_sets(a).ok) return;
     const SwDesc D = a.descs[find_desc<kKeyRowBlock>(a.descs, a.n_desc, t)];
     const int d_in = D.d_in, d_out = D.d_out;
     const int lane = lane_id();
-    const int row0 = (int)(t - D.rb0) * kGemvRows + wave_id() * kGemvRowsPerWave;
-    const T* __restrict__ W = (const T*)D.W;
+    const int row = (int)(t - D.rb0) * kGemvRows + wave_id();
+    if (row >= d_out) return;
+    const T* __restrict__ Wr = (const T*)D.W + (int64_t)row * d_in;
     const T* __restrict__ x = (const T*)D.xv;
-    int rows[kGemvRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kGemvRowsPerWave; ++i) rows[i] = row0 + i < d_out ? row0 + i : d_out - 1;
-    float acc[kGemvRowsPerWave] = {};
+    float acc = 0.f;
     if constexpr (sizeof(T) == 2) {
-        // 8 bf16 per 16-byte chunk; d_in is a multiple of 8
         const int nch = d_in / 8;
-        for (int c = lane; c < nch; c += kWave) {
-            const u32x4 xv = ld128(x + 8 * c);
-            u32x4 wv[kGemvRowsPerWave];
+        int c = lane;
+        for (; c + (kGemvUnroll - 1) * kWave < nch; c += kGemvUnroll * kWave) {
+            u32x4 xv[kGemvUnroll], wv[kGemvUnroll];
 #pragma unroll
-            for (int i = 0; i < kGemvRowsPerWave; ++i) wv[i] = ld128(W + (int64_t)rows[i] * d_in + 8 * c);
+            for (int u = 0; u < kGemvUnroll; ++u) {
+                wv[u] = ld128(Wr + 8 * (c + u * kWave));
+                xv[u] = ld128(x + 8 * (c + u * kWave));
+            }
 #pragma unroll
-            for (int i = 0; i < kGemvRowsPerWave; ++i)
+            for (int u = 0; u < kGemvUnroll; ++u)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    acc[i] = fmaf(bf_lo(wv[i][q]), bf_lo(xv[q]), acc[i]);
-                    acc[i] = fmaf(bf_hi(wv[i][q]), bf_hi(xv[q]), acc[i]);
+                    acc = fmaf(bf_lo(wv[u][q]), bf_lo(xv[u][q]), acc);
+                    acc = fmaf(bf_hi(wv[u][q]), bf_hi(xv[u][q]), acc);
                 }
         }
-    } else {
-        for (int j = lane; j < d_in; j += kWave) {
-            const float xj = gld(x + j);
+        for (; c < nch; c += kWave) {
+            const u32x4 xv = ld128(x + 8 * c), wv = ld128(Wr + 8 * c);
 #pragma unroll
-            for (int i = 0; i < kGemvRowsPerWave; ++i) acc[i] = fmaf(gld(W + (int64_t)rows[i] * d_in + j), xj, acc[i]);
+            for (int q = 0; q < 4; ++q) {
+                acc = fmaf(bf_lo(wv[q]), bf_lo(xv[q]), acc);
+                acc = fmaf(bf_hi(wv[q]), bf_hi(xv[q]), acc);
+            }
         }
+    } else {
+        int j = lane;
+        for (; j + (kGemvUnroll - 1) * kWave < d_in; j += kGemvUnroll * kWave) {
+            float w[kGemvUnroll], xv[kGemvUnroll];
+#pragma unroll
+            for (int u = 0; u < kGemvUnroll; ++u) {
+                w[u] = gld(Wr + j + u * kWave);
+                xv[u] = gld(x + j + u * kWave);
+            }
+#pragma unroll
+            for (int u = 0; u < kGemvUnroll; ++u) acc = fmaf(w[u], xv[u], acc);
+        }
+        for (; j < d_in; j += kWave) acc = fmaf(gld(Wr + j), gld(x + j), acc);
     }
 #pragma unroll
-    for (int i = 0; i < kGemvRowsPerWave; ++i) {
-        float v = acc[i];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-        if (lane == 0 && row0 + i < d_out) gst(D.yv + row0 + i, v);
-    }
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    if (lane == 0) gst(D.yv + row, acc);
 }
 
 // ---- element-wise path: fp32 weights (and any shape) ----------------------
