@@ -41,6 +41,20 @@ def _src_hash(paths):
 
 SWITCH_SOURCES = ["dynamic_lora_moe_amd/csrc/switch.hip", "dynamic_lora_moe_amd/csrc/gfx950.hpp",
                   "dynamic_lora_moe_amd/csrc/internal.hpp"]
+SGMM_SOURCES = ["dynamic_lora_moe_amd/csrc/sgmm.hip", "dynamic_lora_moe_amd/csrc/sgmm.hpp",
+                "dynamic_lora_moe_amd/csrc/gfx950.hpp", "dynamic_lora_moe_amd/csrc/internal.hpp"]
+SGMM_PROFILE_PASSES = 3  # grouped passes per SGMM workload in --profile-kernels
+
+
+def sgmm_algo_bytes(wl, idx):
+    """Algorithmic bytes of one grouped SGMM pass over wl's problems for the rows'
+    sets idx [T][2] (CPU): x once, y read + written, the A/B slices of the experts
+    the rows use, and idx/g."""
+    import numpy as np
+    u = np.unique(idx.numpy())
+    n_used = int((u >= 0).sum())
+    per_layer = sum(wl.T * i * 2 + 2 * wl.T * o * 2 + n_used * wl.r * (i + o) * 2 for _, o, i in wl.projs)
+    return per_layer * wl.layers + wl.T * 16
 
 
 def _traffic(kernel_key, algo_bytes_per_launch):
@@ -55,6 +69,23 @@ def _traffic(kernel_key, algo_bytes_per_launch):
     if not ent or ent.get("source_hash") != _src_hash(SWITCH_SOURCES):
         return None
     return ent.get("bytes_per_launch")
+
+
+def _sgmm_traffic(name):
+    """HBM bytes per step of an SGMM workload (read, written, and the algorithmic
+    bytes of the same profiled steps) from the committed counter summary, if it
+    was taken on the current SGMM source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        ent = json.load(f).get("sgmm_" + name)
+    if not ent or ent.get("source_hash") != _src_hash(SGMM_SOURCES):
+        return None
+    tot = ent["read_per_step"] + ent["write_per_step"]
+    return {"read_per_step": ent["read_per_step"], "write_per_step": ent["write_per_step"],
+            "algo_bytes_per_step": ent["algo_bytes_per_step"], "ratio": tot / ent["algo_bytes_per_step"],
+            "steps_profiled": ent["passes"]}
 
 
 def bench_switch(torch, dlm, synth, steps, warmup, log):
@@ -327,18 +358,10 @@ def bench_sgmm(torch, dlm, synth, name, reps, log):
     assert dlm.sgmm_status(ws) == dlm.DLM_OK
     sec = e0.elapsed_time(e1) / 1e3 / reps
     tokens = wl.T * len(sets)
-    # algorithmic bytes: x once, y read + write, A/B of the experts used, idx/g
-    nbytes = 0
-    for i, _ in sets:
-        u = torch.unique(i.cpu())
-        u = u[u >= 0]
-        per_step = 0
-        for _, _, x, A, B, y in probs:
-            d_in, d_out = x.shape[1], y.shape[1]
-            per_step += wl.T * d_in * 2 + 2 * wl.T * d_out * 2 + len(u) * wl.r * (d_in + d_out) * 2
-        nbytes += per_step + wl.T * 16
+    nbytes = sum(sgmm_algo_bytes(wl, i.cpu()) for i, _ in sets)
     res = {"tokens_per_s": tokens / sec, "ms_per_pass": sec * 1e3, "GBps": nbytes / sec / 1e9,
-           "frac_of_hbm_peak": nbytes / sec / HBM_PEAK, "algo_bytes_per_pass": nbytes}
+           "frac_of_hbm_peak": nbytes / sec / HBM_PEAK, "algo_bytes_per_pass": nbytes,
+           "traffic": _sgmm_traffic(name)}
     if name == "mixed-decode":
         res.update(_per_layer_variant(torch, dlm, wl, probs, sets, reps, sec, log))
         # rows that release their adapters (both slots empty) are left out by the
@@ -481,16 +504,33 @@ def profile_kernels(torch, dlm, synth, n_switch, log):
         L.close()
         del model
         torch.cuda.empty_cache()
+    # grouped SGMM: the prefill pass, then the first mixed-decode steps, each
+    # SGMM_PROFILE_PASSES times (every pass starts with one segment launch)
+    for name in ("sgmm-prefill", "mixed-decode"):
+        wl = synth.WORKLOADS[name]
+        probs = synth.sgmm_problems(wl)
+        idx, g = synth.batched_sets(wl)
+        grp = dlm.SgmmGroup([(x, A, B, y) for _, _, x, A, B, y in probs], wl.E, wl.r, wl.scale)
+        ws = grp.workspace(wl.T)
+        for p in range(SGMM_PROFILE_PASSES):
+            i, gg = (idx, g) if name == "sgmm-prefill" else (idx[p], g[p])
+            grp.run(i.cuda(), gg.cuda(), workspace=ws)
+        torch.cuda.synchronize()
+        assert dlm.sgmm_status(ws) == dlm.DLM_OK
+        grp.close()
+        del probs, ws
+        torch.cuda.empty_cache()
     src = torch.empty(2 ** 29, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1.0)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"profiled {n_switch} switches per workload and one copy of {src.numel() * 2} bytes")
+    log(f"profiled {n_switch} switches per workload, {SGMM_PROFILE_PASSES} passes per SGMM workload "
+        f"and one copy of {src.numel() * 2} bytes")
 
 
-def traffic_from(fetch_csv, write_csv, log):
+def traffic_from(fetch_csv, write_csv, log, out_path=None):
     """Per-launch HBM bytes of the switch kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE in KiB per dispatch) of `--profile-kernels`, each
     scaled by the same counter's reading for the 1 GiB copy (known bytes);
@@ -533,10 +573,58 @@ def traffic_from(fetch_csv, write_csv, log):
             "fetch": out["fetch"], "write": out["write"],
             "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
                        "python3 bench.py --profile-kernels"}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    res.update(_sgmm_traffic_from(fetch_csv, write_csv, read))
+    path = out_path or os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
     log(f"wrote {path}: {res}")
+
+
+def _sgmm_traffic_from(fetch_csv, write_csv, read):
+    """Per-kernel HBM bytes of the grouped SGMM passes of --profile-kernels: the
+    dispatches of the four SGMM kernels, in dispatch order, split into passes at
+    each segment launch; the first SGMM_PROFILE_PASSES passes are the prefill,
+    the next the mixed-decode steps 0, 1, ...  Each counter is scaled by its own
+    reading for the 1 GiB copy."""
+    import csv
+    import synth
+    kinds = ("segment", "shrink", "vsum", "expand")
+    per = {}
+    for part, path, counter in (("read", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        _, cp = read(path, counter, "\0")
+        scale = (2 ** 30 / 1024) / max(cp) * 1024  # bytes per counted KiB
+        with open(path) as f:
+            rows = [r for r in csv.DictReader(f) if r.get("Counter_Name") == counter
+                    and any(f"sgmm_{k}" in r.get("Kernel_Name", "") for k in kinds)]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        passes = []
+        for r in rows:
+            kind = next(k for k in kinds if f"sgmm_{k}" in r["Kernel_Name"])
+            if kind == "segment":
+                passes.append({})
+            if passes:
+                passes[-1][kind] = passes[-1].get(kind, 0.0) + float(r["Counter_Value"]) * scale
+        per[part] = passes
+    n = SGMM_PROFILE_PASSES
+    out = {}
+    if len(per["read"]) < 2 * n or len(per["write"]) < 2 * n:
+        return out
+    for w, name in enumerate(("sgmm-prefill", "mixed-decode")):
+        wl = synth.WORKLOADS[name]
+        idx, _ = synth.batched_sets(wl)
+        algo = [sgmm_algo_bytes(wl, idx if name == "sgmm-prefill" else idx[p]) for p in range(n)]
+        ent = {"source_hash": _src_hash(SGMM_SOURCES), "workload": name, "passes": n,
+               "algo_bytes_per_step": sum(algo) / n, "kernels": {}}
+        for part in ("read", "write"):
+            ps = per[part][w * n:(w + 1) * n]
+            for k in kinds:
+                v = sum(p.get(k, 0.0) for p in ps) / n
+                ent["kernels"].setdefault(k, {})[part] = v
+            ent[f"{part}_per_step"] = sum(sum(p.values()) for p in ps) / n
+        ent["command"] = ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                          "python3 bench.py --profile-kernels")
+        out["sgmm_" + name] = ent
+    return out
 
 
 def main():

@@ -1,0 +1,49 @@
+"""The counter summary bench.py builds from two rocprofv3 --pmc CSVs: each
+counter is scaled by its own reading for the 1 GiB copy, the switch dispatches
+are averaged, and the SGMM dispatches are split into passes at each segment
+launch (prefill passes first, then the mixed-decode steps). Synthetic CSVs in
+the profile run's dispatch order; no GPU."""
+import csv
+import json
+
+import bench
+
+SWITCH = "void dlm::switch_bf16_kernel<1, 256>(dlm::SwitchArgs)"
+SG = ("segment", "shrink", "vsum", "expand")
+
+
+def _csv(path, counter, per_kernel, copy_kib):
+    d = 0
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for v in (100.0, 300.0):
+            d += 1
+            w.writerow([d, SWITCH, counter, v])
+        for wl in range(2):
+            for _ in range(bench.SGMM_PROFILE_PASSES):
+                for k in SG:
+                    d += 1
+                    w.writerow([d, f"void dlm::sgmm_{k}_kernel(dlm::SgmmArgs)", counter, per_kernel[wl][k]])
+        d += 1
+        w.writerow([d, "__amd_rocclr_copyBuffer", counter, copy_kib])
+
+
+def test_traffic_summary_from_counter_csvs(tmp_path):
+    pk = [dict(segment=1.0, shrink=1000.0, vsum=10.0, expand=2000.0),
+          dict(segment=2.0, shrink=3000.0, vsum=20.0, expand=4000.0)]
+    F, W, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
+    _csv(F, "FETCH_SIZE", pk, 2 ** 19)    # the copy's reads counted at half
+    _csv(W, "WRITE_SIZE", pk, 2 ** 20)
+    bench.traffic_from(str(F), str(W), lambda m: None, out_path=str(out))
+    t = json.loads(out.read_text())
+    sw = t["switch_bf16_7b"]
+    assert sw["fetch"]["launches"] == 2 and sw["fetch"]["scale"] == 2.0 and sw["write"]["scale"] == 1.0
+    assert sw["bytes_per_launch"] == 200.0 * 1024 * 2 + 200.0 * 1024
+    pre, mix = t["sgmm_sgmm-prefill"], t["sgmm_mixed-decode"]
+    assert pre["kernels"]["shrink"] == {"read": 1000.0 * 1024 * 2, "write": 1000.0 * 1024}
+    assert mix["kernels"]["expand"] == {"read": 4000.0 * 1024 * 2, "write": 4000.0 * 1024}
+    assert pre["read_per_step"] == sum(pk[0].values()) * 1024 * 2
+    assert mix["write_per_step"] == sum(pk[1].values()) * 1024
+    assert pre["algo_bytes_per_step"] == 1007812608   # 4096 tokens x 7 projections, Zipf pairs
+    assert pre["source_hash"] == bench._src_hash(bench.SGMM_SOURCES)
