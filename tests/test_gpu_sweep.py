@@ -88,3 +88,71 @@ def test_sgmm_sweep(i):
     _check(x, idx, g, A, B, y0, y, scale, f"sgmm sweep {i}")
     none = (idx == -1).all(1)
     assert torch.equal(y.cpu()[none], y0[none])
+
+
+N_ROUTER = 16
+N_PRODUCT = 12
+
+
+def _router_config(i):
+    rng = np.random.default_rng(90000 + i)
+    dt = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+    d = int(rng.choice([1, 7, 64, 100, 520, 1000, 4096, 8192])) if rng.random() < 0.5 else 8 * int(rng.integers(1, 700))
+    return int(rng.integers(1, 300)), d, dt, rng
+
+
+@pytest.mark.parametrize("i", range(N_ROUTER))
+def test_router_sweep(i):
+    from test_gpu_pregate import _check, _xw
+    T, d, dt, rng = _router_config(i)
+    E = int(rng.integers(2, 33))
+    x, Wr = _xw(T, d, E, dt, 91000 + i)
+    _check(x, Wr, f"sweep {i}")
+
+
+@pytest.mark.parametrize("i", range(N_ROUTER))
+def test_centroid_router_sweep(i):
+    from test_gpu_pregate import _check_centroid, _xc
+    T, d, dt, rng = _router_config(100 + i)
+    E, J = int(rng.integers(1, 33)), int(rng.choice([1, 2, 3, 4, 9, 16]))
+    x, C = _xc(T, d, E, J, dt, 92000 + i)
+    _check_centroid(x, C, f"sweep {i} E={E} J={J}")
+
+
+@pytest.mark.parametrize("i", range(N_PRODUCT))
+def test_switch_gemv_sweep(i):
+    """dlm_switch_gemv on random shapes: W' bitwise equal to a plain dlm_switch of
+    a twin, y against the oracle's product with the oracle's switched weights."""
+    from test_gpu_gemv import _bf16_ulp, _check_y, _vectors
+    import oracle
+    from gpu_util import check_bf16, check_f32, gamma
+    shapes, E, r, scale, dt = _switch_config(200 + i)
+    if i % 2 == 0:
+        r = int(np.random.default_rng(93000 + i).choice([1, 4, 8, 16]))  # the fused kernel's ranks
+    print(f"[sweep switch_gemv {i}] shapes={shapes} E={E} r={r} scale={scale} {dt}", flush=True)
+    model = _model(shapes, E, r, dt, 94000 + i)
+    twin = [(W.clone(), A, B) for W, A, B in model]
+    W0s = [W.cpu().clone() for W, _, _ in model]
+    xs, ys = _vectors(shapes, dt, 94000 + i)
+    L = dlm.Layers(model, E, r, scale)
+    L.bind_vectors(xs, ys)
+    Tw = dlm.Layers(twin, E, r, scale)
+    rng = np.random.default_rng(95000 + i)
+    old = (rng.choice(E, size=2, replace=E < 2).tolist(), rng.random(2).astype(np.float32).tolist())
+    new = (rng.choice(E, size=2, replace=E < 2).tolist(), rng.random(2).astype(np.float32).tolist())
+    L.switch_gemv(dev_set(old), dev_set(new))
+    Tw.switch(dev_set(old), dev_set(new))
+    torch.cuda.synchronize()
+    for k, ((W, A, B), (Wt, _, _), w0, x, y) in enumerate(zip(model, twin, W0s, xs, ys)):
+        assert torch.equal(W, Wt), f"sweep {i} w{k}: fused switch differs from dlm_switch"
+        ref, ex, ab = oracle.switch(w0, A.cpu(), B.cpu(), scale, old, new, with_stats=True)
+        if dt == torch.bfloat16:
+            check_bf16(W.cpu(), ref, ex, ab, 4 * r + 2, what=f"sweep {i} w{k}")
+            wtol = np.maximum(2 * _bf16_ulp(ref.double().numpy()), gamma(4 * r + 2) * ab.numpy())
+        else:
+            check_f32(W.cpu(), ex, ab, 4 * r + 2, f"sweep {i} w{k}")
+            wtol = np.maximum(1e-5 * np.abs(ex.numpy()), gamma(4 * r + 2) * ab.numpy())
+        _check_y(y, ref, wtol, x, f"sweep {i} w{k}")
+    assert L.status() == dlm.DLM_OK
+    L.close()
+    Tw.close()
