@@ -156,3 +156,39 @@ def test_switch_gemv_sweep(i):
     assert L.status() == dlm.DLM_OK
     L.close()
     Tw.close()
+
+
+N_GROUP = 10
+
+
+@pytest.mark.parametrize("i", range(N_GROUP))
+def test_sgmm_group_sweep(i):
+    """Random groups of 2-7 problems with their own d_in / d_out (some sharing an
+    A/B bank) run on one segmentation; every problem's y against the oracle."""
+    rng = np.random.default_rng(96000 + i)
+    dt = torch.float32 if i % 5 == 4 else torch.bfloat16
+    T = int(rng.integers(1, 500))
+    E = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    r = _rank(rng)
+    scale = float(rng.choice([0.5, 1.0, 2.0]))
+    n = int(rng.integers(2, 8))
+    probs, banks = [], []
+    for k in range(n):
+        if banks and rng.random() < 0.3:
+            d_in, d_out, A, B = banks[int(rng.integers(len(banks)))]   # a shared bank
+        else:
+            d_in, d_out = 8 * int(rng.integers(1, 200)), 8 * int(rng.integers(1, 80))
+            _, A, B, _ = _problem(1, d_in, d_out, E, r, dt, (97000 + i, k))
+            banks.append((d_in, d_out, A, B))
+        x, _, _, y = _problem(T, d_in, d_out, 1, 1, dt, (98000 + i, k))
+        probs.append((x, A, B, y))
+    print(f"[sweep group {i}] T={T} E={E} r={r} {dt} problems={[(p[0].shape[1], p[3].shape[1]) for p in probs]}",
+          flush=True)
+    idx, g = _sets(T, E, np.random.default_rng(99000 + i))
+    y0s = [y.cpu().clone() for *_, y in probs]
+    grp = dlm.SgmmGroup(probs, E, r, scale)
+    ws = grp.run(idx.cuda(), g.cuda())
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    for k, ((x, A, B, y), y0) in enumerate(zip(probs, y0s)):
+        _check(x, idx, g, A, B, y0, y, scale, f"group sweep {i} problem {k}")
+    grp.close()
