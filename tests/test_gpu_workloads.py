@@ -195,3 +195,39 @@ def test_7b_decode_fused_switch_and_product_per_layer_sampled():
     del model, W0
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_70b_decode_switch_and_product_per_layer_sampled():
+    """dlm_switch_gemv on one layer of the 70B-shaped workload (rank 64: the wide
+    switch, then the product kernel; d_in up to 28672). Sampled rows of W' and y
+    against the oracle, as in the 7B-shaped fused test."""
+    from test_gpu_gemv import _bf16_ulp, _check_y
+    from gpu_util import gamma
+    wl = synth.WORKLOADS["70b-decode"]
+    print("[workload] 70b-decode switch + product: building one layer", flush=True)
+    model = synth.switch_model(wl, layers=[11])
+    x, Wr = synth.router_inputs(wl)
+    ri, rg = oracle.pregate(x.cpu(), Wr.cpu())
+    idx, g = dlm.pregate(x, Wr)
+    xs = [synth.normal_device((W.shape[1],), 1.0, wl.dtype, "cuda", wl.cfg_id, "xin", 11, k)
+          for k, (_, _, W, _, _) in enumerate(model)]
+    ys = [torch.full((W.shape[0],), float("nan"), dtype=torch.float32, device="cuda") for _, _, W, _, _ in model]
+    L = dlm.Layers([(W, A, B) for _, _, W, A, B in model], wl.E, wl.r, wl.scale)
+    L.bind_vectors(xs, ys)
+    t = 9
+    old, new = host_set(ri[t - 1], rg[t - 1]), host_set(ri[t], rg[t])
+    pre = _switch_sampled(wl, model, 4, old, new, "70b product")
+    L.switch_gemv((idx[t - 1], g[t - 1]), (idx[t], g[t]))
+    torch.cuda.synchronize()
+    print("[workload] 70b-decode switch + product: checking", flush=True)
+    _check_sampled(wl, model, pre, old, new, "70b product")
+    for (l, name, W, A, B), (rows, W0r), xv, y in zip(model, pre, xs, ys):
+        ref, ex, ab = oracle.switch_rows(W0r, rows, A.cpu(), B.cpu(), W.shape[0], wl.scale, old, new,
+                                         with_stats=True)
+        wtol = np.maximum(2 * _bf16_ulp(ref.double().numpy()), gamma(4 * wl.r + 2) * ab.numpy())
+        _check_y(y[torch.from_numpy(rows).cuda()], ref, wtol, xv, f"70b product {name}")
+    assert L.status() == dlm.DLM_OK
+    L.close()
+    del model
+    gc.collect()
+    torch.cuda.empty_cache()
