@@ -66,7 +66,7 @@ typedef enum {
 
 typedef enum { DLM_F32 = 0, DLM_BF16 = 1 } dlm_dtype;
 
-/* Limits of this build. */
+/* Compile-time limits of the library. */
 #define DLM_MAX_EXPERTS 32
 #define DLM_MAX_RANK 128
 #define DLM_MAX_CENTROIDS 1024   /* per adapter, dlm_pregate_centroid */
