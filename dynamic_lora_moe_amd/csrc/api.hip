@@ -191,8 +191,8 @@ int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, fl
     hd->per_xcd = (tiles + 7) / 8;
     hd->n_blocks = blocks;
     hd->n_bands = bands;
-    hipError_t e = hipSuccess;
-    if (dtype == DLM_BF16 && switch_packs_a(tile)) {
+    hipError_t e = dtype == DLM_BF16 ? prepare_switch_bf16(tile) : hipSuccess;
+    if (e == hipSuccess && dtype == DLM_BF16 && switch_packs_a(tile)) {
         // ranks 17..64: packed A images for the copy-staged tiles, one block
         size_t elems_total = 0;
         std::vector<size_t> off(n);

@@ -59,6 +59,10 @@ struct SwTile {
 };
 SwTile switch_tile_for_rank(int r);
 
+// Once per handle, on the handle's device, before its first launch: raises the
+// dynamic-LDS limit of the kernel instance the tile uses where it needs more
+// than 64 KB (no stream work; launches then only launch).
+hipError_t prepare_switch_bf16(const SwTile& t);
 hipError_t launch_switch_bf16(const SwitchArgs& a, const SwTile& t, hipStream_t s);
 
 // Rows per block of the product kernel (one row per wave).

@@ -831,35 +831,63 @@ __global__ __launch_bounds__(256) void switch_pack_a_kernel(const uint16_t* __re
 }
 
 template <int R16, int CT>
+constexpr size_t lds_r() {
+    return ((size_t)4 * (CT / 32) * 32 * (R16 * 16) + (size_t)kWaves * 32 * 64) * sizeof(uint16_t);
+}
+
+// Dynamic LDS past 64 KB needs the kernel's attribute raised once, at set-up,
+// so that launches (which a caller may capture into a graph) only launch.
+template <int R16, int CT>
+hipError_t prepare_r() {
+    if (lds_r<R16, CT>() <= 65536) return hipSuccess;
+    return hipFuncSetAttribute((const void*)switch_bf16_kernel<R16, CT>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r<R16, CT>());
+}
+
+template <int R16, int CT>
 hipError_t launch_r(const SwitchArgs& a, hipStream_t s) {
-    const size_t lds = ((size_t)4 * (CT / 32) * 32 * (R16 * 16) + (size_t)kWaves * 32 * 64) * sizeof(uint16_t);
-    if (!grid_fits(8 * a.per_xcd, kWaves * kWave)) return hipErrorInvalidConfiguration;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)switch_bf16_kernel<R16, CT>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     const int64_t grid = 8 * a.per_xcd;
     if (!grid_fits(grid, kWaves * kWave)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((switch_bf16_kernel<R16, CT>), dim3((unsigned)grid), dim3(kWaves * kWave),
-                       lds, s, a);
+                       (lds_r<R16, CT>()), s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 template <int R16>
+constexpr size_t lds_wide() {
+    return ((size_t)2 * 4 * 2 * 32 * (R16 * 16) + (size_t)kWideWBufs * kWW * 32 * 64) * sizeof(uint16_t);
+}
+
+template <int R16>
+hipError_t prepare_wide() {
+    if (lds_wide<R16>() <= 65536) return hipSuccess;
+    return hipFuncSetAttribute((const void*)switch_wide_kernel<R16, kWideSB>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_wide<R16>());
+}
+
+template <int R16>
 hipError_t launch_wide(const SwitchArgs& a, hipStream_t s) {
-    const size_t lds = ((size_t)2 * 4 * 2 * 32 * (R16 * 16) + (size_t)kWideWBufs * kWW * 32 * 64) * sizeof(uint16_t);
-    if (!grid_fits(8 * a.per_xcd, kWW * kWave)) return hipErrorInvalidConfiguration;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)switch_wide_kernel<R16, kWideSB>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     const int64_t grid = 8 * a.per_xcd;
-    hipLaunchKernelGGL((switch_wide_kernel<R16, kWideSB>), dim3((unsigned)grid), dim3(kWW * kWave), lds, s, a);
+    if (!grid_fits(grid, kWW * kWave)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((switch_wide_kernel<R16, kWideSB>), dim3((unsigned)grid), dim3(kWW * kWave),
+                       lds_wide<R16>(), s, a);
     return hipGetLastError();
+}
+
+hipError_t prepare_switch_bf16(const SwTile& t) {
+    switch (t.r16) {
+        case 1: return prepare_r<1, 256>();
+        case 2: return prepare_wide<2>();
+        case 3: return prepare_wide<3>();
+        case 4: return prepare_wide<4>();
+        case 5: return prepare_r<5, 64>();
+        case 6: return prepare_r<6, 64>();
+        case 7: return prepare_r<7, 64>();
+        case 8: return prepare_r<8, 64>();
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_switch_bf16(const SwitchArgs& a, const SwTile& t, hipStream_t s) {
