@@ -15,8 +15,8 @@ from test_gpu_switch import _compare, _model
 
 pytestmark = pytest.mark.gpu
 
-N_SWITCH = 24
-N_SGMM = 24
+N_SWITCH = 48
+N_SGMM = 48
 
 
 def _rank(rng):
@@ -90,8 +90,8 @@ def test_sgmm_sweep(i):
     assert torch.equal(y.cpu()[none], y0[none])
 
 
-N_ROUTER = 16
-N_PRODUCT = 12
+N_ROUTER = 24
+N_PRODUCT = 20
 
 
 def _router_config(i):
@@ -158,7 +158,7 @@ def test_switch_gemv_sweep(i):
     Tw.close()
 
 
-N_GROUP = 10
+N_GROUP = 16
 
 
 @pytest.mark.parametrize("i", range(N_GROUP))
