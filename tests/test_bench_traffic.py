@@ -47,3 +47,17 @@ def test_traffic_summary_from_counter_csvs(tmp_path):
     assert mix["write_per_step"] == sum(pk[1].values()) * 1024
     assert pre["algo_bytes_per_step"] == 1007812608   # 4096 tokens x 7 projections, Zipf pairs
     assert pre["source_hash"] == bench._src_hash(bench.SGMM_SOURCES)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 (or a multi-rank launch) exits
+    with a message before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True,
+                           text=True, timeout=120, env={**os.environ, **env})
+        assert r.returncode == 2, (args, env, r.returncode)
+        assert "one GPU" in r.stderr and not r.stdout.strip()
