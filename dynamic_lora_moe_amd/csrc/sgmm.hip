@@ -250,6 +250,9 @@ __global__ __launch_bounds__(kSegThreads) void sgmm_segment_kernel(
                 atomicOr(&s_tm[p >> 5], m);
             }
         }
+        // every wave has read s_base / s_wc for this batch before the next
+        // batch clears the per-wave counts
+        __syncthreads();
     }
     for (int64_t p = n_pos + tid; p < L.T_pad; p += kSegThreads) {
         perm[p] = -1;
