@@ -16,6 +16,10 @@ must fail).  What each pin holds the oracle to:
             permutation / translation / duplicate invariants
   gemv      merged-weight product against NumPy's binary64 matmul; merged
             product = base product + unmerged adapters + the rounding of W
+  absum     the tolerance scale S each output carries (the sum of the
+            magnitudes of every term of its expression), recomputed from both
+            sides with NumPy whole-matrix products of absolute values; the
+            router's bound gamma_d * max_e sum_j |x_j Wr_je| the same way
   rounding  one nearest-even rounding to bf16 / fp32
 """
 from __future__ import annotations
@@ -334,6 +338,45 @@ def pin_merged_equals_unmerged(lib):
     assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
 
 
+def pin_switch_absum(lib):
+    """S of a switched element = |W| + sum over both sets' used slots of
+    |s g_k| * (|B_e| @ |A_e|): equal both ways (not only a lower bound), so a
+    wrong S cannot widen or narrow the parity floor unnoticed."""
+    rng = _rng(26)
+    for trial in range(10):
+        E, r = int(rng.integers(1, 5)), int(rng.integers(1, 6))
+        d_out, d_in = int(rng.integers(1, 10)), int(rng.integers(1, 10))
+        s = float(rng.choice([1.0, 2.0, 0.5, -1.5]))
+        for dt in (torch.float32, torch.bfloat16):
+            A, B = _rand_bank(rng, E, r, d_in, d_out, dt)
+            W0 = torch.from_numpy(rng.standard_normal((d_out, d_in))).to(dt)
+            old = None if trial % 4 == 0 else _rand_set(rng, E)
+            new = None if trial % 4 == 1 else _rand_set(rng, E)
+            _, _, ab = oracle.switch(W0, A, B, s, old, new, with_stats=True, lib=lib)
+            Ad, Bd = np.abs(A.double().numpy()), np.abs(B.double().numpy())
+            ref = np.abs(W0.double().numpy()).copy()
+            for st in (old, new):
+                if st is None:
+                    continue
+                for e, gk in zip(st[0], st[1]):
+                    if e >= 0:
+                        ref += abs(s * float(np.float32(gk))) * (Bd[e] @ Ad[e])
+            assert np.allclose(ab.numpy(), ref, rtol=1e-12, atol=0), (trial, ab, ref)
+
+
+def pin_router_bound(lib):
+    """The router's decision bound = gamma_d(2^-53) * max_e sum_j |x_j Wr_je|."""
+    rng = _rng(14)
+    for T, d, E in ((5, 1, 2), (17, 33, 8), (9, 300, 5)):
+        x = torch.from_numpy(rng.standard_normal((T, d))).float()
+        Wr = torch.from_numpy(rng.standard_normal((d, E)) * 0.3).float()
+        _, _, _, _, bd = oracle.pregate(x, Wr, with_stats=True, lib=lib)
+        u = 2.0 ** -53
+        gam = d * u / (1.0 - d * u)
+        ref = gam * (np.abs(x.double().numpy()) @ np.abs(Wr.double().numpy())).max(1)
+        assert np.allclose(bd.numpy(), ref, rtol=1e-12, atol=0), (bd, ref)
+
+
 # ------------------------------------------------------------------ gemv ----
 
 def pin_gemv_golden(lib):
@@ -419,6 +462,31 @@ def pin_sgmm_brute(lib):
         assert (ab.numpy() + 1e-12 >= np.abs(ref)).all()
 
 
+def pin_sgmm_absum(lib):
+    """S of an SGMM output = |y| + sum_k |s g_k| * ((|x| @ |A_e|^T) @ |B_e|^T),
+    equal both ways, for used, empty and duplicated slots."""
+    rng = _rng(34)
+    for trial in range(10):
+        E, r = int(rng.integers(1, 5)), int(rng.integers(1, 6))
+        d_in, d_out, T = int(rng.integers(1, 12)), int(rng.integers(1, 9)), int(rng.integers(1, 8))
+        s = float(rng.choice([1.0, 2.0, -0.5]))
+        for dt in (torch.float32, torch.bfloat16):
+            A, B = _rand_bank(rng, E, r, d_in, d_out, dt)
+            x = torch.from_numpy(rng.standard_normal((T, d_in))).to(dt)
+            y0 = torch.from_numpy(rng.standard_normal((T, d_out))).to(dt)
+            idx = rng.integers(-1, E, size=(T, 2)).astype(np.int32)
+            g = (rng.random((T, 2)) - 0.25).astype(np.float32)
+            _, _, ab = oracle.sgmm(x, idx, g, A, B, y0, s, with_stats=True, lib=lib)
+            X, Ad, Bd = np.abs(x.double().numpy()), np.abs(A.double().numpy()), np.abs(B.double().numpy())
+            ref = np.abs(y0.double().numpy()).copy()
+            for t in range(T):
+                for k in range(2):
+                    e = idx[t, k]
+                    if e >= 0:
+                        ref[t] += abs(s * float(g[t, k])) * ((X[t] @ Ad[e].T) @ Bd[e].T)
+            assert np.allclose(ab.numpy(), ref, rtol=1e-12, atol=0), (trial, ab, ref)
+
+
 def pin_sgmm_properties(lib):
     rng = _rng(33)
     E, r, d_in, d_out, T = 4, 4, 16, 8, 12
@@ -466,11 +534,12 @@ def pin_rounding(lib):
 
 ALL_PINS = [
     pin_router_golden, pin_router_brute, pin_router_closed_form, pin_router_permutation,
-    pin_switch_golden, pin_switch_premerge, pin_switch_general, pin_switch_noop,
+    pin_router_bound,
+    pin_switch_golden, pin_switch_premerge, pin_switch_general, pin_switch_absum, pin_switch_noop,
     pin_switch_roundtrip, pin_merged_equals_unmerged,
     pin_gemv_golden, pin_gemv_numpy, pin_gemv_merged,
     pin_centroid_golden, pin_centroid_brute, pin_centroid_invariants,
-    pin_sgmm_golden, pin_sgmm_gemm, pin_sgmm_brute, pin_sgmm_properties,
+    pin_sgmm_golden, pin_sgmm_gemm, pin_sgmm_brute, pin_sgmm_absum, pin_sgmm_properties,
     pin_rounding,
 ]
 

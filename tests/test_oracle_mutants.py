@@ -47,6 +47,20 @@ MUTANTS = [
     ("centroid_abs_not_square", "s += diff * diff;", "s += fabs(diff);"),
     ("centroid_drop_last_dim", "for (int64_t k = 0; k < d; ++k) {\n                    double diff",
      "for (int64_t k = 0; k + 1 < d; ++k) {\n                    double diff"),
+    # the tolerance scale S (absum) and the router's decision bound: every parity
+    # floor is (gamma_n + extra) * S, so an inflated or deflated S must be caught
+    ("switch_absum_x16", "if (absum) absum[q * d_in + j] = S;", "if (absum) absum[q * d_in + j] = 16.0 * S;"),
+    ("switch_absum_no_W", "double S = fabs(w);", "double S = 0.0;"),
+    ("switch_absum_signed", "acc_abs += fabs(b * a);", "acc_abs += b * a;"),
+    ("switch_absum_no_gate", "*S += fabs(s * (double)g[k]) * acc_abs;", "*S += fabs(s) * acc_abs;"),
+    ("sgmm_absum_x16", "if (absum) absum[t * d_out + o] = S;", "if (absum) absum[t * d_out + o] = 16.0 * S;"),
+    ("sgmm_absum_no_y", "double S = fabs(yo);", "double S = 0.0;"),
+    ("sgmm_absum_signed_x", "acc += p;\n                    acc_abs += fabs(p);",
+     "acc += p;\n                    acc_abs += p;"),
+    ("sgmm_absum_signed_B", "acc_abs += va[k * r + rho] * fabs(b);", "acc_abs += va[k * r + rho] * b;"),
+    ("sgmm_absum_one_slot", "S += fabs(c) * acc_abs;", "S += (k == 0) * fabs(c) * acc_abs;"),
+    ("router_bound_half", "bound[t] = gam * mx;", "bound[t] = 0.5 * gam * mx;"),
+    ("router_bound_x1000", "bound[t] = gam * mx;", "bound[t] = 1000.0 * gam * mx;"),
     # an empty slot (-1) read as expert 0 everywhere it is tested
     ("empty_slot_as_expert0", "if (e < 0) continue;", "if (e < 0) e = 0;", 3),
 ]
