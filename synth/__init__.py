@@ -243,11 +243,13 @@ def router_inputs(wl: Workload, device="cuda"):
     return x, Wr
 
 
-def sgmm_problems(wl: Workload, device="cuda"):
+def sgmm_problems(wl: Workload, device="cuda", layers=None):
     """[(layer, proj_name, x, A, B, y0)] of the batched workloads: x [T][d_in] ~ N(0, 1),
-    y0 [T][d_out] ~ N(0, .02^2 d_in) standing in for the base output, A/B ~ N(0, .02)."""
+    y0 [T][d_out] ~ N(0, .02^2 d_in) standing in for the base output, A/B ~ N(0, .02).
+    For the decode workloads (one router set per token) the same recipe gives the
+    unmerged form of their layers, T = the workload's token count."""
     out = []
-    for l in range(wl.layers):
+    for l in (range(wl.layers) if layers is None else layers):
         for pi, (name, o, i) in enumerate(wl.projs):
             x = normal_device((wl.T, i), 1.0, wl.dtype, device, wl.cfg_id, "x", l, pi)
             A = normal_device((wl.E, wl.r, i), 0.02, wl.dtype, device, wl.cfg_id, "A", l, pi)

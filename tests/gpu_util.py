@@ -12,10 +12,29 @@ and 2 bf16 ulp for bf16 with fp32 accumulation):
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
 U32 = 2.0 ** -24
+
+# Where the checks append their statistics, one JSON object per line (the
+# report script tests/parity_stats.py turns them into a table).  Unset: not
+# recorded.
+STATS_ENV = "DLM_PARITY_STATS"
+
+
+def record(kind: str, what: str, stats: dict):
+    """Append one check's statistics to the file named by $DLM_PARITY_STATS."""
+    path = os.environ.get(STATS_ENV)
+    if not path:
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    line = json.dumps({"kind": kind, "test": test, "what": what, **stats})
+    with open(path, "a") as f:
+        f.write(line + "\n")
 
 
 def gamma(n: int, u: float = U32) -> float:
@@ -32,7 +51,8 @@ def ulp_dist_bf16(a: torch.Tensor, b: torch.Tensor) -> np.ndarray:
 
 
 def check_bf16(gpu, ref, exact, absum, n_terms, extra=0.0, what=""):
-    """Compare bf16 results with the oracle; returns the statistics dict."""
+    """Compare bf16 results with the oracle; returns the statistics dict (also
+    recorded, pass or fail, when $DLM_PARITY_STATS is set)."""
     d = ulp_dist_bf16(gpu, ref)
     err = np.abs(gpu.detach().cpu().double().numpy() - exact.numpy())
     floor = (gamma(n_terms) + extra) * absum.numpy()
@@ -43,7 +63,9 @@ def check_bf16(gpu, ref, exact, absum, n_terms, extra=0.0, what=""):
         "n_gt2ulp": int((d > 2).sum()),
         "n_floor_only": int(((d > 2) & (err <= floor)).sum()),
         "n_exact": int((d == 0).sum()),
+        "n_fail": int((~ok).sum()),
     }
+    record("bf16", what, stats)
     if not ok.all():
         bad = np.argwhere(~ok)[:5]
         rows = [(tuple(int(i) for i in b), float(gpu.detach().cpu().double().numpy()[tuple(b)]),
@@ -59,11 +81,17 @@ def check_f32(gpu, exact, absum, n_terms, what=""):
     err = np.abs(g - e)
     tol = np.maximum(1e-5 * np.abs(e), gamma(n_terms) * absum.numpy())
     ok = err <= tol
+    stats = {"n": int(err.size),
+             "max_rel": float((err / np.maximum(np.abs(e), 1e-30)).max()) if err.size else 0.0,
+             "n_rel_gt_1e-5": int((err > 1e-5 * np.abs(e)).sum()),
+             "n_floor_only": int(((err > 1e-5 * np.abs(e)) & ok).sum()),
+             "n_fail": int((~ok).sum())}
+    record("f32", what, stats)
     if not ok.all():
         b = np.argwhere(~ok)[:5]
         raise AssertionError(f"{what}: {int((~ok).sum())} out of tolerance, e.g. "
                              f"{[(tuple(map(int, i)), g[tuple(i)], e[tuple(i)]) for i in b]}")
-    return {"n": int(err.size), "max_rel": float((err / np.maximum(np.abs(e), 1e-30)).max())}
+    return stats
 
 
 def host_set(idx_row, g_row):

@@ -21,7 +21,7 @@ import torch
 import dynamic_lora_moe_amd as dlm
 import oracle
 import synth
-from gpu_util import dev_set, host_set, sample_rows, ulp_dist_bf16
+from gpu_util import dev_set, host_set, record, sample_rows, ulp_dist_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +60,7 @@ def _report(what, gpu_fr, ora_fr, exact, ulp, err_gpu, err_ora, unit):
         "n": int(exact.numel() if isinstance(exact, torch.Tensor) else exact.size),
     }
     print(f"[drift] {what}: {rep}", flush=True)
+    record("drift", what, rep)
     return rep
 
 

@@ -213,3 +213,38 @@ def test_sgmm_empty_batch_is_noop():
     g = torch.empty(0, 2, dtype=torch.float32, device="cuda")
     dlm.sgmm(x, idx, g, A, B, y, 1.0)
     torch.cuda.synchronize()
+
+
+def _host_segmentation(idx: np.ndarray, E: int):
+    """Rows ordered by their unordered expert pair, stably (row order within a
+    pair); rows with two empty slots left out.  Returns (perm, pair keys)."""
+    a = np.minimum(idx[:, 0], idx[:, 1]).astype(np.int64)
+    b = np.maximum(idx[:, 0], idx[:, 1]).astype(np.int64)
+    key = (a + 1) * (E + 1) + (b + 1)
+    live = np.flatnonzero(b >= 0)
+    order = live[np.argsort(key[live], kind="stable")]
+    return order.astype(np.int32), key
+
+
+@pytest.mark.parametrize("T,E,seed", [(9000, 8, 1), (4096, 8, 2), (2500, 32, 3), (1500, 4, 4), (1025, 2, 5)])
+def test_segment_order_equals_host_stable_sort(T, E, seed):
+    """The row order the segmentation writes (the workspace's perm list, after
+    the 256-byte header) is the stable sort of the rows by unordered pair, bit
+    for bit; positions past the live rows hold -1; the header counts match.
+    Covers batches past the first 1024 rows and past the 8192-row key cache."""
+    print(f"[sgmm] segment T={T} E={E}", flush=True)
+    d_in = d_out = 64
+    x, A, B, y = _problem(T, d_in, d_out, E, 16, torch.bfloat16, 3400 + seed)
+    idx, g = _sets(T, E, np.random.default_rng(100 + seed))
+    ws = dlm.sgmm_workspace(T, d_in, E, 16)
+    dlm.sgmm(x, idx.cuda(), g.cuda(), A, B, y, 1.0, ws)
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    T_pad = (T + 31) // 32 * 32
+    w = ws.cpu()
+    hdr = w[:256].view(torch.int32).numpy()
+    perm = w[256:256 + 4 * T_pad].view(torch.int32).numpy()
+    want, _ = _host_segmentation(idx.numpy(), E)
+    n_pos = len(want)
+    assert hdr[1] == n_pos and hdr[2] == (n_pos + 31) // 32
+    assert np.array_equal(perm[:n_pos], want)
+    assert (perm[n_pos:] == -1).all()

@@ -13,7 +13,7 @@ import torch
 import dynamic_lora_moe_amd as dlm
 import oracle
 import synth
-from gpu_util import check_bf16, dev_set, host_set, sample_rows
+from gpu_util import check_bf16, check_f32, dev_set, host_set, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -112,12 +112,82 @@ def _sgmm_check_rows(wl, probs, ys, idx, g, rows, what):
         xs, y0s = x[rt.cuda()].cpu(), y0[rt.cuda()].cpu()
         ref, ex, ab = oracle.sgmm(xs, idx[rt], g[rt], A.cpu(), B.cpu(), y0s, wl.scale,
                                   with_stats=True)
-        st = check_bf16(y[rt.cuda()].cpu(), ref, ex, ab, x.shape[1] + 2 * wl.r + 2, extra=SPLIT,
+        n_terms = x.shape[1] + 2 * wl.r + 2
+        if y.dtype == torch.float32:
+            check_f32(y[rt.cuda()].cpu(), ex, ab, n_terms, what=f"{what} L{l}.{name}")
+            continue
+        st = check_bf16(y[rt.cuda()].cpu(), ref, ex, ab, n_terms, extra=SPLIT,
                         what=f"{what} L{l}.{name}")
         for k in ("n", "n_gt2ulp", "n_floor_only"):
             agg[k] += st[k]
         agg["max_ulp"] = max(agg["max_ulp"], st["max_ulp"])
     print(what, agg, flush=True)
+
+
+@pytest.mark.parametrize("name,layer", [("tiny-fp32", 1), ("7b-decode", 3), ("70b-decode", 7)])
+def test_sgmm_on_router_sets_every_row(name, layer):
+    """The unmerged batched form on the decode workloads' own router sets: one
+    layer's projections (7B-shaped: d up to 11008; 70B-shaped: rank 64, 16
+    experts, d_in up to 28672) as one group over all the workload's tokens
+    (16 / 256 / 128 rows), the router's device output feeding the SGMM.  Every
+    row of every projection is checked against the oracle."""
+    wl = synth.WORKLOADS[name]
+    print(f"[workload] {name} SGMM on router sets: building layer {layer}", flush=True)
+    x, Wr = synth.router_inputs(wl)
+    ri, rg = oracle.pregate(x.cpu(), Wr.cpu())
+    idx, g = dlm.pregate(x, Wr)
+    torch.cuda.synchronize()
+    assert torch.equal(idx.cpu(), ri)
+    probs = synth.sgmm_problems(wl, layers=[layer])
+    ys = [y0.clone() for *_, y0 in probs]
+    grp = dlm.SgmmGroup([(xp, A, B, y) for (_, _, xp, A, B, _), y in zip(probs, ys)], wl.E, wl.r, wl.scale)
+    ws = grp.run(idx, g)
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    print(f"[workload] {name} SGMM on router sets: checking", flush=True)
+    _sgmm_check_rows(wl, probs, ys, ri, rg, np.arange(wl.T), f"{name} router-set SGMM")
+    grp.close()
+    del probs, ys
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_7b_decode_switch_full_layer_every_element():
+    """One switch launch over all 32 layers of the 7B-shaped workload (the
+    benchmark's launch), then one whole layer -- all 7 projections, every row
+    and column, 202 M weights -- against the oracle element by element."""
+    wl = synth.WORKLOADS["7b-decode"]
+    print("[workload] 7b-decode full layer: building", flush=True)
+    model = synth.switch_model(wl)
+    x, Wr = synth.router_inputs(wl)
+    ri, rg = oracle.pregate(x.cpu(), Wr.cpu())
+    idx, g = dlm.pregate(x, Wr)
+    torch.cuda.synchronize()
+    assert torch.equal(idx.cpu(), ri)
+    layer, t = 17, 200
+    mine = [(k, m) for k, m in enumerate(model) if m[0] == layer]
+    W0 = {k: W.cpu() for k, (_, _, W, _, _) in mine}
+    L = dlm.Layers([(W, A, B) for _, _, W, A, B in model], wl.E, wl.r, wl.scale)
+    L.switch((idx[t - 1], g[t - 1]), (idx[t], g[t]))
+    torch.cuda.synchronize()
+    assert L.status() == dlm.DLM_OK
+    L.close()
+    old, new = host_set(ri[t - 1], rg[t - 1]), host_set(ri[t], rg[t])
+    agg = {"n": 0, "n_gt2ulp": 0, "n_floor_only": 0, "max_ulp": 0}
+    for k, (l, name, W, A, B) in mine:
+        print(f"[workload] 7b-decode full layer: checking {name}", flush=True)
+        rows = np.arange(W.shape[0], dtype=np.int64)
+        ref, ex, ab = oracle.switch_rows(W0[k], rows, A.cpu(), B.cpu(), W.shape[0], wl.scale, old, new,
+                                         with_stats=True)
+        st = check_bf16(W.cpu(), ref, ex, ab, 4 * wl.r + 2, what=f"7b full layer L{l}.{name}")
+        for key in ("n", "n_gt2ulp", "n_floor_only"):
+            agg[key] += st[key]
+        agg["max_ulp"] = max(agg["max_ulp"], st["max_ulp"])
+        del ref, ex, ab
+    print("7b full layer", agg, flush=True)
+    assert agg["n"] == sum(o * i for _, o, i in wl.projs)
+    del model
+    gc.collect()
+    torch.cuda.empty_cache()
 
 
 def test_sgmm_prefill_grouped_sampled():
