@@ -70,6 +70,7 @@ def load(path: str = LIB_PATH):
         "dlm_layers_status": ([P, P, P], C.c_int),
         "dlm_sgmm_workspace_size": ([I64, I64, I32, I32, I32, P], C.c_int),
         "dlm_sgmm": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, F, I32, P, C.c_size_t, P], C.c_int),
+        "dlm_sgmm_noalloc": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, F, I32, P, P], C.c_int),
         "dlm_sgmm_group_create": ([P, I32, I32, I32, F, I32, P], C.c_int),
         "dlm_sgmm_group_destroy": ([P], C.c_int),
         "dlm_layers_repack": ([P, P], C.c_int),
@@ -309,6 +310,28 @@ def sgmm(x, idx, g, A, B, y, scale: float, workspace=None, stream=None):
     _check(load().dlm_sgmm(_p(x), _p(idx), _p(g), _p(A), _p(B), _p(y), T, d_in, d_out, E, r,
                            float(scale), _dt(x), _p(workspace), _ws_bytes(workspace), _stream(stream)),
            "dlm_sgmm")
+    return y
+
+
+def sgmm_noalloc(x, idx, g, A, B, y, scale: float, status=None, stream=None):
+    """sgmm() with the workspace in the library's own scratch array (no device
+    allocation by the call; calls overlapping on one device race).  status: an
+    optional int32 [1] device tensor receiving 0, or nonzero if a set was rejected."""
+    _need(x, "x")
+    _need(A, "A")
+    _need(B, "B")
+    T, d_in = x.shape
+    E, r, _ = A.shape
+    d_out = B.shape[1]
+    _like(A, "A", (E, r, d_in), x.dtype, x.device)
+    _like(B, "B", (E, d_out, r), x.dtype, x.device)
+    _like(y, "y", (T, d_out), x.dtype, x.device)
+    _like(idx, "idx", (T, 2), torch.int32, x.device)
+    _like(g, "g", (T, 2), torch.float32, x.device)
+    if status is not None:
+        _like(status, "status", (1,), torch.int32, x.device)
+    _check(load().dlm_sgmm_noalloc(_p(x), _p(idx), _p(g), _p(A), _p(B), _p(y), T, d_in, d_out, E, r,
+                                   float(scale), _dt(x), _p(status), _stream(stream)), "dlm_sgmm_noalloc")
     return y
 
 

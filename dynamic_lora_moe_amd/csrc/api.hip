@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -92,6 +93,14 @@ struct dlm_sgmm_group {
     };
     std::vector<Pack> packs;
 };
+
+// Scratch memory of dlm_sgmm_noalloc: one file-scope device array, which each
+// device that loads the library holds until the process ends.  In host code
+// its name stands for a host-side shadow, not for device memory: the device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever handed to a kernel.
+constexpr size_t kNoAllocScratchBytes = DLM_SGMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 extern "C" {
 
@@ -416,8 +425,10 @@ int check_ws(void* ws, size_t ws_bytes, const SgLayout& L) {
 int run_sgmm(const SgDesc* d_descs, const int32_t* ks_owner, const int32_t* cb_owner,
              const SgDesc& single, int n_prob, int64_t total_cb,
              int64_t total_ks, int64_t d_out_max, const int32_t* idx, const float* g, int64_t T, int E, int r,
-             float scale, int dtype, int packed, void* ws, const SgLayout& L, hipStream_t s) {
+             float scale, int dtype, int packed, void* ws, const SgLayout& L, hipStream_t s,
+             int32_t* status_out = nullptr) {
     SgmmArgs a;
+    a.status_out = status_out;
     a.descs = d_descs;
     a.ks_owner = ks_owner;
     a.cb_owner = cb_owner;
@@ -441,11 +452,12 @@ int run_sgmm(const SgDesc* d_descs, const int32_t* ks_owner, const int32_t* cb_o
     return ok();
 }
 
-}  // namespace
-
-int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, const void* B,
-             void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E, int32_t r, float scale,
-             int32_t dtype, void* workspace, size_t ws_bytes, void* stream) {
+// Host checks shared by dlm_sgmm and dlm_sgmm_noalloc (everything but the
+// workspace).  *done = true: T == 0, nothing to enqueue.
+int check_sgmm_args(const void* x, const int32_t* idx, const float* g, const void* A, const void* B, void* y,
+                    int64_t T, int64_t d_in, int64_t d_out, int32_t E, int32_t r, float scale, int32_t dtype,
+                    bool* done) {
+    *done = false;
     if (T < 0 || T > ((int64_t)1 << 30)) return fail(DLM_ESHAPE, "sgmm: T=%lld out of range", (long long)T);
     if (E < 1 || E > DLM_MAX_EXPERTS) return fail(DLM_ESHAPE, "sgmm: E=%d not in [1, %d]", E, DLM_MAX_EXPERTS);
     if (r < 1 || r > DLM_MAX_RANK) return fail(DLM_ESHAPE, "sgmm: r=%d not in [1, %d]", r, DLM_MAX_RANK);
@@ -454,7 +466,8 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, c
     if (T == 0) {  // nothing to do; the (possibly empty) buffers are not looked at
         if (d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim)
             return fail(DLM_ESHAPE, "sgmm: shape d_in=%lld d_out=%lld", (long long)d_in, (long long)d_out);
-        return ok();
+        *done = true;
+        return DLM_OK;
     }
     dlm_sgmm_problem p{x, A, B, y, d_in, d_out};
     int rc = check_problem(p, dtype, 0);
@@ -463,9 +476,10 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, c
     const size_t es = esize(dtype);
     if (overlap(x, (size_t)T * d_in * es, y, (size_t)T * d_out * es))
         return fail(DLM_EINVAL, "sgmm: x and y overlap");
-    const SgLayout L = sgmm_layout(T, d_in, E, r, 1);
-    rc = check_ws(workspace, ws_bytes, L);
-    if (rc != DLM_OK) return rc;
+    return DLM_OK;
+}
+
+SgDesc single_desc(const void* x, const void* A, const void* B, void* y, int64_t d_in, int64_t d_out) {
     SgDesc d{};
     d.x = x;
     d.A = A;
@@ -477,8 +491,70 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, c
     d.unit0 = 0;
     d.n_ks = (int32_t)((d_in + kSgmmKSlice - 1) / kSgmmKSlice);
     d.ks0 = 0;
+    return d;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on its first use there).
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "sgmm_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DLM_EDEVICE, "sgmm_noalloc: device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "sgmm_noalloc: hipGetSymbolAddress(scratch)");
+        if (!p) return fail(DLM_EHIP, "sgmm_noalloc: scratch has no device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DLM_OK;
+}
+
+}  // namespace
+
+int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, const void* B,
+             void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E, int32_t r, float scale,
+             int32_t dtype, void* workspace, size_t ws_bytes, void* stream) {
+    bool done = false;
+    int rc = check_sgmm_args(x, idx, g, A, B, y, T, d_in, d_out, E, r, scale, dtype, &done);
+    if (rc != DLM_OK) return rc;
+    if (done) return ok();
+    const SgLayout L = sgmm_layout(T, d_in, E, r, 1);
+    rc = check_ws(workspace, ws_bytes, L);
+    if (rc != DLM_OK) return rc;
+    const SgDesc d = single_desc(x, A, B, y, d_in, d_out);
     return run_sgmm(nullptr, nullptr, nullptr, d, 1, d.n_cb, d.n_ks, d_out, idx, g, T, E, r, scale, dtype, 0, workspace, L,
                     (hipStream_t)stream);
+}
+
+int dlm_sgmm_noalloc(const void* x, const int32_t* idx, const float* g, const void* A, const void* B,
+                     void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E, int32_t r, float scale,
+                     int32_t dtype, int32_t* status, void* stream) {
+    bool done = false;
+    int rc = check_sgmm_args(x, idx, g, A, B, y, T, d_in, d_out, E, r, scale, dtype, &done);
+    if (rc != DLM_OK) return rc;
+    if (done) return ok();
+    const SgLayout L = sgmm_layout(T, d_in, E, r, 1);
+    if (L.total > kNoAllocScratchBytes)
+        return fail(DLM_EWORKSPACE, "sgmm_noalloc: needs %zu bytes of scratch, the library's maximum is %zu "
+                    "(use dlm_sgmm with a caller workspace)", L.total, kNoAllocScratchBytes);
+    int sdev = -1, cdev = -1;
+    hipError_t e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e == hipSuccess) e = hipGetDevice(&cdev);
+    if (e != hipSuccess) return hip_fail(e, "sgmm_noalloc: stream device");
+    if (sdev != cdev) return fail(DLM_EINVAL, "sgmm_noalloc: the stream belongs to device %d, not the current %d", sdev, cdev);
+    void* ws = nullptr;
+    rc = scratch_on_current_device(&ws);
+    if (rc != DLM_OK) return rc;
+    const SgDesc d = single_desc(x, A, B, y, d_in, d_out);
+    return run_sgmm(nullptr, nullptr, nullptr, d, 1, d.n_cb, d.n_ks, d_out, idx, g, T, E, r, scale, dtype, 0, ws, L,
+                    (hipStream_t)stream, status);
 }
 
 int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, int32_t r,

@@ -144,7 +144,7 @@ constexpr int kKeyCache = 8192;
 constexpr int kTileCache = kKeyCache / 32;
 __global__ __launch_bounds__(kSegThreads) void sgmm_segment_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ g, int64_t T, int E, char* ws,
-    SgLayout L) {
+    SgLayout L, int32_t* status_out) {
     int32_t* hdr = (int32_t*)(ws + L.hdr);
     int32_t* perm = (int32_t*)(ws + L.perm);
     uint32_t* epk = (uint32_t*)(ws + L.epk);
@@ -289,6 +289,7 @@ __global__ __launch_bounds__(kSegThreads) void sgmm_segment_kernel(
         hdr[SG_ERR] = err;
         hdr[SG_NPOS] = n_pos;
         hdr[SG_NTILES] = n_tiles;
+        if (status_out) *status_out = err;
     }
 }
 
@@ -934,7 +935,7 @@ static bool sgmm_grids_fit(const SgmmArgs& a, int dtype) {
 hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
     if (!sgmm_grids_fit(a, dtype)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(sgmm_segment_kernel, dim3(1), dim3(kSegThreads), 0, s, a.idx, a.g, a.T, a.E,
-                       a.ws, a.L);
+                       a.ws, a.L, a.status_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dtype == 1) {

@@ -60,6 +60,7 @@ struct SgmmArgs {
     float scale;
     char* ws;
     SgLayout L;
+    int32_t* status_out;   // device word that also receives the set-validity flag, or nullptr
 };
 
 hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s);

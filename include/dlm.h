@@ -260,6 +260,31 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A,
              int32_t r, float scale, int32_t dtype, void* workspace, size_t ws_bytes,
              void* stream);
 
+/*
+ * dlm_sgmm for callers that cannot allocate device memory at all (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launches and results as dlm_sgmm, with the workspace in
+ * the library's own scratch array instead of a caller buffer.  The array is a
+ * static device array of DLM_SGMM_NOALLOC_SCRATCH_BYTES, held by every device
+ * that loads the library until the process ends; its device address is looked
+ * up on the first call on a device (which is when the runtime places the array
+ * in that device's memory).  The call itself allocates nothing.
+ *   status (device, may be NULL): receives 0 when every row's set was valid,
+ *     nonzero when the device rejected one (then y is left unchanged) -- the
+ *     workspace status word of dlm_sgmm, written where the caller can read it.
+ * Every other argument as for dlm_sgmm.  `stream` must belong to the current
+ * device (DLM_EINVAL otherwise).  A call whose workspace
+ * (dlm_sgmm_workspace_size(T, d_in, E, r, 1)) exceeds the array returns
+ * DLM_EWORKSPACE before anything is enqueued.
+ * All calls on one device share that device's array and each call overwrites
+ * it: calls that can overlap on one device (different streams, or several host
+ * threads) race and give wrong results; order them on one stream.
+ */
+#define DLM_SGMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int dlm_sgmm_noalloc(const void* x, const int32_t* idx, const float* g, const void* A,
+                     const void* B, void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E,
+                     int32_t r, float scale, int32_t dtype, int32_t* status, void* stream);
+
 /* One problem of a grouped SGMM: every problem shares the rows' sets. */
 typedef struct {
     const void* x;  /* [T][d_in] */
