@@ -293,7 +293,12 @@ def _ws_bytes(workspace) -> int:
 
 
 def sgmm(x, idx, g, A, B, y, scale: float, workspace=None, stream=None):
-    """y += sum_k s g_k (x A_k^T) B_k^T row by row, in place (returns y)."""
+    """y += sum_k s g_k (x A_k^T) B_k^T row by row, in place (returns y).
+
+    With a workspace the call only enqueues; read the device's verdict on the
+    sets with sgmm_status(workspace).  Without one it allocates a workspace,
+    waits for the launches (so the temporary outlives them) and raises
+    DLMError(DLM_EDEVICE) if the device rejected a set (y is then unchanged)."""
     _need(x, "x")
     _need(A, "A")
     _need(B, "B")
@@ -305,11 +310,15 @@ def sgmm(x, idx, g, A, B, y, scale: float, workspace=None, stream=None):
     _like(y, "y", (T, d_out), x.dtype, x.device)
     _like(idx, "idx", (T, 2), torch.int32, x.device)
     _like(g, "g", (T, 2), torch.float32, x.device)
-    if workspace is None:
+    own = workspace is None
+    if own:
         workspace = sgmm_workspace(T, d_in, E, r, 1, x.device)
     _check(load().dlm_sgmm(_p(x), _p(idx), _p(g), _p(A), _p(B), _p(y), T, d_in, d_out, E, r,
                            float(scale), _dt(x), _p(workspace), _ws_bytes(workspace), _stream(stream)),
            "dlm_sgmm")
+    if own and T > 0 and sgmm_status(workspace, stream) != DLM_OK:
+        raise DLMError(DLM_EDEVICE, "dlm_sgmm: the device rejected an expert set (index outside [-1, E) or "
+                                    "a non-finite gate); y is unchanged")
     return y
 
 
@@ -381,16 +390,24 @@ class SgmmGroup:
         _check(load().dlm_sgmm_group_repack(self._h, _stream(stream)), "dlm_sgmm_group_repack")
 
     def run(self, idx, g, T: int | None = None, workspace=None, stream=None):
+        """Run every problem on rows [0, T) of (idx, g); returns the workspace,
+        whose status word sgmm_status() reads (a rejected set leaves every y
+        unchanged)."""
         _need(idx, "idx")
         T = idx.shape[0] if T is None else T
         if not 0 <= T <= self.rows:
             raise ValueError(f"T={T} rows, but the group's problems hold {self.rows}")
         _like(idx[:T], "idx", (T, 2), torch.int32, self.device)
         _like(g[:T], "g", (T, 2), torch.float32, self.device)
-        if workspace is None:
+        own = workspace is None
+        if own:
             workspace = self.workspace(T, idx.device)
         _check(load().dlm_sgmm_group_run(self._h, _p(idx), _p(g), T, _p(workspace),
                                          _ws_bytes(workspace), _stream(stream)), "dlm_sgmm_group_run")
+        if own and stream is not None and stream != torch.cuda.current_stream():
+            # a workspace made here on the current stream is used on `stream`:
+            # keep the allocator from handing it out again before those launches end
+            workspace.record_stream(stream)
         return workspace
 
     def close(self):

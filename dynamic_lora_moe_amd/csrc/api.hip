@@ -2,6 +2,7 @@
 // call before it passes), device descriptor tables, launches and status words.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -54,6 +55,51 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// A byte range a launch reads or writes.  The kernels update buffers in place
+// from many workgroups, so a written range that overlaps any other range of the
+// same call gives a silent race: such calls are refused.
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+    bool write;
+    const char* what;
+    int who;
+};
+
+Span span(const void* p, size_t bytes, bool write, const char* what, int who) {
+    return Span{(uintptr_t)p, (uintptr_t)p + bytes, write, what, who};
+}
+
+// First pair of overlapping spans of which at least one is written, or false.
+// Sorted by start; for each span, the span reaching furthest so far and the
+// written span reaching furthest so far are the only candidates that can
+// overlap it while some earlier written span overlaps it, so one pass finds a
+// conflict whenever there is one.
+bool write_conflict(std::vector<Span> v, Span* a, Span* b) {
+    std::sort(v.begin(), v.end(), [](const Span& x, const Span& y) { return x.lo < y.lo; });
+    int far = -1, farw = -1;
+    for (int k = 0; k < (int)v.size(); ++k) {
+        if (v[k].hi <= v[k].lo) continue;
+        if (far >= 0 && v[far].hi > v[k].lo && (v[k].write || v[far].write)) {
+            *a = v[far];
+            *b = v[k];
+            return true;
+        }
+        if (farw >= 0 && v[farw].hi > v[k].lo) {
+            *a = v[farw];
+            *b = v[k];
+            return true;
+        }
+        if (far < 0 || v[k].hi > v[far].hi) far = k;
+        if (v[k].write && (farw < 0 || v[k].hi > v[farw].hi)) farw = k;
+    }
+    return false;
+}
+
+int conflict_fail(const char* call, const Span& a, const Span& b) {
+    return fail(DLM_EINVAL, "%s: %s %d overlaps %s %d, and one of them is written in place", call, a.what, a.who,
+                b.what, b.who);
+}
+
 }  // namespace
 
 // --------------------------------------------------------------- handles ----
@@ -73,7 +119,26 @@ struct dlm_layers {
     int32_t dtype = 0;
     SwTile tile{};
     int64_t n_tiles = 0, n_elems = 0, per_xcd = 0;
+    std::vector<std::pair<uintptr_t, uintptr_t>> w_spans;  // every W, sorted, disjoint
 };
+
+// Whether [p, p + bytes) touches any weight the handle writes.
+static bool hits_weights(const dlm_layers* h, const void* p, size_t bytes) {
+    if (!p) return false;
+    const uintptr_t lo = (uintptr_t)p, hi = lo + bytes;
+    auto it = std::upper_bound(h->w_spans.begin(), h->w_spans.end(), std::make_pair(lo, UINTPTR_MAX));
+    if (it != h->w_spans.begin() && std::prev(it)->second > lo) return true;
+    return it != h->w_spans.end() && it->first < hi;
+}
+
+static int check_sets(const dlm_layers* h, const int32_t* old_idx, const float* old_g, const int32_t* new_idx,
+                      const float* new_g, const char* call) {
+    if ((old_idx && !old_g) || (new_idx && !new_g)) return fail(DLM_EINVAL, "%s: a set has indices but no gates", call);
+    if (hits_weights(h, old_idx, 8) || hits_weights(h, old_g, 8) || hits_weights(h, new_idx, 8) ||
+        hits_weights(h, new_g, 8))
+        return fail(DLM_EINVAL, "%s: a set lies inside a weight the switch writes", call);
+    return DLM_OK;
+}
 
 struct dlm_sgmm_group {
     SgDesc* d_descs = nullptr;          // device block: descriptors, then the owner tables
@@ -92,6 +157,7 @@ struct dlm_sgmm_group {
         int64_t d_in;
     };
     std::vector<Pack> packs;
+    int64_t checked_T = 0;  // largest row count whose buffers were checked for overlaps
 };
 
 // Scratch memory of dlm_sgmm_noalloc: one file-scope device array, which each
@@ -187,6 +253,18 @@ int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, fl
         tiles += (int64_t)d.n_rt * d.n_ct;
         elems += p.d_out * p.d_in;
     }
+    {
+        std::vector<Span> v;
+        const size_t es = esize(dtype);
+        for (int i = 0; i < n; ++i) {
+            const dlm_proj& p = projs[i];
+            v.push_back(span(p.W, (size_t)p.d_out * p.d_in * es, true, "weight W", i));
+            v.push_back(span(p.A, (size_t)E * r * p.d_in * es, false, "bank A", i));
+            v.push_back(span(p.B, (size_t)E * p.d_out * r * es, false, "bank B", i));
+        }
+        Span a, b;
+        if (write_conflict(std::move(v), &a, &b)) return conflict_fail("layers_create", a, b);
+    }
     dlm_layers* hd = new (std::nothrow) dlm_layers();
     if (!hd) return fail(DLM_ENOMEM, "layers_create: host allocation failed");
     hd->n = n;
@@ -234,6 +312,9 @@ int dlm_layers_create(const dlm_proj* projs, int32_t n, int32_t E, int32_t r, fl
         delete hd;
         return hip_fail(e, "layers_create");
     }
+    for (const SwDesc& q : h)
+        hd->w_spans.emplace_back((uintptr_t)q.W, (uintptr_t)q.W + (size_t)q.d_out * q.d_in * esize(dtype));
+    std::sort(hd->w_spans.begin(), hd->w_spans.end());
     hd->h_descs = std::move(h);
     *out = hd;
     return ok();
@@ -288,8 +369,8 @@ static SwitchArgs switch_args(const dlm_layers* h, const int32_t* old_idx, const
 int dlm_switch(dlm_layers* h, const int32_t* old_idx, const float* old_g, const int32_t* new_idx,
                const float* new_g, void* stream) {
     if (!h) return fail(DLM_EINVAL, "switch: null handle");
-    if ((old_idx && !old_g) || (new_idx && !new_g))
-        return fail(DLM_EINVAL, "switch: a set has indices but no gates");
+    const int rc = check_sets(h, old_idx, old_g, new_idx, new_g, "switch");
+    if (rc != DLM_OK) return rc;
     const SwitchArgs a = switch_args(h, old_idx, old_g, new_idx, new_g);
     const hipError_t e = h->dtype == DLM_BF16 ? launch_switch_bf16(a, h->tile, (hipStream_t)stream)
                                               : launch_switch_generic(a, h->dtype, (hipStream_t)stream);
@@ -309,11 +390,23 @@ int dlm_layers_bind_vectors(dlm_layers* h, const void* const* x, float* const* y
         if (h->dtype == DLM_BF16 && !aligned16(x[i]))
             return fail(DLM_EALIGN, "bind_vectors: x %d not 16-byte aligned", i);
         if (((uintptr_t)y[i] & 3u) != 0) return fail(DLM_EALIGN, "bind_vectors: y %d not 4-byte aligned", i);
-        if (overlap(x[i], (size_t)d[i].d_in * esize(h->dtype), y[i], (size_t)d[i].d_out * 4) ||
-            overlap(d[i].W, (size_t)d[i].d_out * d[i].d_in * esize(h->dtype), y[i], (size_t)d[i].d_out * 4))
-            return fail(DLM_EINVAL, "bind_vectors: y %d overlaps its x or W", i);
         d[i].xv = x[i];
         d[i].yv = y[i];
+    }
+    {
+        // the product reads W, x (and the switch + product also writes W and
+        // reads A, B); y is written
+        std::vector<Span> v;
+        const size_t es = esize(h->dtype);
+        for (int i = 0; i < h->n; ++i) {
+            v.push_back(span(d[i].W, (size_t)d[i].d_out * d[i].d_in * es, true, "weight W", i));
+            v.push_back(span(d[i].A, (size_t)h->E * h->r * d[i].d_in * es, false, "bank A", i));
+            v.push_back(span(d[i].B, (size_t)h->E * d[i].d_out * h->r * es, false, "bank B", i));
+            v.push_back(span(x[i], (size_t)d[i].d_in * es, false, "vector x", i));
+            v.push_back(span(y[i], (size_t)d[i].d_out * 4, true, "vector y", i));
+        }
+        Span a, b;
+        if (write_conflict(std::move(v), &a, &b)) return conflict_fail("bind_vectors", a, b);
     }
     float* part = nullptr;
     // launches still in flight on any stream read the current table and
@@ -354,8 +447,8 @@ int dlm_switch_gemv(dlm_layers* h, const int32_t* old_idx, const float* old_g, c
                     const float* new_g, void* stream) {
     if (!h) return fail(DLM_EINVAL, "switch_gemv: null handle");
     if (!h->bound) return fail(DLM_EINVAL, "switch_gemv: no vectors bound (dlm_layers_bind_vectors)");
-    if ((old_idx && !old_g) || (new_idx && !new_g))
-        return fail(DLM_EINVAL, "switch_gemv: a set has indices but no gates");
+    const int rc = check_sets(h, old_idx, old_g, new_idx, new_g, "switch_gemv");
+    if (rc != DLM_OK) return rc;
     const SwitchArgs a = switch_args(h, old_idx, old_g, new_idx, new_g);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -456,7 +549,7 @@ int run_sgmm(const SgDesc* d_descs, const int32_t* ks_owner, const int32_t* cb_o
 // workspace).  *done = true: T == 0, nothing to enqueue.
 int check_sgmm_args(const void* x, const int32_t* idx, const float* g, const void* A, const void* B, void* y,
                     int64_t T, int64_t d_in, int64_t d_out, int32_t E, int32_t r, float scale, int32_t dtype,
-                    bool* done) {
+                    const void* ws, size_t ws_bytes, bool* done) {
     *done = false;
     if (T < 0 || T > ((int64_t)1 << 30)) return fail(DLM_ESHAPE, "sgmm: T=%lld out of range", (long long)T);
     if (E < 1 || E > DLM_MAX_EXPERTS) return fail(DLM_ESHAPE, "sgmm: E=%d not in [1, %d]", E, DLM_MAX_EXPERTS);
@@ -474,8 +567,12 @@ int check_sgmm_args(const void* x, const int32_t* idx, const float* g, const voi
     if (rc != DLM_OK) return rc;
     if (!idx || !g) return fail(DLM_EINVAL, "sgmm: idx or g is null");
     const size_t es = esize(dtype);
-    if (overlap(x, (size_t)T * d_in * es, y, (size_t)T * d_out * es))
-        return fail(DLM_EINVAL, "sgmm: x and y overlap");
+    std::vector<Span> v = {span(x, (size_t)T * d_in * es, false, "x", 0), span(y, (size_t)T * d_out * es, true, "y", 0),
+                           span(A, (size_t)E * r * d_in * es, false, "A", 0), span(B, (size_t)E * d_out * r * es, false, "B", 0),
+                           span(idx, (size_t)T * 8, false, "idx", 0), span(g, (size_t)T * 8, false, "g", 0)};
+    if (ws) v.push_back(span(ws, ws_bytes, true, "workspace", 0));
+    Span a, b;
+    if (write_conflict(std::move(v), &a, &b)) return conflict_fail("sgmm", a, b);
     return DLM_OK;
 }
 
@@ -522,7 +619,7 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, c
              void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E, int32_t r, float scale,
              int32_t dtype, void* workspace, size_t ws_bytes, void* stream) {
     bool done = false;
-    int rc = check_sgmm_args(x, idx, g, A, B, y, T, d_in, d_out, E, r, scale, dtype, &done);
+    int rc = check_sgmm_args(x, idx, g, A, B, y, T, d_in, d_out, E, r, scale, dtype, workspace, ws_bytes, &done);
     if (rc != DLM_OK) return rc;
     if (done) return ok();
     const SgLayout L = sgmm_layout(T, d_in, E, r, 1);
@@ -537,7 +634,7 @@ int dlm_sgmm_noalloc(const void* x, const int32_t* idx, const float* g, const vo
                      void* y, int64_t T, int64_t d_in, int64_t d_out, int32_t E, int32_t r, float scale,
                      int32_t dtype, int32_t* status, void* stream) {
     bool done = false;
-    int rc = check_sgmm_args(x, idx, g, A, B, y, T, d_in, d_out, E, r, scale, dtype, &done);
+    int rc = check_sgmm_args(x, idx, g, A, B, y, T, d_in, d_out, E, r, scale, dtype, status, status ? 4 : 0, &done);
     if (rc != DLM_OK) return rc;
     if (done) return ok();
     const SgLayout L = sgmm_layout(T, d_in, E, r, 1);
@@ -675,14 +772,36 @@ int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, in
     if (T == 0) return ok();
     if (!idx || !g) return fail(DLM_EINVAL, "sgmm_group_run: idx or g is null");
     const size_t es = esize(h->dtype);
-    for (int i = 0; i < h->n; ++i) {
-        const SgDesc& d = h->h_descs[i];
-        if (overlap(d.x, (size_t)T * d.d_in * es, d.y, (size_t)T * d.d_out * es))
-            return fail(DLM_EINVAL, "sgmm_group_run: problem %d x and y overlap", i);
-    }
     const SgLayout L = sgmm_layout(T, h->d_in_max, h->E, h->r, h->n);
     const int rc = check_ws(workspace, ws_bytes, L);
     if (rc != DLM_OK) return rc;
+    {
+        // every problem's ranges, the sets and the workspace: a written one (y,
+        // workspace) may overlap nothing else.  The problems' extents grow with
+        // T, so a row count up to one already checked needs only the per-call
+        // pointers (sets, workspace) checked again.
+        std::vector<Span> v;
+        const int64_t Tc = T > h->checked_T ? T : h->checked_T;
+        for (int i = 0; i < h->n; ++i) {
+            const SgDesc& d = h->h_descs[i];
+            v.push_back(span(d.x, (size_t)Tc * d.d_in * es, false, "problem x", i));
+            v.push_back(span(d.y, (size_t)Tc * d.d_out * es, true, "problem y", i));
+            v.push_back(span(d.A, (size_t)h->E * h->r * d.d_in * es, false, "problem A", i));
+            v.push_back(span(d.B, (size_t)h->E * d.d_out * h->r * es, false, "problem B", i));
+        }
+        if (T > h->checked_T) {
+            Span a, b;
+            if (write_conflict(v, &a, &b)) return conflict_fail("sgmm_group_run", a, b);
+            h->checked_T = T;
+        }
+        const Span call[3] = {span(idx, (size_t)T * 8, false, "idx", 0), span(g, (size_t)T * 8, false, "g", 0),
+                              span(workspace, ws_bytes, true, "workspace", 0)};
+        for (const Span& c : call)
+            for (const Span& q : v)
+                if (c.hi > q.lo && q.hi > c.lo && (c.write || q.write)) return conflict_fail("sgmm_group_run", c, q);
+        if (overlap(workspace, ws_bytes, idx, (size_t)T * 8) || overlap(workspace, ws_bytes, g, (size_t)T * 8))
+            return fail(DLM_EINVAL, "sgmm_group_run: the workspace overlaps the sets");
+    }
     return run_sgmm(h->d_descs, h->d_ks_owner, h->d_cb_owner, h->h_descs[0], h->n, h->total_cb, h->total_ks, h->d_out_max, idx, g, T, h->E,
                     h->r, h->scale, h->dtype, h->packs.empty() ? 0 : 1, workspace, L, (hipStream_t)stream);
 }

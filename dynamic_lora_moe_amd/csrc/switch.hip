@@ -21,9 +21,11 @@
 //     16-byte LDS read.  B row slices are already k-contiguous and go straight
 //     from global memory into MFMA operand registers.
 //   * The MFMA runs "transposed": M = W columns, N = W rows.  With the columns
-//     of each 32-column block permuted (perm below) the accumulator of lane l
-//     holds 16 consecutive columns of row l%32, so W is read and written with
-//     two 128-bit accesses per lane and per block, no LDS round trip.
+//     of each 32-column block permuted (perm_row below) the accumulator of
+//     lane l holds 16 consecutive columns of row l%32.  W itself is read and
+//     written row-major (8 rows x 128 bytes per wave instruction, coalesced)
+//     and passes through a per-wave swizzled LDS block into and out of that
+//     MFMA layout.
 //   * Each slot has its own fp32 accumulator chain (K = r).  The epilogue
 //     forms S_new = c1*P1 + c0*P0 and S_old the same way (one fma each), then
 //     W - (S_old - S_new) in fp32 and one RNE to bf16.  Identical expressions

@@ -140,14 +140,18 @@ def test_sgmm_workspace_size(lib):
     assert lib.dlm_sgmm_workspace_size(64, 64, 8, 16, 1, None) == dlm.DLM_EINVAL
 
 
+MB = 1 << 20
+
+
 def test_sgmm_validation(lib):
     P = C.c_void_p
     ws = C.c_size_t(0)
     lib.dlm_sgmm_workspace_size(16, 64, 4, 16, 1, C.byref(ws))
-    X, Y = FAKE, FAKE + (1 << 20)
+    # every buffer at its own (fake) address, megabytes apart
+    X, Y, IDX, G, A, B, W = (FAKE + k * MB for k in range(7))
 
-    def call(x=X, idx=FAKE, g=FAKE, A=FAKE, B=FAKE, y=Y, T=16, d_in=64, d_out=64, E=4, r=16,
-             s=1.0, dt=1, w=FAKE, nb=ws.value):
+    def call(x=X, idx=IDX, g=G, A=A, B=B, y=Y, T=16, d_in=64, d_out=64, E=4, r=16,
+             s=1.0, dt=1, w=W, nb=ws.value):
         return lib.dlm_sgmm(P(x), P(idx), P(g), P(A), P(B), P(y), T, d_in, d_out, E, r, s, dt,
                             P(w), nb, None)
 
@@ -163,10 +167,52 @@ def test_sgmm_validation(lib):
     assert call(A=FAKE + 8) == dlm.DLM_EALIGN
     assert call(y=X + 64) == dlm.DLM_EINVAL          # y overlaps x
     assert "overlap" in _err(lib)
+    assert call(y=A + 512) == dlm.DLM_EINVAL         # y overlaps the A bank
+    assert call(y=IDX - 1024) == dlm.DLM_EINVAL      # y runs into the sets
+    assert call(w=Y + 256) == dlm.DLM_EINVAL         # the workspace overlaps y
+    assert "workspace" in _err(lib)
     assert call(w=0) == dlm.DLM_EWORKSPACE
     assert call(nb=ws.value - 1) == dlm.DLM_EWORKSPACE
-    assert call(w=FAKE + 16) == dlm.DLM_EALIGN       # workspace must be 256-byte aligned
+    assert call(w=W + 16) == dlm.DLM_EALIGN          # workspace must be 256-byte aligned
     assert call(T=0) == dlm.DLM_OK                   # nothing to do, nothing touched
+
+
+def test_layers_create_refuses_aliased_buffers(lib):
+    """A weight the switch writes in place may overlap no other weight and no
+    bank (other weights' banks included); banks may share memory (read only)."""
+    h = C.c_void_p()
+    W0, W1, A0, B0 = FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 3 * MB
+    # same weight twice
+    assert lib.dlm_layers_create(_projs((W0, A0, B0, 64, 64), (W0, A0, B0, 64, 64)), 2, 4, 4, 1.0, 1,
+                                 C.byref(h)) == dlm.DLM_EINVAL
+    assert "overlaps" in _err(lib)
+    # a weight running into another weight's bank
+    assert lib.dlm_layers_create(_projs((W0, A0, B0, 64, 64), (A0 - 4096, A0 + 8192, B0, 64, 64)), 2, 4, 4,
+                                 1.0, 1, C.byref(h)) == dlm.DLM_EINVAL
+    # a weight inside its own B bank
+    assert lib.dlm_layers_create(_projs((B0 + 256, A0, B0, 64, 64)), 1, 4, 4, 1.0, 1, C.byref(h)) == dlm.DLM_EINVAL
+    assert h.value is None
+
+
+def test_sgmm_noalloc_validation(lib):
+    P = C.c_void_p
+    X, Y, IDX, G, A, B, S = (FAKE + k * MB for k in range(7))
+
+    def call(x=X, idx=IDX, g=G, A=A, B=B, y=Y, T=16, d_in=64, d_out=64, E=4, r=16, s=1.0, dt=1, st=S):
+        return lib.dlm_sgmm_noalloc(P(x), P(idx), P(g), P(A), P(B), P(y), T, d_in, d_out, E, r, s, dt, P(st),
+                                    None)
+
+    assert call(E=0) == dlm.DLM_ESHAPE
+    assert call(dt=3) == dlm.DLM_EDTYPE
+    assert call(x=0) == dlm.DLM_EINVAL
+    assert call(d_out=60) == dlm.DLM_EALIGN
+    assert call(y=X + 64) == dlm.DLM_EINVAL
+    assert call(st=Y + 4) == dlm.DLM_EINVAL          # the status word inside y
+    # more scratch than the library's array holds: refused before anything runs
+    assert call(T=70000, d_in=8192, r=128, E=8, y=1 << 40, idx=1 << 41, g=1 << 42, A=1 << 43, B=1 << 44,
+                st=1 << 45) == dlm.DLM_EWORKSPACE
+    assert "maximum" in _err(lib)
+    assert call(T=0) == dlm.DLM_OK
 
 
 def test_sgmm_group_create_validation(lib):
@@ -195,7 +241,9 @@ def test_grids_past_32_bits_are_refused_before_any_launch(lib):
         assert "2^32" in _err(lib)
         assert lib.dlm_pregate_centroid(P(FAKE), P(FAKE), T, 64, 8, 4, dt, P(FAKE), P(FAKE),
                                         None) == dlm.DLM_ESHAPE
-        x, y = FAKE, 1 << 44  # x's and y's extents do not overlap
-        assert lib.dlm_sgmm(P(x), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(y), T, 8, 8, 1, 1, 1.0, dt,
-                            P(FAKE), C.c_size_t(1 << 62), None) == dlm.DLM_ESHAPE
+        # x, the sets, the banks, y and the workspace at addresses far enough
+        # apart that their extents at T = 2^30 rows do not overlap
+        x, idx, g, A, B, y, w = FAKE, 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44, 1 << 46
+        assert lib.dlm_sgmm(P(x), P(idx), P(g), P(A), P(B), P(y), T, 8, 8, 1, 1, 1.0, dt,
+                            P(w), C.c_size_t(1 << 45), None) == dlm.DLM_ESHAPE
         assert "2^32" in _err(lib)

@@ -86,3 +86,57 @@ def test_pregate_rejects_short_outputs():
         dlm.pregate(x, Wr, g=g.to(torch.bfloat16))
     with pytest.raises(ValueError):
         dlm.pregate(x, _t(32, 4))
+
+
+def test_aliased_buffers_are_refused_before_launch():
+    """A set stored inside a weight the switch writes, a group workspace that
+    overlaps a problem's y, and a bound output vector inside a weight are all
+    refused on the host (DLM_EINVAL); nothing changes."""
+    E, r = 4, 16
+    W = (0.02 * torch.randn(64, 64, device="cuda")).bfloat16()
+    A = (0.02 * torch.randn(E, r, 64, device="cuda")).bfloat16()
+    B = (0.02 * torch.randn(E, 64, r, device="cuda")).bfloat16()
+    W0 = W.clone()
+    L = dlm.Layers([(W, A, B)], E, r, 1.0)
+    inside = W.view(-1)[64:68].view(torch.int32)   # 8 bytes of W read as idx[2]
+    g = torch.tensor([0.5, 0.5], device="cuda")
+    with pytest.raises(dlm.DLMError) as e:
+        L.switch(None, (inside, g))
+    assert e.value.status == dlm.DLM_EINVAL
+    ys = [W.view(-1)[:128].view(torch.float32)]     # 64 fp32 outputs inside W
+    with pytest.raises(dlm.DLMError) as e:
+        L.bind_vectors([torch.zeros(64, device="cuda").bfloat16()], ys)
+    assert e.value.status == dlm.DLM_EINVAL
+    torch.cuda.synchronize()
+    assert torch.equal(W, W0)
+    L.close()
+    T = 40
+    x = torch.randn(T, 64, device="cuda").bfloat16()
+    y = torch.zeros(T, 64, device="cuda").bfloat16()
+    grp = dlm.SgmmGroup([(x, A, B, y)], E, r, 1.0)
+    n = dlm.sgmm_workspace_size(T, 64, E, r, 1)
+    big = torch.zeros(n + T * 64 * 2 + 256, dtype=torch.uint8, device="cuda")
+    ws_over_y = big[256:256 + n]
+    idx = torch.zeros(T, 2, dtype=torch.int32, device="cuda")
+    gg = torch.zeros(T, 2, device="cuda")
+    grp2 = dlm.SgmmGroup([(x, A, B, big[:T * 64 * 2].view(torch.bfloat16).view(T, 64))], E, r, 1.0)
+    with pytest.raises(dlm.DLMError) as e:
+        grp2.run(idx, gg, workspace=ws_over_y)
+    assert e.value.status == dlm.DLM_EINVAL
+    grp.close()
+    grp2.close()
+
+
+def test_sgmm_without_workspace_raises_on_a_rejected_set():
+    E, r, T = 4, 16, 8
+    x = torch.randn(T, 64, device="cuda").bfloat16()
+    A = (0.02 * torch.randn(E, r, 64, device="cuda")).bfloat16()
+    B = (0.02 * torch.randn(E, 64, r, device="cuda")).bfloat16()
+    y = torch.zeros(T, 64, device="cuda").bfloat16()
+    idx = torch.zeros(T, 2, dtype=torch.int32, device="cuda")
+    idx[3, 1] = E   # out of range
+    g = torch.ones(T, 2, device="cuda")
+    with pytest.raises(dlm.DLMError) as e:
+        dlm.sgmm(x, idx, g, A, B, y, 1.0)
+    assert e.value.status == dlm.DLM_EDEVICE
+    assert (y == 0).all()
