@@ -475,11 +475,90 @@ def cpu_baseline(torch, synth, target_s, log):
     except OSError:
         pass
     log(f"cpu oracle: {layers} layers, {elems} elements in {secs:.1f} s on {threads} threads ({cpu})")
+    cpu = _cpu_description(cpu)
+    legs = [_cpu_switch_one_thread(torch, synth, wl, old, new, log),
+            _cpu_sgmm_prefill(torch, synth, log), _cpu_tiny(torch, synth, log)]
     return {"value": elems * 4 / secs / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"switch (old {old} -> new {new}) of all 7 adapted weights of the first "
                       f"{layers} of 32 layers of the 7B-shaped workload ({elems} elements, "
                       f"{secs:.1f} s of oracle time); weight bytes read+written per second, "
-                      f"binary64 oracle, OpenMP over rows, {threads} threads of {cpu}"}
+                      f"binary64 oracle, OpenMP over rows, {threads} threads of {cpu}",
+            "cpu": cpu, "legs": legs}
+
+
+def _cpu_description(model):
+    """CPU model, family/model/stepping and thread count of this host."""
+    fields = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ":" in ln:
+                    k, v = ln.split(":", 1)
+                    fields.setdefault(k.strip(), v.strip())
+    except OSError:
+        pass
+    fam = "/".join(fields.get(k, "?") for k in ("cpu family", "model", "stepping"))
+    return f"{model} (family/model/stepping {fam}, {os.cpu_count()} logical CPUs)"
+
+
+def _cpu_switch_one_thread(torch, synth, wl, old, new, log):
+    """The same switch on one thread: the q and k weights of layer 0."""
+    import numpy as np
+
+    import oracle
+    n0 = oracle.threads()
+    oracle.set_threads(1)
+    elems, secs = 0, 0.0
+    try:
+        for _, name, W, A, B in synth.switch_model(wl, layers=[0])[:2]:
+            Wh, Ah, Bh = W.cpu(), A.cpu(), B.cpu()
+            t1 = time.perf_counter()
+            oracle.switch_rows(Wh, np.arange(W.shape[0]), Ah, Bh, W.shape[0], wl.scale, old, new)
+            secs += time.perf_counter() - t1
+            elems += W.numel()
+    finally:
+        oracle.set_threads(n0)
+    torch.cuda.empty_cache()
+    log(f"cpu oracle, one thread: {elems} elements in {secs:.1f} s")
+    return {"what": "switch, one thread", "value": elems * 4 / secs / 1e9, "unit": "GB/s", "cores": 1,
+            "sample": f"q and k weights of layer 0 of the 7B-shaped workload ({elems} elements, {secs:.1f} s)"}
+
+
+def _cpu_sgmm_prefill(torch, synth, log):
+    """The whole prefill SGMM pass (4096 tokens x 7 projections) in the oracle."""
+    import oracle
+    wl = synth.WORKLOADS["sgmm-prefill"]
+    idx, g = synth.batched_sets(wl)
+    secs = 0.0
+    for _, _, x, A, B, y in synth.sgmm_problems(wl):
+        xh, Ah, Bh, yh = x.cpu(), A.cpu(), B.cpu(), y.cpu()
+        t1 = time.perf_counter()
+        oracle.sgmm(xh, idx, g, Ah, Bh, yh, wl.scale)
+        secs += time.perf_counter() - t1
+    torch.cuda.empty_cache()
+    log(f"cpu oracle, prefill SGMM: {secs:.2f} s")
+    return {"what": "SGMM prefill pass, all threads", "value": wl.T / secs, "unit": "tokens/s",
+            "cores": oracle.threads(), "seconds_per_pass": secs,
+            "sample": "the whole pass: 4096 tokens x 7 projections (in full)"}
+
+
+def _cpu_tiny(torch, synth, log):
+    """The tiny fp32 workload in full: router on its 16 tokens and its 16 switches."""
+    import oracle
+    wl = synth.WORKLOADS["tiny-fp32"]
+    x, Wr = synth.router_inputs(wl)
+    model = [(W.cpu(), A.cpu(), B.cpu()) for _, _, W, A, B in synth.switch_model(wl)]
+    t1 = time.perf_counter()
+    ri, rg = oracle.pregate(x.cpu(), Wr.cpu())
+    prev = None
+    for t in range(wl.T):
+        new = (ri[t].tolist(), rg[t].tolist())
+        model = [(oracle.switch(W, A, B, wl.scale, prev, new), A, B) for W, A, B in model]
+        prev = new
+    secs = time.perf_counter() - t1
+    log(f"cpu oracle, tiny fp32: {secs * 1e3:.1f} ms")
+    return {"what": "tiny fp32 workload: router + 16 switches, all threads", "value": wl.T / secs,
+            "unit": "switches/s", "cores": oracle.threads(), "sample": "in full"}
 
 
 def profile_kernels(torch, dlm, synth, n_switch, log):
@@ -627,6 +706,34 @@ def _sgmm_traffic_from(fetch_csv, write_csv, read):
     return out
 
 
+def _roofline_all(sw, sw70, sg):
+    """Every metric-bearing cell against 8 TB/s: the fused switch on the 7B- and
+    70B-shaped workloads (per launch) and the SGMM passes (segment, shrink, K-part
+    sum and expand together; per pass or step)."""
+    out = [{"workload": "7b-decode", "kernel": "switch_bf16_kernel<1,256>", "bound": "hbm",
+            "achieved": round(sw["achieved_launch_GBps"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": round(sw["achieved_launch_GBps"] * 1e9 / HBM_PEAK, 4),
+            "traffic": _traffic("switch_bf16_7b", sw["algo_bytes_per_launch"]),
+            "avg_launch_ms": round(sw["switch_ms"], 4)}]
+    if sw70 is not None:
+        out.append({"workload": "70b-decode", "kernel": "switch_wide_kernel<4,64>", "bound": "hbm",
+                    "achieved": round(sw70["achieved_launch_GBps"], 1), "peak": HBM_PEAK / 1e9,
+                    "unit": "GB/s", "frac": round(sw70["frac_of_hbm_peak"], 4),
+                    "traffic": sw70.get("traffic"), "avg_launch_ms": round(sw70["switch_ms"], 4)})
+    for key, name in (("prefill", "sgmm-prefill"), ("mixed_decode", "mixed-decode")):
+        r = sg.get(key)
+        if r is None:
+            continue
+        per = r["ms_per_pass"] if key == "prefill" else r["grouped_ms_per_step"]
+        out.append({"workload": name, "kernel": "sgmm pass: segment, shrink, K-part sum, expand", "bound": "hbm",
+                    "achieved": round(r["GBps"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                    "frac": round(r["frac_of_hbm_peak"], 4),
+                    "traffic": None if r.get("traffic") is None else round(
+                        r["traffic"]["read_per_step"] + r["traffic"]["write_per_step"]),
+                    "avg_ms": round(per, 4)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -711,6 +818,7 @@ def main():
                      "kernel": "switch_bf16_kernel<1,256>",
                      "avg_launch_ms": round(sw["switch_ms"], 4),
                      "algo_bytes_per_launch": sw["algo_bytes_per_launch"]},
+        "roofline_all": _roofline_all(sw, sw70, sg),
         "cpu_baseline": cpu,
         "switch": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in sw.items()},
         "switch_70b": None if sw70 is None else {k: (round(v, 4) if isinstance(v, float) else v)
