@@ -4,14 +4,15 @@
 // gather matrix multiplication"; this is the batched form of the same adapters.
 //
 // Launches:
-//   segment  (one workgroup) every row gets the key of its unordered expert
+//   segment  (one workgroup per 1024 rows; a count launch first when there
+//            are several) every row gets the key of its unordered expert
 //            pair; a stable counting sort lists the rows by key (perm, with
 //            each position's pair and gates beside it), so rows sharing
 //            experts sit next to each other.  The sorted list is cut into
-//            32-row tiles and each tile records the union of the experts its
-//            rows use (a bitmask).  Rows with two empty slots are left out.
-//            The same segmentation serves every problem of a grouped call
-//            (one routing decision per token for all layers).
+//            32-row tiles; the later kernels take each tile's expert union
+//            from its positions' pairs.  Rows with two empty slots are left
+//            out.  The same segmentation serves every problem of a grouped
+//            call (one routing decision per token for all layers).
 //   shrink   per (problem, 512-wide K slice, tile): the slice's partial
 //            v = x_rows A_U^T for the tile's experts U, bf16 MFMA 32x32x16 with
 //            M = tile rows (gathered through perm, staged in LDS), N = (expert,
@@ -43,13 +44,14 @@ SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob) {
     L.tiles_max = L.T_pad / 32;
     L.r_pad = (r + 15) / 16 * 16;
     L.max_ks = (int)((d_in_max + kSgmmKSlice - 1) / kSgmmKSlice);
-    (void)E;
     size_t o = 0;
     L.hdr = o;   o += 256;
     L.perm = o;  o += a256((size_t)L.T_pad * 4);
     L.epk = o;   o += a256((size_t)L.T_pad * 4);
     L.gpk = o;   o += a256((size_t)L.T_pad * 8);
-    L.tmask = o; o += a256((size_t)L.tiles_max * 4);
+    L.n_chunks = (L.T + kSgmmSegRows - 1) / kSgmmSegRows;
+    L.hist = o;  o += a256((size_t)L.n_chunks * (E + 1) * (E + 1) * 4);
+    L.cerr = o;  o += a256((size_t)L.n_chunks * 4);
     L.v = o;     o += a256((size_t)n_prob * L.max_ks * L.T_pad * 2 * L.r_pad * 4);
     L.total = o;
     return L;
@@ -57,7 +59,7 @@ SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob) {
 
 namespace {
 
-constexpr int kSegThreads = 1024;
+constexpr int kSegThreads = 1024;  // rows per segmentation chunk
 constexpr int kSegWaves = kSegThreads / kWave;
 constexpr int kMaxKeys = (32 + 1) * (32 + 1);
 
@@ -131,102 +133,119 @@ __device__ __forceinline__ int block_exscan(int v, int* s_tot, int& total) {
     return before + inc - v;
 }
 
-// One workgroup: a stable counting sort of the rows by key, all bookkeeping in
-// LDS.  Pass 1 counts the keys (and keeps the keys of the first kKeyCache rows
-// in LDS); their exclusive scan gives each key's first position.  Pass 2 takes
-// the rows in batches of kSegThreads, in order: a row's position = its key's
-// first position + rows of that key in earlier batches + in earlier waves of
-// this batch + earlier lanes of its wave with the same key (a lane's
-// same-key mask comes from one ballot per key bit, so the cost does not grow
-// with the number of distinct keys in the wave).  A batch's sets are loaded at
-// its start and first needed when the rows are written out.
-constexpr int kKeyCache = 8192;
-constexpr int kTileCache = kKeyCache / 32;
-__global__ __launch_bounds__(kSegThreads) void sgmm_segment_kernel(
-    const int32_t* __restrict__ idx, const float* __restrict__ g, int64_t T, int E, char* ws,
-    SgLayout L, int32_t* status_out) {
+// The segmentation is a stable counting sort of the rows by key, in chunks of
+// kSegThreads rows (one workgroup each):
+//   count  (only when there is more than one chunk) each chunk's key counts
+//          (LDS atomics) and whether it holds a bad set;
+//   place  each workgroup adds up, per key, every chunk's count (the key's
+//          total) and the earlier chunks' counts; an exclusive scan of the
+//          totals over the keys gives each key's first position.  A row's
+//          position = its key's first position + rows of that key in earlier
+//          chunks + in earlier waves of its chunk + earlier lanes of its wave
+//          with the same key (a lane's same-key mask is one ballot per key bit).
+//          A single-chunk batch counts its own rows here, so it needs one launch.
+// Each position gets its row, pair and gates, so the later kernels read a
+// tile's metadata in one round of independent loads; positions past the live
+// rows get row -1.  The first workgroup writes the header.
+__global__ __launch_bounds__(kSegThreads) void sgmm_seg_count(const int32_t* __restrict__ idx,
+                                                              const float* __restrict__ g, int64_t T, int E,
+                                                              char* ws, SgLayout L) {
+    int32_t* hist = (int32_t*)(ws + L.hist);
+    int32_t* cerr = (int32_t*)(ws + L.cerr);
+    __shared__ int s_cnt[kMaxKeys];
+    __shared__ int s_err;
+    const int tid = threadIdx.x;
+    const int nk = (E + 1) * (E + 1);
+    const int64_t chunk = blockIdx.x;
+    const int64_t t = chunk * kSegThreads + tid;
+    const SegRaw raw = seg_load(idx, g, t, T);
+    if (tid == 0) s_err = 0;
+    for (int k = tid; k < nk; k += kSegThreads) s_cnt[k] = 0;
+    __syncthreads();
+    const SegRow q = seg_row(raw, t < T, E);
+    if (q.bad) s_err = 1;
+    if (q.key >= 0) atomicAdd(&s_cnt[q.key], 1);
+    __syncthreads();
+    for (int k = tid; k < nk; k += kSegThreads) hist[chunk * nk + k] = s_cnt[k];
+    if (tid == 0) cerr[chunk] = s_err;
+}
+
+__global__ __launch_bounds__(kSegThreads) void sgmm_seg_place(const int32_t* __restrict__ idx,
+                                                              const float* __restrict__ g, int64_t T, int E,
+                                                              char* ws, SgLayout L, int32_t* status_out) {
     int32_t* hdr = (int32_t*)(ws + L.hdr);
     int32_t* perm = (int32_t*)(ws + L.perm);
     uint32_t* epk = (uint32_t*)(ws + L.epk);
     float* gpk = (float*)(ws + L.gpk);
-    uint32_t* tmask = (uint32_t*)(ws + L.tmask);
+    const int32_t* hist = (const int32_t*)(ws + L.hist);
+    const int32_t* cerr = (const int32_t*)(ws + L.cerr);
     __shared__ int s_err;
-    __shared__ int s_next[kMaxKeys];   // counts, then the next free position of each key
-    __shared__ int s_base[kMaxKeys];   // first position of each key in the current batch
-    __shared__ uint16_t s_wc[kSegWaves][kMaxKeys];  // per-wave counts of a batch, then
-                                                    // their exclusive prefix over waves
-    __shared__ int16_t s_key[kKeyCache];
-    __shared__ uint32_t s_tm[kTileCache];
-    __shared__ int s_tot[kSegWaves];
+    __shared__ int s_tot[kMaxKeys];    // rows of each key over all chunks
+    __shared__ int s_base[kMaxKeys];   // the key's first position, then this chunk's first
+    __shared__ uint16_t s_wc[kSegWaves][kMaxKeys];  // per-wave counts, then their prefix over waves
+    __shared__ int s_sum[kSegWaves];
     const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
     const int nk = (E + 1) * (E + 1);
     const int nbits = 32 - __builtin_clz((unsigned)(nk - 1));
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    const int64_t chunk = blockIdx.x, n_chunks = gridDim.x;
+    const int64_t t = chunk * kSegThreads + tid;
+    const SegRaw raw = seg_load(idx, g, t, T);  // first needed when the row is placed
     if (tid == 0) s_err = 0;
-    for (int k = tid; k < nk; k += kSegThreads) s_next[k] = 0;
-    for (int q = tid; q < kTileCache; q += kSegThreads) s_tm[q] = 0;
-    __syncthreads();
-
-    // pass 1: key counts (LDS atomics)
-    for (int64_t b0 = 0; b0 < T; b0 += 4 * kSegThreads) {
-        SegRaw raw[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) raw[j] = seg_load(idx, g, b0 + j * kSegThreads + tid, T);
-        __builtin_amdgcn_sched_barrier(0);  // all four rows' loads are issued first
-        SegRow q[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) q[j] = seg_row(raw[j], b0 + j * kSegThreads + tid < T, E);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t t = b0 + j * kSegThreads + tid;
-            if (q[j].bad) s_err = 1;
-            if (t < kKeyCache) s_key[t] = (int16_t)q[j].key;
-            if (q[j].key >= 0) atomicAdd(&s_next[q[j].key], 1);
+    for (int q = tid; q < kSegWaves * nk; q += kSegThreads) s_wc[q / nk][q % nk] = 0;
+    if (n_chunks == 1) {
+        for (int k = tid; k < nk; k += kSegThreads) s_tot[k] = 0;
+        __syncthreads();
+        const SegRow q = seg_row(raw, t < T, E);
+        if (q.bad) s_err = 1;
+        if (q.key >= 0) atomicAdd(&s_tot[q.key], 1);
+        for (int k = tid; k < nk; k += kSegThreads) s_base[k] = 0;
+    } else {
+        // every chunk's counts: the key's total and the earlier chunks' share
+        for (int k = tid; k < nk; k += kSegThreads) {
+            int tot = 0, bef = 0;
+            for (int64_t c = 0; c < n_chunks; ++c) {
+                const int v = gld(hist + c * nk + k);
+                tot += v;
+                bef += c < chunk ? v : 0;
+            }
+            s_tot[k] = tot;
+            s_base[k] = bef;
         }
+        int e = 0;
+        for (int64_t c = tid; c < n_chunks; c += kSegThreads) e |= gld(cerr + c);
+        if (e) s_err = 1;
     }
     __syncthreads();
     const int err = s_err;
 
-    // exclusive scan of the counts in key order (each thread owns a run of keys)
+    // exclusive scan of the totals in key order (each thread owns a run of keys)
     constexpr int kPer = (kMaxKeys + kSegThreads - 1) / kSegThreads;
     int cnt[kPer], run = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int k = tid * kPer + j;
-        cnt[j] = k < nk ? s_next[k] : 0;
+        cnt[j] = k < nk ? s_tot[k] : 0;
         run += cnt[j];
     }
     int n_pos;
-    int base = block_exscan(run, s_tot, n_pos);
+    int start = block_exscan(run, s_sum, n_pos);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int k = tid * kPer + j;
-        if (k < nk) s_next[k] = base;
-        base += cnt[j];
+        if (k < nk) s_base[k] += start;
+        start += cnt[j];
     }
     if (err) n_pos = 0;
-    const int n_tiles = (n_pos + 31) / 32;
-    const bool lds_masks = n_tiles <= kTileCache;
-    __syncthreads();
 
-    // pass 2: place the rows batch by batch
-    for (int64_t b0 = 0; !err && b0 < T; b0 += kSegThreads) {
-        const int64_t t = b0 + tid;
-        const SegRaw raw = seg_load(idx, g, t, T);  // first needed when the row is written
-        static_assert(kKeyCache % kSegThreads == 0, "key cache holds whole batches");
-        for (int q = tid; q < kSegWaves * nk; q += kSegThreads) s_wc[q / nk][q % nk] = 0;
-        __syncthreads();
-        int k;
-        if (b0 + kSegThreads <= kKeyCache)  // batch-uniform: keys from LDS, the loads stay in flight
-            k = t < T ? (int)s_key[t] : -1;
-        else
-            k = seg_row(raw, t < T, E).key;
+    if (!err) {
+        const SegRow cur = seg_row(raw, t < T, E);
+        const int k = cur.key;
         // stable rank within the wave and the wave's count of each key
         const uint64_t same = wave_match(k, nbits);
-        const int rk = (int)__popcll(same & lt_mask);
+        const int rk = (int)__popcll(same & ((1ull << lane) - 1ull));
         if (same && rk == 0) s_wc[w][k] = (uint16_t)__popcll(same);
         __syncthreads();
-        // rows of each key in earlier waves of the batch, in wave order
+        // rows of each key in earlier waves of the chunk, in wave order
         for (int kk = tid; kk < nk; kk += kSegThreads) {
             int acc = 0;
             for (int i = 0; i < kSegWaves; ++i) {
@@ -234,61 +253,27 @@ __global__ __launch_bounds__(kSegThreads) void sgmm_segment_kernel(
                 s_wc[i][kk] = (uint16_t)acc;
                 acc += c;
             }
-            s_base[kk] = s_next[kk];
-            s_next[kk] += acc;
         }
         __syncthreads();
         if (k >= 0) {
-            const SegRow cur = seg_row(raw, true, E);
             const int64_t p = (int64_t)s_base[k] + s_wc[w][k] + rk;
             perm[p] = (int32_t)t;
             epk[p] = ((uint32_t)cur.e0 & 0xffffu) | ((uint32_t)cur.e1 << 16);
             gpk[2 * p] = cur.e0 >= 0 ? cur.g0 : 0.f;
             gpk[2 * p + 1] = cur.e1 >= 0 ? cur.g1 : 0.f;
-            if (lds_masks) {
-                const uint32_t m = (cur.e0 >= 0 ? 1u << cur.e0 : 0u) | (cur.e1 >= 0 ? 1u << cur.e1 : 0u);
-                atomicOr(&s_tm[p >> 5], m);
-            }
         }
-        // every wave has read s_base / s_wc for this batch before the next
-        // batch clears the per-wave counts
-        __syncthreads();
     }
-    for (int64_t p = n_pos + tid; p < L.T_pad; p += kSegThreads) {
+    // positions past the live rows, split over the workgroups
+    for (int64_t p = n_pos + chunk * kSegThreads + tid; p < L.T_pad; p += n_chunks * kSegThreads) {
         perm[p] = -1;
         epk[p] = 0xffffffffu;
         gpk[2 * p] = 0.f;
         gpk[2 * p + 1] = 0.f;
     }
-    __syncthreads();
-
-    // tile masks: from LDS, or (more tiles than LDS keeps) each half-wave ORs
-    // the expert bits of one tile's 32 positions read back from epk
-    if (lds_masks) {
-        for (int q = tid; q < n_tiles; q += kSegThreads) tmask[q] = s_tm[q];
-    } else {
-        for (int64_t q0 = 2 * w; q0 < n_tiles; q0 += 8 * kSegWaves) {
-            uint32_t m[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t q = q0 + 2 * kSegWaves * j + (lane >> 5);
-                const uint32_t ep = q < n_tiles ? epk[q * 32 + (lane & 31)] : 0xffffffffu;
-                const int e0 = (int16_t)(ep & 0xffffu), e1 = (int16_t)(ep >> 16);
-                m[j] = (e0 >= 0 ? 1u << e0 : 0u) | (e1 >= 0 ? 1u << e1 : 0u);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) m[j] |= __shfl_xor(m[j], o, kWave);
-                const int64_t q = q0 + 2 * kSegWaves * j + (lane >> 5);
-                if ((lane & 31) == 0 && q < n_tiles) tmask[q] = m[j];
-            }
-        }
-    }
-    if (tid == 0) {
+    if (chunk == 0 && tid == 0) {
         hdr[SG_ERR] = err;
         hdr[SG_NPOS] = n_pos;
-        hdr[SG_NTILES] = n_tiles;
+        hdr[SG_NTILES] = (n_pos + 31) / 32;
         if (status_out) *status_out = err;
     }
 }
@@ -364,7 +349,6 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
     const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
-    const uint32_t* tmask = (const uint32_t*)(a.ws + a.L.tmask);
     float* v = (float*)(a.ws + a.L.v) + gks * a.L.T_pad * 2 * RPAD;
 
     __shared__ __attribute__((aligned(16))) uint16_t s_x[kXRows * kSgmmKSlice];
@@ -372,20 +356,24 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     __shared__ int s_nU;
     __shared__ int s_row[kXRows], s_e0[kXRows], s_e1[kXRows];
     const int tid = threadIdx.x;
-    if (tid < kXRows) {
-        const bool in = tile0 + tid / 32 < n_tiles;
-        const int p = tile0 * 32 + tid;
-        const int row = in ? gld(perm + p) : -1;
-        const uint32_t ep = in ? gld(epk + p) : 0xffffffffu;
-        s_row[tid] = row;
-        s_e0[tid] = (int16_t)(ep & 0xffffu);
-        s_e1[tid] = (int16_t)(ep >> 16);
-    }
-    if (tid == 0) {
+    static_assert(kXRows <= kWave, "one wave reads the tile's rows");
+    if (tid < kWave) {
+        // the tiles' rows and slots; their expert union from a wave OR
         uint32_t m = 0;
-        for (int j = 0; j < kTM; ++j)
-            if (tile0 + j < n_tiles) m |= gld(tmask + tile0 + j);
-        s_nU = mask_list(m, s_U);
+        if (tid < kXRows) {
+            const bool in = tile0 + tid / 32 < n_tiles;
+            const int p = tile0 * 32 + tid;
+            const int row = in ? gld(perm + p) : -1;
+            const uint32_t ep = in ? gld(epk + p) : 0xffffffffu;
+            const int e0 = (int16_t)(ep & 0xffffu), e1 = (int16_t)(ep >> 16);
+            s_row[tid] = row;
+            s_e0[tid] = e0;
+            s_e1[tid] = e1;
+            m = (e0 >= 0 ? 1u << e0 : 0u) | (e1 >= 0 ? 1u << e1 : 0u);
+        }
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) m |= __shfl_xor(m, o, kWave);
+        if (tid == 0) s_nU = mask_list(m, s_U);
     }
     __syncthreads();
 
@@ -576,7 +564,6 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
     const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
     const float* gpk = (const float*)(a.ws + a.L.gpk);
-    const uint32_t* tmask = (const uint32_t*)(a.ws + a.L.tmask);
     const int tid = threadIdx.x;
     const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
     const int lr = lane >> 3, lc = lane & 7;
@@ -589,7 +576,6 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     for (int i = 0; i < 4; ++i) yrow[i] = gld(perm + tile * 32 + 8 * i + lr);
     const uint32_t ep = gld(epk + tile * 32 + n);
     const float g0 = gld(gpk + 2 * (tile * 32 + n)), g1 = gld(gpk + 2 * (tile * 32 + n) + 1);
-    const uint32_t tm = tid == 0 ? gld(tmask + tile) : 0u;
     const int err = gld(hdr + SG_ERR), n_tiles = gld(hdr + SG_NTILES);
     const int prob = a.descs ? gld(a.cb_owner + t / nt) : 0;
     if (err || tile >= n_tiles) return;
@@ -618,7 +604,14 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     };
     u32x4 ycur[4], ynxt[4];
     if (nblk > 0) load_y(ycur, 0);
-    if (tid == 0) s_nU = mask_list(tm, s_U);
+    if (w == 0) {
+        // the tile's expert union: OR of its positions' pairs (lane n holds position n)
+        const int f0 = (int16_t)(ep & 0xffffu), f1 = (int16_t)(ep >> 16);
+        uint32_t m = (f0 >= 0 ? 1u << f0 : 0u) | (f1 >= 0 ? 1u << f1 : 0u);
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) m |= __shfl_xor(m, o, kWave);
+        if (lane == 0) s_nU = mask_list(m, s_U);
+    }
     __syncthreads();
     const int nU = uniform(s_nU);
 
@@ -922,6 +915,7 @@ hipError_t launch_sgmm_pack_a(const void* A, void* Ap, int E, int r, int64_t d_i
 // Every grid of the call fits (checked before the first launch, so a refused
 // call leaves the workspace and y untouched).
 static bool sgmm_grids_fit(const SgmmArgs& a, int dtype) {
+    if (!grid_fits(a.L.n_chunks, kSegThreads)) return false;
     if (dtype == 1) {
         const int64_t n_units = a.total_ks * ((a.L.tiles_max + kTM - 1) / kTM);
         return grid_fits(8 * ((n_units + 7) / 8), 256) &&
@@ -934,7 +928,15 @@ static bool sgmm_grids_fit(const SgmmArgs& a, int dtype) {
 
 hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
     if (!sgmm_grids_fit(a, dtype)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(sgmm_segment_kernel, dim3(1), dim3(kSegThreads), 0, s, a.idx, a.g, a.T, a.E,
+    static_assert(kSegThreads == kSgmmSegRows, "segmentation chunk");
+    const int64_t n_chunks = a.L.n_chunks;
+    if (n_chunks > 1) {
+        hipLaunchKernelGGL(sgmm_seg_count, dim3((unsigned)n_chunks), dim3(kSegThreads), 0, s, a.idx, a.g, a.T, a.E,
+                           a.ws, a.L);
+        hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+    }
+    hipLaunchKernelGGL(sgmm_seg_place, dim3((unsigned)n_chunks), dim3(kSegThreads), 0, s, a.idx, a.g, a.T, a.E,
                        a.ws, a.L, a.status_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -26,15 +26,19 @@ struct SgDesc {
 struct SgLayout {
     // perm: row at each sorted position (-1 = padding); epk: its expert pair
     // (slot 0 in the low 16 bits, slot 1 in the high, -1 = empty); gpk: its two
-    // gates; tmask: the experts each 32-row tile uses; v: the shrink's results
-    size_t hdr, perm, epk, gpk, tmask, v, total;
-    int64_t T, T_pad, tiles_max;
+    // gates; hist, cerr: each segmentation chunk's key counts and bad-set flag;
+    // v: the shrink's results
+    size_t hdr, perm, epk, gpk, hist, cerr, v, total;
+    int64_t T, T_pad, tiles_max, n_chunks;
     int r_pad;
     int max_ks;  // K slices of the widest problem
 };
 // Width of one shrink K slice.
 constexpr int kSgmmKSlice = 512;
 SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob);
+
+// Rows per segmentation chunk (one workgroup of the segmentation kernels).
+constexpr int kSgmmSegRows = 1024;
 
 // Output columns one SGMM expand work item covers (4 waves x 4 x 64).
 constexpr int kSgmmExpandCols = 1024;
