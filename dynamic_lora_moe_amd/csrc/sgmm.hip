@@ -331,19 +331,8 @@ __device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((c
 // dummy row whose products reach only accumulator entries that are never
 // stored, and k past d_in reads a clamped address whose value is replaced by 0.
 template <int R16, bool PK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R16 == 2 ? 3 : 4)))
-void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
+__device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int tile0, int n_tiles) {
     constexpr int RPAD = R16 * 16;
-    const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
-    if (gld(hdr + SG_ERR)) return;
-    const int64_t bid = blockIdx.x;
-    const int64_t t = (bid & 7) * per_xcd + (bid >> 3);
-    if (t >= n_units) return;
-    const int64_t ntp = (a.L.tiles_max + kTM - 1) / kTM;
-    const int64_t gks = t / ntp;  // slice index over all problems
-    const int tile0 = (int)(t - gks * ntp) * kTM;
-    const int n_tiles = gld(hdr + SG_NTILES);
-    if (tile0 >= n_tiles) return;
     const int prob = a.descs ? gld(a.ks_owner + gks) : 0;
     const SgDesc D = a.descs ? a.descs[prob] : a.single;
     const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
@@ -534,6 +523,27 @@ void sgmm_shrink_bf16(SgmmArgs a, int64_t n_units, int64_t per_xcd) {
     }
 }
 
+// Work items are the live ones only: (problem, K slice, tile) over the tiles
+// the segmentation filled (released rows are left out), numbered with the
+// tile fastest and spread over the 8 XCDs.  The grid is sized for the largest
+// batch the workspace holds (the live count is known on the device only);
+// workgroups past the live items exit after one header load, and as the
+// dispatcher starts workgroups in index order they come last.
+template <int R16, bool PK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R16 == 2 ? 3 : 4)))
+void sgmm_shrink_bf16(SgmmArgs a) {
+    const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
+    const int n_tiles = uniform(gld(hdr + SG_NTILES));
+    if (gld(hdr + SG_ERR)) return;
+    const int64_t n_live = a.total_ks * n_tiles, per = (n_live + 7) / 8;
+    const int64_t bid = blockIdx.x, j = bid >> 3;
+    if (j >= per) return;
+    const int64_t t = (bid & 7) * per + j;
+    if (t >= n_live) return;
+    const int64_t gks = t / n_tiles;  // slice index over all problems
+    shrink_item<R16, PK>(a, gks, (int)(t - gks * n_tiles), n_tiles);
+}
+
 // ---- expand (bf16, MFMA) -----------------------------------------------------
 
 __device__ __forceinline__ int perm_col(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
@@ -548,23 +558,15 @@ static_assert(kECols == kSgmmExpandCols, "expand column group");
 // unions rebuild them per column block in registers.
 constexpr int kQLds = 16;
 
+// work item = (problem, kECols-column group cgg over all problems, tile) with
+// the tile fastest: neighbouring work items (same XCD) reuse the same B column
+// slices.
 template <int R16, bool RVEC>
-__global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_xcd) {
+__device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int tile) {
     constexpr int RPAD = R16 * 16;
-    const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
-    const int64_t bid = blockIdx.x;
-    const int64_t t = (bid & 7) * per_xcd + (bid >> 3);
-    if (t >= a.n_expand_units) return;
-    // work item = (problem, kECols-column group, tile) with the tile fastest:
-    // neighbouring work items (same XCD) reuse the same B column slices.  A
-    // problem's first item is a multiple of the tile count, so the tile is
-    // known before the problem's descriptor.
-    const int64_t nt = a.L.tiles_max;
-    const int tile = (int)(t % nt);
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
     const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
     const float* gpk = (const float*)(a.ws + a.L.gpk);
-    const int tid = threadIdx.x;
     const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
     const int lr = lane >> 3, lc = lane & 7;
     // every load whose address does not depend on another load goes out
@@ -576,11 +578,9 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     for (int i = 0; i < 4; ++i) yrow[i] = gld(perm + tile * 32 + 8 * i + lr);
     const uint32_t ep = gld(epk + tile * 32 + n);
     const float g0 = gld(gpk + 2 * (tile * 32 + n)), g1 = gld(gpk + 2 * (tile * 32 + n) + 1);
-    const int err = gld(hdr + SG_ERR), n_tiles = gld(hdr + SG_NTILES);
-    const int prob = a.descs ? gld(a.cb_owner + t / nt) : 0;
-    if (err || tile >= n_tiles) return;
+    const int prob = a.descs ? gld(a.cb_owner + cgg) : 0;
     const SgDesc D = a.descs ? a.descs[prob] : a.single;
-    const int cg = (int)(t / nt - D.unit0);
+    const int cg = (int)(cgg - D.unit0);
     const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * a.L.T_pad * 2 * RPAD;
 
     __shared__ int s_U[32];
@@ -762,6 +762,21 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a, int64_t per_
     }
 }
 
+// Live work items only, as for the shrink: (column group, live tile).
+template <int R16, bool RVEC>
+__global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a) {
+    const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
+    const int n_tiles = uniform(gld(hdr + SG_NTILES));
+    if (gld(hdr + SG_ERR)) return;
+    const int64_t n_live = a.total_cb * n_tiles, per = (n_live + 7) / 8;
+    const int64_t bid = blockIdx.x, j = bid >> 3;
+    if (j >= per) return;
+    const int64_t t = (bid & 7) * per + j;
+    if (t >= n_live) return;
+    const int64_t cgg = t / n_tiles;
+    expand_item<R16, RVEC>(a, cgg, (int)(t - cgg * n_tiles));
+}
+
 // ---- element-wise path (fp32) ------------------------------------------------
 
 template <typename T> __device__ __forceinline__ float ldf(const T* p, int64_t i);
@@ -874,16 +889,16 @@ __global__ __launch_bounds__(256) void sgmm_pack_a_kernel(const uint16_t* __rest
     st128(Ap + 8 * i, ld128(A + ((e * r + rho) * nq + kq) * 8));
 }
 
+// Grid for at most max_items work items (a multiple of 8: one share per XCD).
+inline int64_t item_grid(int64_t max_items) { return 8 * ((max_items + 7) / 8); }
+
 template <int R16>
 hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
-    const int64_t n_units = a.total_ks * ((a.L.tiles_max + kTM - 1) / kTM);
-    const int64_t sh_per_xcd = (n_units + 7) / 8;
+    const dim3 gs((unsigned)item_grid(a.total_ks * a.L.tiles_max));
     if (a.packed)
-        hipLaunchKernelGGL((sgmm_shrink_bf16<R16, true>), dim3((unsigned)(8 * sh_per_xcd)), dim3(256), 0, s,
-                           a, n_units, sh_per_xcd);
+        hipLaunchKernelGGL((sgmm_shrink_bf16<R16, true>), gs, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((sgmm_shrink_bf16<R16, false>), dim3((unsigned)(8 * sh_per_xcd)), dim3(256), 0, s,
-                           a, n_units, sh_per_xcd);
+        hipLaunchKernelGGL((sgmm_shrink_bf16<R16, false>), gs, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.total_ks > a.n_prob) {  // some problem has more than one K slice
@@ -892,13 +907,11 @@ hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t per_xcd = (a.n_expand_units + 7) / 8;
+    const dim3 ge((unsigned)item_grid(a.n_expand_units));
     if (a.r % 8 == 0)
-        hipLaunchKernelGGL((sgmm_expand_bf16<R16, true>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, a,
-                           per_xcd);
+        hipLaunchKernelGGL((sgmm_expand_bf16<R16, true>), ge, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((sgmm_expand_bf16<R16, false>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, a,
-                           per_xcd);
+        hipLaunchKernelGGL((sgmm_expand_bf16<R16, false>), ge, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -917,10 +930,7 @@ hipError_t launch_sgmm_pack_a(const void* A, void* Ap, int E, int r, int64_t d_i
 static bool sgmm_grids_fit(const SgmmArgs& a, int dtype) {
     if (!grid_fits(a.L.n_chunks, kSegThreads)) return false;
     if (dtype == 1) {
-        const int64_t n_units = a.total_ks * ((a.L.tiles_max + kTM - 1) / kTM);
-        return grid_fits(8 * ((n_units + 7) / 8), 256) &&
-               grid_fits((a.L.T_pad * 2 * a.L.r_pad / 4 + 255) / 256, 256) &&
-               grid_fits(8 * ((a.n_expand_units + 7) / 8), 256);
+        return grid_fits((a.L.T_pad * 2 * a.L.r_pad / 4 + 255) / 256, 256);
     }
     return grid_fits((a.L.T_pad * 2 * a.r + 255) / 256, 256) &&
            grid_fits((a.L.T_pad * a.d_out_max + 255) / 256, 256);

@@ -226,6 +226,50 @@ def test_mixed_decode_grouped_sampled():
     grp.close()
 
 
+def test_mixed_decode_released_rows_full_step():
+    """Rows that release their adapters (both slots empty) at the mixed decode
+    workload's full size: all 224 projections (32 layers x 7) as one group of 64
+    rows on one workspace, three steps in a row -- every row live, then the upper
+    half released, then every third row released and every fifth live row with
+    one slot only.  The live rows of every projection match the oracle element
+    by element; every released row of y is left bitwise as it was."""
+    wl = synth.WORKLOADS["mixed-decode"]
+    print("[workload] mixed-decode released rows: building", flush=True)
+    probs = synth.sgmm_problems(wl)
+    idx, g = synth.batched_sets(wl)
+    ys = [y0.clone() for *_, y0 in probs]
+    grp = dlm.SgmmGroup([(x, A, B, y) for (_, _, x, A, B, _), y in zip(probs, ys)], wl.E, wl.r, wl.scale)
+    ws = grp.workspace(wl.T)
+    rows = np.arange(wl.T)
+    cases = []
+    i0, g0 = idx[5].clone(), g[5].clone()
+    cases.append(("all live", i0, g0))
+    i1, g1 = idx[6].clone(), g[6].clone()
+    i1[wl.T // 2:], g1[wl.T // 2:] = -1, 0.0
+    cases.append(("upper half released", i1, g1))
+    i2, g2 = idx[7].clone(), g[7].clone()
+    i2[0::3], g2[0::3] = -1, 0.0
+    one = np.setdiff1d(np.arange(1, wl.T, 5), np.arange(0, wl.T, 3))
+    i2[one, 1], g2[one, 1] = -1, 0.0
+    cases.append(("every third released", i2, g2))
+    for what, ic, gc_ in cases:
+        for y, (*_, y0) in zip(ys, probs):
+            y.copy_(y0)
+        grp.run(ic.cuda(), gc_.cuda(), workspace=ws)
+        assert dlm.sgmm_status(ws) == dlm.DLM_OK
+        torch.cuda.synchronize()
+        released = (ic == -1).all(1).numpy()
+        print(f"[workload] mixed-decode {what}: {int(released.sum())} released rows, checking", flush=True)
+        rel = torch.from_numpy(np.nonzero(released)[0]).cuda()
+        for (l, name, *_, y0), y in zip(probs, ys):
+            assert torch.equal(y[rel], y0[rel]), f"{what}: released rows of L{l}.{name} changed"
+        _sgmm_check_rows(wl, probs, ys, ic, gc_, rows[~released], f"mixed {what}")
+    grp.close()
+    del probs, ys
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def test_7b_decode_fused_switch_and_product_per_layer_sampled():
     """The decode loop's fused form at its full size: one layer handle of the
     7B-shaped workload (7 projections), dlm_switch_gemv with the router's device
