@@ -147,16 +147,22 @@ def bench_switch(torch, dlm, synth, steps, warmup, log):
 
 
 def bench_decode_loop(torch, dlm, synth, n_tokens, log):
-    """Per-token decode steps on the 7B-shaped workload: router (T = 1) -> switch ->
-    the merged-weight product of every adapted projection, layer by layer, on one
-    stream with the expert sets kept on the device.
-      unfused: router, one switch over all 224 weights, then one product launch per
-               layer (W read twice, written once: 3 x 12.95 GB per token);
-      fused:   router, then per layer the switch fused with the product (2 launches:
-               W read once, written once, plus partial sums).
+    """Per-token decode steps on the 7B-shaped workload, on one stream:
+      base:     the product of every adapted projection with the unchanged base
+                weights, one launch per layer (no adapters: the reference point);
+      layerwise / layerwise_grouped: per-layer routing with unmerged adapters
+                (dynamic_lora_moe_amd.layerwise): per layer a router launch
+                (T = 1, the layer's own router weights, the token's x), the base
+                product, and the adapters as one SGMM call per projection (T = 1)
+                or one grouped SGMM per layer -- W read once per token;
+      unfused:  pre-gated: router once, one switch over all 224 weights, then one
+                product launch per layer (W read twice, written once: 3 x 12.95 GB);
+      fused:    pre-gated: router once, then per layer the switch fused with the
+                product (2 launches: W read once, written once, plus partial sums).
     Each is timed eagerly and replayed from HIP graphs (one per set-buffer parity);
     inputs are synthetic per (layer, projection), tokens come from the router's
-    x.  W returns to its starting sets between the two variants (unmerge)."""
+    x.  W returns to its starting sets after each pre-gated variant (unmerge)."""
+    from dynamic_lora_moe_amd.layerwise import LayerwiseDecode
     wl = synth.WORKLOADS["7b-decode"]
     log(f"decode loop: building {wl.name}")
     model = synth.switch_model(wl)
@@ -173,12 +179,25 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
         h.bind_vectors(xs, yv)
         layers.append(h)
         ys.append((xs, yv))
+    routers = [synth.normal_device((wl.d_model, wl.E), 0.02, wl.dtype, "cuda", wl.cfg_id, "Wr", l)
+               for l in range(wl.layers)]
+    per_layer = [[(W, A, B) for _, _, W, A, B in model[l * P:(l + 1) * P]] for l in range(wl.layers)]
+    lw = {"layerwise": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r, wl.scale),
+          "layerwise_grouped": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r, wl.scale,
+                                               grouped=True)}
     x_tok = torch.empty((1, wl.d_model), dtype=wl.dtype, device="cuda")
     idx = [torch.zeros((1, 2), dtype=torch.int32, device="cuda") for _ in range(2)]
     g = [torch.zeros((1, 2), dtype=torch.float32, device="cuda") for _ in range(2)]
     s = torch.cuda.Stream()
 
     def step(kind, cur, first, stream):
+        if kind == "base":
+            for h in layers:
+                h.gemv(stream=stream)
+            return
+        if kind in lw:
+            lw[kind].step(x_tok, stream=stream)
+            return
         dlm.pregate(x_tok, Wr, idx=idx[cur], g=g[cur], stream=stream)
         new = (idx[cur][0], g[cur][0])
         old = None if first else (idx[1 - cur][0], g[1 - cur][0])
@@ -192,7 +211,8 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
 
     res = {"tokens": n_tokens}
     w_bytes = wl.switch_w_elems() * 2
-    for kind in ("unfused", "fused"):
+    pre_gated = ("unfused", "fused")
+    for kind in ("base", "layerwise", "layerwise_grouped") + pre_gated:
         out = {}
         with torch.cuda.stream(s):
             # eager: token 0 from the merged-in-nothing state, then n-1 switches
@@ -225,23 +245,35 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
             b.record(s)
         torch.cuda.synchronize()
         out["ms_per_token_graph"] = a.elapsed_time(b) / n_tokens
-        lpt = 1 + (whole.launches_per_switch() + wl.layers if kind == "unfused"
-                   else wl.layers * layers[0].launches_per_switch_gemv())
+        if kind == "base":
+            lpt = wl.layers
+        elif kind in lw:
+            lpt = lw[kind].launches_per_token()
+        else:
+            lpt = 1 + (whole.launches_per_switch() + wl.layers if kind == "unfused"
+                       else wl.layers * layers[0].launches_per_switch_gemv())
         out["launches_per_token"] = lpt
-        out["weight_bytes_per_token"] = (3 if kind == "unfused" else 2) * w_bytes
+        out["weight_bytes_per_token"] = {"unfused": 3, "fused": 2}.get(kind, 1) * w_bytes
         out["GBps_graph"] = out["weight_bytes_per_token"] / out["ms_per_token_graph"] / 1e6
-        # back to the starting weights: remove the last token's set
-        cur_last = cur
-        whole.switch((idx[cur_last][0], g[cur_last][0]), None)
+        if kind in pre_gated:
+            # back to the starting weights: remove the last token's set
+            cur_last = cur
+            whole.switch((idx[cur_last][0], g[cur_last][0]), None)
         torch.cuda.synchronize()
         assert whole.status() == dlm.DLM_OK and all(h.status() == dlm.DLM_OK for h in layers)
+        if kind in lw:
+            assert lw[kind].status() == dlm.DLM_OK
+        if "base" in res:
+            out["time_vs_base_graph"] = out["ms_per_token_graph"] / res["base"]["ms_per_token_graph"]
         res[kind] = out
         log(f"decode loop {kind}: {out}")
         del graphs
     for h in layers:
         h.close()
+    for v in lw.values():
+        v.close()
     whole.close()
-    del model, ys
+    del model, ys, lw
     torch.cuda.empty_cache()
     return res
 

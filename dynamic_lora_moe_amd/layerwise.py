@@ -1,0 +1,120 @@
+"""Layer-wise dynamic adapters: the per-layer routing form that token-level
+pre-gating replaces, built from this library's kernels only.
+
+AdaFuse (problem statement and experiments sections) attributes the decode
+slowdown of earlier dynamic-adapter systems to this form: every layer makes its
+own routing decision and applies its adapters unmerged, so a token costs many
+small sequential kernel launches.  Per token and per layer l:
+
+  1. router: dlm_pregate on the layer's router input with the layer's own
+     router weights Wr_l (T = 1) -> the layer's top-2 set (idx_l, g_l);
+  2. base product: dlm_gemv, y_base = W x for every adapted projection of the
+     layer, on the unchanged base weights (fp32 outputs);
+  3. unmerged adapters: y_lora += s g_k (x A_k^T) B_k^T for the layer's set,
+     either one dlm_sgmm call per projection (T = 1; the per-module form) or one
+     grouped SGMM per layer (``grouped=True``: one segmentation for the
+     layer's projections).
+
+The layer's adapted output is y_base + y_lora; the two stay in separate
+buffers (the adding is one more element-wise pass, not timed here).  Nothing
+here computes: each step is an entry point of libdlm.so, and the class only
+holds buffers and issues the calls in order on one stream.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import DLM_OK, Layers, SgmmGroup, pregate, sgmm, sgmm_launches, sgmm_status, sgmm_workspace
+
+
+class LayerwiseDecode:
+    """One decode token through every layer with per-layer routing.
+
+    layers:  per layer, the adapted projections [(W, A, B)] (W [d_out][d_in],
+             A [E][r][d_in], B [E][d_out][r], one dtype); W is never modified.
+    routers: per layer, Wr_l [d_router][E] (the weights' dtype).
+    xs:      per layer, one input vector [d_in] per projection (the weights'
+             dtype), read in place by the base product and the adapters.
+    """
+
+    def __init__(self, layers, routers, xs, E: int, r: int, scale: float, grouped: bool = False):
+        if not len(layers) == len(routers) == len(xs):
+            raise ValueError("one projection list, one router and one input list per layer")
+        self.E, self.r, self.scale, self.grouped = E, r, float(scale), grouped
+        self.routers = list(routers)
+        self.xs = [list(x) for x in xs]
+        W0 = layers[0][0][0]
+        dev, dt = W0.device, W0.dtype
+        self.base, self.y_base, self.y_lora, self.groups = [], [], [], []
+        self.idx = [torch.zeros((1, 2), dtype=torch.int32, device=dev) for _ in layers]
+        self.g = [torch.zeros((1, 2), dtype=torch.float32, device=dev) for _ in layers]
+        self.projs = [list(p) for p in layers]
+        d_in_max = 0
+        for projs, xl in zip(self.projs, self.xs):
+            if len(xl) != len(projs):
+                raise ValueError("one input vector per projection")
+            h = Layers(projs, E, r, scale)
+            yb = [torch.zeros(W.shape[0], dtype=torch.float32, device=dev) for W, _, _ in projs]
+            h.bind_vectors(xl, yb)
+            yl = [torch.zeros((1, W.shape[0]), dtype=dt, device=dev) for W, _, _ in projs]
+            self.base.append(h)
+            self.y_base.append(yb)
+            self.y_lora.append(yl)
+            if grouped:
+                self.groups.append(SgmmGroup([(x[None], A, B, y) for (W, A, B), x, y in zip(projs, xl, yl)],
+                                             E, r, scale))
+            d_in_max = max(d_in_max, max(W.shape[1] for W, _, _ in projs))
+        self.d_in_max, self.dtype = d_in_max, dt
+        n_ws = max(len(p) for p in self.projs) if grouped else 1
+        self.ws = sgmm_workspace(1, d_in_max, E, r, n_ws, dev)
+
+    def step(self, router_x, stream=None):
+        """Enqueue one token: router_x [1][d_router] is every layer's router input."""
+        for l, projs in enumerate(self.projs):
+            pregate(router_x, self.routers[l], idx=self.idx[l], g=self.g[l], stream=stream)
+            self.base[l].gemv(stream=stream)
+            if self.grouped:
+                self.groups[l].run(self.idx[l], self.g[l], workspace=self.ws, stream=stream)
+            else:
+                for (W, A, B), x, y in zip(projs, self.xs[l], self.y_lora[l]):
+                    sgmm(x[None], self.idx[l], self.g[l], A, B, y, self.scale, workspace=self.ws,
+                         stream=stream)
+
+    def reset_lora(self):
+        """Zero the adapter outputs (they accumulate across tokens)."""
+        for yl in self.y_lora:
+            for y in yl:
+                y.zero_()
+
+    def launches_per_token(self) -> int:
+        """Kernel launches one step() makes: per layer the router (1), the base
+        product (dlm_gemv: 1) and the adapters' SGMM launches."""
+        n = 0
+        for projs in self.projs:
+            if self.grouped:
+                sg = sgmm_launches(1, max(W.shape[1] for W, _, _ in projs), self.dtype)
+            else:
+                sg = sum(sgmm_launches(1, W.shape[1], self.dtype) for W, _, _ in projs)
+            n += 2 + sg
+        return n
+
+    def status(self, stream=None) -> int:
+        """DLM_OK, or the first failure the device reported (sets, weights)."""
+        s = sgmm_status(self.ws, stream)
+        if s != DLM_OK:
+            return s
+        for h in self.base:
+            s = h.status(stream)
+            if s != DLM_OK:
+                return s
+        return DLM_OK
+
+    def close(self):
+        for h in self.base:
+            h.close()
+        for grp in self.groups:
+            grp.close()
+        self.base, self.groups = [], []
+
+
+__all__ = ["LayerwiseDecode"]

@@ -242,7 +242,8 @@ int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r,
  *   idx [T][2] int32 (-1 = empty slot), g [T][2] fp32,
  *   A [E][r][d_in], B [E][d_out][r].
  * Launches: segment (rows sorted by their unordered expert pair, 32-row
- * tiles, the experts each tile uses), shrink (v = x A^T on the tile's experts
+ * tiles, the experts each tile uses; a per-1024-row count launch first when
+ * T > 1024), shrink (v = x A^T on the tile's experts
  * over 512-wide K slices, bf16 MFMA, fp32 partial results kept in the
  * workspace), a K-slice sum in a fixed order (only when d_in > 512) and
  * expand (y += (s g v) B^T, MFMA with v*s*g split into two bf16 terms, fp32
@@ -332,6 +333,16 @@ int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, in
  * *code (host) = DLM_OK or DLM_EDEVICE.
  */
 int dlm_sgmm_status(void* workspace, int32_t* code, void* stream);
+
+/*
+ * Number of kernel launches one dlm_sgmm, dlm_sgmm_noalloc or
+ * dlm_sgmm_group_run call makes for T rows and problems with d_in up to
+ * d_in_max: 0 for T = 0, else the segmentation (2 launches when T > 1024,
+ * else 1), the shrink, the K-slice sum (bf16 with d_in_max > 512 only) and the
+ * expand.  Returns -1 (with the last error set) for a negative T, d_in_max < 1
+ * or an unknown dtype.
+ */
+int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t dtype);
 
 #ifdef __cplusplus
 }

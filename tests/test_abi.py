@@ -119,6 +119,25 @@ def test_product_entry_points_validation(lib):
     assert lib.dlm_layers_repack(None, None) == dlm.DLM_EINVAL
 
 
+def test_sgmm_launch_count(lib):
+    f = lib.dlm_sgmm_launches
+    assert f(0, 4096, dlm.DLM_BF16) == 0
+    # segment, shrink, K-slice sum, expand
+    assert f(1, 4096, dlm.DLM_BF16) == 4
+    assert f(1024, 4096, dlm.DLM_BF16) == 4
+    # no K-slice sum for a single 512-wide slice
+    assert f(64, 512, dlm.DLM_BF16) == 3
+    assert f(64, 513, dlm.DLM_BF16) == 4
+    # a count launch before the placement above 1024 rows
+    assert f(1025, 4096, dlm.DLM_BF16) == 5
+    assert f(16, 64, dlm.DLM_F32) == 3
+    assert f(4096, 64, dlm.DLM_F32) == 4
+    assert f(-1, 64, dlm.DLM_BF16) == -1 and "sgmm_launches" in _err(lib)
+    assert f(4, 0, dlm.DLM_BF16) == -1
+    assert f(4, 64, 7) == -1
+    assert dlm.sgmm_launches(1, 11008) == 4
+
+
 def test_sgmm_workspace_size(lib):
     b = C.c_size_t(0)
     assert lib.dlm_sgmm_workspace_size(4096, 11008, 8, 16, 7, C.byref(b)) == dlm.DLM_OK

@@ -270,6 +270,86 @@ def test_mixed_decode_released_rows_full_step():
     torch.cuda.empty_cache()
 
 
+def _layerwise_outputs(lw):
+    return ([t.clone() for t in lw.idx], [t.clone() for t in lw.g],
+            [[y.clone() for y in yl] for yl in lw.y_lora], [[y.clone() for y in yl] for yl in lw.y_base])
+
+
+def test_7b_layerwise_decode_token():
+    """The layer-wise baseline (per-layer routing, unmerged adapters) at the
+    7B-shaped workload's full size, 32 layers x 7 projections, one SGMM call per
+    projection: one token eagerly, checked against the oracle -- every layer's
+    router set (indices bit-exact), every projection's adapter output (T = 1,
+    from zero) element by element, the base products of layers 0 and 31 element
+    by element -- then the same token replayed three times from one HIP graph,
+    each replay bitwise equal to the eager token."""
+    from dynamic_lora_moe_amd.layerwise import LayerwiseDecode
+    wl = synth.WORKLOADS["7b-decode"]
+    print("[workload] 7b-decode layer-wise: building", flush=True)
+    model = synth.switch_model(wl)
+    x, _ = synth.router_inputs(wl)
+    P = len(wl.projs)
+    per_layer = [[(W, A, B) for _, _, W, A, B in model[l * P:(l + 1) * P]] for l in range(wl.layers)]
+    routers = [synth.normal_device((wl.d_model, wl.E), 0.02, wl.dtype, "cuda", wl.cfg_id, "Wr", l)
+               for l in range(wl.layers)]
+    xs = [[synth.normal_device((W.shape[1],), 1.0, wl.dtype, "cuda", wl.cfg_id, "xin", l, k)
+           for k, (W, _, _) in enumerate(projs)] for l, projs in enumerate(per_layer)]
+    lw = LayerwiseDecode(per_layer, routers, xs, wl.E, wl.r, wl.scale)
+    assert lw.launches_per_token() == wl.layers * (2 + P * 4)
+    x_tok = x[3:4].contiguous()
+    lw.step(x_tok)
+    torch.cuda.synchronize()
+    assert lw.status() == dlm.DLM_OK
+    xt = x_tok.cpu()
+    agg = {"n": 0, "n_gt2ulp": 0, "max_ulp": 0}
+    for l, projs in enumerate(per_layer):
+        ri, rg, lg, mg, bd = oracle.pregate(xt, routers[l].cpu(), with_stats=True)
+        assert (mg > 2 * bd).all(), f"layer {l}: a near tie in the router"
+        assert torch.equal(lw.idx[l].cpu(), ri), f"layer {l}: router set"
+        rel = (lw.g[l].cpu() - rg).abs() / rg.abs().clamp_min(1e-30)
+        assert rel.max().item() <= 2.0 ** -22, f"layer {l}: router gates {rel.max()}"
+        for k, ((W, A, B), xv, y) in enumerate(zip(projs, xs[l], lw.y_lora[l])):
+            ref, ex, ab = oracle.sgmm(xv[None].cpu(), ri, rg, A.cpu(), B.cpu(),
+                                      torch.zeros((1, W.shape[0]), dtype=wl.dtype), wl.scale, with_stats=True)
+            st = check_bf16(y.cpu(), ref, ex, ab, W.shape[1] + 2 * wl.r + 2, extra=SPLIT,
+                            what=f"layer-wise L{l} adapter {k}")
+            agg["n"] += st["n"]
+            agg["n_gt2ulp"] += st["n_gt2ulp"]
+            agg["max_ulp"] = max(agg["max_ulp"], st["max_ulp"])
+        if l in (0, wl.layers - 1):
+            print(f"[workload] 7b-decode layer-wise: base products of layer {l}", flush=True)
+            for k, ((W, _, _), xv, yb) in enumerate(zip(projs, xs[l], lw.y_base[l])):
+                _, ex, ab = oracle.gemv(W.cpu(), xv.cpu(), with_stats=True)
+                check_f32(yb.cpu(), ex, ab, W.shape[1], what=f"layer-wise L{l} base {k}")
+    print("layer-wise adapters", agg, flush=True)
+    eager = _layerwise_outputs(lw)
+    s = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(gr, stream=s):
+            lw.step(x_tok, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        lw.reset_lora()
+        for yl in lw.y_base:
+            for y in yl:
+                y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        got = _layerwise_outputs(lw)
+        for a, b in zip(eager, got):
+            for u, v in zip(a, b):
+                for p, q in (zip(u, v) if isinstance(u, list) else [(u, v)]):
+                    assert torch.equal(p, q), f"graph replay {rep} differs from the eager token"
+    assert lw.status() == dlm.DLM_OK
+    del gr
+    lw.close()
+    del model, lw
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def test_7b_decode_fused_switch_and_product_per_layer_sampled():
     """The decode loop's fused form at its full size: one layer handle of the
     7B-shaped workload (7 projections), dlm_switch_gemv with the router's device
