@@ -693,26 +693,29 @@ def traffic_from(fetch_csv, write_csv, log, out_path=None):
 
 def _sgmm_traffic_from(fetch_csv, write_csv, read):
     """Per-kernel HBM bytes of the grouped SGMM passes of --profile-kernels: the
-    dispatches of the four SGMM kernels, in dispatch order, split into passes at
-    each segment launch; the first SGMM_PROFILE_PASSES passes are the prefill,
-    the next the mixed-decode steps 0, 1, ...  Each counter is scaled by its own
-    reading for the 1 GiB copy."""
+    dispatches of the SGMM kernels, in dispatch order, split into passes where a
+    segmentation launch follows another kind (a pass segments with one launch,
+    or with a count launch and a placing launch above 1024 rows); the first
+    SGMM_PROFILE_PASSES passes are the prefill, the next the mixed-decode steps
+    0, 1, ...  Each counter is scaled by its own reading for the 1 GiB copy."""
     import csv
     import synth
     kinds = ("segment", "shrink", "vsum", "expand")
+    names = {"segment": "sgmm_seg_", "shrink": "sgmm_shrink", "vsum": "sgmm_vsum", "expand": "sgmm_expand"}
     per = {}
     for part, path, counter in (("read", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         _, cp = read(path, counter, "\0")
         scale = (2 ** 30 / 1024) / max(cp) * 1024  # bytes per counted KiB
         with open(path) as f:
             rows = [r for r in csv.DictReader(f) if r.get("Counter_Name") == counter
-                    and any(f"sgmm_{k}" in r.get("Kernel_Name", "") for k in kinds)]
+                    and any(names[k] in r.get("Kernel_Name", "") for k in kinds)]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        passes = []
+        passes, prev = [], None
         for r in rows:
-            kind = next(k for k in kinds if f"sgmm_{k}" in r["Kernel_Name"])
-            if kind == "segment":
+            kind = next(k for k in kinds if names[k] in r["Kernel_Name"])
+            if kind == "segment" and prev != "segment":
                 passes.append({})
+            prev = kind
             if passes:
                 passes[-1][kind] = passes[-1].get(kind, 0.0) + float(r["Counter_Value"]) * scale
         per[part] = passes

@@ -1,7 +1,8 @@
 """The counter summary bench.py builds from two rocprofv3 --pmc CSVs: each
 counter is scaled by its own reading for the 1 GiB copy, the switch dispatches
-are averaged, and the SGMM dispatches are split into passes at each segment
-launch (prefill passes first, then the mixed-decode steps). Synthetic CSVs in
+are averaged, and the SGMM dispatches are split into passes at each
+segmentation (one or two launches; prefill passes first, then the
+mixed-decode steps). Synthetic CSVs in
 the profile run's dispatch order; no GPU."""
 import csv
 import json
@@ -10,6 +11,19 @@ import bench
 
 SWITCH = "void dlm::switch_bf16_kernel<1, 256>(dlm::SwitchArgs)"
 SG = ("segment", "shrink", "vsum", "expand")
+_SHRINK = "void dlm::(anonymous namespace)::sgmm_shrink_bf16<1, true>(dlm::SgmmArgs)"
+_VSUM = "dlm::(anonymous namespace)::sgmm_vsum_kernel(dlm::SgmmArgs)"
+_EXPAND = "void dlm::(anonymous namespace)::sgmm_expand_bf16<1, true>(dlm::SgmmArgs)"
+_COUNT = "dlm::(anonymous namespace)::sgmm_seg_count(int const*, float const*, long, int, char*, dlm::SgLayout)"
+_PLACE = ("dlm::(anonymous namespace)::sgmm_seg_place(int const*, float const*, long, int, char*, "
+          "dlm::SgLayout, int*)")
+# (kernel name, share of the kind's counter value) per dispatch: the prefill
+# (4096 rows) segments with a count and a placing launch, mixed decode (64 rows)
+# with the placing launch alone
+KERNELS = [{"segment": [(_COUNT, 0.25), (_PLACE, 0.75)], "shrink": [(_SHRINK, 1.0)], "vsum": [(_VSUM, 1.0)],
+            "expand": [(_EXPAND, 1.0)]},
+           {"segment": [(_PLACE, 1.0)], "shrink": [(_SHRINK, 1.0)], "vsum": [(_VSUM, 1.0)],
+            "expand": [(_EXPAND, 1.0)]}]
 
 
 def _csv(path, counter, per_kernel, copy_kib):
@@ -23,8 +37,9 @@ def _csv(path, counter, per_kernel, copy_kib):
         for wl in range(2):
             for _ in range(bench.SGMM_PROFILE_PASSES):
                 for k in SG:
-                    d += 1
-                    w.writerow([d, f"void dlm::sgmm_{k}_kernel(dlm::SgmmArgs)", counter, per_kernel[wl][k]])
+                    for name, share in KERNELS[wl][k]:
+                        d += 1
+                        w.writerow([d, name, counter, per_kernel[wl][k] * share])
         d += 1
         w.writerow([d, "__amd_rocclr_copyBuffer", counter, copy_kib])
 
@@ -42,6 +57,9 @@ def test_traffic_summary_from_counter_csvs(tmp_path):
     assert sw["bytes_per_launch"] == 200.0 * 1024 * 2 + 200.0 * 1024
     pre, mix = t["sgmm_sgmm-prefill"], t["sgmm_mixed-decode"]
     assert pre["kernels"]["shrink"] == {"read": 1000.0 * 1024 * 2, "write": 1000.0 * 1024}
+    # both segmentation launches of a prefill pass count as its segment
+    assert pre["kernels"]["segment"] == {"read": 1.0 * 1024 * 2, "write": 1.0 * 1024}
+    assert mix["kernels"]["segment"] == {"read": 2.0 * 1024 * 2, "write": 2.0 * 1024}
     assert mix["kernels"]["expand"] == {"read": 4000.0 * 1024 * 2, "write": 4000.0 * 1024}
     assert pre["read_per_step"] == sum(pk[0].values()) * 1024 * 2
     assert mix["write_per_step"] == sum(pk[1].values()) * 1024
