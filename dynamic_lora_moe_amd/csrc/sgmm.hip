@@ -13,13 +13,14 @@
 //            from its positions' pairs.  Rows with two empty slots are left
 //            out.  The same segmentation serves every problem of a grouped
 //            call (one routing decision per token for all layers).
-//   shrink   per (problem, 512-wide K slice, tile): the slice's partial
+//   shrink   per (problem, 2048-wide K slice, live tile): the slice's partial
 //            v = x_rows A_U^T for the tile's experts U, bf16 MFMA 32x32x16 with
-//            M = tile rows (gathered through perm, staged in LDS), N = (expert,
-//            rank); each row keeps the fp32 partial v of its own two slots.
-//   sum      (problems with d_in > 512) the slices' partials added in slice
+//            M = tile rows (gathered through perm, staged in LDS 512 columns at
+//            a time), N = (expert, rank); each row keeps the fp32 partial v of
+//            its own two slots.
+//   sum      (problems with d_in > 2048) the slices' partials added in slice
 //            order.
-//   expand   per (problem, 1024 output columns, tile): y_rows += u B_U^T with
+//   expand   per (problem, 1024 output columns, live tile): y_rows += u B_U^T with
 //            u = s*g*v per (row, expert, rank).  u stays fp32-accurate by
 //            entering the MFMA as two bf16 terms (hi + lo); B slices are
 //            k-contiguous and load straight into operand registers; lane l
@@ -293,41 +294,42 @@ __device__ __forceinline__ int mask_list(uint32_t m, int* out) {
 
 // ---- shrink (bf16, MFMA) -----------------------------------------------------
 
-// Tiles per shrink work item: every A operand feeds one MFMA per tile.  Only
-// one tile per item is built and tested (two measured slower on both
-// workloads); the loops over kTM keep the shape of the multi-tile form.
-constexpr int kTM = 1;
-static_assert(kTM == 1, "only single-tile shrink work items are tested");
-constexpr int kXRows = 32 * kTM;
-// 64-wide K chunks of one slice, and 16-byte chunks of one x row of a slice
-constexpr int kKC = kSgmmKSlice / 64;
-constexpr int kXC = kSgmmKSlice / 8;
+// Rows of one shrink work item (one tile).
+constexpr int kXRows = 32;
+// K is staged through LDS in kShrinkStep-wide steps: 64-wide K chunks of one
+// step, and 16-byte chunks of one x row of a step.  A work item covers one
+// kSgmmKSlice-wide slice, i.e. kShrinkSteps steps, with its accumulators held
+// in registers across them.
+constexpr int kShrinkStep = 512;
+constexpr int kShrinkSteps = kSgmmKSlice / kShrinkStep;
+static_assert(kSgmmKSlice % kShrinkStep == 0, "a slice is a whole number of steps");
+constexpr int kKC = kShrinkStep / 64;
+constexpr int kXC = kShrinkStep / 8;
 // A chunks in flight per wave in the shrink's K loop.  The shrink runs at 4
 // waves per SIMD (3 for ranks 17..32, which would spill at 4): several
-// workgroups per CU, each with a 32 KB x slice.  Measured on the 4096-token
-// prefill: 114 us with 1024-wide slices, a 4-chunk ring and 2 waves per SIMD;
-// 102 us like this at 3 waves per SIMD, 98 us at 4.
+// workgroups per CU, each with a 32 KB x step.
 constexpr int kShrinkRing = 2;
-static_assert(kKC >= kShrinkRing && kKC % kShrinkRing == 0, "slice is a whole number of ring steps");
-static_assert(256 % kXC == 0 && kXRows % (256 / kXC) == 0, "x slice load shape");
-// x slice in LDS: kXRows rows of kSgmmKSlice bf16; the 16-byte chunk c of row m
+static_assert(kKC >= kShrinkRing && kKC % kShrinkRing == 0, "a step is a whole number of ring steps");
+static_assert(256 % kXC == 0 && kXRows % (256 / kXC) == 0, "x step load shape");
+// x step in LDS: kXRows rows of kShrinkStep bf16; the 16-byte chunk c of row m
 // is stored at chunk c ^ (m & 15), so the MFMA-layout reads (16 rows, one chunk)
 // and the row-contiguous writes both touch 16 distinct bank groups.
-__device__ __forceinline__ int x_off(int row, int c) { return row * kSgmmKSlice + ((c ^ (row & 15)) << 3); }
+__device__ __forceinline__ int x_off(int row, int c) { return row * kShrinkStep + ((c ^ (row & 15)) << 3); }
 // per-wave 32x64 bf16 scratch of the expand: rows of eight 16-byte chunks, chunk XOR (row & 7)
 __device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 
-// One work item = (problem, K slice, kTM consecutive tiles), the tiles fastest
-// so the work items that share a slice of A run next to each other on one XCD.
-// The four waves first read the tiles' x rows of the slice, row-contiguous
-// (each x byte is read once), into LDS.  The N blocks (32 columns of (expert,
-// rank) each, over the union of the tiles' experts) are then spread over the
-// waves: with four or more blocks each wave takes whole blocks; with fewer, the
-// waves of one block split the slice's chunks and their sums are added in a
-// fixed order.  The A rows of a block stream from L2 kShrinkRing chunks ahead
-// of the MFMAs, and each A operand serves the kTM tiles.  Each row's two
-// slots get the slice's partial v; a later pass adds the slices up.  Loads are
-// never guarded: a padding row or (expert, rank) column reads an in-bounds
+// One work item = (problem, K slice, tile), the tiles fastest so the work
+// items that share a slice of A run next to each other on one XCD.  The N
+// blocks (32 columns of (expert, rank) each, over the union of the tile's
+// experts) are spread over the four waves: with four or more blocks each wave
+// takes whole blocks (in rounds of four), with fewer the waves of one block
+// split each step's chunks and their sums are added in a fixed order at the
+// end.  Per step the four waves read the tile's x rows of the step,
+// row-contiguous (each x byte once per round), into LDS, and the next step's
+// x is in flight while the MFMAs run; the A rows of a block stream from L2
+// kShrinkRing chunks ahead of the MFMAs.  Each row's two slots get the slice's
+// partial v; a later pass adds the slices up when there are several.  Loads
+// are never guarded: a padding row or (expert, rank) column reads an in-bounds
 // dummy row whose products reach only accumulator entries that are never
 // stored, and k past d_in reads a clamped address whose value is replaced by 0.
 template <int R16, bool PK>
@@ -340,17 +342,17 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
     const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
     float* v = (float*)(a.ws + a.L.v) + gks * a.L.T_pad * 2 * RPAD;
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[kXRows * kSgmmKSlice];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kXRows * kShrinkStep];
     __shared__ int s_U[32];
     __shared__ int s_nU;
     __shared__ int s_row[kXRows], s_e0[kXRows], s_e1[kXRows];
     const int tid = threadIdx.x;
     static_assert(kXRows <= kWave, "one wave reads the tile's rows");
     if (tid < kWave) {
-        // the tiles' rows and slots; their expert union from a wave OR
+        // the tile's rows and slots; their expert union from a wave OR
         uint32_t m = 0;
         if (tid < kXRows) {
-            const bool in = tile0 + tid / 32 < n_tiles;
+            const bool in = tile0 < n_tiles;
             const int p = tile0 * 32 + tid;
             const int row = in ? gld(perm + p) : -1;
             const uint32_t ep = in ? gld(epk + p) : 0xffffffffu;
@@ -369,45 +371,57 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
     const int d_in = uniform(D.d_in), r = a.r;
     const uint16_t* __restrict__ x = (const uint16_t*)D.x;
     const uint16_t* __restrict__ A = (const uint16_t*)(PK ? D.Ap : D.A);
+    // steps of this slice inside d_in (the same for every wave)
+    const int n_steps = (d_in - k0 + kShrinkStep - 1) / kShrinkStep < kShrinkSteps
+                            ? (d_in - k0 + kShrinkStep - 1) / kShrinkStep : kShrinkSteps;
 
-    // 1) x slice: thread tid reads chunk tid % kXC of rows tid / kXC + kXR j
+    // x step: thread tid reads chunk tid % kXC of rows tid / kXC + kXR j
     constexpr int kXR = 256 / kXC;           // rows per load instruction
     constexpr int kXL = kXRows / kXR;        // load instructions per thread
     const int xc = tid % kXC, xr0 = tid / kXC;
-    const int xk = k0 + 8 * xc;
-    const bool xok = xk < d_in;
-    u32x4 xv[kXL];
+    auto load_x = [&](u32x4 (&xv)[kXL], int kb) {
+        const bool ok = kb + 8 * xc < d_in;
 #pragma unroll
-    for (int j = 0; j < kXL; ++j) {
-        const int rr = s_row[xr0 + kXR * j];
-        xv[j] = ld128(x + (int64_t)(rr >= 0 ? rr : 0) * d_in + (xok ? xk : 0));
-    }
+        for (int j = 0; j < kXL; ++j) {
+            const int rr = s_row[xr0 + kXR * j];
+            xv[j] = ld128(x + (int64_t)(rr >= 0 ? rr : 0) * d_in + (ok ? kb + 8 * xc : 0));
+        }
+    };
+    auto store_x = [&](const u32x4 (&xv)[kXL], int kb) {
+        const bool ok = kb + 8 * xc < d_in;
+#pragma unroll
+        for (int j = 0; j < kXL; ++j)
+            *(u32x4*)(s_x + x_off(xr0 + kXR * j, xc)) = ok ? xv[j] : u32x4{0u, 0u, 0u, 0u};
+    };
+    u32x4 xv[kXL];
+    load_x(xv, k0);
 
     const int nU = uniform(s_nU);
     const int NB = (nU * RPAD + 31) / 32;
     const int G = NB < 4 ? NB : 4;  // blocks in flight
     const int P = 4 / G;            // waves per block (1 when G == 3)
-    const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
+    const int n_rounds = (NB + G - 1) / G;
+    const int w = wave_id(), lane = lane_id();
     const int gw = w % G, kp = w / G;
     const int nmy = kKC / P;        // chunks per wave: chunk kp + P i
 
     // MFMA step s2 of chunk kc takes, in half-wave h, the 8-wide k group
-    // kq = (k0 + 64 kc) / 8 + 2 s2 + h: the two halves read adjacent groups, so
+    // kq = (kb + 64 kc) / 8 + 2 s2 + h: the two halves read adjacent groups, so
     // in the packed A layout one load covers contiguous runs of 32 bytes x rank.
     const int nq = d_in / 8;
     const int64_t qstride = PK ? 8 * r : 8;  // elements from group kq to kq + 1
     // A group past d_in loads a clamped address and is replaced by zeros where
     // the MFMA takes it: a select right after the load would wait for it.
-    auto load_a = [&](u32x4 (&dst)[4], const uint16_t* abase, int kc) {
+    auto load_a = [&](u32x4 (&dst)[4], const uint16_t* abase, int kc, int kb, int h) {
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-            const int kq = k0 / 8 + 8 * kc + 2 * s2 + h;
+            const int kq = kb / 8 + 8 * kc + 2 * s2 + h;
             dst[s2] = ld128(abase + (kq < nq ? kq : nq - 1) * qstride);
         }
     };
     // first element of this lane's (expert, rank) row in A (row start) or in
     // the packed A (its 8 values of group 0)
-    auto a_row = [&](int blk, int& u, int& rho) {
+    auto a_row = [&](int blk, int n, int& u, int& rho) {
         const int nn = blk * 32 + n;
         u = nn / RPAD;
         rho = nn % RPAD;
@@ -415,111 +429,107 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
         const int64_t e = ok ? s_U[u] : 0, rr = ok ? rho : 0;
         return PK ? A + e * r * d_in + rr * 8 : A + (e * r + rr) * d_in;
     };
-    auto mma = [&](const u32x4 (&ab)[4], int kc, f32x16 (&acc)[kTM]) {
+    auto mma = [&](const u32x4 (&ab)[4], int kc, int kb, int h, int n, f32x16& acc) {
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-            const bool in = k0 / 8 + 8 * kc + 2 * s2 + h < nq;
+            const bool in = kb / 8 + 8 * kc + 2 * s2 + h < nq;
             const u32x4 av = in ? ab[s2] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int j = 0; j < kTM; ++j) {
-                const u32x4 xo = *(const u32x4*)(s_x + x_off(32 * j + n, 8 * kc + 2 * s2 + h));
-                acc[j] = mfma32(xo, av, acc[j]);
-            }
+            const u32x4 xo = *(const u32x4*)(s_x + x_off(n, 8 * kc + 2 * s2 + h));
+            acc = mfma32(xo, av, acc);
         }
     };
-    auto store_v = [&](const f32x16 (&acc)[kTM], int u, int rho) {
+    auto store_v = [&](const f32x16& acc, int u, int rho, int h) {
         if (u >= nU || rho >= r) return;
         const int e = s_U[u];
 #pragma unroll
-        for (int j = 0; j < kTM; ++j)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = 32 * j + 8 * (i >> 2) + 4 * h + (i & 3);
-                if (s_row[m] < 0) continue;
-                float* vp = v + ((int64_t)(tile0 * 32 + m) * 2) * RPAD + rho;
-                if (s_e0[m] == e) gst(vp, acc[j][i]);
-                if (s_e1[m] == e) gst(vp + RPAD, acc[j][i]);
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int m = 8 * (i >> 2) + 4 * h + (i & 3);
+            if (s_row[m] < 0) continue;
+            float* vp = v + ((int64_t)(tile0 * 32 + m) * 2) * RPAD + rho;
+            if (s_e0[m] == e) gst(vp, acc[i]);
+            if (s_e1[m] == e) gst(vp + RPAD, acc[i]);
+        }
     };
-
-    // first block's A: its first chunks are in flight while x lands in LDS
     u32x4 ab[kShrinkRing][4];
-    int u, rho;
-    const uint16_t* arow = a_row(gw, u, rho);
-    const bool act = kp < P;
-#pragma unroll
-    for (int j = 0; j < kShrinkRing; ++j)
-        if (act && j < nmy) load_a(ab[j], arow, kp + P * j);
-
-#pragma unroll
-    for (int j = 0; j < kXL; ++j) {
-        const u32x4 val = xok ? xv[j] : u32x4{0u, 0u, 0u, 0u};
-        *(u32x4*)(s_x + x_off(xr0 + kXR * j, xc)) = val;
-    }
-    __syncthreads();
-
-    // K loop of one block over this wave's chunks, A kShrinkRing chunks ahead
-    auto run_block = [&](f32x16 (&acc)[kTM]) {
+    // K loop of one block over this wave's chunks of one step, A kShrinkRing
+    // chunks ahead (the first kShrinkRing are loaded before the step starts)
+    auto run_block = [&](f32x16& acc, const uint16_t* arow, int kb, int h, int n) {
 #pragma unroll 1
         for (int i = 0; i < nmy; i += kShrinkRing) {
 #pragma unroll
             for (int j = 0; j < kShrinkRing; ++j) {
                 if (i + j < nmy) {
-                    mma(ab[j], kp + P * (i + j), acc);
-                    if (i + j + kShrinkRing < nmy) load_a(ab[j], arow, kp + P * (i + j + kShrinkRing));
+                    mma(ab[j], kp + P * (i + j), kb, h, n, acc);
+                    if (i + j + kShrinkRing < nmy) load_a(ab[j], arow, kp + P * (i + j + kShrinkRing), kb, h);
                 }
             }
         }
     };
 
-    if (P == 1) {
-        if (!act) return;
-        for (int blk = gw; blk < NB; blk += G) {
-            if (blk != gw) {
-                arow = a_row(blk, u, rho);
+#pragma unroll 1
+    for (int rd = 0; rd < n_rounds; ++rd) {
+        // this wave's block of the round (waves past the blocks only stage x)
+        const int blk = gw + rd * G;
+        const bool mine = kp < P && blk < NB;
+        f32x16 acc = f32x16{};
+#pragma unroll 1
+        for (int ss = 0; ss < n_steps; ++ss) {
+            const int kb = k0 + ss * kShrinkStep;
+            // the lane index is opaque to this loop: the addresses derived from
+            // it are rebuilt per step instead of being held across steps
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int h = ln >> 5, n = ln & 31;
+            int u, rho;
+            const uint16_t* arow = a_row(mine ? blk : gw, n, u, rho);
+            // this step's first A chunks are in flight while x lands in LDS
 #pragma unroll
-                for (int j = 0; j < kShrinkRing; ++j)
-                    if (j < nmy) load_a(ab[j], arow, j);
-            }
-            f32x16 acc[kTM];
-#pragma unroll
-            for (int j = 0; j < kTM; ++j) acc[j] = f32x16{};
-            run_block(acc);
-            store_v(acc, u, rho);
+            for (int j = 0; j < kShrinkRing; ++j)
+                if (mine && j < nmy) load_a(ab[j], arow, kp + P * j, kb, h);
+            __syncthreads();  // the previous step's MFMAs are done with the LDS
+            store_x(xv, kb);
+            __syncthreads();
+            // next x step (or the next round's first): one call site, so the
+            // loads land in the same registers on every path
+            const int kn = ss + 1 < n_steps ? kb + kShrinkStep : k0;
+            if (ss + 1 < n_steps || rd + 1 < n_rounds) load_x(xv, kn);
+            if (mine) run_block(acc, arow, kb, h, n);
         }
-        return;
-    }
-    // one block per group of P waves: parts 1..P-1 go through LDS (the x
-    // slice is no longer read) and the part-0 wave adds them in order
-    f32x16 acc[kTM];
-#pragma unroll
-    for (int j = 0; j < kTM; ++j) acc[j] = f32x16{};
-    run_block(acc);
-    __syncthreads();
-    f32x4* red = (f32x4*)s_x;  // [wave][tile][4][lane]
-    static_assert(4 * kTM * 4 * kWave * 16 <= kXRows * kSgmmKSlice * 2, "reduction fits the x slice");
-    if (kp > 0) {
-#pragma unroll
-        for (int j = 0; j < kTM; ++j)
+        // (opaque again: the 16 v addresses of store_v are built here, not
+        // held across the rounds)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int h = ln >> 5, n = ln & 31;
+        int u, rho;
+        (void)a_row(mine ? blk : gw, n, u, rho);
+        if (P == 1) {
+            if (mine) store_v(acc, u, rho, h);
+            continue;
+        }
+        // one block per group of P waves (a single round): parts 1..P-1 go
+        // through LDS (the x step is no longer read) and the part-0 wave adds
+        // them in order
+        __syncthreads();
+        f32x4* red = (f32x4*)s_x;  // [wave][4][lane]
+        static_assert(4 * 4 * kWave * 16 <= kXRows * kShrinkStep * 2, "reduction fits the x step");
+        if (kp > 0) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                red[((w * kTM + j) * 4 + q) * kWave + lane] =
-                    f32x4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
-    }
-    __syncthreads();
-    if (kp == 0) {
-        for (int p = 1; p < P; ++p) {
-            const int wp = gw + p * G;
-#pragma unroll
-            for (int j = 0; j < kTM; ++j)
+                red[(w * 4 + q) * kWave + lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        }
+        __syncthreads();
+        if (kp == 0) {
+            for (int p = 1; p < P; ++p) {
+                const int wp = gw + p * G;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const f32x4 o = red[((wp * kTM + j) * 4 + q) * kWave + lane];
+                    const f32x4 o = red[(wp * 4 + q) * kWave + lane];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[j][4 * q + c] += o[c];
+                    for (int c = 0; c < 4; ++c) acc[4 * q + c] += o[c];
                 }
+            }
+            store_v(acc, u, rho, h);
         }
-        store_v(acc, u, rho);
     }
 }
 

@@ -33,8 +33,9 @@ struct SgLayout {
     int r_pad;
     int max_ks;  // K slices of the widest problem
 };
-// Width of one shrink K slice.
-constexpr int kSgmmKSlice = 512;
+// Width of one shrink K slice (one work item; its fp32 partial v is summed
+// with the other slices' afterwards).
+constexpr int kSgmmKSlice = 2048;
 SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob);
 
 // Rows per segmentation chunk (one workgroup of the segmentation kernels).

@@ -229,7 +229,7 @@ int dlm_layers_status(dlm_layers* h, int32_t* code, void* stream);
  * Workspace bytes dlm_sgmm / dlm_sgmm_group_run need for T rows, problems with
  * d_in up to d_in_max, E experts, rank r and n_problems problems sharing one
  * set of rows: row segmentation, the shrink's per-K-slice partial results
- * (fp32, [n_problems][ceil(d_in_max / 512)][T][2][r]) and the device status
+ * (fp32, [n_problems][ceil(d_in_max / 2048)][T][2][r]) and the device status
  * word.  *bytes is host memory.
  */
 int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r,
@@ -244,8 +244,9 @@ int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r,
  * Launches: segment (rows sorted by their unordered expert pair, 32-row
  * tiles, the experts each tile uses; a per-1024-row count launch first when
  * T > 1024), shrink (v = x A^T on the tile's experts
- * over 512-wide K slices, bf16 MFMA, fp32 partial results kept in the
- * workspace), a K-slice sum in a fixed order (only when d_in > 512) and
+ * over 2048-wide K slices staged through LDS 512 columns at a time, bf16
+ * MFMA, fp32 partial results kept in the workspace), a K-slice sum in a fixed
+ * order (only when d_in > 2048) and
  * expand (y += (s g v) B^T, MFMA with v*s*g split into two bf16 terms, fp32
  * accumulate, one bf16 rounding of y).  Results are bitwise reproducible run to run.
  * Rows whose two slots are empty are not touched.
@@ -321,7 +322,7 @@ int dlm_sgmm_group_repack(dlm_sgmm_group* h, void* stream);
 
 /*
  * Run every problem of the group for T rows: one segment launch shared by all
- * problems, then one shrink, one K-slice sum (only when some d_in > 512) and
+ * problems, then one shrink, one K-slice sum (only when some d_in > 2048) and
  * one expand launch covering all problems.
  * workspace: >= dlm_sgmm_workspace_size(T, max d_in, E, r, n_problems) bytes.
  */
@@ -338,7 +339,7 @@ int dlm_sgmm_status(void* workspace, int32_t* code, void* stream);
  * Number of kernel launches one dlm_sgmm, dlm_sgmm_noalloc or
  * dlm_sgmm_group_run call makes for T rows and problems with d_in up to
  * d_in_max: 0 for T = 0, else the segmentation (2 launches when T > 1024,
- * else 1), the shrink, the K-slice sum (bf16 with d_in_max > 512 only) and the
+ * else 1), the shrink, the K-slice sum (bf16 with d_in_max > 2048 only) and the
  * expand.  Returns -1 (with the last error set) for a negative T, d_in_max < 1
  * or an unknown dtype.
  */

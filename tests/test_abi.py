@@ -125,9 +125,9 @@ def test_sgmm_launch_count(lib):
     # segment, shrink, K-slice sum, expand
     assert f(1, 4096, dlm.DLM_BF16) == 4
     assert f(1024, 4096, dlm.DLM_BF16) == 4
-    # no K-slice sum for a single 512-wide slice
-    assert f(64, 512, dlm.DLM_BF16) == 3
-    assert f(64, 513, dlm.DLM_BF16) == 4
+    # no K-slice sum for a single 2048-wide slice
+    assert f(64, 2048, dlm.DLM_BF16) == 3
+    assert f(64, 2049, dlm.DLM_BF16) == 4
     # a count launch before the placement above 1024 rows
     assert f(1025, 4096, dlm.DLM_BF16) == 5
     assert f(16, 64, dlm.DLM_F32) == 3
@@ -141,9 +141,9 @@ def test_sgmm_launch_count(lib):
 def test_sgmm_workspace_size(lib):
     b = C.c_size_t(0)
     assert lib.dlm_sgmm_workspace_size(4096, 11008, 8, 16, 7, C.byref(b)) == dlm.DLM_OK
-    # the shrink's partial results dominate: 7 problems x 22 K slices of 512 x
+    # the shrink's partial results dominate: 7 problems x 6 K slices of 2048 x
     # 4096 rows x 2 slots x 16 x 4 bytes
-    assert b.value >= 7 * 22 * 4096 * 2 * 16 * 4
+    assert b.value >= 7 * 6 * 4096 * 2 * 16 * 4
     assert b.value % 256 == 0
     one = C.c_size_t(0)
     assert lib.dlm_sgmm_workspace_size(4096, 1024, 8, 16, 7, C.byref(one)) == dlm.DLM_OK

@@ -65,12 +65,14 @@ CASES = [
     (50, 200, 96, 4, 40, 1.0, torch.bfloat16),       # rank 40 (3 rank chunks)
     (40, 136, 72, 4, 80, 1.0, torch.bfloat16),       # rank 80 (5)
     (33, 64, 64, 2, 96, 1.0, torch.bfloat16),        # rank 96 (6)
-    (20, 520, 40, 3, 100, 0.5, torch.bfloat16),      # rank 100 (7): r % 8 != 0, two K slices
+    (20, 520, 40, 3, 100, 0.5, torch.bfloat16),      # rank 100 (7): r % 8 != 0, two LDS steps
     (300, 256, 264, 8, 16, 1.0, torch.bfloat16),
-    (40, 2056, 72, 8, 16, 1.0, torch.bfloat16),      # five K slices of 512, the last 8 wide
-    (70, 1096, 136, 16, 64, 0.5, torch.bfloat16),    # three K slices, many N blocks per tile
-    (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # two whole slices, largest rank
-    (9, 1500, 24, 4, 8, 1.0, torch.float32),         # fp32 past one slice width
+    (40, 2056, 72, 8, 16, 1.0, torch.bfloat16),      # two K slices of 2048, the last 8 wide
+    (40, 4104, 72, 8, 16, 1.0, torch.bfloat16),      # three K slices, 4 + 4 + 1 LDS steps
+    (70, 1096, 136, 16, 64, 0.5, torch.bfloat16),    # three LDS steps, rounds of N blocks per tile
+    (70, 4616, 136, 16, 64, 0.5, torch.bfloat16),    # rounds of N blocks over three K slices
+    (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # two whole LDS steps, largest rank
+    (9, 2100, 24, 4, 8, 1.0, torch.float32),         # fp32 past one slice width
     (9000, 64, 72, 8, 16, 1.0, torch.bfloat16),      # more rows than the segment's LDS caches
     (12, 64, 64, 1, 16, 1.0, torch.bfloat16),         # one expert: every used slot is expert 0
     (7, 8, 8, 2, 1, 1.0, torch.bfloat16),             # rank 1, one 8-wide chunk of d_in
