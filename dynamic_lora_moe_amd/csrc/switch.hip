@@ -33,6 +33,8 @@
 //     slots are put in a canonical order first so slot order cannot matter.
 //   * W goes through the caches with default policy: nontemporal hints on this
 //     stream measured ~1.5x slower on MI355X.
+#include <type_traits>
+
 #include "gfx950.hpp"
 #include "internal.hpp"
 
@@ -499,36 +501,47 @@ __device__ __forceinline__ void switch_wide_tile(const SwitchArgs& a, const Sets
         }
     }
 
+    // One sub-band: per 32-column half, the MFMAs of slots 0 and 1, then those
+    // of slots 2 and 3 while the VALU forms S_new from slots 0 and 1, then the
+    // next half's slot-0/1 MFMAs while the VALU finishes this half (S_old, the
+    // new weights, their rounding and the write back to the W buffer): the
+    // matrix cores and the VALU work side by side instead of in turns, with no
+    // more accumulators alive than the four slots of one half plus two.
     auto unit = [&](int sb) {
         const uint16_t* Acur = As + (sb & 1) * BUF_ELEMS;
         uint16_t* ws = Wb + (sb % kWideWBufs) * WBUF + w * WBLK;
-#pragma unroll 1
-        for (int b = 0; b < 2; ++b) {
-            u32x4 wm[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) wm[q] = *(const u32x4*)(ws + w_off(n, 4 * b + 2 * h + q));
-            // rank chunk outermost: the four slots' MFMAs of a chunk are
-            // independent and issue back to back; each slot sums its chunks in
-            // order (an inactive slot multiplies zeros)
-            f32x16 P[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+        auto a_op = [&](int b, int slot, int ks) {
             const uint16_t* ap = Acur + b * 32 * RPAD + n * RPAD;
-            // the next chunk's four A operands are read while this chunk's MFMAs run
-            u32x4 ao[2][4];
-#pragma unroll
-            for (int slot = 0; slot < 4; ++slot)
-                ao[0][slot] = *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, h) << 3));
+            return *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, 2 * ks + h) << 3));
+        };
+        // slots s0 and s0 + 1 of half b over every rank chunk (each slot sums
+        // its chunks in order; the next chunk's operands are read meanwhile)
+        auto mfma_pair = [&](int b, int s0, f32x16& Pa, f32x16& Pb) {
+            u32x4 ao[2][2];
+            ao[0][0] = a_op(b, s0, 0);
+            ao[0][1] = a_op(b, s0 + 1, 0);
 #pragma unroll
             for (int ks = 0; ks < R16; ++ks) {
                 if (ks + 1 < R16) {
-#pragma unroll
-                    for (int slot = 0; slot < 4; ++slot)
-                        ao[(ks + 1) & 1][slot] =
-                            *(const u32x4*)(ap + slot * SLOT_ELEMS + (a_chunk_swz<R16>(n, 2 * ks + 2 + h) << 3));
+                    ao[(ks + 1) & 1][0] = a_op(b, s0, ks + 1);
+                    ao[(ks + 1) & 1][1] = a_op(b, s0 + 1, ks + 1);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int slot = 0; slot < 4; ++slot) P[slot] = mfma32(ao[ks & 1][slot], bcur[slot][ks], P[slot]);
+                Pa = mfma32(ao[ks & 1][0], bcur[s0][ks], Pa);
+                Pb = mfma32(ao[ks & 1][1], bcur[s0 + 1][ks], Pb);
             }
+        };
+        auto load_wm = [&](int b, u32x4 (&wm)[2]) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) wm[q] = *(const u32x4*)(ws + w_off(n, 4 * b + 2 * h + q));
+        };
+        // S_new of the 16 outputs from slots 0 and 1
+        auto s_new = [&](const f32x16& P0, const f32x16& P1, float (&sn)[16]) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sn[i] = fmaf(sc.c[1], P1[i], sc.c[0] * P0[i]);
+        };
+        // S_old, W' = RNE(W - (S_old - S_new)) and the write back of half b
+        auto finish = [&](int b, const u32x4 (&wm)[2], const float (&sn)[16], const f32x16& P2,
+                          const f32x16& P3) {
             uint32_t ow[8];
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
@@ -537,10 +550,9 @@ __device__ __forceinline__ void switch_wide_tile(const SwitchArgs& a, const Sets
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int i = 2 * p + j;
-                    const float sn = fmaf(sc.c[1], P[1][i], sc.c[0] * P[0][i]);
-                    const float so = fmaf(sc.c[3], P[3][i], sc.c[2] * P[2][i]);
+                    const float so = fmaf(sc.c[3], P3[i], sc.c[2] * P2[i]);
                     const float wf = j ? bf_hi(word) : bf_lo(word);
-                    o2[j] = wf - (so - sn);
+                    o2[j] = wf - (so - sn[i]);
                 }
                 ow[p] = pack2_bf16(o2[0], o2[1]);
             }
@@ -548,6 +560,41 @@ __device__ __forceinline__ void switch_wide_tile(const SwitchArgs& a, const Sets
             for (int q = 0; q < 2; ++q)
                 *(u32x4*)(ws + w_off(n, 4 * b + 2 * h + q)) =
                     u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
+        };
+        u32x4 wm0[2], wm1[2];
+        load_wm(0, wm0);
+        load_wm(1, wm1);
+        float sn0[16], sn1[16];
+        f32x16 H0[2] = {f32x16{}, f32x16{}}, H1[2] = {f32x16{}, f32x16{}};
+        // interleave the MFMAs of a region with its VALU work: one MFMA, then
+        // NV VALU instructions, for each of the region's 2 R16 MFMAs
+        auto interleave = [&](auto nv) {
+#pragma unroll
+            for (int i = 0; i < 2 * R16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, decltype(nv)::value, 0);  // VALU
+            }
+        };
+        mfma_pair(0, 0, H0[0], H0[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            f32x16 Q0[2] = {f32x16{}, f32x16{}};
+            mfma_pair(0, 2, Q0[0], Q0[1]);
+            s_new(H0[0], H0[1], sn0);
+            interleave(std::integral_constant<int, 32 / (2 * R16)>{});
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_pair(1, 0, H1[0], H1[1]);
+            finish(0, wm0, sn0, Q0[0], Q0[1]);
+            interleave(std::integral_constant<int, 96 / (2 * R16)>{});
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        {
+            f32x16 Q1[2] = {f32x16{}, f32x16{}};
+            mfma_pair(1, 2, Q1[0], Q1[1]);
+            s_new(H1[0], H1[1], sn1);
+            interleave(std::integral_constant<int, 32 / (2 * R16)>{});
+            __builtin_amdgcn_sched_barrier(0);
+            finish(1, wm1, sn1, Q1[0], Q1[1]);
         }
         const int col = col_base + sb * 64 + 8 * lc;
 #pragma unroll
