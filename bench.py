@@ -155,6 +155,8 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
                 (T = 1, the layer's own router weights, the token's x), the base
                 product, and the adapters as one SGMM call per projection (T = 1)
                 or one grouped SGMM per layer -- W read once per token;
+      pregated_unmerged: the router once per token, then per layer the base
+                product and one grouped SGMM with that set;
       unfused:  pre-gated: router once, one switch over all 224 weights, then one
                 product launch per layer (W read twice, written once: 3 x 12.95 GB);
       fused:    pre-gated: router once, then per layer the switch fused with the
@@ -184,7 +186,9 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
     per_layer = [[(W, A, B) for _, _, W, A, B in model[l * P:(l + 1) * P]] for l in range(wl.layers)]
     lw = {"layerwise": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r, wl.scale),
           "layerwise_grouped": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r, wl.scale,
-                                               grouped=True)}
+                                               grouped=True),
+          "pregated_unmerged": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r, wl.scale,
+                                               grouped=True, route_once=True)}
     x_tok = torch.empty((1, wl.d_model), dtype=wl.dtype, device="cuda")
     idx = [torch.zeros((1, 2), dtype=torch.int32, device="cuda") for _ in range(2)]
     g = [torch.zeros((1, 2), dtype=torch.float32, device="cuda") for _ in range(2)]
@@ -212,7 +216,7 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
     res = {"tokens": n_tokens}
     w_bytes = wl.switch_w_elems() * 2
     pre_gated = ("unfused", "fused")
-    for kind in ("base", "layerwise", "layerwise_grouped") + pre_gated:
+    for kind in ("base", "layerwise", "layerwise_grouped", "pregated_unmerged") + pre_gated:
         out = {}
         with torch.cuda.stream(s):
             # eager: token 0 from the merged-in-nothing state, then n-1 switches

@@ -817,12 +817,13 @@ int dlm_sgmm_status(void* workspace, int32_t* code, void* stream) {
     return ok();
 }
 
-int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t dtype) {
-    if (T < 0 || d_in_max < 1 || (dtype != DLM_F32 && dtype != DLM_BF16)) {
-        fail(DLM_EINVAL, "sgmm_launches: T < 0, d_in_max < 1 or unknown dtype");
+int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t n_problems, int32_t dtype) {
+    if (T < 0 || d_in_max < 1 || n_problems < 1 || (dtype != DLM_F32 && dtype != DLM_BF16)) {
+        fail(DLM_EINVAL, "sgmm_launches: T < 0, d_in_max < 1, n_problems < 1 or unknown dtype");
         return -1;
     }
     if (T == 0) return 0;
+    if (dtype == DLM_BF16 && T <= kSgmmSmallT && n_problems == 1) return 1;
     const int seg = T > kSgmmSegRows ? 2 : 1;
     if (dtype == DLM_F32) return seg + 2;
     return seg + 2 + (d_in_max > kSgmmKSlice ? 1 : 0);

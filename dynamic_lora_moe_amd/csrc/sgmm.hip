@@ -787,6 +787,172 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a) {
     expand_item<R16, RVEC>(a, cgg, (int)(t - cgg * n_tiles));
 }
 
+// ---- few rows (bf16, T <= kSgmmSmallT): one launch ---------------------------
+
+// One problem (a group keeps the segmented path: there the K-sliced shrink
+// spreads each problem's A over several workgroups, which a column group
+// computing its own rank vectors cannot).  Work item = one kSgmmExpandCols-
+// column group.  The workgroup
+// checks every row's set (a rejected set makes the whole call a no-op, as in
+// the segmented path), computes its problem's rank vectors
+//     v[t][k][rho] = sum_j x[t][j] A[e_tk][rho][j]
+// (all 512 threads over the 16-byte chunks of K, 16 dot products at a time, then a
+// fixed-order reduction: every column group of a problem gets the same bits),
+// then for its
+// columns y[t][o] = round(y[t][o] + (c_t0 p_t0 + c_t1 p_t1)) with
+// p_tk = sum_rho v[t][k][rho] B[e_tk][o][rho] and c = s g.  Rows with two empty
+// slots are not written.  For one decode token per layer this is one launch
+// instead of four, which is what the per-token latency is made of.
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+constexpr int kSmallThreads = 512;
+__global__ __launch_bounds__(kSmallThreads) void sgmm_small_bf16(SgmmArgs a) {
+    constexpr int kMaxR = 128;
+    constexpr int kDots = 16;  // dot products swept together
+    constexpr int kSW = kSmallThreads / kWave;
+    __shared__ float s_v[kSgmmSmallT][2][kMaxR];
+    __shared__ float s_red[kSW][kDots];
+    const int T = (int)a.T, E = a.E, r = a.r, tid = threadIdx.x;
+    const int w = wave_id(), lane = lane_id();
+    // every thread reads the same words: the decisions below are uniform
+    bool bad = false;
+    for (int q = 0; q < 2 * T; ++q) {
+        const int e = gld(a.idx + q);
+        const float g = gld(a.g + q);
+        if (e < -1 || e >= E || (e >= 0 && !__builtin_isfinite(g))) bad = true;
+    }
+    const int64_t cgg = blockIdx.x;
+    if (cgg == 0 && tid == 0) {
+        int32_t* hdr = (int32_t*)(a.ws + a.L.hdr);
+        gst(hdr + SG_ERR, bad ? 1 : 0);
+        if (a.status_out) gst(a.status_out, bad ? 1 : 0);
+    }
+    if (bad) return;
+    const int prob = a.descs ? gld(a.cb_owner + cgg) : 0;
+    const SgDesc D = a.descs ? a.descs[prob] : a.single;
+    const int cg = (int)(cgg - D.unit0);
+    const int d_in = D.d_in, d_out = D.d_out;
+    const uint16_t* __restrict__ x = (const uint16_t*)D.x;
+    const uint16_t* __restrict__ A = (const uint16_t*)D.A;
+    const uint16_t* __restrict__ B = (const uint16_t*)D.B;
+    uint16_t* __restrict__ y = (uint16_t*)D.y;
+
+    // 1) rank vectors: kDots dot products (t, k, rho) at a time; thread tid
+    //    takes the 16-byte chunks tid, tid + 512, ... of K with all of a chunk's
+    //    loads issued before its FMAs, then each dot product's 256 partial sums
+    //    are added in a fixed order (wave butterfly, then the waves in order)
+    const int nd = T * 2 * r, nc = d_in / 8;
+    for (int d0 = 0; d0 < nd; d0 += kDots) {
+        float p[kDots];
+#pragma unroll
+        for (int i = 0; i < kDots; ++i) p[i] = 0.f;
+        for (int c = tid; c < nc; c += kSmallThreads) {
+            u32x4 xv[kSgmmSmallT], av[kDots];
+#pragma unroll
+            for (int t = 0; t < kSgmmSmallT; ++t)
+                if (t < T) xv[t] = ld128(x + (int64_t)t * d_in + 8 * c);
+#pragma unroll
+            for (int i = 0; i < kDots; ++i) {
+                const int d = d0 + i < nd ? d0 + i : nd - 1;
+                const int t = d / (2 * r), k = (d / r) & 1, rho = d % r;
+                const int e = gld(a.idx + 2 * t + k);
+                av[i] = ld128(A + ((int64_t)(e >= 0 ? e : 0) * r + rho) * d_in + 8 * c);
+            }
+#pragma unroll
+            for (int i = 0; i < kDots; ++i) {
+                const int d = d0 + i < nd ? d0 + i : nd - 1;
+                const int t = d / (2 * r);
+                u32x4 xt = xv[0];
+#pragma unroll
+                for (int tt = 1; tt < kSgmmSmallT; ++tt)
+                    if (t == tt) xt = xv[tt];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    p[i] = fmaf(bf_lo(xt[q]), bf_lo(av[i][q]), p[i]);
+                    p[i] = fmaf(bf_hi(xt[q]), bf_hi(av[i][q]), p[i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kDots; ++i) {
+            const float sw = wave_sum_f(p[i]);
+            if (lane == 0) s_red[w][i] = sw;
+        }
+        __syncthreads();
+        if (tid < kDots && d0 + tid < nd) {
+            const int d = d0 + tid;
+            const int t = d / (2 * r), k = (d / r) & 1, rho = d % r;
+            const int e = gld(a.idx + 2 * t + k);
+            float sv = s_red[0][tid];
+#pragma unroll
+            for (int ww = 1; ww < kSW; ++ww) sv += s_red[ww][tid];
+            s_v[t][k][rho] = e >= 0 ? sv : 0.f;
+        }
+        __syncthreads();
+    }
+
+    // 2) four consecutive columns per thread of the first 256 (d_out is a
+    //    multiple of 8, so a thread's columns are all in range or all out)
+    const int col = cg * kSgmmExpandCols + 4 * tid;
+    if (tid >= kSgmmExpandCols / 4 || col >= d_out) return;
+    const bool rvec = (r & 7) == 0;
+    for (int t = 0; t < T; ++t) {
+        const int e0 = gld(a.idx + 2 * t), e1 = gld(a.idx + 2 * t + 1);
+        if (e0 < 0 && e1 < 0) continue;
+        float part[2][4];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = k ? e1 : e0;
+            const float c = e >= 0 ? a.scale * gld(a.g + 2 * t + k) : 0.f;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            if (e >= 0) {
+                const uint16_t* br = B + ((int64_t)e * d_out + col) * r;  // 4 rows of r, contiguous
+                if (rvec) {
+                    // 16-byte rank chunks of the four rows, 8 in flight
+                    for (int r0 = 0; r0 < r; r0 += 16) {
+                        u32x4 bv[4][2];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; ++h2) {
+                                const int rr = r0 + 8 * h2 < r ? r0 + 8 * h2 : r0;
+                                bv[j][h2] = ld128(br + j * r + rr);
+                            }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; ++h2) {
+                                if (r0 + 8 * h2 >= r) continue;
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const int rho = r0 + 8 * h2 + 2 * q;
+                                    acc[j] = fmaf(s_v[t][k][rho], bf_lo(bv[j][h2][q]), acc[j]);
+                                    acc[j] = fmaf(s_v[t][k][rho + 1], bf_hi(bv[j][h2][q]), acc[j]);
+                                }
+                            }
+                    }
+                } else {
+                    for (int rho = 0; rho < r; ++rho)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[j] = fmaf(s_v[t][k][rho], bf_to_f(br[j * r + rho]), acc[j]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part[k][j] = c * acc[j];
+        }
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        uint16_t* yp = y + (int64_t)t * d_out + col;
+        const u32x2 yv = *(gcptr<u32x2>)yp;
+        const uint32_t o0 = pack2_bf16(bf_lo(yv[0]) + (part[0][0] + part[1][0]), bf_hi(yv[0]) + (part[0][1] + part[1][1]));
+        const uint32_t o1 = pack2_bf16(bf_lo(yv[1]) + (part[0][2] + part[1][2]), bf_hi(yv[1]) + (part[0][3] + part[1][3]));
+        *(gptr<u32x2>)yp = u32x2{o0, o1};
+    }
+}
+
 // ---- element-wise path (fp32) ------------------------------------------------
 
 template <typename T> __device__ __forceinline__ float ldf(const T* p, int64_t i);
@@ -947,6 +1113,11 @@ static bool sgmm_grids_fit(const SgmmArgs& a, int dtype) {
 }
 
 hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
+    if (dtype == 1 && a.T <= kSgmmSmallT && a.n_prob == 1) {
+        if (!grid_fits(a.total_cb, kSmallThreads)) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(sgmm_small_bf16, dim3((unsigned)a.total_cb), dim3(kSmallThreads), 0, s, a);
+        return hipGetLastError();
+    }
     if (!sgmm_grids_fit(a, dtype)) return hipErrorInvalidConfiguration;
     static_assert(kSegThreads == kSgmmSegRows, "segmentation chunk");
     const int64_t n_chunks = a.L.n_chunks;

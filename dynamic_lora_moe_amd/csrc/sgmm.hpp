@@ -44,6 +44,11 @@ constexpr int kSgmmSegRows = 1024;
 // Output columns one SGMM expand work item covers (4 waves x 4 x 64).
 constexpr int kSgmmExpandCols = 1024;
 
+// Single-problem calls with at most this many rows (bf16) take one launch:
+// each column group computes the rank vectors itself instead of a
+// segmentation, a shrink and a K-slice sum running first.
+constexpr int kSgmmSmallT = 4;
+
 // Header words of the workspace.
 enum { SG_ERR = 0, SG_NPOS = 1, SG_NTILES = 2 };
 

@@ -15,6 +15,11 @@ small sequential kernel launches.  Per token and per layer l:
      grouped SGMM per layer (``grouped=True``: one segmentation for the
      layer's projections).
 
+With ``route_once=True`` the router runs once per token (the first layer's
+router weights) and every layer applies that set: the pre-gated decision of
+AdaFuse (Chinese digest, method section; Korean digest section 2-ga) with the
+adapters still unmerged, so one router launch per token instead of one per layer.
+
 The layer's adapted output is y_base + y_lora; the two stay in separate
 buffers (the adding is one more element-wise pass, not timed here).  Nothing
 here computes: each step is an entry point of libdlm.so, and the class only
@@ -28,7 +33,8 @@ from . import DLM_OK, Layers, SgmmGroup, pregate, sgmm, sgmm_launches, sgmm_stat
 
 
 class LayerwiseDecode:
-    """One decode token through every layer with per-layer routing.
+    """One decode token through every layer with per-layer routing (or, with
+    route_once, one routing decision for all layers).
 
     layers:  per layer, the adapted projections [(W, A, B)] (W [d_out][d_in],
              A [E][r][d_in], B [E][d_out][r], one dtype); W is never modified.
@@ -37,10 +43,12 @@ class LayerwiseDecode:
              dtype), read in place by the base product and the adapters.
     """
 
-    def __init__(self, layers, routers, xs, E: int, r: int, scale: float, grouped: bool = False):
+    def __init__(self, layers, routers, xs, E: int, r: int, scale: float, grouped: bool = False,
+                 route_once: bool = False):
         if not len(layers) == len(routers) == len(xs):
             raise ValueError("one projection list, one router and one input list per layer")
         self.E, self.r, self.scale, self.grouped = E, r, float(scale), grouped
+        self.route_once = route_once
         self.routers = list(routers)
         self.xs = [list(x) for x in xs]
         W0 = layers[0][0][0]
@@ -71,13 +79,15 @@ class LayerwiseDecode:
     def step(self, router_x, stream=None):
         """Enqueue one token: router_x [1][d_router] is every layer's router input."""
         for l, projs in enumerate(self.projs):
-            pregate(router_x, self.routers[l], idx=self.idx[l], g=self.g[l], stream=stream)
+            s = 0 if self.route_once else l  # the set this layer applies
+            if l == s:
+                pregate(router_x, self.routers[l], idx=self.idx[l], g=self.g[l], stream=stream)
             self.base[l].gemv(stream=stream)
             if self.grouped:
-                self.groups[l].run(self.idx[l], self.g[l], workspace=self.ws, stream=stream)
+                self.groups[l].run(self.idx[s], self.g[s], workspace=self.ws, stream=stream)
             else:
                 for (W, A, B), x, y in zip(projs, self.xs[l], self.y_lora[l]):
-                    sgmm(x[None], self.idx[l], self.g[l], A, B, y, self.scale, workspace=self.ws,
+                    sgmm(x[None], self.idx[s], self.g[s], A, B, y, self.scale, workspace=self.ws,
                          stream=stream)
 
     def reset_lora(self):
@@ -87,15 +97,16 @@ class LayerwiseDecode:
                 y.zero_()
 
     def launches_per_token(self) -> int:
-        """Kernel launches one step() makes: per layer the router (1), the base
-        product (dlm_gemv: 1) and the adapters' SGMM launches."""
-        n = 0
+        """Kernel launches one step() makes: the router (once per layer, or once
+        per token with route_once), per layer the base product (dlm_gemv: 1) and
+        the adapters' SGMM launches."""
+        n = 1 if self.route_once else len(self.projs)
         for projs in self.projs:
             if self.grouped:
-                sg = sgmm_launches(1, max(W.shape[1] for W, _, _ in projs), self.dtype)
+                sg = sgmm_launches(1, max(W.shape[1] for W, _, _ in projs), len(projs), self.dtype)
             else:
-                sg = sum(sgmm_launches(1, W.shape[1], self.dtype) for W, _, _ in projs)
-            n += 2 + sg
+                sg = sum(sgmm_launches(1, W.shape[1], 1, self.dtype) for W, _, _ in projs)
+            n += 1 + sg
         return n
 
     def status(self, stream=None) -> int:

@@ -121,21 +121,28 @@ def test_product_entry_points_validation(lib):
 
 def test_sgmm_launch_count(lib):
     f = lib.dlm_sgmm_launches
-    assert f(0, 4096, dlm.DLM_BF16) == 0
+    assert f(0, 4096, 1, dlm.DLM_BF16) == 0
+    # one problem, up to 4 rows: one launch; a group keeps the segmented path
+    assert f(1, 4096, 1, dlm.DLM_BF16) == 1
+    assert f(4, 11008, 1, dlm.DLM_BF16) == 1
+    assert f(1, 4096, 7, dlm.DLM_BF16) == 4
     # segment, shrink, K-slice sum, expand
-    assert f(1, 4096, dlm.DLM_BF16) == 4
-    assert f(1024, 4096, dlm.DLM_BF16) == 4
+    assert f(5, 4096, 1, dlm.DLM_BF16) == 4
+    assert f(1024, 4096, 7, dlm.DLM_BF16) == 4
     # no K-slice sum for a single 2048-wide slice
-    assert f(64, 2048, dlm.DLM_BF16) == 3
-    assert f(64, 2049, dlm.DLM_BF16) == 4
+    assert f(64, 2048, 1, dlm.DLM_BF16) == 3
+    assert f(64, 2049, 1, dlm.DLM_BF16) == 4
     # a count launch before the placement above 1024 rows
-    assert f(1025, 4096, dlm.DLM_BF16) == 5
-    assert f(16, 64, dlm.DLM_F32) == 3
-    assert f(4096, 64, dlm.DLM_F32) == 4
-    assert f(-1, 64, dlm.DLM_BF16) == -1 and "sgmm_launches" in _err(lib)
-    assert f(4, 0, dlm.DLM_BF16) == -1
-    assert f(4, 64, 7) == -1
-    assert dlm.sgmm_launches(1, 11008) == 4
+    assert f(1025, 4096, 1, dlm.DLM_BF16) == 5
+    assert f(1, 64, 1, dlm.DLM_F32) == 3
+    assert f(4096, 64, 1, dlm.DLM_F32) == 4
+    assert f(-1, 64, 1, dlm.DLM_BF16) == -1 and "sgmm_launches" in _err(lib)
+    assert f(4, 0, 1, dlm.DLM_BF16) == -1
+    assert f(4, 64, 0, dlm.DLM_BF16) == -1
+    assert f(4, 64, 1, 7) == -1
+    assert dlm.sgmm_launches(1, 11008) == 1
+    assert dlm.sgmm_launches(1, 11008, 7) == 4
+    assert dlm.sgmm_launches(64, 11008) == 4
 
 
 def test_sgmm_workspace_size(lib):

@@ -54,6 +54,10 @@ CASES = [
     (16, 64, 64, 4, 4, 1.0, torch.float32),          # tiny fp32 workload shape
     (33, 96, 40, 3, 5, 2.0, torch.float32),
     (1, 64, 64, 8, 16, 1.0, torch.bfloat16),
+    (2, 4104, 1032, 8, 16, 1.0, torch.bfloat16),     # few rows (one launch), a ragged last column group
+    (3, 200, 264, 8, 4, 2.0, torch.bfloat16),        # few rows, r < 16 and r % 8 != 0
+    (4, 520, 40, 3, 100, 0.5, torch.bfloat16),       # few rows, rank 100
+    (4, 64, 2056, 32, 128, 1.0, torch.bfloat16),     # few rows, largest rank and expert count
     (5, 200, 264, 8, 16, 2.0, torch.bfloat16),       # ragged everything
     (33, 64, 72, 2, 16, 1.0, torch.bfloat16),
     (100, 136, 520, 8, 4, 1.0, torch.bfloat16),      # r < 16, r % 8 != 0
@@ -150,6 +154,43 @@ def test_sgmm_bad_set_is_a_noop_with_status():
     dlm.sgmm(x, idx.cuda(), g.cuda(), A, B, y, 1.0, ws)
     assert dlm.sgmm_status(ws) == dlm.DLM_OK
     _check(x, idx, g, A, B, y0.cpu(), y, 1.0, "after bad set")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_sgmm_few_rows_single_launch(T):
+    """Single-problem calls with at most four rows take one launch: every row
+    form -- two experts, one slot empty, the same expert twice, both slots
+    empty -- against the oracle on three problems of different shapes, each
+    run alone (one launch) and all three as a group (the segmented path); a
+    rejected set leaves y untouched and sets the status word."""
+    E, r = 8, 16
+    shapes = [(4104, 1032), (200, 264), (11008, 4096)]
+    print(f"[sgmm] few rows T={T}", flush=True)
+    probs = [_problem(T, i, o, E, r, torch.bfloat16, 3400 + 10 * T + k) for k, (i, o) in enumerate(shapes)]
+    idx = torch.tensor([[1, 5], [2, -1], [3, 3], [-1, -1]][:T], dtype=torch.int32)
+    g = torch.tensor([[0.7, 0.3], [1.0, 0.5], [0.6, 0.4], [0.5, 0.5]][:T], dtype=torch.float32)
+    assert dlm.sgmm_launches(T, 11008) == 1 and dlm.sgmm_launches(T, 11008, 3) > 1
+    y0s = [p[3].clone() for p in probs]
+    grp = dlm.SgmmGroup(probs, E, r, 2.0)
+    ws = grp.run(idx.cuda(), g.cuda())
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    none = (idx == -1).all(1)
+    for k, (x, A, B, y) in enumerate(probs):
+        _check(x, idx, g, A, B, y0s[k].cpu(), y, 2.0, f"few rows T={T} problem {k}")
+        assert torch.equal(y.cpu()[none], y0s[k].cpu()[none])
+        y1 = y0s[k].clone()
+        dlm.sgmm(x, idx.cuda(), g.cuda(), A, B, y1, 2.0)
+        _check(x, idx, g, A, B, y0s[k].cpu(), y1, 2.0, f"few rows T={T} problem {k} alone")
+        assert torch.equal(y1.cpu()[none], y0s[k].cpu()[none])
+    bad = idx.clone()
+    bad[0, 0] = E
+    x0, A0, B0, _ = probs[0]
+    y2 = y0s[0].clone()
+    ws1 = dlm.sgmm_workspace(T, shapes[0][0], E, r)
+    dlm.sgmm(x0, bad.cuda(), g.cuda(), A0, B0, y2, 2.0, ws1)
+    assert dlm.sgmm_status(ws1) == dlm.DLM_EDEVICE
+    assert torch.equal(y2, y0s[0])
+    grp.close()
 
 
 def test_sgmm_group_matches_single_calls():

@@ -282,7 +282,9 @@ def test_7b_layerwise_decode_token():
     router set (indices bit-exact), every projection's adapter output (T = 1,
     from zero) element by element, the base products of layers 0 and 31 element
     by element -- then the same token replayed three times from one HIP graph,
-    each replay bitwise equal to the eager token."""
+    each replay bitwise equal to the eager token.  Then the pre-gated unmerged
+    form on the same layers (one router per token, one grouped SGMM per layer):
+    every adapter output against the oracle with the first layer's set."""
     from dynamic_lora_moe_amd.layerwise import LayerwiseDecode
     wl = synth.WORKLOADS["7b-decode"]
     print("[workload] 7b-decode layer-wise: building", flush=True)
@@ -295,7 +297,7 @@ def test_7b_layerwise_decode_token():
     xs = [[synth.normal_device((W.shape[1],), 1.0, wl.dtype, "cuda", wl.cfg_id, "xin", l, k)
            for k, (W, _, _) in enumerate(projs)] for l, projs in enumerate(per_layer)]
     lw = LayerwiseDecode(per_layer, routers, xs, wl.E, wl.r, wl.scale)
-    assert lw.launches_per_token() == wl.layers * (2 + P * 4)
+    assert lw.launches_per_token() == wl.layers * (2 + P * 1)
     x_tok = x[3:4].contiguous()
     lw.step(x_tok)
     torch.cuda.synchronize()
@@ -344,8 +346,26 @@ def test_7b_layerwise_decode_token():
                     assert torch.equal(p, q), f"graph replay {rep} differs from the eager token"
     assert lw.status() == dlm.DLM_OK
     del gr
+    # the same layers routed once per token (the first layer's router), one
+    # grouped SGMM per layer: every layer's adapters use that one set
+    po = LayerwiseDecode(per_layer, routers, xs, wl.E, wl.r, wl.scale, grouped=True, route_once=True)
+    assert po.launches_per_token() == 1 + wl.layers * (1 + 4)
+    po.step(x_tok)
+    torch.cuda.synchronize()
+    assert po.status() == dlm.DLM_OK
+    ri, rg = oracle.pregate(xt, routers[0].cpu())
+    assert torch.equal(po.idx[0].cpu(), ri)
+    for l, projs in enumerate(per_layer):
+        for k, ((W, A, B), xv, y) in enumerate(zip(projs, xs[l], po.y_lora[l])):
+            ref, ex, ab = oracle.sgmm(xv[None].cpu(), ri, rg, A.cpu(), B.cpu(),
+                                      torch.zeros((1, W.shape[0]), dtype=wl.dtype), wl.scale, with_stats=True)
+            check_bf16(y.cpu(), ref, ex, ab, W.shape[1] + 2 * wl.r + 2, extra=SPLIT,
+                       what=f"pre-gated unmerged L{l} adapter {k}")
+        for yb, yb0 in zip(po.y_base[l], eager[3][l]):
+            assert torch.equal(yb, yb0), f"layer {l}: base product differs between the two forms"
+    po.close()
     lw.close()
-    del model, lw
+    del model, lw, po
     gc.collect()
     torch.cuda.empty_cache()
 
