@@ -157,6 +157,8 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
                 or one grouped SGMM per layer -- W read once per token;
       pregated_unmerged: the router once per token, then per layer the base
                 product and one grouped SGMM with that set;
+      pregated_unmerged_2s: the same with each layer's SGMM on a second stream
+                beside its base product (joined before the next layer);
       unfused:  pre-gated: router once, one switch over all 224 weights, then one
                 product launch per layer (W read twice, written once: 3 x 12.95 GB);
       fused:    pre-gated: router once, then per layer the switch fused with the
@@ -202,6 +204,9 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
         if kind in lw:
             lw[kind].step(x_tok, stream=stream)
             return
+        if kind == "pregated_unmerged_2s":
+            lw["pregated_unmerged"].step(x_tok, stream=stream, side=side)
+            return
         dlm.pregate(x_tok, Wr, idx=idx[cur], g=g[cur], stream=stream)
         new = (idx[cur][0], g[cur][0])
         old = None if first else (idx[1 - cur][0], g[1 - cur][0])
@@ -216,7 +221,8 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
     res = {"tokens": n_tokens}
     w_bytes = wl.switch_w_elems() * 2
     pre_gated = ("unfused", "fused")
-    for kind in ("base", "layerwise", "layerwise_grouped", "pregated_unmerged") + pre_gated:
+    side = torch.cuda.Stream()
+    for kind in ("base", "layerwise", "layerwise_grouped", "pregated_unmerged", "pregated_unmerged_2s") + pre_gated:
         out = {}
         with torch.cuda.stream(s):
             # eager: token 0 from the merged-in-nothing state, then n-1 switches
@@ -253,6 +259,8 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
             lpt = wl.layers
         elif kind in lw:
             lpt = lw[kind].launches_per_token()
+        elif kind == "pregated_unmerged_2s":
+            lpt = lw["pregated_unmerged"].launches_per_token()
         else:
             lpt = 1 + (whole.launches_per_switch() + wl.layers if kind == "unfused"
                        else wl.layers * layers[0].launches_per_switch_gemv())

@@ -823,7 +823,7 @@ int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t n_problems, int32_t d
         return -1;
     }
     if (T == 0) return 0;
-    if (dtype == DLM_BF16 && T <= kSgmmSmallT && n_problems == 1) return 1;
+    if (dtype == DLM_BF16 && T <= kSgmmSmallT) return n_problems == 1 ? 1 : 2;
     const int seg = T > kSgmmSegRows ? 2 : 1;
     if (dtype == DLM_F32) return seg + 2;
     return seg + 2 + (d_in_max > kSgmmKSlice ? 1 : 0);

@@ -787,22 +787,27 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a) {
     expand_item<R16, RVEC>(a, cgg, (int)(t - cgg * n_tiles));
 }
 
-// ---- few rows (bf16, T <= kSgmmSmallT): one launch ---------------------------
+// ---- few rows (bf16, T <= kSgmmSmallT) -----------------------------------------
 
-// One problem (a group keeps the segmented path: there the K-sliced shrink
-// spreads each problem's A over several workgroups, which a column group
-// computing its own rank vectors cannot).  Work item = one kSgmmExpandCols-
-// column group.  The workgroup
-// checks every row's set (a rejected set makes the whole call a no-op, as in
-// the segmented path), computes its problem's rank vectors
-//     v[t][k][rho] = sum_j x[t][j] A[e_tk][rho][j]
-// (all 512 threads over the 16-byte chunks of K, 16 dot products at a time, then a
-// fixed-order reduction: every column group of a problem gets the same bits),
-// then for its
-// columns y[t][o] = round(y[t][o] + (c_t0 p_t0 + c_t1 p_t1)) with
-// p_tk = sum_rho v[t][k][rho] B[e_tk][o][rho] and c = s g.  Rows with two empty
-// slots are not written.  For one decode token per layer this is one launch
-// instead of four, which is what the per-token latency is made of.
+// With at most kSgmmSmallT rows there is nothing to segment: every workgroup
+// reads all rows' sets itself (a rejected set makes the whole call a no-op, as
+// in the segmented path) and works on all rows at once.
+//   * one problem: one launch.  Each kSgmmExpandCols-column group computes the
+//     rank vectors v[t][k][rho] = sum_j x[t][j] A[e_tk][rho][j] over all of K,
+//     then its columns.
+//   * a group: two launches.  One workgroup per (problem, kSgmmKSlice-wide K
+//     slice) writes the slice's partial v to the workspace; then each column
+//     group adds its problem's slices in slice order and updates its columns.
+//     The K slices spread a problem's A over several workgroups, which a
+//     column group computing all of v by itself cannot.
+// The dot products run with all threads over the 16-byte chunks of K, 16 or
+// 32 of them at a time and every load of a chunk issued before its FMAs, then a
+// fixed-order reduction (wave butterfly, then the waves in order): every
+// column group of a problem gets the same bits.  The columns:
+//     y[t][o] = round(y[t][o] + (c_t0 p_t0 + c_t1 p_t1)),
+//     p_tk = sum_rho v[t][k][rho] B[e_tk][o][rho],  c = s g,
+// four consecutive columns per thread; rows with two empty slots are not
+// written.  For one decode token this is one or two launches instead of four.
 __device__ __forceinline__ float wave_sum_f(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -810,60 +815,53 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 }
 
 constexpr int kSmallThreads = 512;
-__global__ __launch_bounds__(kSmallThreads) void sgmm_small_bf16(SgmmArgs a) {
-    constexpr int kMaxR = 128;
-    constexpr int kDots = 16;  // dot products swept together
-    constexpr int kSW = kSmallThreads / kWave;
-    __shared__ float s_v[kSgmmSmallT][2][kMaxR];
-    __shared__ float s_red[kSW][kDots];
-    const int T = (int)a.T, E = a.E, r = a.r, tid = threadIdx.x;
-    const int w = wave_id(), lane = lane_id();
-    // every thread reads the same words: the decisions below are uniform
+constexpr int kSmallMaxR = 128;
+
+// Every thread checks every row's set; workgroup 0 publishes the verdict.
+__device__ __forceinline__ bool small_sets_bad(const SgmmArgs& a) {
     bool bad = false;
-    for (int q = 0; q < 2 * T; ++q) {
+    for (int q = 0; q < 2 * (int)a.T; ++q) {
         const int e = gld(a.idx + q);
         const float g = gld(a.g + q);
-        if (e < -1 || e >= E || (e >= 0 && !__builtin_isfinite(g))) bad = true;
+        if (e < -1 || e >= a.E || (e >= 0 && !__builtin_isfinite(g))) bad = true;
     }
-    const int64_t cgg = blockIdx.x;
-    if (cgg == 0 && tid == 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         int32_t* hdr = (int32_t*)(a.ws + a.L.hdr);
         gst(hdr + SG_ERR, bad ? 1 : 0);
         if (a.status_out) gst(a.status_out, bad ? 1 : 0);
     }
-    if (bad) return;
-    const int prob = a.descs ? gld(a.cb_owner + cgg) : 0;
-    const SgDesc D = a.descs ? a.descs[prob] : a.single;
-    const int cg = (int)(cgg - D.unit0);
-    const int d_in = D.d_in, d_out = D.d_out;
-    const uint16_t* __restrict__ x = (const uint16_t*)D.x;
-    const uint16_t* __restrict__ A = (const uint16_t*)D.A;
-    const uint16_t* __restrict__ B = (const uint16_t*)D.B;
-    uint16_t* __restrict__ y = (uint16_t*)D.y;
+    return bad;
+}
 
-    // 1) rank vectors: kDots dot products (t, k, rho) at a time; thread tid
-    //    takes the 16-byte chunks tid, tid + 512, ... of K with all of a chunk's
-    //    loads issued before its FMAs, then each dot product's 256 partial sums
-    //    are added in a fixed order (wave butterfly, then the waves in order)
-    const int nd = T * 2 * r, nc = d_in / 8;
-    for (int d0 = 0; d0 < nd; d0 += kDots) {
-        float p[kDots];
+// v[t][k][rho] over the 16-byte K chunks [c0, c1), handed to out(d, value) for
+// dot product d = (t * 2 + k) * r + rho (0 for an empty slot), kSmallDots of
+// them per sweep over the chunks.  Uses s_red[waves][kSmallDots]; every
+// thread calls it.
+template <int kSmallDots, typename Out>
+__device__ __forceinline__ void small_dots(const SgmmArgs& a, const uint16_t* __restrict__ x,
+                                           const uint16_t* __restrict__ A, int d_in, int c0, int c1,
+                                           float (*s_red)[kSmallDots], Out out) {
+    constexpr int kSW = kSmallThreads / kWave;
+    const int T = (int)a.T, r = a.r, tid = threadIdx.x, w = wave_id(), lane = lane_id();
+    const int nd = T * 2 * r;
+    for (int d0 = 0; d0 < nd; d0 += kSmallDots) {
+        float p[kSmallDots];
 #pragma unroll
-        for (int i = 0; i < kDots; ++i) p[i] = 0.f;
-        for (int c = tid; c < nc; c += kSmallThreads) {
-            u32x4 xv[kSgmmSmallT], av[kDots];
+        for (int i = 0; i < kSmallDots; ++i) p[i] = 0.f;
+        for (int c = c0 + tid; c < c1; c += kSmallThreads) {
+            u32x4 xv[kSgmmSmallT], av[kSmallDots];
 #pragma unroll
             for (int t = 0; t < kSgmmSmallT; ++t)
                 if (t < T) xv[t] = ld128(x + (int64_t)t * d_in + 8 * c);
 #pragma unroll
-            for (int i = 0; i < kDots; ++i) {
+            for (int i = 0; i < kSmallDots; ++i) {
                 const int d = d0 + i < nd ? d0 + i : nd - 1;
                 const int t = d / (2 * r), k = (d / r) & 1, rho = d % r;
                 const int e = gld(a.idx + 2 * t + k);
                 av[i] = ld128(A + ((int64_t)(e >= 0 ? e : 0) * r + rho) * d_in + 8 * c);
             }
 #pragma unroll
-            for (int i = 0; i < kDots; ++i) {
+            for (int i = 0; i < kSmallDots; ++i) {
                 const int d = d0 + i < nd ? d0 + i : nd - 1;
                 const int t = d / (2 * r);
                 u32x4 xt = xv[0];
@@ -878,25 +876,31 @@ __global__ __launch_bounds__(kSmallThreads) void sgmm_small_bf16(SgmmArgs a) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < kDots; ++i) {
+        for (int i = 0; i < kSmallDots; ++i) {
             const float sw = wave_sum_f(p[i]);
             if (lane == 0) s_red[w][i] = sw;
         }
         __syncthreads();
-        if (tid < kDots && d0 + tid < nd) {
+        if (tid < kSmallDots && d0 + tid < nd) {
             const int d = d0 + tid;
-            const int t = d / (2 * r), k = (d / r) & 1, rho = d % r;
-            const int e = gld(a.idx + 2 * t + k);
+            const int t = d / (2 * r), k = (d / r) & 1;
             float sv = s_red[0][tid];
 #pragma unroll
             for (int ww = 1; ww < kSW; ++ww) sv += s_red[ww][tid];
-            s_v[t][k][rho] = e >= 0 ? sv : 0.f;
+            out(d, gld(a.idx + 2 * t + k) >= 0 ? sv : 0.f);
         }
         __syncthreads();
     }
+}
 
-    // 2) four consecutive columns per thread of the first 256 (d_out is a
-    //    multiple of 8, so a thread's columns are all in range or all out)
+// The columns of column group cg from v (LDS, [t][k][kSmallMaxR]).
+__device__ __forceinline__ void small_columns(const SgmmArgs& a, const SgDesc& D, int cg,
+                                              float (*s_v)[2][kSmallMaxR]) {
+    const int T = (int)a.T, r = a.r, tid = threadIdx.x, d_out = D.d_out;
+    const uint16_t* __restrict__ B = (const uint16_t*)D.B;
+    uint16_t* __restrict__ y = (uint16_t*)D.y;
+    // four consecutive columns per thread of the first 256 (d_out is a
+    // multiple of 8, so a thread's columns are all in range or all out)
     const int col = cg * kSgmmExpandCols + 4 * tid;
     if (tid >= kSgmmExpandCols / 4 || col >= d_out) return;
     const bool rvec = (r & 7) == 0;
@@ -951,6 +955,72 @@ __global__ __launch_bounds__(kSmallThreads) void sgmm_small_bf16(SgmmArgs a) {
         const uint32_t o1 = pack2_bf16(bf_lo(yv[1]) + (part[0][2] + part[1][2]), bf_hi(yv[1]) + (part[0][3] + part[1][3]));
         *(gptr<u32x2>)yp = u32x2{o0, o1};
     }
+}
+
+// One problem (a.single also describes a one-problem group): one workgroup per
+// column group, v over all of K.
+__global__ __launch_bounds__(kSmallThreads) void sgmm_small_bf16(SgmmArgs a) {
+    __shared__ float s_v[kSgmmSmallT][2][kSmallMaxR];
+    __shared__ float s_red[kSmallThreads / kWave][16];
+    if (small_sets_bad(a)) return;
+    const SgDesc D = a.single;
+    const int r = a.r;
+    small_dots<16>(a, (const uint16_t*)D.x, (const uint16_t*)D.A, D.d_in, 0, D.d_in / 8, s_red,
+               [&](int d, float v) { s_v[d / (2 * r)][(d / r) & 1][d % r] = v; });
+    small_columns(a, D, (int)blockIdx.x, s_v);
+}
+
+// A group, first launch: one workgroup per (problem, K slice); the slice's
+// partial v goes to the workspace as v[slice][t][k][rho] (rows padded to r_pad).
+__global__ __launch_bounds__(kSmallThreads) void sgmm_small_shrink_bf16(SgmmArgs a) {
+    // a 2048-wide slice is 256 chunks: half the threads would sweep nothing,
+    // so the sweep covers 32 dot products (one for rank 16 and one row)
+    __shared__ float s_red[kSmallThreads / kWave][32];
+    if (small_sets_bad(a)) return;
+    const int64_t gks = blockIdx.x;
+    const int prob = gld(a.ks_owner + gks);
+    const SgDesc D = a.descs[prob];
+    const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
+    const int k1 = k0 + kSgmmKSlice < D.d_in ? k0 + kSgmmKSlice : D.d_in;
+    const int r = a.r, RPAD = a.L.r_pad;
+    float* v = (float*)(a.ws + a.L.v) + gks * a.L.T_pad * 2 * RPAD;
+    small_dots<32>(a, (const uint16_t*)D.x, (const uint16_t*)D.A, D.d_in, k0 / 8, k1 / 8, s_red,
+               [&](int d, float val) { gst(v + (d / r) * RPAD + d % r, val); });
+}
+
+// A group, second launch: one workgroup per column group; v = the problem's
+// slices added in slice order.
+__global__ __launch_bounds__(kSmallThreads) void sgmm_small_expand_bf16(SgmmArgs a) {
+    __shared__ float s_v[kSgmmSmallT][2][kSmallMaxR];
+    bool bad = false;  // the first launch published the verdict
+    for (int q = 0; q < 2 * (int)a.T; ++q) {
+        const int e = gld(a.idx + q);
+        const float g = gld(a.g + q);
+        if (e < -1 || e >= a.E || (e >= 0 && !__builtin_isfinite(g))) bad = true;
+    }
+    if (bad) return;
+    const int64_t cgg = blockIdx.x;
+    const int prob = gld(a.cb_owner + cgg);
+    const SgDesc D = a.descs[prob];
+    const int r = a.r, RPAD = a.L.r_pad, nd = (int)a.T * 2 * r;
+    const int64_t stride = a.L.T_pad * 2 * RPAD;  // floats per slice
+    const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * stride;
+    for (int d = threadIdx.x; d < nd; d += kSmallThreads) {
+        const int o = (d / r) * RPAD + d % r;
+        // the slices' partials eight at a time, all loads first, added in order
+        float sv = 0.f;
+        for (int s0 = 0; s0 < D.n_ks; s0 += 8) {
+            float pv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pv[j] = s0 + j < D.n_ks ? gld(v + (s0 + j) * stride + o) : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (s0 + j < D.n_ks) sv = (s0 + j == 0) ? pv[j] : sv + pv[j];
+        }
+        s_v[d / (2 * r)][(d / r) & 1][d % r] = sv;
+    }
+    __syncthreads();
+    small_columns(a, D, (int)(cgg - D.unit0), s_v);
 }
 
 // ---- element-wise path (fp32) ------------------------------------------------
@@ -1113,9 +1183,17 @@ static bool sgmm_grids_fit(const SgmmArgs& a, int dtype) {
 }
 
 hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
-    if (dtype == 1 && a.T <= kSgmmSmallT && a.n_prob == 1) {
-        if (!grid_fits(a.total_cb, kSmallThreads)) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(sgmm_small_bf16, dim3((unsigned)a.total_cb), dim3(kSmallThreads), 0, s, a);
+    if (dtype == 1 && a.T <= kSgmmSmallT) {
+        if (!grid_fits(a.total_cb, kSmallThreads) || !grid_fits(a.total_ks, kSmallThreads))
+            return hipErrorInvalidConfiguration;
+        if (a.n_prob == 1) {
+            hipLaunchKernelGGL(sgmm_small_bf16, dim3((unsigned)a.total_cb), dim3(kSmallThreads), 0, s, a);
+            return hipGetLastError();
+        }
+        hipLaunchKernelGGL(sgmm_small_shrink_bf16, dim3((unsigned)a.total_ks), dim3(kSmallThreads), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(sgmm_small_expand_bf16, dim3((unsigned)a.total_cb), dim3(kSmallThreads), 0, s, a);
         return hipGetLastError();
     }
     if (!sgmm_grids_fit(a, dtype)) return hipErrorInvalidConfiguration;

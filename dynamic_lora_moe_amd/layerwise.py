@@ -76,19 +76,38 @@ class LayerwiseDecode:
         n_ws = max(len(p) for p in self.projs) if grouped else 1
         self.ws = sgmm_workspace(1, d_in_max, E, r, n_ws, dev)
 
-    def step(self, router_x, stream=None):
-        """Enqueue one token: router_x [1][d_router] is every layer's router input."""
+    def step(self, router_x, stream=None, side=None):
+        """Enqueue one token: router_x [1][d_router] is every layer's router input.
+
+        side: a second stream (default priority) for the adapters.  A layer's
+        base product and its adapters read only the layer's input, so with
+        side the adapters run beside the base product: side waits for the
+        router, and the next layer waits for both (the adapters' output feeds
+        the next layer's input in a model)."""
+        main = stream if stream is not None else torch.cuda.current_stream()
+        ad = side if side is not None else main
+        if side is not None and not hasattr(self, "_ev"):
+            self._ev = [(torch.cuda.Event(), torch.cuda.Event()) for _ in self.projs]
         for l, projs in enumerate(self.projs):
             s = 0 if self.route_once else l  # the set this layer applies
             if l == s:
-                pregate(router_x, self.routers[l], idx=self.idx[l], g=self.g[l], stream=stream)
-            self.base[l].gemv(stream=stream)
+                pregate(router_x, self.routers[l], idx=self.idx[l], g=self.g[l], stream=main)
+            if side is not None:
+                fork, join = self._ev[l]
+                fork.record(main)
+                side.wait_event(fork)
+            # the adapters are enqueued first, so their few workgroups are
+            # dispatched before the base product fills the machine
             if self.grouped:
-                self.groups[l].run(self.idx[s], self.g[s], workspace=self.ws, stream=stream)
+                self.groups[l].run(self.idx[s], self.g[s], workspace=self.ws, stream=ad)
             else:
                 for (W, A, B), x, y in zip(projs, self.xs[l], self.y_lora[l]):
                     sgmm(x[None], self.idx[s], self.g[s], A, B, y, self.scale, workspace=self.ws,
-                         stream=stream)
+                         stream=ad)
+            self.base[l].gemv(stream=main)
+            if side is not None:
+                join.record(side)
+                main.wait_event(join)
 
     def reset_lora(self):
         """Zero the adapter outputs (they accumulate across tokens)."""

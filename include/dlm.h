@@ -249,10 +249,11 @@ int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r,
  * order (only when d_in > 2048) and
  * expand (y += (s g v) B^T, MFMA with v*s*g split into two bf16 terms, fp32
  * accumulate, one bf16 rounding of y).  A bf16 call with at most 4 rows (a
- * decode step) takes a single launch instead: each 1024-column group computes
- * its rows' rank vectors itself (fp32 dot products), then adds s*g*v*B^T to
- * its columns with one rounding (dlm_sgmm and one-problem groups only).
- * Results are bitwise reproducible run to run.
+ * decode step) skips the segmentation: with one problem a single launch, in
+ * which each 1024-column group computes the rows' rank vectors (fp32 dot
+ * products over all of K) and adds s*g*v*B^T to its columns with one rounding;
+ * with several, one launch for the rank vectors per 2048-wide K slice and one
+ * for the columns.  Results are bitwise reproducible run to run.
  * Rows whose two slots are empty are not touched.
  * A row with an index outside [-1, E) or a non-finite gate on a used slot makes
  * the whole call a no-op on y and sets the workspace status word (read it with
@@ -342,7 +343,7 @@ int dlm_sgmm_status(void* workspace, int32_t* code, void* stream);
 /*
  * Number of kernel launches one dlm_sgmm, dlm_sgmm_noalloc or
  * dlm_sgmm_group_run call makes for T rows and n_problems problems with d_in
- * up to d_in_max: 0 for T = 0, 1 for bf16 with T <= 4 and one problem, else
+ * up to d_in_max: 0 for T = 0; for bf16 with T <= 4, 1 (one problem) or 2; else
  * the segmentation (2 launches when T > 1024, else 1), the shrink, the K-slice
  * sum (bf16 with d_in_max > 2048 only) and the expand.  Returns -1 (with the
  * last error set) for a negative T, d_in_max < 1, n_problems < 1 or an unknown

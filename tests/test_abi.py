@@ -122,10 +122,10 @@ def test_product_entry_points_validation(lib):
 def test_sgmm_launch_count(lib):
     f = lib.dlm_sgmm_launches
     assert f(0, 4096, 1, dlm.DLM_BF16) == 0
-    # one problem, up to 4 rows: one launch; a group keeps the segmented path
+    # up to 4 rows: one launch for one problem, two for a group
     assert f(1, 4096, 1, dlm.DLM_BF16) == 1
     assert f(4, 11008, 1, dlm.DLM_BF16) == 1
-    assert f(1, 4096, 7, dlm.DLM_BF16) == 4
+    assert f(1, 4096, 7, dlm.DLM_BF16) == 2
     # segment, shrink, K-slice sum, expand
     assert f(5, 4096, 1, dlm.DLM_BF16) == 4
     assert f(1024, 4096, 7, dlm.DLM_BF16) == 4
@@ -141,7 +141,7 @@ def test_sgmm_launch_count(lib):
     assert f(4, 64, 0, dlm.DLM_BF16) == -1
     assert f(4, 64, 1, 7) == -1
     assert dlm.sgmm_launches(1, 11008) == 1
-    assert dlm.sgmm_launches(1, 11008, 7) == 4
+    assert dlm.sgmm_launches(1, 11008, 7) == 2
     assert dlm.sgmm_launches(64, 11008) == 4
 
 

@@ -158,18 +158,18 @@ def test_sgmm_bad_set_is_a_noop_with_status():
 
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_sgmm_few_rows_single_launch(T):
-    """Single-problem calls with at most four rows take one launch: every row
-    form -- two experts, one slot empty, the same expert twice, both slots
-    empty -- against the oracle on three problems of different shapes, each
-    run alone (one launch) and all three as a group (the segmented path); a
-    rejected set leaves y untouched and sets the status word."""
+    """Calls with at most four rows skip the segmentation: every row form --
+    two experts, one slot empty, the same expert twice, both slots empty --
+    against the oracle on three problems of different shapes, each run alone
+    (one launch) and all three as a group (two launches); a rejected set
+    leaves y untouched and sets the status word, alone and in a group."""
     E, r = 8, 16
     shapes = [(4104, 1032), (200, 264), (11008, 4096)]
     print(f"[sgmm] few rows T={T}", flush=True)
     probs = [_problem(T, i, o, E, r, torch.bfloat16, 3400 + 10 * T + k) for k, (i, o) in enumerate(shapes)]
     idx = torch.tensor([[1, 5], [2, -1], [3, 3], [-1, -1]][:T], dtype=torch.int32)
     g = torch.tensor([[0.7, 0.3], [1.0, 0.5], [0.6, 0.4], [0.5, 0.5]][:T], dtype=torch.float32)
-    assert dlm.sgmm_launches(T, 11008) == 1 and dlm.sgmm_launches(T, 11008, 3) > 1
+    assert dlm.sgmm_launches(T, 11008) == 1 and dlm.sgmm_launches(T, 11008, 3) == 2
     y0s = [p[3].clone() for p in probs]
     grp = dlm.SgmmGroup(probs, E, r, 2.0)
     ws = grp.run(idx.cuda(), g.cuda())
@@ -190,6 +190,10 @@ def test_sgmm_few_rows_single_launch(T):
     dlm.sgmm(x0, bad.cuda(), g.cuda(), A0, B0, y2, 2.0, ws1)
     assert dlm.sgmm_status(ws1) == dlm.DLM_EDEVICE
     assert torch.equal(y2, y0s[0])
+    before = [p[3].clone() for p in probs]
+    ws = grp.run(bad.cuda(), g.cuda())
+    assert dlm.sgmm_status(ws) == dlm.DLM_EDEVICE
+    assert all(torch.equal(p[3], b) for p, b in zip(probs, before))
     grp.close()
 
 

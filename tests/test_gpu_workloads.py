@@ -349,7 +349,7 @@ def test_7b_layerwise_decode_token():
     # the same layers routed once per token (the first layer's router), one
     # grouped SGMM per layer: every layer's adapters use that one set
     po = LayerwiseDecode(per_layer, routers, xs, wl.E, wl.r, wl.scale, grouped=True, route_once=True)
-    assert po.launches_per_token() == 1 + wl.layers * (1 + 4)
+    assert po.launches_per_token() == 1 + wl.layers * (1 + 2)
     po.step(x_tok)
     torch.cuda.synchronize()
     assert po.status() == dlm.DLM_OK
@@ -363,6 +363,31 @@ def test_7b_layerwise_decode_token():
                        what=f"pre-gated unmerged L{l} adapter {k}")
         for yb, yb0 in zip(po.y_base[l], eager[3][l]):
             assert torch.equal(yb, yb0), f"layer {l}: base product differs between the two forms"
+    # adapters on a second stream beside the base products: the same bits,
+    # eagerly and from a graph replayed twice
+    one = _layerwise_outputs(po)
+    side = torch.cuda.Stream()
+    po.reset_lora()
+    po.step(x_tok, side=side)
+    torch.cuda.synchronize()
+    for u, v in zip(one[2], _layerwise_outputs(po)[2]):
+        assert all(torch.equal(p, q) for p, q in zip(u, v)), "two-stream step differs"
+    gr2 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(gr2, stream=s):
+            po.step(x_tok, stream=s, side=side)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        po.reset_lora()
+        torch.cuda.synchronize()
+        gr2.replay()
+        torch.cuda.synchronize()
+        got = _layerwise_outputs(po)
+        for a, b in ((one[2], got[2]), (one[3], got[3])):
+            for u, v in zip(a, b):
+                assert all(torch.equal(p, q) for p, q in zip(u, v)), f"two-stream replay {rep} differs"
+    del gr2
+    assert po.status() == dlm.DLM_OK
     po.close()
     lw.close()
     del model, lw, po
