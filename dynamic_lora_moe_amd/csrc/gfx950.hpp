@@ -41,7 +41,8 @@ template <typename T> __device__ __forceinline__ T gld(const T* p) { return *(gc
 template <typename T> __device__ __forceinline__ void gst(T* p, T v) { *(gptr<T>)p = v; }
 
 // 128-bit global load/store.  `nt` marks streaming data that is touched once
-// (weights being switched) so it does not evict reused adapter slices.
+// (weights being switched or multiplied, x rows, y rows) so it does not evict
+// reused adapter slices from L2.
 __device__ __forceinline__ u32x4 ld128(const void* p) { return *(gcptr<u32x4>)p; }
 __device__ __forceinline__ u32x4 ld128_nt(const void* p) {
     return __builtin_nontemporal_load((gcptr<u32x4>)p);
@@ -66,6 +67,11 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 // instruction: its data is in LDS once the wave's vmcnt has passed it.
 __device__ __forceinline__ void copy16_to_lds(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds((gcptr<void>)g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+// The same for data read once (the nt cache policy, so it does not displace
+// data that is reused from L2).
+__device__ __forceinline__ void copy16_to_lds_nt(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds((gcptr<void>)g, (__attribute__((address_space(3))) void*)lds, 16, 0, 2);
 }
 
 // Wait until at most N vector-memory instructions of this wave are in flight.

@@ -384,7 +384,7 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
 #pragma unroll
         for (int j = 0; j < kXL; ++j) {
             const int rr = s_row[xr0 + kXR * j];
-            xv[j] = ld128(x + (int64_t)(rr >= 0 ? rr : 0) * d_in + (ok ? kb + 8 * xc : 0));
+            xv[j] = ld128_nt(x + (int64_t)(rr >= 0 ? rr : 0) * d_in + (ok ? kb + 8 * xc : 0));
         }
     };
     auto store_x = [&](const u32x4 (&xv)[kXL], int kb) {
@@ -609,7 +609,7 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool ok = yrow[i] >= 0 && col < d_out;
-            yv[i] = ld128(y + (ok ? (int64_t)yrow[i] * d_out + col : 0));
+            yv[i] = ld128_nt(y + (ok ? (int64_t)yrow[i] * d_out + col : 0));
         }
     };
     u32x4 ycur[4], ynxt[4];
