@@ -763,7 +763,7 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const u32x4 o = *(const u32x4*)(ys + y_off(8 * i + lr, lc));
-            if (yrow[i] >= 0 && col < d_out) st128(y + (int64_t)yrow[i] * d_out + col, o);
+            if (yrow[i] >= 0 && col < d_out) st128_nt(y + (int64_t)yrow[i] * d_out + col, o);
         }
         if (blk + 1 < nblk) {
 #pragma unroll
