@@ -437,10 +437,11 @@ def bench_sgmm(torch, dlm, synth, name, reps, log):
 
 def _per_layer_variant(torch, dlm, wl, probs, sets, reps, sec_grouped, log):
     """The mixed decode step as one group per layer (7 projections each): one
-    segmentation per layer, 4 launches per layer, run eagerly and replayed from a
-    HIP graph captured once (the step's sets are copied into the graph's static
-    input buffers before each replay).  Beside the grouped call, whose single
-    segmentation serves all layers (4 launches per step)."""
+    segmentation per layer, 3 launches per layer (segment, shrink, expand), run
+    eagerly and replayed from a HIP graph captured once (the step's sets are
+    copied into the graph's static input buffers before each replay).  Beside
+    the grouped call, whose single segmentation serves all layers (3 launches
+    per step)."""
     layers = sorted({l for l, *_ in probs})
     per = [dlm.SgmmGroup([(x, A, B, y) for l2, _, x, A, B, y in probs if l2 == l], wl.E, wl.r, wl.scale)
            for l in layers]
@@ -484,7 +485,10 @@ def _per_layer_variant(torch, dlm, wl, probs, sets, reps, sec_grouped, log):
     for gp in per:
         gp.close()
     log(f"mixed decode per layer: eager {eager * 1e3:.3f} ms/step, graph {graphed * 1e3:.3f} ms/step")
-    return {"launches_per_step_grouped": 4, "launches_per_step_per_layer": 4 * len(layers),
+    d_in_max = max(x.shape[1] for *_, x, A, B, y in probs)
+    per_layer_n = len(probs) // len(layers)
+    return {"launches_per_step_grouped": dlm.sgmm_launches(wl.T, d_in_max, wl.r, len(probs)),
+            "launches_per_step_per_layer": len(layers) * dlm.sgmm_launches(wl.T, d_in_max, wl.r, per_layer_n),
             "per_layer_eager_ms_per_step": eager * 1e3, "per_layer_graph_ms_per_step": graphed * 1e3,
             "grouped_ms_per_step": sec_grouped * 1e3 / len(sets)}
 

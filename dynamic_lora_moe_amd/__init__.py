@@ -78,7 +78,7 @@ def load(path: str = LIB_PATH):
         "dlm_gemv": ([P, P], C.c_int),
         "dlm_switch_gemv": ([P, P, P, P, P, P], C.c_int),
         "dlm_switch_gemv_launches": ([P], C.c_int),
-        "dlm_sgmm_launches": ([I64, I64, I32, I32], C.c_int),
+        "dlm_sgmm_launches": ([I64, I64, I32, I32, I32], C.c_int),
         "dlm_sgmm_group_repack": ([P, P], C.c_int),
         "dlm_sgmm_group_run": ([P, P, P, I64, P, C.c_size_t, P], C.c_int),
         "dlm_sgmm_status": ([P, P, P], C.c_int),
@@ -345,13 +345,13 @@ def sgmm_noalloc(x, idx, g, A, B, y, scale: float, status=None, stream=None):
     return y
 
 
-def sgmm_launches(T: int, d_in_max: int, n_problems: int = 1, dtype=torch.bfloat16) -> int:
+def sgmm_launches(T: int, d_in_max: int, r: int, n_problems: int = 1, dtype=torch.bfloat16) -> int:
     """Kernel launches of one sgmm / sgmm_noalloc (n_problems = 1) or
-    SgmmGroup.run call."""
+    SgmmGroup.run call at rank r."""
     dt = {torch.float32: DLM_F32, torch.bfloat16: DLM_BF16}.get(dtype)
     if dt is None:
         raise TypeError(f"unsupported dtype {dtype}")
-    n = load().dlm_sgmm_launches(T, d_in_max, n_problems, dt)
+    n = load().dlm_sgmm_launches(T, d_in_max, r, n_problems, dt)
     if n < 0:
         raise DLMError(DLM_EINVAL, load().dlm_last_error().decode())
     return n

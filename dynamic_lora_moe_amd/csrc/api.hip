@@ -817,16 +817,17 @@ int dlm_sgmm_status(void* workspace, int32_t* code, void* stream) {
     return ok();
 }
 
-int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t n_problems, int32_t dtype) {
-    if (T < 0 || d_in_max < 1 || n_problems < 1 || (dtype != DLM_F32 && dtype != DLM_BF16)) {
-        fail(DLM_EINVAL, "sgmm_launches: T < 0, d_in_max < 1, n_problems < 1 or unknown dtype");
+int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t r, int32_t n_problems, int32_t dtype) {
+    if (T < 0 || d_in_max < 1 || r < 1 || r > DLM_MAX_RANK || n_problems < 1 ||
+        (dtype != DLM_F32 && dtype != DLM_BF16)) {
+        fail(DLM_EINVAL, "sgmm_launches: T < 0, d_in_max < 1, r outside [1, DLM_MAX_RANK], n_problems < 1 or unknown dtype");
         return -1;
     }
     if (T == 0) return 0;
     if (dtype == DLM_BF16 && T <= kSgmmSmallT) return n_problems == 1 ? 1 : 2;
     const int seg = T > kSgmmSegRows ? 2 : 1;
     if (dtype == DLM_F32) return seg + 2;
-    return seg + 2 + (d_in_max > kSgmmKSlice ? 1 : 0);
+    return seg + 2 + (d_in_max > kSgmmKSlice && r > kSgmmFoldRank ? 1 : 0);
 }
 
 }  // extern "C"

@@ -18,10 +18,13 @@
 //            M = tile rows (gathered through perm, staged in LDS 512 columns at
 //            a time), N = (expert, rank); each row keeps the fp32 partial v of
 //            its own two slots.
-//   sum      (problems with d_in > 2048) the slices' partials added in slice
-//            order.
+//   sum      (ranks above 64, problems with d_in > 2048) the slices' partials
+//            added in slice order.
 //   expand   per (problem, 1024 output columns, live tile): y_rows += u B_U^T with
-//            u = s*g*v per (row, expert, rank).  u stays fp32-accurate by
+//            u = s*g*v per (row, expert, rank); up to rank 64 it first adds
+//            the K slices' partials of its tile in slice order into LDS (the
+//            sum launch's order, so the result is the same bit for bit).  u
+//            stays fp32-accurate by
 //            entering the MFMA as two bf16 terms (hi + lo); B slices are
 //            k-contiguous and load straight into operand registers; lane l
 //            ends with 16 consecutive outputs of one row (two 128-bit y
@@ -567,6 +570,12 @@ static_assert(kECols == kSgmmExpandCols, "expand column group");
 // are built once into LDS when the tile's union has at most kQLds pairs; larger
 // unions rebuild them per column block in registers.
 constexpr int kQLds = 16;
+// Up to this many 16-rank chunks the expand adds the K slices of its tile's v
+// itself (the tile's v block fits the y scratch); larger ranks get a K-slice
+// sum launch between the shrink and the expand.
+constexpr int kExpandFoldR16 = kSgmmFoldRank / 16;
+static_assert(32 * 2 * 16 * kExpandFoldR16 * 4 <= 4 * 32 * 64 * 2, "v block fits the y scratch");
+static_assert(32 * 2 * 16 * kExpandFoldR16 * 4 <= kQLds * 2 * kWave * 16, "v block fits the operand table");
 
 // work item = (problem, kECols-column group cgg over all problems, tile) with
 // the tile fastest: neighbouring work items (same XCD) reuse the same B column
@@ -574,6 +583,7 @@ constexpr int kQLds = 16;
 template <int R16, bool RVEC>
 __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int tile) {
     constexpr int RPAD = R16 * 16;
+    constexpr bool FOLD = R16 <= kExpandFoldR16;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
     const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
     const float* gpk = (const float*)(a.ws + a.L.gpk);
@@ -630,17 +640,64 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
     const int e0 = (int16_t)(ep & 0xffffu), e1 = (int16_t)(ep >> 16);
     const float c0 = a.scale * g0;
     const float c1 = a.scale * g1;
-    const float* v0 = v + ((int64_t)(tile * 32 + n) * 2) * RPAD;
+    // v of this lane's row: the tile's summed copy in LDS (FOLD), else slice 0
+    // of the workspace (already summed by the K-slice sum launch)
+    const int nq = nU * R16;
+    const bool shared_u = nq <= kQLds;
+    float* s_v = shared_u ? (float*)&s_y[0][0] : (float*)&s_u[0][0][0];
+    if constexpr (FOLD) {
+        // the tile's v block (32 rows x 2 slots x RPAD floats, contiguous in
+        // each slice) with the problem's K slices added in slice order; it
+        // takes the y scratch while the shared operands are built, else the
+        // operand table, which a union too large for the table leaves unused
+        const int nks = uniform(D.n_ks);
+        const int64_t stride = a.L.T_pad * 2 * RPAD;
+        const float* vt = v + (int64_t)tile * 32 * 2 * RPAD + 4 * threadIdx.x;
+        constexpr int KB = 8 / R16;  // slices in flight per round
+        u32x4 acc[R16];
+#pragma unroll
+        for (int k = 0; k < R16; ++k) acc[k] = ld128(vt + 1024 * k);
+        for (int ks = 1; ks < nks; ks += KB) {
+            u32x4 p[KB][R16];
+#pragma unroll
+            for (int j = 0; j < KB; ++j)
+#pragma unroll
+                for (int k = 0; k < R16; ++k)
+                    if (ks + j < nks) p[j][k] = ld128(vt + (ks + j) * stride + 1024 * k);
+#pragma unroll
+            for (int j = 0; j < KB; ++j)
+#pragma unroll
+                for (int k = 0; k < R16; ++k)
+                    if (ks + j < nks)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            acc[k][c] = __float_as_uint(__uint_as_float(acc[k][c]) + __uint_as_float(p[j][k][c]));
+        }
+#pragma unroll
+        for (int k = 0; k < R16; ++k) *(u32x4*)(s_v + 4 * threadIdx.x + 1024 * k) = acc[k];
+        __syncthreads();
+    }
+    const float* v0 = FOLD ? s_v + n * 2 * RPAD : v + ((int64_t)(tile * 32 + n) * 2) * RPAD;
     const float* v1 = v0 + RPAD;
     // row-side operand of (expert U[q / R16], ranks 16(q % R16) + 8h + [0,8)):
-    // u = s*g*v as hi + lo bf16 (v = the K slices' sum, kept in slice 0).  v of a slot that is not this expert, or of a
+    // u = s*g*v as hi + lo bf16 (v = the K slices' sum).  v of a slot that is not this expert, or of a
     // padding rank, is never written: it is selected away, not multiplied by 0.
     auto make_u = [&](int q, u32x4& bhi, u32x4& blo) {
         const int e = s_U[q / R16];
         const int rho0 = (q % R16) * 16 + 8 * h;
         const bool m0 = (e0 == e), m1 = (e1 == e);
-        const u32x4 p0 = ld128(v0 + rho0), p1 = ld128(v0 + rho0 + 4);
-        const u32x4 q0 = ld128(v1 + rho0), q1 = ld128(v1 + rho0 + 4);
+        u32x4 p0, p1, q0, q1;
+        if constexpr (FOLD) {
+            p0 = *(const u32x4*)(v0 + rho0);
+            p1 = *(const u32x4*)(v0 + rho0 + 4);
+            q0 = *(const u32x4*)(v1 + rho0);
+            q1 = *(const u32x4*)(v1 + rho0 + 4);
+        } else {
+            p0 = ld128(v0 + rho0);
+            p1 = ld128(v0 + rho0 + 4);
+            q0 = ld128(v1 + rho0);
+            q1 = ld128(v1 + rho0 + 4);
+        }
         float va[8], vb[8];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -690,8 +747,6 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
         return ao;
     };
 
-    const int nq = nU * R16;
-    const bool shared_u = nq <= kQLds;
     if (shared_u) {
         for (int q = w; q < nq; q += 4) make_u(q, s_u[q][0][lane], s_u[q][1][lane]);
     }
@@ -1147,7 +1202,7 @@ hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((sgmm_shrink_bf16<R16, false>), gs, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.total_ks > a.n_prob) {  // some problem has more than one K slice
+    if (R16 > kExpandFoldR16 && a.total_ks > a.n_prob) {  // K slices the expand does not add itself
         const dim3 gs((unsigned)((a.L.T_pad * 2 * a.L.r_pad / 4 + 255) / 256), (unsigned)a.n_prob);
         hipLaunchKernelGGL(sgmm_vsum_kernel, gs, dim3(256), 0, s, a);
         e = hipGetLastError();

@@ -36,6 +36,9 @@ struct SgLayout {
 // Width of one shrink K slice (one work item; its fp32 partial v is summed
 // with the other slices' afterwards).
 constexpr int kSgmmKSlice = 2048;
+// Up to this rank the expand adds a tile's K-slice partials itself; above it a
+// K-slice sum launch runs between the shrink and the expand.
+constexpr int kSgmmFoldRank = 64;
 SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob);
 
 // Rows per segmentation chunk (one workgroup of the segmentation kernels).

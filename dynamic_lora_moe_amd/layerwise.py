@@ -122,9 +122,9 @@ class LayerwiseDecode:
         n = 1 if self.route_once else len(self.projs)
         for projs in self.projs:
             if self.grouped:
-                sg = sgmm_launches(1, max(W.shape[1] for W, _, _ in projs), len(projs), self.dtype)
+                sg = sgmm_launches(1, max(W.shape[1] for W, _, _ in projs), self.r, len(projs), self.dtype)
             else:
-                sg = sum(sgmm_launches(1, W.shape[1], 1, self.dtype) for W, _, _ in projs)
+                sg = sum(sgmm_launches(1, W.shape[1], self.r, 1, self.dtype) for W, _, _ in projs)
             n += 1 + sg
         return n
 

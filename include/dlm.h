@@ -246,9 +246,10 @@ int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r,
  * T > 1024), shrink (v = x A^T on the tile's experts
  * over 2048-wide K slices staged through LDS 512 columns at a time, bf16
  * MFMA, fp32 partial results kept in the workspace), a K-slice sum in a fixed
- * order (only when d_in > 2048) and
+ * order (only when d_in > 2048 and r > 64) and
  * expand (y += (s g v) B^T, MFMA with v*s*g split into two bf16 terms, fp32
- * accumulate, one bf16 rounding of y).  A bf16 call with at most 4 rows (a
+ * accumulate, one bf16 rounding of y; up to rank 64 it adds the K slices'
+ * partials of its tile itself, in the same fixed order).  A bf16 call with at most 4 rows (a
  * decode step) skips the segmentation: with one problem a single launch, in
  * which each 1024-column group computes the rows' rank vectors (fp32 dot
  * products over all of K) and adds s*g*v*B^T to its columns with one rounding;
@@ -327,8 +328,8 @@ int dlm_sgmm_group_repack(dlm_sgmm_group* h, void* stream);
 
 /*
  * Run every problem of the group for T rows: one segment launch shared by all
- * problems, then one shrink, one K-slice sum (only when some d_in > 2048) and
- * one expand launch covering all problems.
+ * problems, then one shrink, one K-slice sum (only when some d_in > 2048 and
+ * r > 64) and one expand launch covering all problems.
  * workspace: >= dlm_sgmm_workspace_size(T, max d_in, E, r, n_problems) bytes.
  */
 int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, int64_t T,
@@ -342,14 +343,15 @@ int dlm_sgmm_status(void* workspace, int32_t* code, void* stream);
 
 /*
  * Number of kernel launches one dlm_sgmm, dlm_sgmm_noalloc or
- * dlm_sgmm_group_run call makes for T rows and n_problems problems with d_in
- * up to d_in_max: 0 for T = 0; for bf16 with T <= 4, 1 (one problem) or 2; else
- * the segmentation (2 launches when T > 1024, else 1), the shrink, the K-slice
- * sum (bf16 with d_in_max > 2048 only) and the expand.  Returns -1 (with the
- * last error set) for a negative T, d_in_max < 1, n_problems < 1 or an unknown
- * dtype.
+ * dlm_sgmm_group_run call makes for T rows and n_problems problems of rank r
+ * with d_in up to d_in_max: 0 for T = 0; for bf16 with T <= 4, 1 (one problem)
+ * or 2; else the segmentation (2 launches when T > 1024, else 1), the shrink,
+ * the K-slice sum (bf16 with d_in_max > 2048 and r > 64 only: at lower ranks
+ * the expand adds the slices itself) and the expand.  Returns -1 (with the last
+ * error set) for a negative T, d_in_max < 1, r outside [1, DLM_MAX_RANK],
+ * n_problems < 1 or an unknown dtype.
  */
-int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t n_problems, int32_t dtype);
+int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t r, int32_t n_problems, int32_t dtype);
 
 #ifdef __cplusplus
 }

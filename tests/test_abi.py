@@ -121,28 +121,33 @@ def test_product_entry_points_validation(lib):
 
 def test_sgmm_launch_count(lib):
     f = lib.dlm_sgmm_launches
-    assert f(0, 4096, 1, dlm.DLM_BF16) == 0
+    assert f(0, 4096, 16, 1, dlm.DLM_BF16) == 0
     # up to 4 rows: one launch for one problem, two for a group
-    assert f(1, 4096, 1, dlm.DLM_BF16) == 1
-    assert f(4, 11008, 1, dlm.DLM_BF16) == 1
-    assert f(1, 4096, 7, dlm.DLM_BF16) == 2
-    # segment, shrink, K-slice sum, expand
-    assert f(5, 4096, 1, dlm.DLM_BF16) == 4
-    assert f(1024, 4096, 7, dlm.DLM_BF16) == 4
-    # no K-slice sum for a single 2048-wide slice
-    assert f(64, 2048, 1, dlm.DLM_BF16) == 3
-    assert f(64, 2049, 1, dlm.DLM_BF16) == 4
+    assert f(1, 4096, 16, 1, dlm.DLM_BF16) == 1
+    assert f(4, 11008, 64, 1, dlm.DLM_BF16) == 1
+    assert f(1, 4096, 128, 7, dlm.DLM_BF16) == 2
+    # segment, shrink, expand; the expand adds the K slices up to rank 64
+    assert f(5, 4096, 16, 1, dlm.DLM_BF16) == 3
+    assert f(1024, 4096, 64, 7, dlm.DLM_BF16) == 3
+    # above rank 64 a K-slice sum launch runs when there are several slices
+    assert f(64, 4096, 65, 1, dlm.DLM_BF16) == 4
+    assert f(64, 2048, 128, 1, dlm.DLM_BF16) == 3
+    assert f(64, 2049, 128, 1, dlm.DLM_BF16) == 4
     # a count launch before the placement above 1024 rows
-    assert f(1025, 4096, 1, dlm.DLM_BF16) == 5
-    assert f(1, 64, 1, dlm.DLM_F32) == 3
-    assert f(4096, 64, 1, dlm.DLM_F32) == 4
-    assert f(-1, 64, 1, dlm.DLM_BF16) == -1 and "sgmm_launches" in _err(lib)
-    assert f(4, 0, 1, dlm.DLM_BF16) == -1
-    assert f(4, 64, 0, dlm.DLM_BF16) == -1
-    assert f(4, 64, 1, 7) == -1
-    assert dlm.sgmm_launches(1, 11008) == 1
-    assert dlm.sgmm_launches(1, 11008, 7) == 2
-    assert dlm.sgmm_launches(64, 11008) == 4
+    assert f(1025, 4096, 16, 1, dlm.DLM_BF16) == 4
+    assert f(1025, 4096, 80, 1, dlm.DLM_BF16) == 5
+    assert f(1, 64, 16, 1, dlm.DLM_F32) == 3
+    assert f(4096, 64, 16, 1, dlm.DLM_F32) == 4
+    assert f(-1, 64, 16, 1, dlm.DLM_BF16) == -1 and "sgmm_launches" in _err(lib)
+    assert f(4, 0, 16, 1, dlm.DLM_BF16) == -1
+    assert f(4, 64, 0, 1, dlm.DLM_BF16) == -1
+    assert f(4, 64, 129, 1, dlm.DLM_BF16) == -1
+    assert f(4, 64, 16, 0, dlm.DLM_BF16) == -1
+    assert f(4, 64, 16, 1, 7) == -1
+    assert dlm.sgmm_launches(1, 11008, 16) == 1
+    assert dlm.sgmm_launches(1, 11008, 16, 7) == 2
+    assert dlm.sgmm_launches(64, 11008, 16) == 3
+    assert dlm.sgmm_launches(64, 11008, 128) == 4
 
 
 def test_sgmm_workspace_size(lib):

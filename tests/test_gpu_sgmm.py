@@ -75,6 +75,8 @@ CASES = [
     (40, 4104, 72, 8, 16, 1.0, torch.bfloat16),      # three K slices, 4 + 4 + 1 LDS steps
     (70, 1096, 136, 16, 64, 0.5, torch.bfloat16),    # three LDS steps, rounds of N blocks per tile
     (70, 4616, 136, 16, 64, 0.5, torch.bfloat16),    # rounds of N blocks over three K slices
+    (40, 4104, 72, 4, 80, 1.0, torch.bfloat16),      # rank 80 over three K slices: the K-slice sum launch
+    (36, 2056, 1096, 3, 128, 0.5, torch.bfloat16),   # largest rank over two K slices, a ragged column group
     (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # two whole LDS steps, largest rank
     (9, 2100, 24, 4, 8, 1.0, torch.float32),         # fp32 past one slice width
     (9000, 64, 72, 8, 16, 1.0, torch.bfloat16),      # more rows than the segment's LDS caches
@@ -169,7 +171,7 @@ def test_sgmm_few_rows_single_launch(T):
     probs = [_problem(T, i, o, E, r, torch.bfloat16, 3400 + 10 * T + k) for k, (i, o) in enumerate(shapes)]
     idx = torch.tensor([[1, 5], [2, -1], [3, 3], [-1, -1]][:T], dtype=torch.int32)
     g = torch.tensor([[0.7, 0.3], [1.0, 0.5], [0.6, 0.4], [0.5, 0.5]][:T], dtype=torch.float32)
-    assert dlm.sgmm_launches(T, 11008) == 1 and dlm.sgmm_launches(T, 11008, 3) == 2
+    assert dlm.sgmm_launches(T, 11008, r) == 1 and dlm.sgmm_launches(T, 11008, r, 3) == 2
     y0s = [p[3].clone() for p in probs]
     grp = dlm.SgmmGroup(probs, E, r, 2.0)
     ws = grp.run(idx.cuda(), g.cuda())

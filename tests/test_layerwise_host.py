@@ -19,6 +19,7 @@ def _fake(projs, route_once, grouped):
     lw = LayerwiseDecode.__new__(LayerwiseDecode)
     lw.projs = projs
     lw.route_once, lw.grouped = route_once, grouped
+    lw.r = 16
     lw.dtype = torch.bfloat16
     return lw
 
@@ -29,8 +30,8 @@ def test_launches_per_token_adds_the_library_counts(route_once, grouped):
     shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
     layers = [[(_W(o, i), None, None) for o, i in shapes] for _ in range(3)]
     lw = _fake(layers, route_once, grouped)
-    per_layer = (dlm.sgmm_launches(1, 11008, len(shapes)) if grouped
-                 else sum(dlm.sgmm_launches(1, i, 1) for _, i in shapes))
+    per_layer = (dlm.sgmm_launches(1, 11008, 16, len(shapes)) if grouped
+                 else sum(dlm.sgmm_launches(1, i, 16, 1) for _, i in shapes))
     routers = 1 if route_once else len(layers)
     assert lw.launches_per_token() == routers + len(layers) * (1 + per_layer)
 
