@@ -711,7 +711,7 @@ def _sgmm_traffic_from(fetch_csv, write_csv, read):
     """Per-kernel HBM bytes of the grouped SGMM passes of --profile-kernels: the
     dispatches of the SGMM kernels, in dispatch order, split into passes where a
     segmentation launch follows another kind (a pass segments with one launch,
-    or with a count launch and a placing launch above 1024 rows); the first
+    or with a count launch and a placing launch above 8192 rows); the first
     SGMM_PROFILE_PASSES passes are the prefill, the next the mixed-decode steps
     0, 1, ...  Each counter is scaled by its own reading for the 1 GiB copy."""
     import csv

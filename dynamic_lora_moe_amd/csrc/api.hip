@@ -141,9 +141,9 @@ static int check_sets(const dlm_layers* h, const int32_t* old_idx, const float* 
 }
 
 struct dlm_sgmm_group {
-    SgDesc* d_descs = nullptr;          // device block: descriptors, then the owner tables
-    const int32_t* d_ks_owner = nullptr;
-    const int32_t* d_cb_owner = nullptr;
+    SgDesc* d_descs = nullptr;          // device block: descriptors, then their per-unit copies
+    const SgDesc* d_ks_desc = nullptr;
+    const SgDesc* d_cb_desc = nullptr;
     std::vector<SgDesc> h_descs;
     int32_t n = 0;
     int32_t E = 0, r = 0;
@@ -515,7 +515,7 @@ int check_ws(void* ws, size_t ws_bytes, const SgLayout& L) {
     return DLM_OK;
 }
 
-int run_sgmm(const SgDesc* d_descs, const int32_t* ks_owner, const int32_t* cb_owner,
+int run_sgmm(const SgDesc* d_descs, const SgDesc* ks_desc, const SgDesc* cb_desc,
              const SgDesc& single, int n_prob, int64_t total_cb,
              int64_t total_ks, int64_t d_out_max, const int32_t* idx, const float* g, int64_t T, int E, int r,
              float scale, int dtype, int packed, void* ws, const SgLayout& L, hipStream_t s,
@@ -523,8 +523,8 @@ int run_sgmm(const SgDesc* d_descs, const int32_t* ks_owner, const int32_t* cb_o
     SgmmArgs a;
     a.status_out = status_out;
     a.descs = d_descs;
-    a.ks_owner = ks_owner;
-    a.cb_owner = cb_owner;
+    a.ks_desc = ks_desc;
+    a.cb_desc = cb_desc;
     a.packed = packed;
     a.single = single;
     a.n_prob = n_prob;
@@ -719,18 +719,19 @@ int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, i
         }
         if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
     }
-    // one device block: the descriptors, then the owner of every K slice and of
-    // every expand column group (work items find their problem with one load)
+    // one device block: the descriptors, then a copy of the owning problem's
+    // descriptor for every K slice and every expand column group (a work item
+    // reads its problem with one load, not an owner index and then the table)
     const size_t desc_bytes = (sizeof(SgDesc) * n + 255) & ~(size_t)255;
-    const size_t ks_bytes = ((size_t)ks * 4 + 255) & ~(size_t)255;
-    std::vector<char> blob(desc_bytes + ks_bytes + (size_t)cb * 4);
+    const size_t ks_bytes = (sizeof(SgDesc) * (size_t)ks + 255) & ~(size_t)255;
+    std::vector<char> blob(desc_bytes + ks_bytes + sizeof(SgDesc) * (size_t)cb);
     std::memcpy(blob.data(), h->h_descs.data(), sizeof(SgDesc) * n);
-    int32_t* ks_owner = (int32_t*)(blob.data() + desc_bytes);
-    int32_t* cb_owner = (int32_t*)(blob.data() + desc_bytes + ks_bytes);
+    SgDesc* ks_desc = (SgDesc*)(blob.data() + desc_bytes);
+    SgDesc* cb_desc = (SgDesc*)(blob.data() + desc_bytes + ks_bytes);
     for (int i = 0; i < n; ++i) {
         const SgDesc& d = h->h_descs[i];
-        for (int k = 0; k < d.n_ks; ++k) ks_owner[d.ks0 + k] = i;
-        for (int k = 0; k < d.n_cb; ++k) cb_owner[d.unit0 + k] = i;
+        for (int k = 0; k < d.n_ks; ++k) ks_desc[d.ks0 + k] = d;
+        for (int k = 0; k < d.n_cb; ++k) cb_desc[d.unit0 + k] = d;
     }
     if (e == hipSuccess) e = hipMalloc((void**)&h->d_descs, blob.size());
     if (e == hipSuccess) e = hipMemcpy(h->d_descs, blob.data(), blob.size(), hipMemcpyHostToDevice);
@@ -740,8 +741,8 @@ int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, i
         delete h;
         return hip_fail(e, "sgmm_group_create");
     }
-    h->d_ks_owner = (const int32_t*)((const char*)h->d_descs + desc_bytes);
-    h->d_cb_owner = (const int32_t*)((const char*)h->d_descs + desc_bytes + ks_bytes);
+    h->d_ks_desc = (const SgDesc*)((const char*)h->d_descs + desc_bytes);
+    h->d_cb_desc = (const SgDesc*)((const char*)h->d_descs + desc_bytes + ks_bytes);
     *out = h;
     return ok();
 }
@@ -802,7 +803,7 @@ int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, in
         if (overlap(workspace, ws_bytes, idx, (size_t)T * 8) || overlap(workspace, ws_bytes, g, (size_t)T * 8))
             return fail(DLM_EINVAL, "sgmm_group_run: the workspace overlaps the sets");
     }
-    return run_sgmm(h->d_descs, h->d_ks_owner, h->d_cb_owner, h->h_descs[0], h->n, h->total_cb, h->total_ks, h->d_out_max, idx, g, T, h->E,
+    return run_sgmm(h->d_descs, h->d_ks_desc, h->d_cb_desc, h->h_descs[0], h->n, h->total_cb, h->total_ks, h->d_out_max, idx, g, T, h->E,
                     h->r, h->scale, h->dtype, h->packs.empty() ? 0 : 1, workspace, L, (hipStream_t)stream);
 }
 
@@ -825,7 +826,7 @@ int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t r, int32_t n_problems
     }
     if (T == 0) return 0;
     if (dtype == DLM_BF16 && T <= kSgmmSmallT) return n_problems == 1 ? 1 : 2;
-    const int seg = T > kSgmmSegRows ? 2 : 1;
+    const int seg = T > kSgmmSegFewRows ? 2 : 1;
     if (dtype == DLM_F32) return seg + 2;
     return seg + 2 + (d_in_max > kSgmmKSlice && r > kSgmmFoldRank ? 1 : 0);
 }

@@ -64,6 +64,9 @@ SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob) {
 namespace {
 
 constexpr int kSegThreads = 1024;  // rows per segmentation chunk
+// Up to this many chunks every placing workgroup counts all rows itself, so the
+// segmentation is one launch; more chunks get a count launch first.
+constexpr int kSegFewChunks = kSgmmSegFewRows / kSgmmSegRows;
 constexpr int kSegWaves = kSegThreads / kWave;
 constexpr int kMaxKeys = (32 + 1) * (32 + 1);
 
@@ -139,15 +142,16 @@ __device__ __forceinline__ int block_exscan(int v, int* s_tot, int& total) {
 
 // The segmentation is a stable counting sort of the rows by key, in chunks of
 // kSegThreads rows (one workgroup each):
-//   count  (only when there is more than one chunk) each chunk's key counts
-//          (LDS atomics) and whether it holds a bad set;
+//   count  (only above kSegFewChunks chunks) each chunk's key counts (LDS
+//          atomics) and whether it holds a bad set;
 //   place  each workgroup adds up, per key, every chunk's count (the key's
 //          total) and the earlier chunks' counts; an exclusive scan of the
 //          totals over the keys gives each key's first position.  A row's
 //          position = its key's first position + rows of that key in earlier
 //          chunks + in earlier waves of its chunk + earlier lanes of its wave
 //          with the same key (a lane's same-key mask is one ballot per key bit).
-//          A single-chunk batch counts its own rows here, so it needs one launch.
+//          Up to kSegFewChunks chunks every workgroup counts all rows here
+//          instead, so the batch needs one launch.
 // Each position gets its row, pair and gates, so the later kernels read a
 // tile's metadata in one round of independent loads; positions past the live
 // rows get row -1.  The first workgroup writes the header.
@@ -203,6 +207,33 @@ __global__ __launch_bounds__(kSegThreads) void sgmm_seg_place(const int32_t* __r
         if (q.bad) s_err = 1;
         if (q.key >= 0) atomicAdd(&s_tot[q.key], 1);
         for (int k = tid; k < nk; k += kSegThreads) s_base[k] = 0;
+    } else if (n_chunks <= kSegFewChunks) {
+        // every chunk's rows counted here: the keys' totals and the earlier
+        // chunks' share, one LDS atomic per distinct key of a wave; all the
+        // chunks' sets are loaded before the first is counted
+        SegRaw rr[kSegFewChunks];
+#pragma unroll
+        for (int c = 0; c < kSegFewChunks; ++c)
+            if (c < n_chunks && c != chunk) rr[c] = seg_load(idx, g, (int64_t)c * kSegThreads + tid, T);
+        for (int k = tid; k < nk; k += kSegThreads) {
+            s_tot[k] = 0;
+            s_base[k] = 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < kSegFewChunks; ++c) {
+            if (c < n_chunks) {
+                const int64_t tc = (int64_t)c * kSegThreads + tid;
+                const SegRow q = seg_row(c == chunk ? raw : rr[c], tc < T, E);
+                if (q.bad) s_err = 1;
+                const uint64_t same = wave_match(q.key, nbits);
+                if (same && (same & ((1ull << lane) - 1ull)) == 0) {
+                    const int n = (int)__popcll(same);
+                    atomicAdd(&s_tot[q.key], n);
+                    if (c < chunk) atomicAdd(&s_base[q.key], n);
+                }
+            }
+        }
     } else {
         // every chunk's counts: the key's total and the earlier chunks' share
         for (int k = tid; k < nk; k += kSegThreads) {
@@ -338,8 +369,7 @@ __device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((c
 template <int R16, bool PK>
 __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int tile0, int n_tiles) {
     constexpr int RPAD = R16 * 16;
-    const int prob = a.descs ? gld(a.ks_owner + gks) : 0;
-    const SgDesc D = a.descs ? a.descs[prob] : a.single;
+    const SgDesc D = a.descs ? a.ks_desc[gks] : a.single;
     const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
     const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
@@ -590,7 +620,7 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
     const int w = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
     const int lr = lane >> 3, lc = lane & 7;
     // every load whose address does not depend on another load goes out
-    // first: the header words, the owner of the column group, the tile's rows
+    // first: the header words, the column group's problem descriptor, the tile's rows
     // (row-major lane map: instruction i holds row 8i + lr, chunk lc), slots,
     // gates and expert mask
     int yrow[4];
@@ -598,8 +628,7 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
     for (int i = 0; i < 4; ++i) yrow[i] = gld(perm + tile * 32 + 8 * i + lr);
     const uint32_t ep = gld(epk + tile * 32 + n);
     const float g0 = gld(gpk + 2 * (tile * 32 + n)), g1 = gld(gpk + 2 * (tile * 32 + n) + 1);
-    const int prob = a.descs ? gld(a.cb_owner + cgg) : 0;
-    const SgDesc D = a.descs ? a.descs[prob] : a.single;
+    const SgDesc D = a.descs ? a.cb_desc[cgg] : a.single;
     const int cg = (int)(cgg - D.unit0);
     const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * a.L.T_pad * 2 * RPAD;
 
@@ -1033,8 +1062,7 @@ __global__ __launch_bounds__(kSmallThreads) void sgmm_small_shrink_bf16(SgmmArgs
     __shared__ float s_red[kSmallThreads / kWave][32];
     if (small_sets_bad(a)) return;
     const int64_t gks = blockIdx.x;
-    const int prob = gld(a.ks_owner + gks);
-    const SgDesc D = a.descs[prob];
+    const SgDesc D = a.ks_desc[gks];
     const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
     const int k1 = k0 + kSgmmKSlice < D.d_in ? k0 + kSgmmKSlice : D.d_in;
     const int r = a.r, RPAD = a.L.r_pad;
@@ -1055,8 +1083,7 @@ __global__ __launch_bounds__(kSmallThreads) void sgmm_small_expand_bf16(SgmmArgs
     }
     if (bad) return;
     const int64_t cgg = blockIdx.x;
-    const int prob = gld(a.cb_owner + cgg);
-    const SgDesc D = a.descs[prob];
+    const SgDesc D = a.cb_desc[cgg];
     const int r = a.r, RPAD = a.L.r_pad, nd = (int)a.T * 2 * r;
     const int64_t stride = a.L.T_pad * 2 * RPAD;  // floats per slice
     const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * stride;
@@ -1254,7 +1281,7 @@ hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
     if (!sgmm_grids_fit(a, dtype)) return hipErrorInvalidConfiguration;
     static_assert(kSegThreads == kSgmmSegRows, "segmentation chunk");
     const int64_t n_chunks = a.L.n_chunks;
-    if (n_chunks > 1) {
+    if (n_chunks > kSegFewChunks) {
         hipLaunchKernelGGL(sgmm_seg_count, dim3((unsigned)n_chunks), dim3(kSegThreads), 0, s, a.idx, a.g, a.T, a.E,
                            a.ws, a.L);
         hipError_t e0 = hipGetLastError();

@@ -43,6 +43,9 @@ SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob);
 
 // Rows per segmentation chunk (one workgroup of the segmentation kernels).
 constexpr int kSgmmSegRows = 1024;
+// Up to this many rows the segmentation is one launch (each workgroup counts
+// every chunk's rows); above it a count launch runs first.
+constexpr int kSgmmSegFewRows = 8192;
 
 // Output columns one SGMM expand work item covers (4 waves x 4 x 64).
 constexpr int kSgmmExpandCols = 1024;
@@ -56,9 +59,9 @@ constexpr int kSgmmSmallT = 4;
 enum { SG_ERR = 0, SG_NPOS = 1, SG_NTILES = 2 };
 
 struct SgmmArgs {
-    const SgDesc* descs;   // device table, or nullptr to use `single`
-    const int32_t* ks_owner;  // problem of each K slice (device; with descs)
-    const int32_t* cb_owner;  // problem of each expand column group (device; with descs)
+    const SgDesc* descs;    // device table, or nullptr to use `single`
+    const SgDesc* ks_desc;  // the owning problem's descriptor per K slice (device; with descs)
+    const SgDesc* cb_desc;  // the owning problem's descriptor per expand column group (device; with descs)
     SgDesc single;
     int32_t n_prob;
     int64_t n_expand_units;  // tiles_max * total_cb

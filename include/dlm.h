@@ -243,7 +243,7 @@ int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r,
  *   A [E][r][d_in], B [E][d_out][r].
  * Launches: segment (rows sorted by their unordered expert pair, 32-row
  * tiles, the experts each tile uses; a per-1024-row count launch first when
- * T > 1024), shrink (v = x A^T on the tile's experts
+ * T > 8192), shrink (v = x A^T on the tile's experts
  * over 2048-wide K slices staged through LDS 512 columns at a time, bf16
  * MFMA, fp32 partial results kept in the workspace), a K-slice sum in a fixed
  * order (only when d_in > 2048 and r > 64) and
@@ -345,7 +345,7 @@ int dlm_sgmm_status(void* workspace, int32_t* code, void* stream);
  * Number of kernel launches one dlm_sgmm, dlm_sgmm_noalloc or
  * dlm_sgmm_group_run call makes for T rows and n_problems problems of rank r
  * with d_in up to d_in_max: 0 for T = 0; for bf16 with T <= 4, 1 (one problem)
- * or 2; else the segmentation (2 launches when T > 1024, else 1), the shrink,
+ * or 2; else the segmentation (2 launches when T > 8192, else 1), the shrink,
  * the K-slice sum (bf16 with d_in_max > 2048 and r > 64 only: at lower ranks
  * the expand adds the slices itself) and the expand.  Returns -1 (with the last
  * error set) for a negative T, d_in_max < 1, r outside [1, DLM_MAX_RANK],

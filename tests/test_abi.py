@@ -133,11 +133,14 @@ def test_sgmm_launch_count(lib):
     assert f(64, 4096, 65, 1, dlm.DLM_BF16) == 4
     assert f(64, 2048, 128, 1, dlm.DLM_BF16) == 3
     assert f(64, 2049, 128, 1, dlm.DLM_BF16) == 4
-    # a count launch before the placement above 1024 rows
-    assert f(1025, 4096, 16, 1, dlm.DLM_BF16) == 4
-    assert f(1025, 4096, 80, 1, dlm.DLM_BF16) == 5
+    # one segmentation launch up to 8192 rows, a count launch before the
+    # placement above
+    assert f(8192, 4096, 16, 1, dlm.DLM_BF16) == 3
+    assert f(8193, 4096, 16, 1, dlm.DLM_BF16) == 4
+    assert f(8193, 4096, 80, 1, dlm.DLM_BF16) == 5
     assert f(1, 64, 16, 1, dlm.DLM_F32) == 3
-    assert f(4096, 64, 16, 1, dlm.DLM_F32) == 4
+    assert f(4096, 64, 16, 1, dlm.DLM_F32) == 3
+    assert f(8193, 64, 16, 1, dlm.DLM_F32) == 4
     assert f(-1, 64, 16, 1, dlm.DLM_BF16) == -1 and "sgmm_launches" in _err(lib)
     assert f(4, 0, 16, 1, dlm.DLM_BF16) == -1
     assert f(4, 64, 0, 1, dlm.DLM_BF16) == -1

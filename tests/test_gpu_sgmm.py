@@ -80,6 +80,7 @@ CASES = [
     (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # two whole LDS steps, largest rank
     (9, 2100, 24, 4, 8, 1.0, torch.float32),         # fp32 past one slice width
     (9000, 64, 72, 8, 16, 1.0, torch.bfloat16),      # more rows than the segment's LDS caches
+    (3000, 72, 40, 4, 8, 1.0, torch.float32),        # fp32, one segmentation launch over three chunks
     (12, 64, 64, 1, 16, 1.0, torch.bfloat16),         # one expert: every used slot is expert 0
     (7, 8, 8, 2, 1, 1.0, torch.bfloat16),             # rank 1, one 8-wide chunk of d_in
     (3, 16, 8, 1, 1, 3.0, torch.float32),
@@ -137,13 +138,22 @@ def test_sgmm_single_set_matches_gemm_reference():
     _check(x, idx, g, A, B, y0, y, 2.0, "single set")
 
 
-def test_sgmm_bad_set_is_a_noop_with_status():
-    T, d_in, d_out, E, r = 40, 64, 64, 4, 16
+@pytest.mark.parametrize("T,bads", [
+    (40, [((7, 0), 4), ((3, 1), -2), ((20, 0), None)]),
+    # one segmentation launch over three chunks: the bad row in another chunk
+    # than most workgroups' own
+    (3000, [((2990, 0), 4), ((5, 1), -2), ((1500, 0), None)]),
+    # count launch first (more than 8192 rows)
+    (9000, [((8500, 1), 4), ((100, 0), None)]),
+])
+def test_sgmm_bad_set_is_a_noop_with_status(T, bads):
+    d_in, d_out, E, r = 64, 64, 4, 16
+    print(f"[sgmm] bad sets T={T}", flush=True)
     x, A, B, y = _problem(T, d_in, d_out, E, r, torch.bfloat16, 3102)
     y0 = y.clone()
     idx, g = _sets(T, E, np.random.default_rng(9), 0, 0, 0)
     ws = dlm.sgmm_workspace(T, d_in, E, r)
-    for bad_i, bad_g in [((7, 0), 4), ((3, 1), -2), ((20, 0), None)]:
+    for bad_i, bad_g in bads:
         ii, gg = idx.clone(), g.clone()
         if bad_g is None:
             gg[bad_i] = float("nan")
@@ -275,7 +285,8 @@ def _host_segmentation(idx: np.ndarray, E: int):
     return order.astype(np.int32), key
 
 
-@pytest.mark.parametrize("T,E,seed", [(9000, 8, 1), (4096, 8, 2), (2500, 32, 3), (1500, 4, 4), (1025, 2, 5)])
+@pytest.mark.parametrize("T,E,seed", [(9000, 8, 1), (4096, 8, 2), (2500, 32, 3), (1500, 4, 4), (1025, 2, 5),
+                                      (8192, 16, 6), (8193, 3, 7)])
 def test_segment_order_equals_host_stable_sort(T, E, seed):
     """The row order the segmentation writes (the workspace's perm list, after
     the 256-byte header) is the stable sort of the rows by unordered pair, bit
