@@ -76,6 +76,10 @@ CASES = [
     (70, 1096, 136, 16, 64, 0.5, torch.bfloat16),    # three LDS steps, rounds of N blocks per tile
     (70, 4616, 136, 16, 64, 0.5, torch.bfloat16),    # rounds of N blocks over three K slices
     (40, 4104, 72, 4, 80, 1.0, torch.bfloat16),      # rank 80 over three K slices: the K-slice sum launch
+    (60, 4104, 200, 8, 24, 1.0, torch.bfloat16),     # two rank chunks, three K slices added by the expand
+    (70, 2568, 520, 16, 32, 1.0, torch.bfloat16),    # two whole rank chunks, two K slices
+    (45, 6152, 136, 4, 40, 0.5, torch.bfloat16),     # three rank chunks (r % 16 != 0), four K slices
+    (33, 4608, 64, 8, 48, 2.0, torch.bfloat16),      # three whole rank chunks, three K slices
     (36, 2056, 1096, 3, 128, 0.5, torch.bfloat16),   # largest rank over two K slices, a ragged column group
     (100, 1024, 64, 8, 128, 1.0, torch.bfloat16),    # two whole LDS steps, largest rank
     (9, 2100, 24, 4, 8, 1.0, torch.float32),         # fp32 past one slice width
@@ -209,9 +213,13 @@ def test_sgmm_few_rows_single_launch(T):
     grp.close()
 
 
-def test_sgmm_group_matches_single_calls():
-    T, E, r = 50, 8, 16
-    shapes = [(64, 128), (200, 64), (96, 264)]
+@pytest.mark.parametrize("r,shapes", [
+    (16, [(64, 128), (200, 64), (96, 264)]),
+    # several K slices per problem (the expand adds them), different counts per problem
+    (24, [(4104, 136), (2056, 64), (96, 1040)]),
+])
+def test_sgmm_group_matches_single_calls(r, shapes):
+    T, E = 50, 8
     probs = [_problem(T, i, o, E, r, torch.bfloat16, 3200 + k) for k, (i, o) in enumerate(shapes)]
     idx, g = _sets(T, E, np.random.default_rng(11))
     y0s = [p[3].clone() for p in probs]

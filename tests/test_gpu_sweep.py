@@ -90,6 +90,31 @@ def test_sgmm_sweep(i):
     assert torch.equal(y.cpu()[none], y0[none])
 
 
+N_SGMM_WIDE = 8
+
+
+@pytest.mark.parametrize("i", range(N_SGMM_WIDE))
+def test_sgmm_sweep_several_k_slices(i):
+    """Random shapes with d_in past one 2048-wide K slice (2 to 5 slices), every
+    rank class: the expand adds the slices' partials itself up to rank 64, a
+    K-slice sum launch does it above."""
+    rng = np.random.default_rng(83000 + i)
+    T = int(rng.integers(1, 300))
+    d_in = 8 * int(rng.integers(257, 1250))
+    d_out = 8 * int(rng.integers(1, 60))
+    E = int(rng.choice([1, 2, 4, 8, 16]))
+    r = _rank(rng)
+    scale = float(rng.choice([0.5, 1.0, 2.0]))
+    print(f"[sweep sgmm wide {i}] T={T} d_in={d_in} d_out={d_out} E={E} r={r} scale={scale}", flush=True)
+    x, A, B, y = _problem(T, d_in, d_out, E, r, torch.bfloat16, 84000 + i)
+    idx, g = _sets(T, E, np.random.default_rng(85000 + i))
+    y0 = y.cpu().clone()
+    ws = dlm.sgmm_workspace(T, d_in, E, r)
+    dlm.sgmm(x, idx.cuda(), g.cuda(), A, B, y, scale, ws)
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    _check(x, idx, g, A, B, y0, y, scale, f"sgmm wide sweep {i}")
+
+
 N_ROUTER = 24
 N_PRODUCT = 20
 
