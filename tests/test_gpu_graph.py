@@ -193,3 +193,97 @@ def test_switch_gemv_per_layer_graph_replays_match_eager():
     for h, _, _ in layers:
         assert h.status() == dlm.DLM_OK
         h.close()
+
+
+# ---- launch counts: the kernel nodes of a captured call -----------------------
+
+_HIP = None
+
+
+def _kernel_nodes(graph) -> int:
+    """Kernel nodes of a captured (not instantiated) graph, read with
+    hipGraphGetNodes / hipGraphNodeGetType (hipGraphNodeTypeKernel = 0)."""
+    import ctypes
+    global _HIP
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+    h = ctypes.c_void_p(graph.raw_cuda_graph())
+    n = ctypes.c_size_t(0)
+    assert _HIP.hipGraphGetNodes(h, None, ctypes.byref(n)) == 0
+    nodes = (ctypes.c_void_p * max(n.value, 1))()
+    assert _HIP.hipGraphGetNodes(h, nodes, ctypes.byref(n)) == 0
+    kernels = 0
+    for i in range(n.value):
+        kind = ctypes.c_int(-1)
+        assert _HIP.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(kind)) == 0
+        kernels += kind.value == 0
+    return kernels
+
+
+def _captured(fn) -> int:
+    """Kernel launches fn makes, counted from a capture of it (never replayed)."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph(keep_graph=True)
+    with torch.cuda.graph(g):
+        fn()
+    n = _kernel_nodes(g)
+    g.reset()
+    return n
+
+
+@pytest.mark.parametrize("T,shapes,E,r,dt,group,want", [
+    (2, [(4104, 1032)], 8, 16, torch.bfloat16, False, 1),                       # few rows, one launch
+    (3, [(4104, 1032), (200, 264), (11008, 4096)], 8, 16, torch.bfloat16, True, 2),  # few rows, a group
+    (64, [(4104, 200), (2056, 64)], 8, 16, torch.bfloat16, True, 3),           # segment, shrink, expand
+    (64, [(4104, 72)], 4, 80, torch.bfloat16, False, 4),                        # + the K-slice sum (r > 64)
+    (9000, [(64, 72)], 8, 16, torch.bfloat16, False, 4),                        # + the count launch (T > 8192)
+    (40, [(72, 40)], 4, 8, torch.float32, False, 3),                            # fp32
+])
+def test_sgmm_launch_count_matches_captured_kernels(T, shapes, E, r, dt, group, want):
+    """dlm_sgmm_launches (the count the layer-wise decode and the bench report)
+    equals the kernel nodes a capture of the call records."""
+    from test_gpu_sgmm import _problem, _sets as _sgmm_sets
+    print(f"[graph] launch count T={T} shapes={shapes} r={r} {dt} group={group}", flush=True)
+    probs = [_problem(T, i, o, E, r, dt, 5100 + k) for k, (i, o) in enumerate(shapes)]
+    idx, g = _sgmm_sets(T, E, np.random.default_rng(5200))
+    idx, g = idx.cuda(), g.cuda()
+    d_in_max = max(i for i, _ in shapes)
+    assert dlm.sgmm_launches(T, d_in_max, r, len(shapes), dt) == want
+    if group:
+        grp = dlm.SgmmGroup(probs, E, r, 1.0)
+        ws = grp.workspace(T)
+        grp.run(idx, g, workspace=ws)  # first call outside the capture
+        assert _captured(lambda: grp.run(idx, g, workspace=ws)) == want
+        grp.close()
+    else:
+        (x, A, B, y), = probs
+        ws = dlm.sgmm_workspace(T, shapes[0][0], E, r)
+        dlm.sgmm(x, idx, g, A, B, y, 1.0, ws)
+        assert _captured(lambda: dlm.sgmm(x, idx, g, A, B, y, 1.0, ws)) == want
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+
+
+def test_switch_launch_counts_match_captured_kernels():
+    """dlm_switch: one launch for every weight of every layer; dlm_switch_gemv:
+    the counted two; dlm_gemv: one."""
+    print("[graph] switch launch counts", flush=True)
+    E, r = 4, 16
+    shapes = [(264, 512), (512, 264), (96, 1040)]
+    model = []
+    for k, (o, i) in enumerate(shapes):
+        W = synth.normal_device((o, i), 0.05, torch.bfloat16, "cuda", (5300, k), "W")
+        A = synth.normal_device((E, r, i), 0.05, torch.bfloat16, "cuda", (5300, k), "A")
+        B = synth.normal_device((E, o, r), 0.05, torch.bfloat16, "cuda", (5300, k), "B")
+        model.append((W, A, B))
+    L = dlm.Layers(model, E, r, 1.0)
+    xs = [synth.normal_device((i,), 1.0, torch.bfloat16, "cuda", (5301, k), "x") for k, (_, i) in enumerate(shapes)]
+    ys = [torch.zeros(o, dtype=torch.float32, device="cuda") for o, _ in shapes]
+    L.bind_vectors(xs, ys)
+    new = (torch.tensor([1, 3], dtype=torch.int32, device="cuda"), torch.tensor([0.6, 0.4], device="cuda"))
+    old = (torch.tensor([0, -1], dtype=torch.int32, device="cuda"), torch.tensor([1.0, 0.0], device="cuda"))
+    L.switch(None, old)
+    assert _captured(lambda: L.switch(old, new)) == L.launches_per_switch() == 1
+    assert _captured(lambda: L.switch_gemv(old, new)) == L.launches_per_switch_gemv() == 2
+    assert _captured(lambda: L.gemv()) == 1
+    assert L.status() == dlm.DLM_OK
+    L.close()
