@@ -296,7 +296,7 @@ def _ws_bytes(workspace) -> int:
 def sgmm(x, idx, g, A, B, y, scale: float, workspace=None, stream=None):
     """y += sum_k s g_k (x A_k^T) B_k^T row by row, in place (returns y).
 
-    With a workspace the call only enqueues; read the device's verdict on the
+    With a workspace the call only enqueues; read the device's decision on the
     sets with sgmm_status(workspace).  Without one it allocates a workspace,
     waits for the launches (so the temporary outlives them) and raises
     DLMError(DLM_EDEVICE) if the device rejected a set (y is then unchanged)."""

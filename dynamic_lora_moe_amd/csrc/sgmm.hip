@@ -901,7 +901,7 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 constexpr int kSmallThreads = 512;
 constexpr int kSmallMaxR = 128;
 
-// Every thread checks every row's set; workgroup 0 publishes the verdict.
+// Every thread checks every row's set; workgroup 0 publishes the result.
 __device__ __forceinline__ bool small_sets_bad(const SgmmArgs& a) {
     bool bad = false;
     for (int q = 0; q < 2 * (int)a.T; ++q) {
@@ -1075,7 +1075,7 @@ __global__ __launch_bounds__(kSmallThreads) void sgmm_small_shrink_bf16(SgmmArgs
 // slices added in slice order.
 __global__ __launch_bounds__(kSmallThreads) void sgmm_small_expand_bf16(SgmmArgs a) {
     __shared__ float s_v[kSgmmSmallT][2][kSmallMaxR];
-    bool bad = false;  // the first launch published the verdict
+    bool bad = false;  // the first launch published the result
     for (int q = 0; q < 2 * (int)a.T; ++q) {
         const int e = gld(a.idx + q);
         const float g = gld(a.g + q);
