@@ -378,7 +378,10 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
     __shared__ __attribute__((aligned(16))) uint16_t s_x[kXRows * kShrinkStep];
     __shared__ int s_U[32];
     __shared__ int s_nU;
-    __shared__ int s_row[kXRows], s_e0[kXRows], s_e1[kXRows];
+    __shared__ int s_row[kXRows];
+    // per row: slot 0's expert + 1 (bits 0-5), slot 1's + 1 (bits 6-11), bit 12
+    // set for a padding position (no row)
+    __shared__ __attribute__((aligned(16))) uint16_t s_slots[kXRows];
     const int tid = threadIdx.x;
     static_assert(kXRows <= kWave, "one wave reads the tile's rows");
     if (tid < kWave) {
@@ -391,8 +394,7 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
             const uint32_t ep = in ? gld(epk + p) : 0xffffffffu;
             const int e0 = (int16_t)(ep & 0xffffu), e1 = (int16_t)(ep >> 16);
             s_row[tid] = row;
-            s_e0[tid] = e0;
-            s_e1[tid] = e1;
+            s_slots[tid] = (uint16_t)((e0 + 1) | ((e1 + 1) << 6) | (row < 0 ? 1 << 12 : 0));
             m = (e0 >= 0 ? 1u << e0 : 0u) | (e1 >= 0 ? 1u << e1 : 0u);
         }
 #pragma unroll
@@ -474,13 +476,20 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
     auto store_v = [&](const f32x16& acc, int u, int rho, int h) {
         if (u >= nU || rho >= r) return;
         const int e = s_U[u];
+        // the slots of this lane's 16 rows (8j + 4h + [0,4)): four 8-byte LDS
+        // reads issued together, not a dependent read before every store
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        u32x2_t sl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sl[j] = *(const u32x2_t*)(s_slots + 8 * j + 4 * h);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int m = 8 * (i >> 2) + 4 * h + (i & 3);
-            if (s_row[m] < 0) continue;
+            const uint32_t s = (sl[i >> 2][(i & 3) >> 1] >> (16 * (i & 1))) & 0xffffu;
+            if (s >> 12) continue;
             float* vp = v + ((int64_t)(tile0 * 32 + m) * 2) * RPAD + rho;
-            if (s_e0[m] == e) gst(vp, acc[i]);
-            if (s_e1[m] == e) gst(vp + RPAD, acc[i]);
+            if ((int)(s & 63u) - 1 == e) gst(vp, acc[i]);
+            if ((int)((s >> 6) & 63u) - 1 == e) gst(vp + RPAD, acc[i]);
         }
     };
     u32x4 ab[kShrinkRing][4];
