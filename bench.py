@@ -159,6 +159,9 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
                 product and one grouped SGMM with that set;
       pregated_unmerged_2s: the same with each layer's SGMM on a second stream
                 beside its base product (joined before the next layer);
+      pregated_unmerged_fused: the router once per token, then per layer one
+                dlm_gemv_unmerged (2 launches: the adapters' down-projections,
+                then the base product with their up-projections added);
       unfused:  pre-gated: router once, one switch over all 224 weights, then one
                 product launch per layer (W read twice, written once: 3 x 12.95 GB);
       fused:    pre-gated: router once, then per layer the switch fused with the
@@ -190,7 +193,9 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
           "layerwise_grouped": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r, wl.scale,
                                                grouped=True),
           "pregated_unmerged": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r, wl.scale,
-                                               grouped=True, route_once=True)}
+                                               grouped=True, route_once=True),
+          "pregated_unmerged_fused": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r,
+                                                     wl.scale, route_once=True, fused=True)}
     x_tok = torch.empty((1, wl.d_model), dtype=wl.dtype, device="cuda")
     idx = [torch.zeros((1, 2), dtype=torch.int32, device="cuda") for _ in range(2)]
     g = [torch.zeros((1, 2), dtype=torch.float32, device="cuda") for _ in range(2)]
@@ -222,7 +227,8 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
     w_bytes = wl.switch_w_elems() * 2
     pre_gated = ("unfused", "fused")
     side = torch.cuda.Stream()
-    for kind in ("base", "layerwise", "layerwise_grouped", "pregated_unmerged", "pregated_unmerged_2s") + pre_gated:
+    for kind in ("base", "layerwise", "layerwise_grouped", "pregated_unmerged", "pregated_unmerged_2s",
+                 "pregated_unmerged_fused") + pre_gated:
         out = {}
         with torch.cuda.stream(s):
             # eager: token 0 from the merged-in-nothing state, then n-1 switches

@@ -78,6 +78,8 @@ def load(path: str = LIB_PATH):
         "dlm_gemv": ([P, P], C.c_int),
         "dlm_switch_gemv": ([P, P, P, P, P, P], C.c_int),
         "dlm_switch_gemv_launches": ([P], C.c_int),
+        "dlm_gemv_unmerged": ([P, P, P, P], C.c_int),
+        "dlm_gemv_unmerged_launches": ([P], C.c_int),
         "dlm_sgmm_launches": ([I64, I64, I32, I32, I32], C.c_int),
         "dlm_sgmm_group_repack": ([P, P], C.c_int),
         "dlm_sgmm_group_run": ([P, P, P, I64, P, C.c_size_t, P], C.c_int),
@@ -256,6 +258,17 @@ class Layers:
 
     def launches_per_switch_gemv(self) -> int:
         return load().dlm_switch_gemv_launches(self._h)
+
+    def gemv_unmerged(self, new, stream=None):
+        """y_i = W_i x_i + s sum_k g_k B_k (A_k x_i) for the set new = (idx
+        int32[2], g fp32[2]) on the device (bound vectors); W is not modified."""
+        ni, ng = _set_ptrs(new)
+        if not ni:
+            raise ValueError("gemv_unmerged needs a set (idx, g)")
+        _check(load().dlm_gemv_unmerged(self._h, ni, ng, _stream(stream)), "dlm_gemv_unmerged")
+
+    def launches_per_gemv_unmerged(self) -> int:
+        return load().dlm_gemv_unmerged_launches(self._h)
 
     def repack(self, stream=None):
         """Refresh the packed A copy (ranks 17..64, bf16) after changing an A bank in place."""

@@ -110,6 +110,8 @@ struct dlm_layers {
     void* d_pack = nullptr;       // packed A images of every weight, then the zero image (wide tiles)
     void* d_zimg = nullptr;
     float* d_part = nullptr;      // partial products of the fused switch + product (bound vectors)
+    float* d_vpart = nullptr;     // rank-vector partials of the unmerged product (bound vectors)
+    int64_t n_ks = 0;             // their K slices over all weights
     bool bound = false;           // dlm_layers_bind_vectors has been called
     int64_t n_blocks = 0, n_bands = 0;  // product blocks (kGemvRows rows) and 256-row bands over all weights
     std::vector<SwDesc> h_descs;
@@ -337,6 +339,7 @@ int dlm_layers_destroy(dlm_layers* h) {
     if (h->d_err) (void)hipFree(h->d_err);
     if (h->d_pack) (void)hipFree(h->d_pack);
     if (h->d_part) (void)hipFree(h->d_part);
+    if (h->d_vpart) (void)hipFree(h->d_vpart);
     delete h;
     if (e != hipSuccess) return hip_fail(e, "layers_destroy");
     return ok();
@@ -356,6 +359,7 @@ static SwitchArgs switch_args(const dlm_layers* h, const int32_t* old_idx, const
     a.new_g = new_g;
     a.err = h->d_err;
     a.zimg = h->d_zimg;
+    a.vpart = h->d_vpart;
     if (h->dtype == DLM_BF16) {
         a.n_units = h->n_tiles;
         a.per_xcd = h->per_xcd;
@@ -409,9 +413,18 @@ int dlm_layers_bind_vectors(dlm_layers* h, const void* const* x, float* const* y
         if (write_conflict(std::move(v), &a, &b)) return conflict_fail("bind_vectors", a, b);
     }
     float* part = nullptr;
+    float* vpart = nullptr;
+    // the unmerged product's K slices: per weight a prefix and a count
+    int64_t n_ks = 0;
+    for (int i = 0; i < h->n; ++i) {
+        d[i].ks0 = n_ks;
+        d[i].n_ks = (int32_t)((d[i].d_in + kLoraKSlice - 1) / kLoraKSlice);
+        n_ks += d[i].n_ks;
+    }
     // launches still in flight on any stream read the current table and
-    // partial buffer: let them finish before either is replaced
+    // partial buffers: let them finish before any is replaced
     hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMalloc((void**)&vpart, (size_t)n_ks * 2 * h->r * sizeof(float));
     if (e == hipSuccess && switch_gemv_fused(h->tile, h->dtype)) {
         size_t total = 0;
         for (const SwDesc& q : d) total += (size_t)q.n_ct * q.d_out;
@@ -425,10 +438,14 @@ int dlm_layers_bind_vectors(dlm_layers* h, const void* const* x, float* const* y
     if (e == hipSuccess) e = hipMemcpy(h->d_descs, d.data(), sizeof(SwDesc) * h->n, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         if (part) (void)hipFree(part);
+        if (vpart) (void)hipFree(vpart);
         return hip_fail(e, "bind_vectors");
     }
     if (h->d_part) (void)hipFree(h->d_part);
+    if (h->d_vpart) (void)hipFree(h->d_vpart);
     h->d_part = part;
+    h->d_vpart = vpart;
+    h->n_ks = n_ks;
     h->h_descs = std::move(d);
     h->bound = true;
     return ok();
@@ -464,6 +481,20 @@ int dlm_switch_gemv(dlm_layers* h, const int32_t* old_idx, const float* old_g, c
 }
 
 int dlm_switch_gemv_launches(const dlm_layers* h) { return h ? 2 : 0; }
+
+int dlm_gemv_unmerged(dlm_layers* h, const int32_t* idx, const float* g, void* stream) {
+    if (!h) return fail(DLM_EINVAL, "gemv_unmerged: null handle");
+    if (!h->bound) return fail(DLM_EINVAL, "gemv_unmerged: no vectors bound (dlm_layers_bind_vectors)");
+    if (!idx || !g) return fail(DLM_EINVAL, "gemv_unmerged: idx or g is null");
+    const int rc = check_sets(h, nullptr, nullptr, idx, g, "gemv_unmerged");
+    if (rc != DLM_OK) return rc;
+    const SwitchArgs a = switch_args(h, nullptr, nullptr, idx, g);
+    const hipError_t e = launch_gemv_unmerged(a, h->n_ks, h->n_blocks, h->dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gemv_unmerged launch");
+    return ok();
+}
+
+int dlm_gemv_unmerged_launches(const dlm_layers* h) { return h ? 2 : 0; }
 
 int dlm_layers_status(dlm_layers* h, int32_t* code, void* stream) {
     if (!h || !code) return fail(DLM_EINVAL, "layers_status: null argument");

@@ -34,6 +34,8 @@ struct SwDesc {
     float* part;        // [n_ct][d_out] fp32 per-column-tile partial products (fused path)
     int64_t rb0;        // index of its first kGemvRows-row block in a product launch
     int64_t rt0;        // index of its first 256-row band in a partial-sum launch
+    int64_t ks0;        // index of its first kLoraKSlice-wide K slice (unmerged product)
+    int32_t n_ks;       // its K slices
 };
 
 struct SwitchArgs {
@@ -49,6 +51,7 @@ struct SwitchArgs {
     const float* new_g;
     int32_t* err;
     const void* zimg;   // one all-zero A image (inactive slots of the wide tiles)
+    float* vpart;       // unmerged product: per K slice the partial rank vectors [2][r]
 };
 
 // Tile geometry of the bf16 MFMA switch for a padded rank.
@@ -79,6 +82,17 @@ hipError_t launch_gemv(const SwitchArgs& a, int64_t n_blocks, int dtype, hipStre
 bool switch_gemv_fused(const SwTile& t, int dtype);
 hipError_t launch_switch_gemv_bf16(const SwitchArgs& a, hipStream_t s);
 hipError_t launch_gemv_reduce(const SwitchArgs& a, int64_t n_bands, hipStream_t s);
+
+// The product with one set's adapters unmerged (W untouched):
+//   y = W x + sum_k c_k B_{e_k} (A_{e_k} x),  c = s g,
+// in two launches: the rank vectors A_e x per (weight, kLoraKSlice-wide K
+// slice, group of 8 rank vectors) into a.vpart (n_ks_total slices), then the
+// product, each row adding its adapters' B row times the slices' sum.  Sets
+// the switch rejects write nothing (the first launch sets the error word).
+// a.new_idx / a.new_g must be non-null and a.old_idx null.
+constexpr int kLoraKSlice = 2048;
+hipError_t launch_gemv_unmerged(const SwitchArgs& a, int64_t n_ks_total, int64_t n_blocks, int dtype,
+                                hipStream_t s);
 
 // Packed A images used by the wide tiles (ranks 17..64, bf16): for expert e and
 // 64-column block cb of a weight, one contiguous image of the block's A slice

@@ -69,22 +69,42 @@ struct Sets {
     bool ok;
 };
 
-// Reads both sets from device memory (every thread reads the same words, so
-// every decision below is uniform), validates them and orders each set's two
-// slots canonically by (expert, coefficient).
-__device__ __forceinline__ Sets read_sets(const SwitchArgs& a) {
-    Sets s;
-    s.ok = true;
+// The two sets' raw words (an absent set reads as both slots empty).
+struct SetWords {
+    int e[4];
+    float g[4];
+};
+
+__device__ __forceinline__ SetWords load_sets(const SwitchArgs& a) {
+    SetWords w;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int32_t* ip = h == 0 ? a.new_idx : a.old_idx;
         const float* gp = h == 0 ? a.new_g : a.old_g;
-        int e0 = -1, e1 = -1;
-        float c0 = 0.f, c1 = 0.f;
+        w.e[2 * h] = w.e[2 * h + 1] = -1;
+        w.g[2 * h] = w.g[2 * h + 1] = 0.f;
         if (ip != nullptr) {
-            e0 = ip[0];
-            e1 = ip[1];
-            const float g0 = gp[0], g1 = gp[1];
+            w.e[2 * h] = ip[0];
+            w.e[2 * h + 1] = ip[1];
+            w.g[2 * h] = gp[0];
+            w.g[2 * h + 1] = gp[1];
+        }
+    }
+    return w;
+}
+
+// Validates both sets (every thread reads the same words, so every decision
+// below is uniform) and orders each set's two slots canonically by (expert,
+// coefficient).
+__device__ __forceinline__ Sets check_sets(const SwitchArgs& a, const SetWords& w) {
+    Sets s;
+    s.ok = true;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int e0 = w.e[2 * h], e1 = w.e[2 * h + 1];
+        float c0 = 0.f, c1 = 0.f;
+        {
+            const float g0 = w.g[2 * h], g1 = w.g[2 * h + 1];
             if (e0 < -1 || e0 >= a.E || e1 < -1 || e1 >= a.E) s.ok = false;
             if (e0 >= 0 && !__builtin_isfinite(g0)) s.ok = false;
             if (e1 >= 0 && !__builtin_isfinite(g1)) s.ok = false;
@@ -103,12 +123,16 @@ __device__ __forceinline__ Sets read_sets(const SwitchArgs& a) {
     return s;
 }
 
+// Reads both sets from device memory and validates them.
+__device__ __forceinline__ Sets read_sets(const SwitchArgs& a) { return check_sets(a, load_sets(a)); }
+
 // Which prefix a launch's work units are numbered by.
-enum { kKeyElem = 0, kKeyTile = 1, kKeyRowBlock = 2, kKeyBand = 3 };
+enum { kKeyElem = 0, kKeyTile = 1, kKeyRowBlock = 2, kKeyBand = 3, kKeyKSlice = 4 };
 
 template <int K>
 __device__ __forceinline__ int64_t desc_key(const SwDesc& d) {
-    return K == kKeyElem ? d.elem0 : (K == kKeyTile ? d.tile0 : (K == kKeyRowBlock ? d.rb0 : d.rt0));
+    return K == kKeyElem ? d.elem0
+                         : (K == kKeyTile ? d.tile0 : (K == kKeyRowBlock ? d.rb0 : (K == kKeyBand ? d.rt0 : d.ks0)));
 }
 
 template <int K>
@@ -751,17 +775,11 @@ constexpr int kGemvUnroll = 4;  // 16-byte chunks of the row in flight per lane
 // Blocks run last-first: in a layer the longest rows (the MLP's down
 // projection) come last, so they start early instead of forming the tail.
 
+// W row . x for one wave: lanes over 16-byte chunks of the row (kGemvUnroll in
+// flight), fp32 FMA chains, then a fixed-order butterfly (every lane ends with
+// the row's sum).
 template <typename T>
-__global__ __launch_bounds__(kWaves* kWave) void gemv_kernel(SwitchArgs a, int64_t n_blocks) {
-    const int64_t t = n_blocks - 1 - (int64_t)blockIdx.x;
-    if (t < 0 || !read_sets(a).ok) return;
-    const SwDesc D = a.descs[find_desc<kKeyRowBlock>(a.descs, a.n_desc, t)];
-    const int d_in = D.d_in, d_out = D.d_out;
-    const int lane = lane_id();
-    const int row = (int)(t - D.rb0) * kGemvRows + wave_id();
-    if (row >= d_out) return;
-    const T* __restrict__ Wr = (const T*)D.W + (int64_t)row * d_in;
-    const T* __restrict__ x = (const T*)D.xv;
+__device__ __forceinline__ float row_dot(const T* __restrict__ Wr, const T* __restrict__ x, int d_in, int lane) {
     float acc = 0.f;
     if constexpr (sizeof(T) == 2) {
         const int nch = d_in / 8;
@@ -805,7 +823,221 @@ __global__ __launch_bounds__(kWaves* kWave) void gemv_kernel(SwitchArgs a, int64
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    return acc;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWaves* kWave) void gemv_kernel(SwitchArgs a, int64_t n_blocks) {
+    const int64_t t = n_blocks - 1 - (int64_t)blockIdx.x;
+    if (t < 0 || !read_sets(a).ok) return;
+    const SwDesc D = a.descs[find_desc<kKeyRowBlock>(a.descs, a.n_desc, t)];
+    const int d_in = D.d_in, d_out = D.d_out;
+    const int lane = lane_id();
+    const int row = (int)(t - D.rb0) * kGemvRows + wave_id();
+    if (row >= d_out) return;
+    const float acc = row_dot<T>((const T*)D.W + (int64_t)row * d_in, (const T*)D.xv, d_in, lane);
     if (lane == 0) gst(D.yv + row, acc);
+}
+
+// ---- the product with one set's adapters unmerged ---------------------------
+//
+// The pre-gated decision with the adapters left unmerged (the token's set,
+// made once, applied by every layer; W is never rewritten):
+//     y = W x + c_0 B_{e_0} (A_{e_0} x) + c_1 B_{e_1} (A_{e_1} x),  c = s g.
+// First launch: one workgroup per (weight, kLoraKSlice-wide K slice, group of
+// kLoraDots rank vectors) computes the slice's partials sum_j x[j] A[e_k][rho][j]
+// of its group's dots d = k r + rho (each thread one 16-byte chunk of the slice,
+// every load of a chunk issued before its FMAs, a wave butterfly, then the waves
+// in order).  Second launch: the product kernel, each row then adding
+// sum_{k, rho} (c_k v_k[rho]) B[e_k][row][rho], with v_k the slices' partials
+// added in slice order; lane l takes the terms (k, rho) = (l / r, l % r) for
+// l = lane, lane + 64, ..., they are added with the product's butterfly, and
+// y = W x + terms (one more rounding).  The operands of the first term and its
+// first slices are loaded before the row's stream, so their latency is hidden
+// behind it.  The first launch is short and latency-bound, so its work is cut
+// finely (a 7B-shaped layer: 72 workgroups) and its descriptor lookup is one
+// vector load and a ballot instead of a dependent search.
+constexpr int kLoraDots = 8;
+constexpr int kLoraPre = 8;  // slices of the first term loaded ahead
+
+// The fields the first launch reads of the weight holding K slice u (ks0
+// ascends over the descriptors).  Up to 64 descriptors, lane i loads key and
+// fields of descriptor i in one round and the holder's copy is read from its
+// lane; past 64, a ballot per 64 keys finds the holder, then its fields load.
+struct LoraDesc {
+    int64_t ks0;
+    const void* xv;
+    const void* A;
+    int d_in;
+};
+
+__device__ __forceinline__ int64_t lane64(int64_t v, int l) {
+    const uint64_t b = (uint64_t)v;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ LoraDesc lora_desc(const SwDesc* __restrict__ d, int n, int64_t u) {
+    LoraDesc D;
+    const int lane = lane_id();
+    if (n <= kWave) {
+        int64_t key = INT64_MAX, xv = 0, A = 0;
+        int d_in = 0;
+        if (lane < n) {
+            key = d[lane].ks0;
+            xv = (int64_t)d[lane].xv;
+            A = (int64_t)d[lane].A;
+            d_in = d[lane].d_in;
+        }
+        const int sel = __popcll(__ballot(key <= u)) - 1;  // descriptor 0 starts at slice 0
+        D.ks0 = lane64(key, sel);
+        D.xv = (const void*)lane64(xv, sel);
+        D.A = (const void*)lane64(A, sel);
+        D.d_in = __builtin_amdgcn_readlane(d_in, sel);
+        return D;
+    }
+    int idx = -1;
+    for (int b0 = 0; b0 < n; b0 += kWave) {
+        const int i = b0 + lane;
+        const uint64_t m = __ballot(i < n && d[i].ks0 <= u);
+        idx += __popcll(m);
+        if (m != ~0ull) break;
+    }
+    idx = uniform(idx);
+    D.ks0 = d[idx].ks0;
+    D.xv = d[idx].xv;
+    D.A = d[idx].A;
+    D.d_in = d[idx].d_in;
+    return D;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWaves* kWave) void lora_shrink_kernel(SwitchArgs a, int n_dg) {
+    // the grid is exactly the work units (slices x dot groups, < 2^31); the
+    // set is always given (the entry point refuses a null one) and there is
+    // no old set, so the set words load unconditionally, in flight with the
+    // descriptor round
+    const int u = blockIdx.x;
+    const int gks = u / n_dg;
+    const int d0 = (u - gks * n_dg) * kLoraDots;
+    SetWords sw;
+    sw.e[0] = a.new_idx[0];
+    sw.e[1] = a.new_idx[1];
+    sw.g[0] = a.new_g[0];
+    sw.g[1] = a.new_g[1];
+    sw.e[2] = sw.e[3] = -1;
+    sw.g[2] = sw.g[3] = 0.f;
+    const LoraDesc D = lora_desc(a.descs, a.n_desc, gks);
+    const Sets sc = check_sets(a, sw);
+    if (!sc.ok) {
+        if (u == 0 && threadIdx.x == 0) *a.err = 1;
+        return;
+    }
+    const int d_in = D.d_in, r = a.r, nd = 2 * r;
+    const int k0 = (int)(gks - D.ks0) * kLoraKSlice;
+    const int k1 = k0 + kLoraKSlice < d_in ? k0 + kLoraKSlice : d_in;
+    const T* __restrict__ x = (const T*)D.xv;
+    const T* __restrict__ A = (const T*)D.A;
+    __shared__ float s_red[kWaves][kLoraDots];
+    const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
+    float p[kLoraDots];
+#pragma unroll
+    for (int i = 0; i < kLoraDots; ++i) p[i] = 0.f;
+    // dot d = k r + rho; past nd the last dot again (not stored)
+    auto a_row = [&](int i) {
+        const int d = d0 + i < nd ? d0 + i : nd - 1;
+        const int k = d >= r ? 1 : 0;
+        const int e = k ? sc.e[1] : sc.e[0];
+        return A + ((int64_t)(e >= 0 ? e : 0) * r + (d - k * r)) * d_in;
+    };
+    if constexpr (sizeof(T) == 2) {
+        for (int c = k0 / 8 + tid; c < k1 / 8; c += kWaves * kWave) {
+            const u32x4 xv = ld128(x + 8 * c);
+            u32x4 av[kLoraDots];
+#pragma unroll
+            for (int i = 0; i < kLoraDots; ++i) av[i] = ld128(a_row(i) + 8 * c);
+#pragma unroll
+            for (int i = 0; i < kLoraDots; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    p[i] = fmaf(bf_lo(xv[q]), bf_lo(av[i][q]), p[i]);
+                    p[i] = fmaf(bf_hi(xv[q]), bf_hi(av[i][q]), p[i]);
+                }
+        }
+    } else {
+        for (int j = k0 + tid; j < k1; j += kWaves * kWave) {
+            const float xv = gld(x + j);
+#pragma unroll
+            for (int i = 0; i < kLoraDots; ++i) p[i] = fmaf(xv, gld(a_row(i) + j), p[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kLoraDots; ++i) {
+        float sw = p[i];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) sw += __shfl_xor(sw, o, kWave);
+        if (lane == 0) s_red[w][i] = sw;
+    }
+    __syncthreads();
+    if (tid < kLoraDots && d0 + tid < nd) {
+        const int d = d0 + tid;
+        float sv = s_red[0][tid];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) sv += s_red[ww][tid];
+        const int e = d >= r ? sc.e[1] : sc.e[0];
+        gst(a.vpart + (int64_t)gks * nd + d, e >= 0 ? sv : 0.f);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ float elem_f(const T* p) {
+    if constexpr (sizeof(T) == 2) return bf_to_f(gld((const uint16_t*)p));
+    else return gld((const float*)p);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWaves* kWave) void gemv_lora_kernel(SwitchArgs a, int64_t n_blocks) {
+    const int64_t t = n_blocks - 1 - (int64_t)blockIdx.x;
+    if (t < 0) return;
+    const Sets sc = read_sets(a);
+    if (!sc.ok) return;
+    const SwDesc D = a.descs[find_desc<kKeyRowBlock>(a.descs, a.n_desc, t)];
+    const int d_in = D.d_in, d_out = D.d_out, r = a.r, nd = 2 * r, n_ks = D.n_ks;
+    const int lane = lane_id();
+    const int row = (int)(t - D.rb0) * kGemvRows + wave_id();
+    if (row >= d_out) return;
+    const T* __restrict__ B = (const T*)D.B;
+    const float* vp = a.vpart + D.ks0 * nd;  // slice s of this weight at vp + s * nd
+    // term l = lane (the first of this lane's): B element and the first slices
+    const int k_f = lane >= r ? 1 : 0, e_f = k_f ? sc.e[1] : sc.e[0];
+    const bool on_f = lane < nd && e_f >= 0;
+    float b_f = 0.f, pv[kLoraPre];
+    if (on_f) b_f = elem_f(B + ((int64_t)e_f * d_out + row) * r + (lane - k_f * r));
+#pragma unroll
+    for (int s = 0; s < kLoraPre; ++s) pv[s] = (on_f && s < n_ks) ? gld(vp + s * nd + lane) : 0.f;
+
+    const float acc = row_dot<T>((const T*)D.W + (int64_t)row * d_in, (const T*)D.xv, d_in, lane);
+
+    float ad = 0.f;
+    if (on_f) {
+        float v = pv[0];
+#pragma unroll
+        for (int s = 1; s < kLoraPre; ++s)
+            if (s < n_ks) v += pv[s];
+        for (int s = kLoraPre; s < n_ks; ++s) v += gld(vp + s * nd + lane);
+        ad = (sc.c[k_f] * v) * b_f;
+    }
+    for (int l = lane + kWave; l < nd; l += kWave) {  // ranks above 32: more terms per lane
+        const int k = l >= r ? 1 : 0, e = k ? sc.e[1] : sc.e[0];
+        if (e < 0) continue;
+        float v = gld(vp + l);
+        for (int s = 1; s < n_ks; ++s) v += gld(vp + s * nd + l);
+        ad = fmaf(sc.c[k] * v, elem_f(B + ((int64_t)e * d_out + row) * r + (l - k * r)), ad);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ad += __shfl_xor(ad, o, kWave);
+    if (lane == 0) gst(D.yv + row, acc + ad);
 }
 
 // ---- element-wise path: fp32 weights (and any shape) ----------------------
@@ -992,6 +1224,27 @@ hipError_t launch_gemv_reduce(const SwitchArgs& a, int64_t n_bands, hipStream_t 
     if (n_bands == 0) return hipSuccess;
     if (!grid_fits(n_bands, 256)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)n_bands), dim3(256), 0, s, a, n_bands);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_unmerged(const SwitchArgs& a, int64_t n_ks_total, int64_t n_blocks, int dtype,
+                                hipStream_t s) {
+    if (n_blocks == 0) return hipSuccess;
+    const int n_dg = (2 * a.r + kLoraDots - 1) / kLoraDots;
+    const int64_t n_units = n_ks_total * n_dg;
+    if (!grid_fits(n_units, kWaves * kWave) || !grid_fits(n_blocks, kWaves * kWave))
+        return hipErrorInvalidConfiguration;
+    if (dtype == 0)
+        hipLaunchKernelGGL(lora_shrink_kernel<float>, dim3((unsigned)n_units), dim3(kWaves * kWave), 0, s, a, n_dg);
+    else
+        hipLaunchKernelGGL(lora_shrink_kernel<uint16_t>, dim3((unsigned)n_units), dim3(kWaves * kWave), 0, s, a, n_dg);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (dtype == 0)
+        hipLaunchKernelGGL(gemv_lora_kernel<float>, dim3((unsigned)n_blocks), dim3(kWaves * kWave), 0, s, a, n_blocks);
+    else
+        hipLaunchKernelGGL(gemv_lora_kernel<uint16_t>, dim3((unsigned)n_blocks), dim3(kWaves * kWave), 0, s, a,
+                           n_blocks);
     return hipGetLastError();
 }
 

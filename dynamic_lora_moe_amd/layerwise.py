@@ -15,13 +15,18 @@ small sequential kernel launches.  Per token and per layer l:
      grouped SGMM per layer (``grouped=True``: one segmentation for the
      layer's projections).
 
+With ``fused=True`` steps 2 and 3 are one dlm_gemv_unmerged call per layer:
+the adapters' down-projections of the layer's inputs, then the base product
+with the adapters' up-projections added in the same pass (two launches for the
+layer, the result in the fp32 base outputs; the weights stay unmerged).
+
 With ``route_once=True`` the router runs once per token (the first layer's
 router weights) and every layer applies that set: the pre-gated decision of
 AdaFuse (Chinese digest, method section; Korean digest section 2-ga) with the
 adapters still unmerged, so one router launch per token instead of one per layer.
 
-The layer's adapted output is y_base + y_lora; the two stay in separate
-buffers (the adding is one more element-wise pass, not timed here).  Nothing
+Unfused, the layer's adapted output is y_base + y_lora; the two stay in
+separate buffers (the adding is one more element-wise pass, not timed here).  Nothing
 here computes: each step is an entry point of libdlm.so, and the class only
 holds buffers and issues the calls in order on one stream.
 """
@@ -44,10 +49,12 @@ class LayerwiseDecode:
     """
 
     def __init__(self, layers, routers, xs, E: int, r: int, scale: float, grouped: bool = False,
-                 route_once: bool = False):
+                 route_once: bool = False, fused: bool = False):
         if not len(layers) == len(routers) == len(xs):
             raise ValueError("one projection list, one router and one input list per layer")
-        self.E, self.r, self.scale, self.grouped = E, r, float(scale), grouped
+        if fused and grouped:
+            raise ValueError("fused applies the adapters inside the product; grouped has no meaning there")
+        self.E, self.r, self.scale, self.grouped, self.fused = E, r, float(scale), grouped, fused
         self.route_once = route_once
         self.routers = list(routers)
         self.xs = [list(x) for x in xs]
@@ -64,7 +71,7 @@ class LayerwiseDecode:
             h = Layers(projs, E, r, scale)
             yb = [torch.zeros(W.shape[0], dtype=torch.float32, device=dev) for W, _, _ in projs]
             h.bind_vectors(xl, yb)
-            yl = [torch.zeros((1, W.shape[0]), dtype=dt, device=dev) for W, _, _ in projs]
+            yl = [] if fused else [torch.zeros((1, W.shape[0]), dtype=dt, device=dev) for W, _, _ in projs]
             self.base.append(h)
             self.y_base.append(yb)
             self.y_lora.append(yl)
@@ -74,7 +81,7 @@ class LayerwiseDecode:
             d_in_max = max(d_in_max, max(W.shape[1] for W, _, _ in projs))
         self.d_in_max, self.dtype = d_in_max, dt
         n_ws = max(len(p) for p in self.projs) if grouped else 1
-        self.ws = sgmm_workspace(1, d_in_max, E, r, n_ws, dev)
+        self.ws = None if fused else sgmm_workspace(1, d_in_max, E, r, n_ws, dev)
 
     def step(self, router_x, stream=None, side=None):
         """Enqueue one token: router_x [1][d_router] is every layer's router input.
@@ -92,6 +99,9 @@ class LayerwiseDecode:
             s = 0 if self.route_once else l  # the set this layer applies
             if l == s:
                 pregate(router_x, self.routers[l], idx=self.idx[l], g=self.g[l], stream=main)
+            if self.fused:
+                self.base[l].gemv_unmerged((self.idx[s][0], self.g[s][0]), stream=main)
+                continue
             if side is not None:
                 fork, join = self._ev[l]
                 fork.record(main)
@@ -110,7 +120,8 @@ class LayerwiseDecode:
                 main.wait_event(join)
 
     def reset_lora(self):
-        """Zero the adapter outputs (they accumulate across tokens)."""
+        """Zero the adapter outputs (they accumulate across tokens; the fused
+        form overwrites its outputs and has none)."""
         for yl in self.y_lora:
             for y in yl:
                 y.zero_()
@@ -118,9 +129,13 @@ class LayerwiseDecode:
     def launches_per_token(self) -> int:
         """Kernel launches one step() makes: the router (once per layer, or once
         per token with route_once), per layer the base product (dlm_gemv: 1) and
-        the adapters' SGMM launches."""
+        the adapters' SGMM launches, or with fused the layer's dlm_gemv_unmerged
+        launches."""
         n = 1 if self.route_once else len(self.projs)
-        for projs in self.projs:
+        for l, projs in enumerate(self.projs):
+            if self.fused:
+                n += self.base[l].launches_per_gemv_unmerged()
+                continue
             if self.grouped:
                 sg = sgmm_launches(1, max(W.shape[1] for W, _, _ in projs), self.r, len(projs), self.dtype)
             else:
@@ -130,7 +145,7 @@ class LayerwiseDecode:
 
     def status(self, stream=None) -> int:
         """DLM_OK, or the first failure the device reported (sets, weights)."""
-        s = sgmm_status(self.ws, stream)
+        s = DLM_OK if self.ws is None else sgmm_status(self.ws, stream)
         if s != DLM_OK:
             return s
         for h in self.base:

@@ -192,7 +192,9 @@ int dlm_switch_launches(const dlm_layers* h);
  *   flight on any stream finish with the previous binding), then the pointers
  *   are copied into the device table; the buffers stay owned by the caller.  bf16 handles with
  *   r <= 16 also get a partial-product buffer (sum of ceil(d_in_i/256) *
- *   d_out_i floats), freed by destroy.  Binding again replaces the vectors.
+ *   d_out_i floats), and every handle a buffer for dlm_gemv_unmerged's rank
+ *   vectors (sum of ceil(d_in_i/2048) * 2 r floats), freed by destroy.
+ *   Binding again replaces the vectors.
  */
 int dlm_layers_bind_vectors(dlm_layers* h, const void* const* x, float* const* y);
 
@@ -216,6 +218,28 @@ int dlm_switch_gemv(dlm_layers* h, const int32_t* old_idx, const float* old_g,
 
 /* Number of kernel launches one dlm_switch_gemv call makes (always 2). */
 int dlm_switch_gemv_launches(const dlm_layers* h);
+
+/*
+ * The decode product with one set's adapters left unmerged: for every weight
+ * with its bound vectors,
+ *   y_i = W_i x_i + s * sum_k g_k * B_{e_k,i} (A_{e_k,i} x_i)          (fp32 y)
+ * W is not modified.  The set is made once per token and applied by every
+ * adapted layer (AdaFuse, KR digest section 2-ga, token-level pre-gating); the
+ * adapters are the per-row gated LoRA product of the SGMM formula, applied
+ * to the token's input here instead of merged into W.
+ *   idx [2] int32, g [2] fp32 (device): the set, in dlm_switch's format.
+ * Two launches, no allocation: the rank vectors A_e x per (weight,
+ * 2048-wide K slice) into the handle's buffer (dlm_layers_bind_vectors), then
+ * the product, each output row adding its adapters' B row times the slices'
+ * sum (slices added in order; every result bitwise reproducible, and the
+ * same for the set's two slots in either order).  A set dlm_switch would
+ * reject leaves y unchanged and sets the error word (dlm_layers_status).
+ * DLM_EINVAL if no vectors are bound or idx / g is null.
+ */
+int dlm_gemv_unmerged(dlm_layers* h, const int32_t* idx, const float* g, void* stream);
+
+/* Number of kernel launches one dlm_gemv_unmerged call makes (always 2). */
+int dlm_gemv_unmerged_launches(const dlm_layers* h);
 
 /*
  * Synchronise `stream`, then read and clear the handle's device error word:

@@ -116,6 +116,8 @@ def test_product_entry_points_validation(lib):
     assert lib.dlm_gemv(None, None) == dlm.DLM_EINVAL
     assert lib.dlm_switch_gemv(None, None, None, None, None, None) == dlm.DLM_EINVAL
     assert lib.dlm_switch_gemv_launches(None) == 0
+    assert lib.dlm_gemv_unmerged(None, None, None, None) == dlm.DLM_EINVAL
+    assert lib.dlm_gemv_unmerged_launches(None) == 0
     assert lib.dlm_layers_repack(None, None) == dlm.DLM_EINVAL
 
 

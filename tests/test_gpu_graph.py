@@ -264,8 +264,8 @@ def test_sgmm_launch_count_matches_captured_kernels(T, shapes, E, r, dt, group, 
 
 
 def test_switch_launch_counts_match_captured_kernels():
-    """dlm_switch: one launch for every weight of every layer; dlm_switch_gemv:
-    the counted two; dlm_gemv: one."""
+    """dlm_switch: one launch for every weight of every layer; dlm_switch_gemv
+    and dlm_gemv_unmerged: the counted two; dlm_gemv: one."""
     print("[graph] switch launch counts", flush=True)
     E, r = 4, 16
     shapes = [(264, 512), (512, 264), (96, 1040)]
@@ -285,5 +285,6 @@ def test_switch_launch_counts_match_captured_kernels():
     assert _captured(lambda: L.switch(old, new)) == L.launches_per_switch() == 1
     assert _captured(lambda: L.switch_gemv(old, new)) == L.launches_per_switch_gemv() == 2
     assert _captured(lambda: L.gemv()) == 1
+    assert _captured(lambda: L.gemv_unmerged(new)) == L.launches_per_gemv_unmerged() == 2
     assert L.status() == dlm.DLM_OK
     L.close()

@@ -284,7 +284,10 @@ def test_7b_layerwise_decode_token():
     by element -- then the same token replayed three times from one HIP graph,
     each replay bitwise equal to the eager token.  Then the pre-gated unmerged
     form on the same layers (one router per token, one grouped SGMM per layer):
-    every adapter output against the oracle with the first layer's set."""
+    every adapter output against the oracle with the first layer's set.  Last
+    the fused unmerged form (one router per token, one dlm_gemv_unmerged per
+    layer): layers 0, 15 and 31 against the oracle's product plus its unmerged
+    adapters, every layer's output bitwise equal across two graph replays."""
     from dynamic_lora_moe_amd.layerwise import LayerwiseDecode
     wl = synth.WORKLOADS["7b-decode"]
     print("[workload] 7b-decode layer-wise: building", flush=True)
@@ -389,8 +392,41 @@ def test_7b_layerwise_decode_token():
     del gr2
     assert po.status() == dlm.DLM_OK
     po.close()
+    # the fused unmerged form: the adapters' terms inside the base product
+    pf = LayerwiseDecode(per_layer, routers, xs, wl.E, wl.r, wl.scale, route_once=True, fused=True)
+    assert pf.launches_per_token() == 1 + wl.layers * 2
+    pf.step(x_tok)
+    torch.cuda.synchronize()
+    assert pf.status() == dlm.DLM_OK
+    assert torch.equal(pf.idx[0].cpu(), ri)
+    for l in (0, 15, wl.layers - 1):
+        print(f"[workload] 7b-decode fused unmerged: layer {l}", flush=True)
+        for k, ((W, A, B), xv, yb) in enumerate(zip(per_layer[l], xs[l], pf.y_base[l])):
+            _, ex_w, ab_w = oracle.gemv(W.cpu(), xv.cpu(), with_stats=True)
+            _, ex_a, ab_a = oracle.sgmm(xv[None].cpu(), ri, rg, A.cpu(), B.cpu(),
+                                        torch.zeros((1, W.shape[0]), dtype=wl.dtype), wl.scale, with_stats=True)
+            check_f32(yb.cpu(), ex_w + ex_a[0], ab_w + ab_a[0], W.shape[1] + 2 * wl.r + 32,
+                      what=f"fused unmerged L{l} proj {k}")
+    fused_eager = [[y.clone() for y in yl] for yl in pf.y_base]
+    gr3 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(gr3, stream=s):
+            pf.step(x_tok, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for yl in pf.y_base:
+            for y in yl:
+                y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        gr3.replay()
+        torch.cuda.synchronize()
+        for u, v in zip(fused_eager, pf.y_base):
+            assert all(torch.equal(p, q) for p, q in zip(u, v)), f"fused replay {rep} differs"
+    del gr3
+    assert pf.status() == dlm.DLM_OK
+    pf.close()
     lw.close()
-    del model, lw, po
+    del model, lw, po, pf
     gc.collect()
     torch.cuda.empty_cache()
 
