@@ -217,3 +217,42 @@ def test_sgmm_group_sweep(i):
     for k, ((x, A, B, y), y0) in enumerate(zip(probs, y0s)):
         _check(x, idx, g, A, B, y0, y, scale, f"group sweep {i} problem {k}")
     grp.close()
+
+
+N_UNMERGED = 24
+
+
+def _unmerged_config(i):
+    rng = np.random.default_rng(96000 + i)
+    dt = torch.float32 if rng.random() < 0.2 else torch.bfloat16
+    shapes = []
+    for _ in range(int(rng.integers(1, 5))):
+        d_out = int(rng.integers(1, 600))
+        d_in = 8 * int(rng.integers(1, 1600 if rng.random() < 0.5 else 160))  # up to 7 K slices
+        shapes.append((d_out, d_in))
+    E = int(rng.choice([1, 2, 3, 4, 8, 16, 32]))
+    e = rng.choice(E, size=2, replace=E < 2).tolist()
+    if rng.random() < 0.2:
+        e[int(rng.integers(0, 2))] = -1
+    g = rng.random(2).astype(np.float32).tolist()
+    return shapes, E, _rank(rng), float(rng.choice([0.5, 1.0, 2.0])), dt, (e, g)
+
+
+@pytest.mark.parametrize("i", range(N_UNMERGED))
+def test_gemv_unmerged_sweep(i):
+    """dlm_gemv_unmerged on random shapes and sets: y against the oracle's
+    product plus its unmerged adapters (the hand-picked cases' bound), W
+    untouched."""
+    from test_gpu_unmerged import _check, _model as _um_model, _vectors as _um_vectors
+    shapes, E, r, scale, dt, s = _unmerged_config(i)
+    print(f"[sweep unmerged {i}] shapes={shapes} E={E} r={r} scale={scale} {dt} set={s}", flush=True)
+    model = _um_model(shapes, E, r, dt, 97000 + i)
+    W0 = [W.clone() for W, _, _ in model]
+    xs, ys = _um_vectors(shapes, dt, 97000 + i)
+    L = dlm.Layers(model, E, r, scale)
+    L.bind_vectors(xs, ys)
+    L.gemv_unmerged(dev_set(s))
+    assert L.status() == dlm.DLM_OK
+    _check(model, xs, ys, s, E, r, scale, f"sweep unmerged {i}")
+    assert all(torch.equal(W, w0) for (W, _, _), w0 in zip(model, W0))
+    L.close()
