@@ -117,3 +117,25 @@ def test_gemv_unmerged_bad_set_leaves_y_and_sets_status():
     assert L.status() == dlm.DLM_OK
     _check(model, xs, ys, good, 8, 16, 1.0, "after bad sets")
     L.close()
+
+
+def test_gemv_unmerged_more_than_64_weights():
+    """A handle of 70 weights: past 64 descriptors the first launch finds each
+    K slice's weight by a ballot per 64 keys instead of one lane per
+    descriptor.  Weights 62-66 span several K slices, so slices on both sides
+    of the 64-descriptor boundary belong to multi-slice weights."""
+    rng = np.random.default_rng(4400)
+    shapes = []
+    for i in range(70):
+        d_in = 8 * int(rng.integers(260, 700)) if 62 <= i <= 66 else 8 * int(rng.integers(1, 64))
+        shapes.append((int(rng.integers(1, 48)), d_in))
+    model = _model(shapes, 8, 16, torch.bfloat16, 4400)
+    xs, ys = _vectors(shapes, torch.bfloat16, 4400)
+    L = dlm.Layers(model, 8, 16, 1.5)
+    L.bind_vectors(xs, ys)
+    s = ([5, 2], [0.35, 0.65])
+    L.gemv_unmerged((torch.tensor(s[0], dtype=torch.int32, device="cuda"),
+                     torch.tensor(s[1], dtype=torch.float32, device="cuda")))
+    assert L.status() == dlm.DLM_OK
+    _check(model, xs, ys, s, 8, 16, 1.5, "70 weights")
+    L.close()
