@@ -782,7 +782,9 @@ def _roofline_all(sw, sw70, sg):
         if r is None:
             continue
         per = r["ms_per_pass"] if key == "prefill" else r["grouped_ms_per_step"]
-        out.append({"workload": name, "kernel": "sgmm pass: segment, shrink, K-part sum, expand", "bound": "hbm",
+        # both workloads are rank 16 with at most 8192 rows: three launches
+        out.append({"workload": name, "kernel": "sgmm pass: segment, shrink, expand (adds the K slices)",
+                    "bound": "hbm",
                     "achieved": round(r["GBps"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                     "frac": round(r["frac_of_hbm_peak"], 4),
                     "traffic": None if r.get("traffic") is None else round(
