@@ -162,6 +162,8 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
       pregated_unmerged_fused: the router once per token, then per layer one
                 dlm_gemv_unmerged (2 launches: the adapters' down-projections,
                 then the base product with their up-projections added);
+      layerwise_fused: the same with a router per layer (the layer's own
+                router weights, T = 1);
       unfused:  pre-gated: router once, one switch over all 224 weights, then one
                 product launch per layer (W read twice, written once: 3 x 12.95 GB);
       fused:    pre-gated: router once, then per layer the switch fused with the
@@ -195,7 +197,9 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
           "pregated_unmerged": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r, wl.scale,
                                                grouped=True, route_once=True),
           "pregated_unmerged_fused": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r,
-                                                     wl.scale, route_once=True, fused=True)}
+                                                     wl.scale, route_once=True, fused=True),
+          "layerwise_fused": LayerwiseDecode(per_layer, routers, [xs for xs, _ in ys], wl.E, wl.r, wl.scale,
+                                             fused=True)}
     x_tok = torch.empty((1, wl.d_model), dtype=wl.dtype, device="cuda")
     idx = [torch.zeros((1, 2), dtype=torch.int32, device="cuda") for _ in range(2)]
     g = [torch.zeros((1, 2), dtype=torch.float32, device="cuda") for _ in range(2)]
@@ -228,7 +232,7 @@ def bench_decode_loop(torch, dlm, synth, n_tokens, log):
     pre_gated = ("unfused", "fused")
     side = torch.cuda.Stream()
     for kind in ("base", "layerwise", "layerwise_grouped", "pregated_unmerged", "pregated_unmerged_2s",
-                 "pregated_unmerged_fused") + pre_gated:
+                 "pregated_unmerged_fused", "layerwise_fused") + pre_gated:
         out = {}
         with torch.cuda.stream(s):
             # eager: token 0 from the merged-in-nothing state, then n-1 switches

@@ -228,9 +228,9 @@ int dlm_switch_gemv_launches(const dlm_layers* h);
  * adapters are the per-row gated LoRA product of the SGMM formula, applied
  * to the token's input here instead of merged into W.
  *   idx [2] int32, g [2] fp32 (device): the set, in dlm_switch's format.
- * Two launches, no allocation: the rank vectors A_e x per (weight,
- * 2048-wide K slice) into the handle's buffer (dlm_layers_bind_vectors), then
- * the product, each output row adding its adapters' B row times the slices'
+ * Two launches, no allocation: the rank vectors' partials A_e x per (weight,
+ * 2048-wide K slice, group of 8 rank vectors) into the handle's buffer
+ * (dlm_layers_bind_vectors), then the product, each output row adding its adapters' B row times the slices'
  * sum (slices added in order; every result bitwise reproducible, and the
  * same for the set's two slots in either order).  A set dlm_switch would
  * reject leaves y unchanged and sets the error word (dlm_layers_status).
