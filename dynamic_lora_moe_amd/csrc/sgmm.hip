@@ -603,6 +603,9 @@ __device__ __forceinline__ int perm_col(int m) { return 16 * ((m >> 2) & 1) + 4 
 // Columns of one expand work item: 4 waves x kEB blocks x 64 columns.
 constexpr int kEB = 4;
 constexpr int kECols = 4 * kEB * 64;
+// Items per XCD run as half items at the end of an expand launch: about the
+// expand workgroups resident on one XCD (32 CUs x 3).
+constexpr int kExpandSplit = 96;
 static_assert(kECols == kSgmmExpandCols, "expand column group");
 // The row-side MFMA operands (u = s*g*v as hi + lo bf16, per (expert, 16-rank
 // chunk) pair q and lane) are the same for the four waves of a work item: they
@@ -620,7 +623,7 @@ static_assert(32 * 2 * 16 * kExpandFoldR16 * 4 <= kQLds * 2 * kWave * 16, "v blo
 // the tile fastest: neighbouring work items (same XCD) reuse the same B column
 // slices.
 template <int R16, bool RVEC>
-__device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int tile) {
+__device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int tile, int half) {
     constexpr int RPAD = R16 * 16;
     constexpr bool FOLD = R16 <= kExpandFoldR16;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
@@ -647,8 +650,11 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
     __shared__ __attribute__((aligned(16))) u32x4 s_u[kQLds][2][kWave];
 
     const int d_out = uniform(D.d_out), r = a.r;
-    const int cw = cg * kECols + w * (kEB * 64);  // this wave's first column
-    const int nblk = cw >= d_out ? 0 : ((d_out - cw + 63) / 64 < kEB ? (d_out - cw + 63) / 64 : kEB);
+    // this wave's first column and blocks: kEB blocks of the whole item, or
+    // kEB / 2 of one of its halves (the same columns split in two items)
+    const int eb = half < 0 ? kEB : kEB / 2;
+    const int cw = cg * kECols + (half < 0 ? 0 : half * (kECols / 2)) + w * (eb * 64);
+    const int nblk = cw >= d_out ? 0 : ((d_out - cw + 63) / 64 < eb ? (d_out - cw + 63) / 64 : eb);
     const uint16_t* __restrict__ B = (const uint16_t*)D.B;
     uint16_t* __restrict__ y = (uint16_t*)D.y;
     uint16_t* ys = s_y[w];
@@ -865,19 +871,31 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
     }
 }
 
-// Live work items only, as for the shrink: (column group, live tile).
+// Live work items only, as for the shrink: (column group, live tile).  The
+// last kExpandSplit items of each XCD's share run as two half items each
+// (kECols / 2 columns), dispatched last: a launch drains for about one item's
+// duration while its last items finish, and half items halve that.  Every
+// column is computed the same way in either form.
 template <int R16, bool RVEC>
 __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a) {
     const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
     const int n_tiles = uniform(gld(hdr + SG_NTILES));
     if (gld(hdr + SG_ERR)) return;
     const int64_t n_live = a.total_cb * n_tiles, per = (n_live + 7) / 8;
+    const int64_t m = per < kExpandSplit ? per : kExpandSplit;
     const int64_t bid = blockIdx.x, j = bid >> 3;
-    if (j >= per) return;
-    const int64_t t = (bid & 7) * per + j;
+    if (j >= per + m) return;
+    int64_t jj = j;
+    int half = -1;
+    if (j >= per - m) {
+        const int64_t k = j - (per - m);
+        jj = per - m + (k >> 1);
+        half = (int)(k & 1);
+    }
+    const int64_t t = (bid & 7) * per + jj;
     if (t >= n_live) return;
     const int64_t cgg = t / n_tiles;
-    expand_item<R16, RVEC>(a, cgg, (int)(t - cgg * n_tiles));
+    expand_item<R16, RVEC>(a, cgg, (int)(t - cgg * n_tiles), half);
 }
 
 // ---- few rows (bf16, T <= kSgmmSmallT) -----------------------------------------
@@ -1244,7 +1262,8 @@ hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const dim3 ge((unsigned)item_grid(a.n_expand_units));
+    const int64_t per_max = (a.n_expand_units + 7) / 8;
+    const dim3 ge((unsigned)(8 * (per_max + (per_max < kExpandSplit ? per_max : kExpandSplit))));
     if (a.r % 8 == 0)
         hipLaunchKernelGGL((sgmm_expand_bf16<R16, true>), ge, dim3(256), 0, s, a);
     else
@@ -1267,7 +1286,10 @@ hipError_t launch_sgmm_pack_a(const void* A, void* Ap, int E, int r, int64_t d_i
 static bool sgmm_grids_fit(const SgmmArgs& a, int dtype) {
     if (!grid_fits(a.L.n_chunks, kSegThreads)) return false;
     if (dtype == 1) {
-        return grid_fits((a.L.T_pad * 2 * a.L.r_pad / 4 + 255) / 256, 256);
+        const int64_t per_max = (a.n_expand_units + 7) / 8;
+        return grid_fits((a.L.T_pad * 2 * a.L.r_pad / 4 + 255) / 256, 256) &&
+               grid_fits(item_grid(a.total_ks * a.L.tiles_max), 256) &&
+               grid_fits(8 * (per_max + (per_max < kExpandSplit ? per_max : kExpandSplit)), 256);
     }
     return grid_fits((a.L.T_pad * 2 * a.r + 255) / 256, 256) &&
            grid_fits((a.L.T_pad * a.d_out_max + 255) / 256, 256);
