@@ -340,9 +340,66 @@ def bench_switch_70b(torch, dlm, synth, n_timed, log):
     return res
 
 
+def _per_call_us(torch, call, n=20, replays=5):
+    """(eager, graph) microseconds per call: n calls timed with HIP events as
+    issued from Python (the binding's host work included: a short kernel then
+    waits for the host), and the same n calls captured in a HIP graph and
+    replayed (the device's time per call, launch gaps included)."""
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) / n * 1e3
+    s = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(gr, stream=s):
+            for _ in range(n):
+                call()
+    torch.cuda.synchronize()
+    gr.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(replays):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph = e0.elapsed_time(e1) / (n * replays) * 1e3
+    del gr
+    return eager, graph
+
+
+def bench_hbm_copy(torch, log, nbytes=2 << 30, reps=10):
+    """What a plain device-to-device copy (torch, bf16) achieves on this
+    machine: read + write bytes per second, HIP events over `reps` copies of
+    `nbytes`.  Reported beside the 8 TB/s peak, which stays the denominator."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    res = {"GBps": 2 * nbytes / sec / 1e9, "bytes_copied": nbytes, "ms_per_copy": sec * 1e3,
+           "what": "torch device-to-device copy, read + write bytes per second"}
+    log(f"hbm copy: {res}")
+    return res
+
+
 def bench_router(torch, dlm, synth, log):
-    """Router latency per call (HIP events, 20 calls after 3 warm-up) at T = 1
-    and at the full token count of the 7B- and 70B-shaped workloads."""
+    """Router latency per call at T = 1 and at the full token count of the 7B-
+    and 70B-shaped workloads: from a replayed HIP graph of 20 calls (the
+    device's time) and eagerly from Python (host work included)."""
     out = {}
     for name in ("7b-decode", "70b-decode"):
         wl = synth.WORKLOADS[name]
@@ -351,17 +408,9 @@ def bench_router(torch, dlm, synth, log):
             xt = x[:T].contiguous()
             idx = torch.empty(T, 2, dtype=torch.int32, device="cuda")
             g = torch.empty(T, 2, dtype=torch.float32, device="cuda")
-            for _ in range(3):
-                dlm.pregate(xt, Wr, idx, g)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(20):
-                dlm.pregate(xt, Wr, idx, g)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / 20 * 1e3
+            eager, us = _per_call_us(torch, lambda: dlm.pregate(xt, Wr, idx, g))
             nbytes = (xt.numel() + Wr.numel()) * xt.element_size()
-            out[f"{name}_T{T}"] = {"us_per_call": us, "GBps_x_Wr": nbytes / us / 1e3}
+            out[f"{name}_T{T}"] = {"us_per_call": us, "us_per_call_eager": eager, "GBps_x_Wr": nbytes / us / 1e3}
         # the nearest-centroid pre-gate on the same tokens: J = 4 synthetic
         # centroids per adapter, N(0, 1) like the tokens
         J = 4
@@ -370,16 +419,8 @@ def bench_router(torch, dlm, synth, log):
             xt = x[:T].contiguous()
             idx = torch.empty(T, 2, dtype=torch.int32, device="cuda")
             g = torch.empty(T, 2, dtype=torch.float32, device="cuda")
-            for _ in range(3):
-                dlm.pregate_centroid(xt, C, idx, g)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(20):
-                dlm.pregate_centroid(xt, C, idx, g)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / 20 * 1e3
-            out[f"{name}_centroid_J{J}_T{T}"] = {"us_per_call": us,
+            eager, us = _per_call_us(torch, lambda: dlm.pregate_centroid(xt, C, idx, g))
+            out[f"{name}_centroid_J{J}_T{T}"] = {"us_per_call": us, "us_per_call_eager": eager,
                                                  "GBps_x_C": (xt.numel() + C.numel()) * xt.element_size() / us / 1e3}
     return out
 
@@ -416,6 +457,20 @@ def bench_sgmm(torch, dlm, synth, name, reps, log):
     res = {"tokens_per_s": tokens / sec, "ms_per_pass": sec * 1e3, "GBps": nbytes / sec / 1e9,
            "frac_of_hbm_peak": nbytes / sec / HBM_PEAK, "algo_bytes_per_pass": nbytes,
            "traffic": _sgmm_traffic(name)}
+    # spread per unit (a prefill pass, a mixed-decode step): one more round with
+    # an event pair around every unit (the events add their own small gaps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sets]
+    per_unit = []
+    for _ in range(reps if len(sets) == 1 else 1):
+        for (i, gg), (a, b) in zip(sets, evs):
+            a.record(stream)
+            grp.run(i, gg, workspace=ws)
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_unit += [a.elapsed_time(b) for a, b in evs]
+    per_unit.sort()
+    res["unit_ms_p50"] = per_unit[len(per_unit) // 2]
+    res["unit_ms_p90"] = per_unit[min(len(per_unit) - 1, int(0.9 * len(per_unit)))]
     if name == "mixed-decode":
         res.update(_per_layer_variant(torch, dlm, wl, probs, sets, reps, sec, log))
         # rows that release their adapters (both slots empty) are left out by the
@@ -835,6 +890,7 @@ def main():
     if args.profile_kernels:
         profile_kernels(torch, dlm, synth, args.profile_kernels, log)
         return
+    copy = bench_hbm_copy(torch, log)
     sw = bench_switch(torch, dlm, synth, args.steps, args.warmup, log)
     log(f"switch: {sw}")
     dec = None
@@ -882,6 +938,7 @@ def main():
                      "avg_launch_ms": round(sw["switch_ms"], 4),
                      "algo_bytes_per_launch": sw["algo_bytes_per_launch"]},
         "roofline_all": _roofline_all(sw, sw70, sg),
+        "hbm_copy_achievable": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in copy.items()},
         "cpu_baseline": cpu,
         "switch": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in sw.items()},
         "switch_70b": None if sw70 is None else {k: (round(v, 4) if isinstance(v, float) else v)
