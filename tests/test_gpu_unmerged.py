@@ -139,3 +139,29 @@ def test_gemv_unmerged_more_than_64_weights():
     assert L.status() == dlm.DLM_OK
     _check(model, xs, ys, s, 8, 16, 1.5, "70 weights")
     L.close()
+
+
+def test_gemv_unmerged_requires_bound_vectors_and_follows_a_rebind():
+    """Without bound vectors the call is refused before anything is enqueued;
+    after a second binding (new vectors, the partials buffer reallocated) the
+    product uses the new vectors."""
+    shapes = [(64, 4104), (40, 16)]
+    model = _model(shapes, 8, 16, torch.bfloat16, 4500)
+    L = dlm.Layers(model, 8, 16, 1.0)
+    s = ([1, 6], [0.25, 0.75])
+    st = (torch.tensor(s[0], dtype=torch.int32, device="cuda"), torch.tensor(s[1], dtype=torch.float32, device="cuda"))
+    with pytest.raises(RuntimeError):
+        L.gemv_unmerged(st)
+    xs, ys = _vectors(shapes, torch.bfloat16, 4500)
+    L.bind_vectors(xs, ys)
+    L.gemv_unmerged(st)
+    assert L.status() == dlm.DLM_OK
+    _check(model, xs, ys, s, 8, 16, 1.0, "first binding")
+    xs2, ys2 = _vectors(shapes, torch.bfloat16, 4501)
+    L.bind_vectors(xs2, ys2)
+    before = [y.clone() for y in ys]
+    L.gemv_unmerged(st)
+    assert L.status() == dlm.DLM_OK
+    _check(model, xs2, ys2, s, 8, 16, 1.0, "second binding")
+    assert all(torch.equal(a, b) for a, b in zip(before, ys))  # the old outputs are left alone
+    L.close()
