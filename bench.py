@@ -501,12 +501,12 @@ def bench_sgmm(torch, dlm, synth, name, reps, log):
 
 
 def _per_layer_variant(torch, dlm, wl, probs, sets, reps, sec_grouped, log):
-    """The mixed decode step as one group per layer (7 projections each): one
-    segmentation per layer, 3 launches per layer (segment, shrink, expand), run
-    eagerly and replayed from a HIP graph captured once (the step's sets are
-    copied into the graph's static input buffers before each replay).  Beside
-    the grouped call, whose single segmentation serves all layers (3 launches
-    per step)."""
+    """The mixed decode step as one group per layer (7 projections each; 64
+    rows, so each group orders its rows inside its shrink and expand: 2
+    launches per layer), run eagerly and replayed from a HIP graph captured
+    once (the step's sets are copied into the graph's static input buffers
+    before each replay).  Beside the grouped call over all 224 projections (2
+    launches per step)."""
     layers = sorted({l for l, *_ in probs})
     per = [dlm.SgmmGroup([(x, A, B, y) for l2, _, x, A, B, y in probs if l2 == l], wl.E, wl.r, wl.scale)
            for l in layers]
@@ -776,7 +776,9 @@ def _sgmm_traffic_from(fetch_csv, write_csv, read):
     """Per-kernel HBM bytes of the grouped SGMM passes of --profile-kernels: the
     dispatches of the SGMM kernels, in dispatch order, split into passes where a
     segmentation launch follows another kind (a pass segments with one launch,
-    or with a count launch and a placing launch above 8192 rows); the first
+    or with a count launch and a placing launch above 8192 rows) or a shrink
+    launch follows anything but a segmentation (up to 64 rows a pass has no
+    segmentation launch: the shrink and expand order the rows); the first
     SGMM_PROFILE_PASSES passes are the prefill, the next the mixed-decode steps
     0, 1, ...  Each counter is scaled by its own reading for the 1 GiB copy."""
     import csv
@@ -794,7 +796,7 @@ def _sgmm_traffic_from(fetch_csv, write_csv, read):
         passes, prev = [], None
         for r in rows:
             kind = next(k for k in kinds if names[k] in r["Kernel_Name"])
-            if kind == "segment" and prev != "segment":
+            if (kind == "segment" and prev != "segment") or (kind == "shrink" and prev != "segment"):
                 passes.append({})
             prev = kind
             if passes:
@@ -841,8 +843,10 @@ def _roofline_all(sw, sw70, sg):
         if r is None:
             continue
         per = r["ms_per_pass"] if key == "prefill" else r["grouped_ms_per_step"]
-        # both workloads are rank 16 with at most 8192 rows: three launches
-        out.append({"workload": name, "kernel": "sgmm pass: segment, shrink, expand (adds the K slices)",
+        # rank 16: segment, shrink, expand; up to 64 rows no segmentation launch
+        kern = ("sgmm step: shrink, expand (rows ordered in both)" if key == "mixed_decode"
+                else "sgmm pass: segment, shrink, expand (adds the K slices)")
+        out.append({"workload": name, "kernel": kern,
                     "bound": "hbm",
                     "achieved": round(r["GBps"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                     "frac": round(r["frac_of_hbm_peak"], 4),

@@ -553,6 +553,7 @@ int run_sgmm(const SgDesc* d_descs, const SgDesc* ks_desc, const SgDesc* cb_desc
              int32_t* status_out = nullptr) {
     SgmmArgs a;
     a.status_out = status_out;
+    a.inline_seg = 0;  // launch_sgmm decides
     a.descs = d_descs;
     a.ks_desc = ks_desc;
     a.cb_desc = cb_desc;
@@ -859,7 +860,9 @@ int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t r, int32_t n_problems
     if (dtype == DLM_BF16 && T <= kSgmmSmallT) return n_problems == 1 ? 1 : 2;
     const int seg = T > kSgmmSegFewRows ? 2 : 1;
     if (dtype == DLM_F32) return seg + 2;
-    return seg + 2 + (d_in_max > kSgmmKSlice && r > kSgmmFoldRank ? 1 : 0);
+    const int vsum = d_in_max > kSgmmKSlice && r > kSgmmFoldRank ? 1 : 0;
+    if (T <= kSgmmInlineRows && !vsum) return 2;  // the rows ordered inside the shrink and expand
+    return seg + 2 + vsum;
 }
 
 }  // extern "C"

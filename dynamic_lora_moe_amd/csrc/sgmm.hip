@@ -313,6 +313,48 @@ __global__ __launch_bounds__(kSegThreads) void sgmm_seg_place(const int32_t* __r
     }
 }
 
+// With at most kWave rows the shrink and expand workgroups order the rows
+// themselves, in the segmentation's order: lane i of the calling wave holds
+// row i, and a live row's position is the number of live rows with a smaller
+// key (one ballot per key bit, from the top: at a bit where this key has a 1,
+// the live rows that agree with it above that bit and have a 0 there are
+// smaller), plus the live rows with the same key and a smaller index.  Each
+// live lane writes its position of s_perm / s_ep (and s_g if given): row, pair
+// and gates as the segmentation writes them; positions past the live rows get
+// row -1.  Returns the live-row count, or -1 if any row's set is bad (nothing
+// may then be written).  One wave, every lane; the caller synchronises before
+// the arrays are read.
+__device__ __forceinline__ int inline_order(const SgmmArgs& a, int32_t* s_perm, uint32_t* s_ep, f32x2* s_g) {
+    const int lane = lane_id();
+    const SegRow q = seg_row(seg_load(a.idx, a.g, lane, a.T), lane < a.T, a.E);
+    const bool bad = __ballot(q.bad) != 0ull;
+    const int key = q.key;
+    const int nk = (a.E + 1) * (a.E + 1);
+    const int nbits = 32 - __builtin_clz((unsigned)(nk - 1));
+    const uint64_t live = __ballot(key >= 0);
+    uint64_t eq = live;  // live lanes whose key agrees with this one on the bits seen so far
+    int less = 0;
+    for (int bit = nbits - 1; bit >= 0; --bit) {
+        const uint64_t ones = __ballot(key >= 0 && ((key >> bit) & 1));
+        const bool one = key >= 0 && ((key >> bit) & 1);
+        if (one) less += (int)__popcll(eq & ~ones);
+        eq &= one ? ones : (live & ~ones);
+    }
+    const int n_pos = (int)__popcll(live);
+    if (key >= 0) {
+        const int pos = less + (int)__popcll(eq & ((1ull << lane) - 1ull));
+        s_perm[pos] = lane;
+        s_ep[pos] = ((uint32_t)q.e0 & 0xffffu) | ((uint32_t)q.e1 << 16);
+        if (s_g) s_g[pos] = f32x2{q.e0 >= 0 ? q.g0 : 0.f, q.e1 >= 0 ? q.g1 : 0.f};
+    }
+    if (lane >= n_pos) {
+        s_perm[lane] = -1;
+        s_ep[lane] = 0xffffffffu;
+        if (s_g) s_g[lane] = f32x2{0.f, 0.f};
+    }
+    return bad ? -1 : n_pos;
+}
+
 // ---- helpers ---------------------------------------------------------------
 
 // Experts set in a tile mask, ascending.
@@ -366,8 +408,11 @@ __device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((c
 // are never guarded: a padding row or (expert, rank) column reads an in-bounds
 // dummy row whose products reach only accumulator entries that are never
 // stored, and k past d_in reads a clamped address whose value is replaced by 0.
+// i_perm / i_ep: the rows' order computed in the workgroup (inline_order), or
+// nullptr to read the segmentation's from the workspace.
 template <int R16, bool PK>
-__device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int tile0, int n_tiles) {
+__device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int tile0, int n_tiles,
+                                            const int32_t* i_perm, const uint32_t* i_ep) {
     constexpr int RPAD = R16 * 16;
     const SgDesc D = a.descs ? a.ks_desc[gks] : a.single;
     const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
@@ -390,8 +435,8 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
         if (tid < kXRows) {
             const bool in = tile0 < n_tiles;
             const int p = tile0 * 32 + tid;
-            const int row = in ? gld(perm + p) : -1;
-            const uint32_t ep = in ? gld(epk + p) : 0xffffffffu;
+            const int row = in ? (i_perm ? i_perm[p] : gld(perm + p)) : -1;
+            const uint32_t ep = in ? (i_ep ? i_ep[p] : gld(epk + p)) : 0xffffffffu;
             const int e0 = (int16_t)(ep & 0xffffu), e1 = (int16_t)(ep >> 16);
             s_row[tid] = row;
             s_slots[tid] = (uint16_t)((e0 + 1) | ((e1 + 1) << 6) | (row < 0 ? 1 << 12 : 0));
@@ -584,16 +629,42 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
 template <int R16, bool PK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R16 == 2 ? 3 : 4)))
 void sgmm_shrink_bf16(SgmmArgs a) {
-    const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
-    const int n_tiles = uniform(gld(hdr + SG_NTILES));
-    if (gld(hdr + SG_ERR)) return;
+    int32_t* hdr = (int32_t*)(a.ws + a.L.hdr);
+    __shared__ int32_t s_iperm[kWave];
+    __shared__ uint32_t s_iep[kWave];
+    __shared__ int s_inpos;
+    int n_tiles;
+    if (a.inline_seg) {
+        // this workgroup orders the rows itself; workgroup 0 publishes the
+        // header and the status word as the segmentation launch would
+        if (threadIdx.x < kWave) {
+            const int np = inline_order(a, s_iperm, s_iep, nullptr);
+            if (threadIdx.x == 0) {
+                s_inpos = np;
+                if (blockIdx.x == 0) {
+                    gst(hdr + SG_ERR, np < 0 ? 1 : 0);
+                    gst(hdr + SG_NPOS, np < 0 ? 0 : np);
+                    gst(hdr + SG_NTILES, np < 0 ? 0 : (np + 31) / 32);
+                    if (a.status_out) gst(a.status_out, np < 0 ? 1 : 0);
+                }
+            }
+        }
+        __syncthreads();
+        const int np = s_inpos;
+        if (np < 0) return;
+        n_tiles = (np + 31) / 32;
+    } else {
+        n_tiles = uniform(gld(hdr + SG_NTILES));
+        if (gld(hdr + SG_ERR)) return;
+    }
     const int64_t n_live = a.total_ks * n_tiles, per = (n_live + 7) / 8;
     const int64_t bid = blockIdx.x, j = bid >> 3;
     if (j >= per) return;
     const int64_t t = (bid & 7) * per + j;
     if (t >= n_live) return;
     const int64_t gks = t / n_tiles;  // slice index over all problems
-    shrink_item<R16, PK>(a, gks, (int)(t - gks * n_tiles), n_tiles);
+    shrink_item<R16, PK>(a, gks, (int)(t - gks * n_tiles), n_tiles, a.inline_seg ? s_iperm : nullptr,
+                         a.inline_seg ? s_iep : nullptr);
 }
 
 // ---- expand (bf16, MFMA) -----------------------------------------------------
@@ -622,8 +693,11 @@ static_assert(32 * 2 * 16 * kExpandFoldR16 * 4 <= kQLds * 2 * kWave * 16, "v blo
 // work item = (problem, kECols-column group cgg over all problems, tile) with
 // the tile fastest: neighbouring work items (same XCD) reuse the same B column
 // slices.
+// i_perm / i_ep / i_g: the rows' order computed in the workgroup
+// (inline_order), or nullptr to read the segmentation's from the workspace.
 template <int R16, bool RVEC>
-__device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int tile, int half) {
+__device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int tile, int half,
+                                            const int32_t* i_perm, const uint32_t* i_ep, const f32x2* i_g) {
     constexpr int RPAD = R16 * 16;
     constexpr bool FOLD = R16 <= kExpandFoldR16;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
@@ -636,10 +710,21 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
     // (row-major lane map: instruction i holds row 8i + lr, chunk lc), slots,
     // gates and expert mask
     int yrow[4];
+    uint32_t ep;
+    float g0, g1;
+    if (i_perm) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) yrow[i] = gld(perm + tile * 32 + 8 * i + lr);
-    const uint32_t ep = gld(epk + tile * 32 + n);
-    const float g0 = gld(gpk + 2 * (tile * 32 + n)), g1 = gld(gpk + 2 * (tile * 32 + n) + 1);
+        for (int i = 0; i < 4; ++i) yrow[i] = i_perm[tile * 32 + 8 * i + lr];
+        ep = i_ep[tile * 32 + n];
+        g0 = i_g[tile * 32 + n].x;
+        g1 = i_g[tile * 32 + n].y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yrow[i] = gld(perm + tile * 32 + 8 * i + lr);
+        ep = gld(epk + tile * 32 + n);
+        g0 = gld(gpk + 2 * (tile * 32 + n));
+        g1 = gld(gpk + 2 * (tile * 32 + n) + 1);
+    }
     const SgDesc D = a.descs ? a.cb_desc[cgg] : a.single;
     const int cg = (int)(cgg - D.unit0);
     const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * a.L.T_pad * 2 * RPAD;
@@ -879,8 +964,24 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
 template <int R16, bool RVEC>
 __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a) {
     const int32_t* hdr = (const int32_t*)(a.ws + a.L.hdr);
-    const int n_tiles = uniform(gld(hdr + SG_NTILES));
-    if (gld(hdr + SG_ERR)) return;
+    __shared__ int32_t s_iperm[kWave];
+    __shared__ uint32_t s_iep[kWave];
+    __shared__ f32x2 s_ig[kWave];
+    __shared__ int s_inpos;
+    int n_tiles;
+    if (a.inline_seg) {
+        if (threadIdx.x < kWave) {
+            const int np = inline_order(a, s_iperm, s_iep, s_ig);
+            if (threadIdx.x == 0) s_inpos = np;
+        }
+        __syncthreads();
+        const int np = s_inpos;
+        if (np < 0) return;
+        n_tiles = (np + 31) / 32;
+    } else {
+        n_tiles = uniform(gld(hdr + SG_NTILES));
+        if (gld(hdr + SG_ERR)) return;
+    }
     const int64_t n_live = a.total_cb * n_tiles, per = (n_live + 7) / 8;
     const int64_t m = per < kExpandSplit ? per : kExpandSplit;
     const int64_t bid = blockIdx.x, j = bid >> 3;
@@ -895,7 +996,8 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a) {
     const int64_t t = (bid & 7) * per + jj;
     if (t >= n_live) return;
     const int64_t cgg = t / n_tiles;
-    expand_item<R16, RVEC>(a, cgg, (int)(t - cgg * n_tiles), half);
+    expand_item<R16, RVEC>(a, cgg, (int)(t - cgg * n_tiles), half, a.inline_seg ? s_iperm : nullptr,
+                           a.inline_seg ? s_iep : nullptr, a.inline_seg ? s_ig : nullptr);
 }
 
 // ---- few rows (bf16, T <= kSgmmSmallT) -----------------------------------------
@@ -1271,6 +1373,21 @@ hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The MFMA launches for the workspace's padded rank.
+hipError_t launch_mfma_r(const SgmmArgs& a, hipStream_t s) {
+    switch (a.L.r_pad / 16) {
+        case 1: return launch_mfma<1>(a, s);
+        case 2: return launch_mfma<2>(a, s);
+        case 3: return launch_mfma<3>(a, s);
+        case 4: return launch_mfma<4>(a, s);
+        case 5: return launch_mfma<5>(a, s);
+        case 6: return launch_mfma<6>(a, s);
+        case 7: return launch_mfma<7>(a, s);
+        case 8: return launch_mfma<8>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_sgmm_pack_a(const void* A, void* Ap, int E, int r, int64_t d_in, hipStream_t s) {
@@ -1310,6 +1427,16 @@ hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
         return hipGetLastError();
     }
     if (!sgmm_grids_fit(a, dtype)) return hipErrorInvalidConfiguration;
+    // at most one wave of rows and no K-slice sum launch: the shrink and
+    // expand workgroups order the rows themselves, no segmentation launch
+    static_assert(kSgmmInlineRows <= kWave, "inline ordering: one row per lane");
+    const bool inl = dtype == 1 && a.T <= kSgmmInlineRows &&
+                     !(a.L.r_pad / 16 > kExpandFoldR16 && a.total_ks > a.n_prob);
+    if (inl) {
+        SgmmArgs b = a;
+        b.inline_seg = 1;
+        return launch_mfma_r(b, s);
+    }
     static_assert(kSegThreads == kSgmmSegRows, "segmentation chunk");
     const int64_t n_chunks = a.L.n_chunks;
     if (n_chunks > kSegFewChunks) {
@@ -1322,19 +1449,7 @@ hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
                        a.ws, a.L, a.status_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (dtype == 1) {
-        switch (a.L.r_pad / 16) {
-            case 1: return launch_mfma<1>(a, s);
-            case 2: return launch_mfma<2>(a, s);
-            case 3: return launch_mfma<3>(a, s);
-            case 4: return launch_mfma<4>(a, s);
-            case 5: return launch_mfma<5>(a, s);
-            case 6: return launch_mfma<6>(a, s);
-            case 7: return launch_mfma<7>(a, s);
-            case 8: return launch_mfma<8>(a, s);
-            default: return hipErrorInvalidValue;
-        }
-    }
+    if (dtype == 1) return launch_mfma_r(a, s);
     // fp32: element-wise kernels, grid sized for the most rows possible
     const dim3 g1((unsigned)((a.L.T_pad * 2 * a.r + 255) / 256), (unsigned)a.n_prob);
     hipLaunchKernelGGL(sgmm_shrink_generic<float>, g1, dim3(256), 0, s, a);

@@ -55,6 +55,12 @@ constexpr int kSgmmExpandCols = 1024;
 // segmentation, a shrink and a K-slice sum running first.
 constexpr int kSgmmSmallT = 4;
 
+// Up to this many rows (one wave's lanes) the shrink and expand workgroups
+// order the rows themselves (the segmentation's order, computed by one wave),
+// so there is no segmentation launch; batches that need the K-slice sum launch
+// keep it.
+constexpr int kSgmmInlineRows = 64;
+
 // Header words of the workspace.
 enum { SG_ERR = 0, SG_NPOS = 1, SG_NTILES = 2 };
 
@@ -77,6 +83,7 @@ struct SgmmArgs {
     char* ws;
     SgLayout L;
     int32_t* status_out;   // device word that also receives the set-validity flag, or nullptr
+    int32_t inline_seg;    // 1: the shrink and expand order the rows themselves (launch_sgmm sets it)
 };
 
 hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s);

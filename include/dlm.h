@@ -278,7 +278,11 @@ int dlm_sgmm_workspace_size(int64_t T, int64_t d_in_max, int32_t E, int32_t r,
  * which each 1024-column group computes the rows' rank vectors (fp32 dot
  * products over all of K) and adds s*g*v*B^T to its columns with one rounding;
  * with several, one launch for the rank vectors per 2048-wide K slice and one
- * for the columns.  Results are bitwise reproducible run to run.
+ * for the columns.  A bf16 call with 5 to 64 rows and no K-slice sum launch
+ * has no segmentation launch either: every shrink and expand workgroup orders
+ * the rows itself, in the same order (one wave, one row per lane), so the
+ * results are those of the segmented launches bit for bit.  Results are
+ * bitwise reproducible run to run.
  * Rows whose two slots are empty are not touched.
  * A row with an index outside [-1, E) or a non-finite gate on a used slot makes
  * the whole call a no-op on y and sets the workspace status word (read it with
@@ -352,8 +356,9 @@ int dlm_sgmm_group_repack(dlm_sgmm_group* h, void* stream);
 
 /*
  * Run every problem of the group for T rows: one segment launch shared by all
- * problems, then one shrink, one K-slice sum (only when some d_in > 2048 and
- * r > 64) and one expand launch covering all problems.
+ * problems (none up to 64 rows without a K-slice sum, as for dlm_sgmm), then
+ * one shrink, one K-slice sum (only when some d_in > 2048 and r > 64) and one
+ * expand launch covering all problems.
  * workspace: >= dlm_sgmm_workspace_size(T, max d_in, E, r, n_problems) bytes.
  */
 int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, int64_t T,
@@ -369,9 +374,10 @@ int dlm_sgmm_status(void* workspace, int32_t* code, void* stream);
  * Number of kernel launches one dlm_sgmm, dlm_sgmm_noalloc or
  * dlm_sgmm_group_run call makes for T rows and n_problems problems of rank r
  * with d_in up to d_in_max: 0 for T = 0; for bf16 with T <= 4, 1 (one problem)
- * or 2; else the segmentation (2 launches when T > 8192, else 1), the shrink,
- * the K-slice sum (bf16 with d_in_max > 2048 and r > 64 only: at lower ranks
- * the expand adds the slices itself) and the expand.  Returns -1 (with the last
+ * or 2; for bf16 with T <= 64 and no K-slice sum, 2 (shrink and expand); else
+ * the segmentation (2 launches when T > 8192, else 1), the shrink, the K-slice
+ * sum (bf16 with d_in_max > 2048 and r > 64 only: at lower ranks the expand
+ * adds the slices itself) and the expand.  Returns -1 (with the last
  * error set) for a negative T, d_in_max < 1, r outside [1, DLM_MAX_RANK],
  * n_problems < 1 or an unknown dtype.
  */

@@ -1,8 +1,9 @@
 """The counter summary bench.py builds from two rocprofv3 --pmc CSVs: each
 counter is scaled by its own reading for the 1 GiB copy, the switch dispatches
 are averaged, and the SGMM dispatches are split into passes at each
-segmentation (one or two launches; prefill passes first, then the
-mixed-decode steps). Synthetic CSVs in
+segmentation (one or two launches) or, where a pass has none (up to 64
+rows), at its shrink launch; prefill passes first, then the mixed-decode
+steps. Synthetic CSVs in
 the profile run's dispatch order; no GPU."""
 import csv
 import json
@@ -19,10 +20,10 @@ _PLACE = ("dlm::(anonymous namespace)::sgmm_seg_place(int const*, float const*, 
           "dlm::SgLayout, int*)")
 # (kernel name, share of the kind's counter value) per dispatch: the prefill
 # (4096 rows) segments with a count and a placing launch, mixed decode (64 rows)
-# with the placing launch alone
+# has no segmentation launch (its shrink and expand order the rows)
 KERNELS = [{"segment": [(_COUNT, 0.25), (_PLACE, 0.75)], "shrink": [(_SHRINK, 1.0)], "vsum": [(_VSUM, 1.0)],
             "expand": [(_EXPAND, 1.0)]},
-           {"segment": [(_PLACE, 1.0)], "shrink": [(_SHRINK, 1.0)], "vsum": [(_VSUM, 1.0)],
+           {"segment": [], "shrink": [(_SHRINK, 1.0)], "vsum": [(_VSUM, 1.0)],
             "expand": [(_EXPAND, 1.0)]}]
 
 
@@ -59,10 +60,11 @@ def test_traffic_summary_from_counter_csvs(tmp_path):
     assert pre["kernels"]["shrink"] == {"read": 1000.0 * 1024 * 2, "write": 1000.0 * 1024}
     # both segmentation launches of a prefill pass count as its segment
     assert pre["kernels"]["segment"] == {"read": 1.0 * 1024 * 2, "write": 1.0 * 1024}
-    assert mix["kernels"]["segment"] == {"read": 2.0 * 1024 * 2, "write": 2.0 * 1024}
+    assert mix["kernels"]["segment"] == {"read": 0.0, "write": 0.0}
+    assert mix["kernels"]["shrink"] == {"read": 3000.0 * 1024 * 2, "write": 3000.0 * 1024}
     assert mix["kernels"]["expand"] == {"read": 4000.0 * 1024 * 2, "write": 4000.0 * 1024}
     assert pre["read_per_step"] == sum(pk[0].values()) * 1024 * 2
-    assert mix["write_per_step"] == sum(pk[1].values()) * 1024
+    assert mix["write_per_step"] == (sum(pk[1].values()) - pk[1]["segment"]) * 1024
     assert pre["algo_bytes_per_step"] == 1007812608   # 4096 tokens x 7 projections, Zipf pairs
     assert pre["source_hash"] == bench._src_hash(bench.SGMM_SOURCES)
 

@@ -316,3 +316,33 @@ def test_segment_order_equals_host_stable_sort(T, E, seed):
     assert hdr[1] == n_pos and hdr[2] == (n_pos + 31) // 32
     assert np.array_equal(perm[:n_pos], want)
     assert (perm[n_pos:] == -1).all()
+
+
+@pytest.mark.parametrize("T,d_in,d_out,E,r,seed", [(64, 4104, 520, 8, 16, 1), (37, 200, 72, 16, 40, 2),
+                                                   (64, 136, 64, 4, 128, 3), (6, 64, 1096, 2, 24, 4)])
+def test_inline_row_order_equals_the_segmentation(T, d_in, d_out, E, r, seed):
+    """Up to 64 rows the shrink and expand order the rows themselves (no
+    segmentation launch).  The same rows followed by released rows up to 65
+    (the segmentation launch runs, and released rows take no position) must
+    give bitwise the same y for the first T rows, leave the released rows
+    alone, and agree with the oracle; the header words the shrink publishes
+    match the segmentation's."""
+    print(f"[sgmm] inline order T={T} d_in={d_in} r={r}", flush=True)
+    T2 = 65
+    x, A, B, y = _problem(T2, d_in, d_out, E, r, torch.bfloat16, 3600 + seed)
+    idx, g = _sets(T2, E, np.random.default_rng(200 + seed))
+    idx[T:] = -1
+    assert dlm.sgmm_launches(T, d_in, r) == 2 and dlm.sgmm_launches(T2, d_in, r) == 3
+    y0 = y.clone()
+    ya, yb = y[:T].clone(), y.clone()
+    ws = dlm.sgmm_workspace(T2, d_in, E, r)
+    dlm.sgmm(x[:T].contiguous(), idx[:T].contiguous().cuda(), g[:T].contiguous().cuda(), A, B, ya, 1.0, ws)
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    hdr_a = ws[:256].cpu().view(torch.int32).numpy()[:3].copy()
+    dlm.sgmm(x, idx.cuda(), g.cuda(), A, B, yb, 1.0, ws)
+    assert dlm.sgmm_status(ws) == dlm.DLM_OK
+    hdr_b = ws[:256].cpu().view(torch.int32).numpy()[:3].copy()
+    assert np.array_equal(hdr_a, hdr_b), (hdr_a, hdr_b)
+    assert torch.equal(ya, yb[:T]), "inline order differs from the segmentation"
+    assert torch.equal(yb[T:], y0[T:]), "a released row was written"
+    _check(x[:T], idx[:T], g[:T], A, B, y0[:T].cpu(), ya, 1.0, f"inline order T={T}")
