@@ -4,8 +4,9 @@
 //
 // One wave64 per token.  Each lane accumulates the E logits over its share of
 // the columns in binary64 (the products of fp32 or bf16 operands are exact in
-// binary64), a fixed butterfly sums the 64 partials, and lane 0 takes the
-// top two (ties -> lower index) and the renormalised pair of weights
+// binary64), a fixed butterfly sums the 64 partials, then lane e holds logit e
+// and a cross-lane reduction over the wave takes the top two (ties -> lower
+// index); lane 0 stores them and the renormalised pair of weights
 // g0 = 1/(1+exp(l1-l0)), g1 = exp(l1-l0)/(1+exp(l1-l0)).
 #include "dlm.h"
 #include "gfx950.hpp"
@@ -24,35 +25,64 @@ template <> __device__ __forceinline__ double ldv<uint16_t>(const uint16_t* p, i
 
 constexpr int kTokPerBlock = 4;
 
-// Lane 0 takes the top two of the summed logits l by strict '>' scans (equal
-// logits keep the lower index; a NaN logit never compares greater, so the
-// indices stay in range and distinct) and the renormalised pair of weights.
-template <int EMAX>
-__device__ __forceinline__ void top2_store(const double (&l)[EMAX], int E, int64_t t, int32_t* idx, float* g) {
-    int i0 = 0;
-    double l0 = l[0];
+// Index of the largest key over the wave, equal keys resolved to the lower
+// index, by a xor butterfly: every lane ends with the same winner whatever
+// order the pairs meet in, since "larger key, then lower index" is a total
+// order on the (key, index) pairs.
+__device__ __forceinline__ int wave_argmax(double key, int i) {
 #pragma unroll
-    for (int e = 1; e < EMAX; ++e)
-        if (e < E && l[e] > l0) { l0 = l[e]; i0 = e; }
-    int i1 = (i0 == 0) ? 1 : 0;
-    double l1 = (i0 == 0) ? l[1] : l[0];
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e)
-        if (e < E && e != i0 && l[e] > l1) { l1 = l[e]; i1 = e; }
-    const double q = exp(l1 - l0);  // <= 1
-    idx[2 * t] = i0;
-    idx[2 * t + 1] = i1;
-    g[2 * t] = (float)(1.0 / (1.0 + q));
-    g[2 * t + 1] = (float)(q / (1.0 + q));
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double k2 = __shfl_xor(key, o, kWave);
+        const int i2 = __shfl_xor(i, o, kWave);
+        if (k2 > key || (k2 == key && i2 < i)) {
+            key = k2;
+            i = i2;
+        }
+    }
+    return i;
 }
 
-// Sum each logit over the wave (fixed butterfly); lane 0 stores the result.
+// Top two of the logits held one per lane (lane e < E holds expert e's) by two
+// wave argmax rounds, then lane 0 stores them and the renormalised weights.
+// The keys make each round a strict '>' scan from its lowest candidate index
+// (expert 0 for slot 0, the lowest expert other than slot 0's for slot 1):
+// equal logits keep the lower index, and a NaN logit is kept where the scan
+// starts (the largest key there) and never taken elsewhere (the smallest key),
+// so the indices stay in range and distinct.  Lanes past E, and slot 0's lane
+// in the second round, carry indices above every expert's and lose every tie.
+__device__ __forceinline__ void wave_top2_store(double l, int E, int64_t t, int32_t* idx, float* g) {
+    const int lane = lane_id();
+    const double inf = __builtin_huge_val();
+    const bool nan = l != l;
+    const bool on = lane < E;
+    const double k0 = !on ? -inf : (nan ? (lane == 0 ? inf : -inf) : l);
+    const int i0 = uniform(wave_argmax(k0, on ? lane : kWave + lane));
+    const int j0 = i0 == 0 ? 1 : 0;
+    const bool on1 = on && lane != i0;
+    const double k1 = !on1 ? -inf : (nan ? (lane == j0 ? inf : -inf) : l);
+    const int i1 = uniform(wave_argmax(k1, on1 ? lane : kWave + lane));
+    const double l0 = __shfl(l, i0, kWave), l1 = __shfl(l, i1, kWave);
+    if (lane == 0) {
+        const double q = exp(l1 - l0);  // <= 1
+        idx[2 * t] = i0;
+        idx[2 * t + 1] = i1;
+        g[2 * t] = (float)(1.0 / (1.0 + q));
+        g[2 * t + 1] = (float)(q / (1.0 + q));
+    }
+}
+
+// Sum each logit over the wave (fixed butterfly), then the wave's top two.
 template <int EMAX>
 __device__ __forceinline__ void top2(double (&acc)[EMAX], int E, int64_t t, int32_t* idx, float* g) {
+    const int lane = lane_id();
+    double mine = 0.0;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e)
-        if (e < E) acc[e] = wave_sum(acc[e]);
-    if (lane_id() == 0) top2_store<EMAX>(acc, E, t, idx, g);
+        if (e < E) {
+            acc[e] = wave_sum(acc[e]);
+            if (lane == e) mine = acc[e];
+        }
+    wave_top2_store(mine, E, t, idx, g);
 }
 
 template <typename T, int EMAX>
@@ -143,15 +173,15 @@ __global__ __launch_bounds__(kVecWaves* kWave) void pregate_bf16_vec(
         for (int e = 0; e < EMAX; ++e) s_part[w][e] = acc[e];
     }
     __syncthreads();
-    if (w != 0 || lane != 0) return;
-    double l[EMAX];
+    if (w != 0) return;
+    // lane e: logit e, the waves' sums added in wave order; then the top two
+    double l = 0.0;
+    if (lane < E) {
+        l = s_part[0][lane];
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-        l[e] = s_part[0][e];
-#pragma unroll
-        for (int q = 1; q < kVecWaves; ++q) l[e] += s_part[q][e];
+        for (int q = 1; q < kVecWaves; ++q) l += s_part[q][lane];
     }
-    top2_store<EMAX>(l, E, t, idx, g);
+    wave_top2_store(l, E, t, idx, g);
 }
 
 // Nearest-centroid pre-gate (the ARIADNE page: training-free routing by the
