@@ -181,3 +181,51 @@ def test_centroid_router_empty_batch_is_noop():
     C = torch.zeros(4, 2, 64, dtype=torch.bfloat16, device="cuda")
     idx, g = dlm.pregate_centroid(x, C)
     assert idx.shape == (0, 2)
+
+
+def _scan_top2(l):
+    """Strict '>' scans from the lowest candidate index, as the oracle's."""
+    i0 = 0
+    for e in range(1, len(l)):
+        if l[e] > l[i0]:
+            i0 = e
+    i1 = 1 if i0 == 0 else 0
+    for e in range(len(l)):
+        if e != i0 and l[e] > l[i1]:
+            i1 = e
+    return [i0, i1]
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("E", [2, 3, 8, 17, 32])
+def test_router_top2_on_crafted_logits(E, dt):
+    """The wavefront top two on logit vectors set exactly (one token, x a unit
+    vector, Wr's first row the logits): NaN where slot 0's scan starts, where
+    slot 1's starts and elsewhere, infinities, many-way ties.  Indices are
+    bit-exact against the oracle's scans (bf16 with E a multiple of 8 takes the
+    vectorised kernel, the rest the one-wave kernel); weights are compared on
+    the finite vectors."""
+    nan, inf = float("nan"), float("inf")
+    fixed = [[nan] + [1.0] * (E - 1), [1.0, nan] + [2.0] * (E - 2), [5.0, nan] + [3.0] * (E - 2),
+             [-inf] * E, [inf] * E, [0.5] * E, [nan] * E, [1.0] * (E - 1) + [nan],
+             [2.0, 2.0] + [nan] * (E - 2), [-inf, nan] + [-inf] * (E - 2), [0.0] * (E - 1) + [inf],
+             [-1.0] * (E - 2) + [0.5, 0.5]]
+    rng = np.random.default_rng(1000 + E)
+    pool = np.array([nan, inf, -inf, -1.0, 0.0, 0.5, 1.0, 2.0])
+    cases = [v[:E] for v in fixed] + [list(rng.choice(pool, size=E, p=[.1, .05, .1, .15, .15, .15, .15, .15]))
+                                      for _ in range(40)]
+    d = 8
+    x = torch.zeros(1, d, dtype=dt)
+    x[0, 0] = 1.0
+    print(f"[pregate] crafted logits E={E} {dt}: {len(cases)} vectors", flush=True)
+    for c, lv in enumerate(cases):
+        Wr = torch.zeros(d, E, dtype=dt)
+        Wr[0] = torch.tensor(lv, dtype=torch.float64).to(dt)
+        idx, g = dlm.pregate(x.cuda(), Wr.cuda())
+        torch.cuda.synchronize()
+        ri, rg = oracle.pregate(x, Wr)
+        got = idx[0].cpu().tolist()
+        assert got == ri[0].tolist() == _scan_top2(Wr[0].double().tolist()), (c, lv, got, ri[0].tolist())
+        if all(np.isfinite(lv)):
+            gg, rr = g[0].cpu(), rg[0]
+            assert ((gg - rr).abs() / rr.abs().clamp_min(1e-30)).max().item() <= 2.0 ** -22, (c, lv, gg, rr)
