@@ -776,15 +776,17 @@ def _sgmm_traffic_from(fetch_csv, write_csv, read):
     """Per-kernel HBM bytes of the grouped SGMM passes of --profile-kernels: the
     dispatches of the SGMM kernels, in dispatch order, split into passes where a
     segmentation launch follows another kind (a pass segments with one launch,
-    or with a count launch and a placing launch above 8192 rows) or a shrink
-    launch follows anything but a segmentation (up to 64 rows a pass has no
+    or with a count launch and a placing launch above 8192 rows; up to rank 64
+    the shrink and expand then run as one launch) or a shrink launch follows
+    anything but a segmentation (above rank 64, up to 64 rows, a pass has no
     segmentation launch: the shrink and expand order the rows); the first
     SGMM_PROFILE_PASSES passes are the prefill, the next the mixed-decode steps
     0, 1, ...  Each counter is scaled by its own reading for the 1 GiB copy."""
     import csv
     import synth
-    kinds = ("segment", "shrink", "vsum", "expand")
-    names = {"segment": "sgmm_seg_", "shrink": "sgmm_shrink", "vsum": "sgmm_vsum", "expand": "sgmm_expand"}
+    kinds = ("segment", "shrink", "vsum", "expand", "fused")
+    names = {"segment": "sgmm_seg_", "shrink": "sgmm_shrink", "vsum": "sgmm_vsum", "expand": "sgmm_expand",
+             "fused": "sgmm_fused"}
     per = {}
     for part, path, counter in (("read", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         _, cp = read(path, counter, "\0")
@@ -844,8 +846,8 @@ def _roofline_all(sw, sw70, sg):
             continue
         per = r["ms_per_pass"] if key == "prefill" else r["grouped_ms_per_step"]
         # rank 16: segment, shrink, expand; up to 64 rows no segmentation launch
-        kern = ("sgmm step: shrink, expand (rows ordered in both)" if key == "mixed_decode"
-                else "sgmm pass: segment, shrink, expand (adds the K slices)")
+        kern = ("sgmm step: segment, then shrink + expand in one launch" if key == "mixed_decode"
+                else "sgmm pass: segment, then shrink + expand in one launch")
         out.append({"workload": name, "kernel": kern,
                     "bound": "hbm",
                     "achieved": round(r["GBps"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",

@@ -152,6 +152,7 @@ struct dlm_sgmm_group {
     float scale = 1.f;
     int32_t dtype = 0;
     int64_t total_cb = 0, total_ks = 0, d_out_max = 0, d_in_max = 0;
+    int32_t w_max = 0;  // largest K slices + column groups of one problem
     // packed copies of the distinct A banks (bf16 groups), owned by the handle
     struct Pack {
         const void* A;
@@ -548,10 +549,11 @@ int check_ws(void* ws, size_t ws_bytes, const SgLayout& L) {
 
 int run_sgmm(const SgDesc* d_descs, const SgDesc* ks_desc, const SgDesc* cb_desc,
              const SgDesc& single, int n_prob, int64_t total_cb,
-             int64_t total_ks, int64_t d_out_max, const int32_t* idx, const float* g, int64_t T, int E, int r,
-             float scale, int dtype, int packed, void* ws, const SgLayout& L, hipStream_t s,
+             int64_t total_ks, int64_t d_out_max, int32_t w_max, const int32_t* idx, const float* g, int64_t T,
+             int E, int r, float scale, int dtype, int packed, void* ws, const SgLayout& L, hipStream_t s,
              int32_t* status_out = nullptr) {
     SgmmArgs a;
+    a.w_max = w_max;
     a.status_out = status_out;
     a.inline_seg = 0;  // launch_sgmm decides
     a.descs = d_descs;
@@ -658,7 +660,8 @@ int dlm_sgmm(const void* x, const int32_t* idx, const float* g, const void* A, c
     rc = check_ws(workspace, ws_bytes, L);
     if (rc != DLM_OK) return rc;
     const SgDesc d = single_desc(x, A, B, y, d_in, d_out);
-    return run_sgmm(nullptr, nullptr, nullptr, d, 1, d.n_cb, d.n_ks, d_out, idx, g, T, E, r, scale, dtype, 0, workspace, L,
+    return run_sgmm(nullptr, nullptr, nullptr, d, 1, d.n_cb, d.n_ks, d_out, d.n_cb + d.n_ks, idx, g, T, E, r, scale,
+                    dtype, 0, workspace, L,
                     (hipStream_t)stream);
 }
 
@@ -682,7 +685,8 @@ int dlm_sgmm_noalloc(const void* x, const int32_t* idx, const float* g, const vo
     rc = scratch_on_current_device(&ws);
     if (rc != DLM_OK) return rc;
     const SgDesc d = single_desc(x, A, B, y, d_in, d_out);
-    return run_sgmm(nullptr, nullptr, nullptr, d, 1, d.n_cb, d.n_ks, d_out, idx, g, T, E, r, scale, dtype, 0, ws, L,
+    return run_sgmm(nullptr, nullptr, nullptr, d, 1, d.n_cb, d.n_ks, d_out, d.n_cb + d.n_ks, idx, g, T, E, r, scale,
+                    dtype, 0, ws, L,
                     (hipStream_t)stream, status);
 }
 
@@ -721,6 +725,7 @@ int dlm_sgmm_group_create(const dlm_sgmm_problem* probs, int32_t n, int32_t E, i
         ks += d.n_ks;
         if (probs[i].d_out > dmax) dmax = probs[i].d_out;
         if (probs[i].d_in > dimax) dimax = probs[i].d_in;
+        if (d.n_ks + d.n_cb > h->w_max) h->w_max = d.n_ks + d.n_cb;
     }
     h->n = n;
     h->E = E;
@@ -835,7 +840,8 @@ int dlm_sgmm_group_run(dlm_sgmm_group* h, const int32_t* idx, const float* g, in
         if (overlap(workspace, ws_bytes, idx, (size_t)T * 8) || overlap(workspace, ws_bytes, g, (size_t)T * 8))
             return fail(DLM_EINVAL, "sgmm_group_run: the workspace overlaps the sets");
     }
-    return run_sgmm(h->d_descs, h->d_ks_desc, h->d_cb_desc, h->h_descs[0], h->n, h->total_cb, h->total_ks, h->d_out_max, idx, g, T, h->E,
+    return run_sgmm(h->d_descs, h->d_ks_desc, h->d_cb_desc, h->h_descs[0], h->n, h->total_cb, h->total_ks, h->d_out_max,
+                    h->w_max, idx, g, T, h->E,
                     h->r, h->scale, h->dtype, h->packs.empty() ? 0 : 1, workspace, L, (hipStream_t)stream);
 }
 
@@ -861,6 +867,10 @@ int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t r, int32_t n_problems
     const int seg = T > kSgmmSegFewRows ? 2 : 1;
     if (dtype == DLM_F32) return seg + 2;
     const int vsum = d_in_max > kSgmmKSlice && r > kSgmmFoldRank ? 1 : 0;
+    const bool fold = (r + 15) / 16 * 16 <= kSgmmFoldRank;
+    const bool fused_ks = (d_in_max + kSgmmKSlice - 1) / kSgmmKSlice <= kSgmmFusedMaxKs;
+    if (fold && fused_ks && kSgmmFused > 0 && (kSgmmFused > 1 || T > kSgmmInlineRows))
+        return seg + 1;  // one launch after the segmentation
     if (T <= kSgmmInlineRows && !vsum) return 2;  // the rows ordered inside the shrink and expand
     return seg + 2 + vsum;
 }

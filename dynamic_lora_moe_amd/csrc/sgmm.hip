@@ -57,6 +57,8 @@ SgLayout sgmm_layout(int64_t T, int64_t d_in_max, int E, int r, int n_prob) {
     L.hist = o;  o += a256((size_t)L.n_chunks * (E + 1) * (E + 1) * 4);
     L.cerr = o;  o += a256((size_t)L.n_chunks * 4);
     L.v = o;     o += a256((size_t)n_prob * L.max_ks * L.T_pad * 2 * L.r_pad * 4);
+    L.dep = o;   o += a256((size_t)n_prob * L.max_ks * L.tiles_max * 4);
+    L.xcd = o;   o += a256((size_t)8 * kSgmmXcdWords * 4);
     L.total = o;
     return L;
 }
@@ -140,6 +142,74 @@ __device__ __forceinline__ int block_exscan(int v, int* s_tot, int& total) {
     return before + inc - v;
 }
 
+// Work ranges of the one-launch shrink + expand (one workgroup, all threads;
+// run by the segmentation once the live tile count nt is known).  The
+// (problem, tile) pairs, problem-major, are split into 8 contiguous ranges of
+// about equal weight, one per XCD, a pair weighing its problem's K slices +
+// column groups (its shrink + expand items): the pair whose weight interval
+// holds x/8 of the total starts XCD x's range.  Per XCD it writes
+//   [0] p_a  [1] t_a  [2] p_b  [3] t_b     first pair, last problem and its tiles
+//   [4] shrink items of p_a  [5] of the problems between  [6] all its shrink items
+//   [7] ks0(p_a)  [8] ks0(p_a + 1)  [9] ks0(p_b)
+//   [10] expand items of p_a  [11] of the problems between  [12] all its expand items
+//   [13] unit0(p_a)  [14] unit0(p_a + 1)  [15] unit0(p_b)
+// and clears the shrink counts of every (problem, tile).
+__device__ void sgmm_fused_ranges(char* ws, const SgLayout& L, const SgDesc* __restrict__ descs,
+                                  const SgDesc& single, int32_t n_prob, int64_t total_ks, int64_t total_cb,
+                                  int64_t nt) {
+    int32_t* dep = (int32_t*)(ws + L.dep);
+    int32_t* tab = (int32_t*)(ws + L.xcd);
+    const int tid = threadIdx.x;
+    for (int64_t i = tid; i < total_ks * L.tiles_max; i += kSegThreads) dep[i] = 0;
+    __shared__ int64_t s_qb[9];
+    const int64_t Wt = (total_ks + total_cb) * nt;
+    if (tid < 9) s_qb[tid] = (int64_t)n_prob * nt;
+    if (tid == 0) s_qb[0] = 0;
+    __syncthreads();
+    for (int p = tid; p < n_prob; p += kSegThreads) {
+        const SgDesc& Dp = descs ? descs[p] : single;
+        const int64_t w = Dp.n_ks + Dp.n_cb, lo = (Dp.ks0 + Dp.unit0) * nt, hi = lo + w * nt;
+        for (int x = 1; x < 8; ++x) {
+            const int64_t sx = x * Wt / 8;
+            if (sx >= lo && sx < hi) s_qb[x] = (int64_t)p * nt + (sx - lo + w - 1) / w;
+        }
+    }
+    __syncthreads();
+    if (tid < 8) {
+        int32_t e[kSgmmXcdWords] = {};
+        const int64_t qa = s_qb[tid], qb = s_qb[tid + 1];
+        if (qb > qa) {
+            const int pa = (int)(qa / nt), ta = (int)(qa % nt);
+            const int pb = (int)((qb - 1) / nt), tb = (int)((qb - 1) % nt) + 1;
+            const SgDesc& Da = descs ? descs[pa] : single;
+            const SgDesc& Db = descs ? descs[pb] : single;
+            const int cnt_a = (pa == pb ? tb : (int)nt) - ta;
+            e[0] = pa;
+            e[1] = ta;
+            e[2] = pb;
+            e[3] = tb;
+            e[4] = Da.n_ks * cnt_a;
+            e[7] = (int32_t)Da.ks0;
+            e[10] = Da.n_cb * cnt_a;
+            e[13] = (int32_t)Da.unit0;
+            e[6] = e[4];
+            e[12] = e[10];
+            if (pb > pa) {
+                const SgDesc& Da1 = descs ? descs[pa + 1] : single;
+                e[5] = (int32_t)((Db.ks0 - Da1.ks0) * nt);
+                e[8] = (int32_t)Da1.ks0;
+                e[9] = (int32_t)Db.ks0;
+                e[6] = e[4] + e[5] + Db.n_ks * tb;
+                e[11] = (int32_t)((Db.unit0 - Da1.unit0) * nt);
+                e[14] = (int32_t)Da1.unit0;
+                e[15] = (int32_t)Db.unit0;
+                e[12] = e[10] + e[11] + Db.n_cb * tb;
+            }
+        }
+        for (int k = 0; k < kSgmmXcdWords; ++k) tab[tid * kSgmmXcdWords + k] = e[k];
+    }
+}
+
 // The segmentation is a stable counting sort of the rows by key, in chunks of
 // kSegThreads rows (one workgroup each):
 //   count  (only above kSegFewChunks chunks) each chunk's key counts (LDS
@@ -180,7 +250,10 @@ __global__ __launch_bounds__(kSegThreads) void sgmm_seg_count(const int32_t* __r
 
 __global__ __launch_bounds__(kSegThreads) void sgmm_seg_place(const int32_t* __restrict__ idx,
                                                               const float* __restrict__ g, int64_t T, int E,
-                                                              char* ws, SgLayout L, int32_t* status_out) {
+                                                              char* ws, SgLayout L, int32_t* status_out,
+                                                              const SgDesc* __restrict__ descs, SgDesc single,
+                                                              int32_t n_prob, int64_t total_ks, int64_t total_cb,
+                                                              int32_t fused) {
     int32_t* hdr = (int32_t*)(ws + L.hdr);
     int32_t* perm = (int32_t*)(ws + L.perm);
     uint32_t* epk = (uint32_t*)(ws + L.epk);
@@ -311,6 +384,8 @@ __global__ __launch_bounds__(kSegThreads) void sgmm_seg_place(const int32_t* __r
         hdr[SG_NTILES] = (n_pos + 31) / 32;
         if (status_out) *status_out = err;
     }
+    if (fused && chunk == 0) sgmm_fused_ranges(ws, L, descs, single, n_prob, total_ks, total_cb,
+                                               err ? 0 : (n_pos + 31) / 32);
 }
 
 // With at most kWave rows the shrink and expand workgroups order the rows
@@ -410,9 +485,30 @@ __device__ __forceinline__ int y_off(int row, int chunk) { return row * 64 + ((c
 // stored, and k past d_in reads a clamped address whose value is replaced by 0.
 // i_perm / i_ep: the rows' order computed in the workgroup (inline_order), or
 // nullptr to read the segmentation's from the workspace.
+// This wave's XCD (HW_REG_XCC_ID, bits 3:0).
+__device__ __forceinline__ int xcc_id() { return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u); }
+
+// LDS of one shrink work item.
+struct ShrinkLds {
+    __attribute__((aligned(16))) uint16_t x[kXRows * kShrinkStep];
+    int U[32];
+    int nU;
+    int row[kXRows];
+    // per row: slot 0's expert + 1 (bits 0-5), slot 1's + 1 (bits 6-11), bit 12
+    // set for a padding position (no row)
+    __attribute__((aligned(16))) uint16_t slots[kXRows];
+};
+
+// dep: the one-launch form's counts of finished shrink items per (problem,
+// tile), or nullptr.  With it the item, once its v stores are in L2, adds one
+// (and its XCD id + 1 in the upper half-word) to its (problem, tile) count; the
+// expand items of that pair wait for the problem's K-slice count.  Both run on
+// the same XCD, so the count and v meet in that XCD's L2 (the vector L1 writes
+// through).
 template <int R16, bool PK>
 __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int tile0, int n_tiles,
-                                            const int32_t* i_perm, const uint32_t* i_ep) {
+                                            const int32_t* i_perm, const uint32_t* i_ep, ShrinkLds& sm,
+                                            int32_t* dep = nullptr) {
     constexpr int RPAD = R16 * 16;
     const SgDesc D = a.descs ? a.ks_desc[gks] : a.single;
     const int k0 = (int)(gks - D.ks0) * kSgmmKSlice;
@@ -420,13 +516,11 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
     const uint32_t* epk = (const uint32_t*)(a.ws + a.L.epk);
     float* v = (float*)(a.ws + a.L.v) + gks * a.L.T_pad * 2 * RPAD;
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[kXRows * kShrinkStep];
-    __shared__ int s_U[32];
-    __shared__ int s_nU;
-    __shared__ int s_row[kXRows];
-    // per row: slot 0's expert + 1 (bits 0-5), slot 1's + 1 (bits 6-11), bit 12
-    // set for a padding position (no row)
-    __shared__ __attribute__((aligned(16))) uint16_t s_slots[kXRows];
+    uint16_t* s_x = sm.x;
+    int* s_U = sm.U;
+    int& s_nU = sm.nU;
+    int* s_row = sm.row;
+    uint16_t* s_slots = sm.slots;
     const int tid = threadIdx.x;
     static_assert(kXRows <= kWave, "one wave reads the tile's rows");
     if (tid < kWave) {
@@ -618,6 +712,14 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, int64_t gks, int 
             store_v(acc, u, rho, h);
         }
     }
+    if (dep) {
+        // every thread's v stores have reached L2 before the count moves
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_fetch_add(dep + D.ks0 * a.L.tiles_max + tile0, 1 + ((xcc_id() + 1) << 16), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // Work items are the live ones only: (problem, K slice, tile) over the tiles
@@ -663,8 +765,9 @@ void sgmm_shrink_bf16(SgmmArgs a) {
     const int64_t t = (bid & 7) * per + j;
     if (t >= n_live) return;
     const int64_t gks = t / n_tiles;  // slice index over all problems
+    __shared__ ShrinkLds sm;
     shrink_item<R16, PK>(a, gks, (int)(t - gks * n_tiles), n_tiles, a.inline_seg ? s_iperm : nullptr,
-                         a.inline_seg ? s_iep : nullptr);
+                         a.inline_seg ? s_iep : nullptr, sm);
 }
 
 // ---- expand (bf16, MFMA) -----------------------------------------------------
@@ -695,9 +798,23 @@ static_assert(32 * 2 * 16 * kExpandFoldR16 * 4 <= kQLds * 2 * kWave * 16, "v blo
 // slices.
 // i_perm / i_ep / i_g: the rows' order computed in the workgroup
 // (inline_order), or nullptr to read the segmentation's from the workspace.
+// LDS of one expand work item.
+struct ExpandLds {
+    int U[32];
+    int nU;
+    __attribute__((aligned(16))) uint16_t y[4][32 * 64];
+    __attribute__((aligned(16))) u32x4 u[kQLds][2][kWave];
+};
+
+// Bounded wait of the one-launch form (about a second): past it the item sets
+// the error word to 2 and goes on.
+constexpr int kDepSpinMax = 1 << 20;
+
+// dep: the one-launch form's shrink counts (see shrink_item), or nullptr.
 template <int R16, bool RVEC>
 __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int tile, int half,
-                                            const int32_t* i_perm, const uint32_t* i_ep, const f32x2* i_g) {
+                                            const int32_t* i_perm, const uint32_t* i_ep, const f32x2* i_g,
+                                            ExpandLds& sm, const int32_t* dep = nullptr) {
     constexpr int RPAD = R16 * 16;
     constexpr bool FOLD = R16 <= kExpandFoldR16;
     const int32_t* perm = (const int32_t*)(a.ws + a.L.perm);
@@ -729,10 +846,10 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
     const int cg = (int)(cgg - D.unit0);
     const float* v = (const float*)(a.ws + a.L.v) + D.ks0 * a.L.T_pad * 2 * RPAD;
 
-    __shared__ int s_U[32];
-    __shared__ int s_nU;
-    __shared__ __attribute__((aligned(16))) uint16_t s_y[4][32 * 64];
-    __shared__ __attribute__((aligned(16))) u32x4 s_u[kQLds][2][kWave];
+    int* s_U = sm.U;
+    int& s_nU = sm.nU;
+    uint16_t (*s_y)[32 * 64] = sm.y;
+    u32x4 (*s_u)[2][kWave] = sm.u;
 
     const int d_out = uniform(D.d_out), r = a.r;
     // this wave's first column and blocks: kEB blocks of the whole item, or
@@ -760,6 +877,25 @@ __device__ __forceinline__ void expand_item(const SgmmArgs& a, int64_t cgg, int 
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) m |= __shfl_xor(m, o, kWave);
         if (lane == 0) s_nU = mask_list(m, s_U);
+    }
+    if (dep && threadIdx.x == 0) {
+        // the tile's v is complete once every K slice's shrink item has counted
+        const int32_t* c = dep + D.ks0 * a.L.tiles_max + tile;
+        const int need = D.n_ks;
+        int cv = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int spins = 0; (cv & 0xffff) < need;) {
+            if (++spins > kDepSpinMax) {
+                gst((int32_t*)(a.ws + a.L.hdr) + SG_ERR, 2);
+                if (a.status_out) gst(a.status_out, 2);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            cv = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if ((cv & 0xffff) >= need && (cv >> 16) != need * (xcc_id() + 1)) {
+            gst((int32_t*)(a.ws + a.L.hdr) + SG_ERR, 3);
+            if (a.status_out) gst(a.status_out, 3);
+        }
     }
     __syncthreads();
     const int nU = uniform(s_nU);
@@ -996,8 +1132,89 @@ __global__ __launch_bounds__(256) void sgmm_expand_bf16(SgmmArgs a) {
     const int64_t t = (bid & 7) * per + jj;
     if (t >= n_live) return;
     const int64_t cgg = t / n_tiles;
+    __shared__ ExpandLds sm;
     expand_item<R16, RVEC>(a, cgg, (int)(t - cgg * n_tiles), half, a.inline_seg ? s_iperm : nullptr,
-                           a.inline_seg ? s_iep : nullptr, a.inline_seg ? s_ig : nullptr);
+                           a.inline_seg ? s_iep : nullptr, a.inline_seg ? s_ig : nullptr, sm);
+}
+
+// ---- one launch: shrink then expand ---------------------------------------------
+// After the segmentation (which wrote each XCD's work range and cleared the
+// counts): workgroup b runs item b / 8 of XCD b % 8's range -- first the range's
+// shrink items (problem by problem, K slice by K slice, tiles fastest), then
+// its expand items (column group by column group, tiles fastest).  An expand
+// item waits for its (problem, tile)'s K-slice count, which only shrink items
+// of the same range -- lower item numbers on the same XCD, dispatched earlier --
+// raise, so every wait ends; the last of a launch's shrink items overlap the
+// first expand items instead of draining alone.  Each item's arithmetic is that
+// of the two-launch form, so y gets the same bits.  The workgroups go to the
+// XCDs round-robin (from an XCD that depends on what ran before, as HIP-graph
+// replays show), so equal b % 8 means one XCD; the counts also carry their
+// producers' XCD ids, and an expand item whose producers ran on another XCD
+// sets the error word to 3.
+union FusedLds {
+    ShrinkLds s;
+    ExpandLds e;
+};
+
+template <int R16, bool PK, bool RVEC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void sgmm_fused_bf16(SgmmArgs a) {
+    int32_t* hdr = (int32_t*)(a.ws + a.L.hdr);
+    __shared__ FusedLds lds;
+    const int x = (int)(blockIdx.x & 7), j = (int)(blockIdx.x >> 3);
+    const u32x4* tab = (const u32x4*)(a.ws + a.L.xcd) + x * (kSgmmXcdWords / 4);
+    const int n_tiles = gld(hdr + SG_NTILES), err = gld(hdr + SG_ERR);
+    u32x4 tw[kSgmmXcdWords / 4];
+#pragma unroll
+    for (int k = 0; k < kSgmmXcdWords / 4; ++k) tw[k] = ld128(tab + k);
+    if (uniform(err) == 1) return;  // a bad set: the call is a no-op
+    int e[kSgmmXcdWords];
+#pragma unroll
+    for (int k = 0; k < kSgmmXcdWords; ++k) e[k] = uniform((int)tw[k / 4][k % 4]);
+    const int nt = uniform(n_tiles);
+    int32_t* dep = (int32_t*)(a.ws + a.L.dep);
+    const int n_s = e[6], n_e = e[12];
+    const int cnt_a = (e[0] == e[2] ? e[3] : nt) - e[1];
+    if (j < n_s) {
+        int64_t g;
+        int t;
+        if (j < e[4]) {
+            g = e[7] + j / cnt_a;
+            t = e[1] + j % cnt_a;
+        } else if (j < e[4] + e[5]) {
+            const int u = j - e[4];
+            g = e[8] + u / nt;
+            t = u % nt;
+        } else {
+            const int u = j - e[4] - e[5];
+            g = e[9] + u / e[3];
+            t = u % e[3];
+        }
+        shrink_item<R16, PK>(a, g, t, nt, nullptr, nullptr, lds.s, dep);
+    } else if (j < n_s + n_e) {
+        const int jj = j - n_s;
+        int64_t c;
+        int t;
+        if (jj < e[10]) {
+            c = e[13] + jj / cnt_a;
+            t = e[1] + jj % cnt_a;
+        } else if (jj < e[10] + e[11]) {
+            const int u = jj - e[10];
+            c = e[14] + u / nt;
+            t = u % nt;
+        } else {
+            const int u = jj - e[10] - e[11];
+            c = e[15] + u / e[3];
+            t = u % e[3];
+        }
+        expand_item<R16, RVEC>(a, c, t, -1, nullptr, nullptr, nullptr, lds.e, dep);
+    }
+}
+
+// Items one XCD's range can hold: its weight is at most an eighth of the
+// total plus one pair's (see sgmm_fused_ranges).
+inline int64_t fused_per_xcd(const SgmmArgs& a) {
+    return ((a.total_ks + a.total_cb) * a.L.tiles_max + 7) / 8 + 1 + a.w_max;
 }
 
 // ---- few rows (bf16, T <= kSgmmSmallT) -----------------------------------------
@@ -1373,6 +1590,29 @@ hipError_t launch_mfma(const SgmmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int R16>
+hipError_t launch_fused(const SgmmArgs& a, hipStream_t s) {
+    const dim3 gf((unsigned)(8 * fused_per_xcd(a)));
+    if (a.packed) {
+        if (a.r % 8 == 0) hipLaunchKernelGGL((sgmm_fused_bf16<R16, true, true>), gf, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((sgmm_fused_bf16<R16, true, false>), gf, dim3(256), 0, s, a);
+    } else {
+        if (a.r % 8 == 0) hipLaunchKernelGGL((sgmm_fused_bf16<R16, false, true>), gf, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((sgmm_fused_bf16<R16, false, false>), gf, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_r(const SgmmArgs& a, hipStream_t s) {
+    switch (a.L.r_pad / 16) {
+        case 1: return launch_fused<1>(a, s);
+        case 2: return launch_fused<2>(a, s);
+        case 3: return launch_fused<3>(a, s);
+        case 4: return launch_fused<4>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 // The MFMA launches for the workspace's padded rank.
 hipError_t launch_mfma_r(const SgmmArgs& a, hipStream_t s) {
     switch (a.L.r_pad / 16) {
@@ -1405,7 +1645,7 @@ static bool sgmm_grids_fit(const SgmmArgs& a, int dtype) {
     if (dtype == 1) {
         const int64_t per_max = (a.n_expand_units + 7) / 8;
         return grid_fits((a.L.T_pad * 2 * a.L.r_pad / 4 + 255) / 256, 256) &&
-               grid_fits(item_grid(a.total_ks * a.L.tiles_max), 256) &&
+               grid_fits(item_grid(a.total_ks * a.L.tiles_max), 256) && grid_fits(8 * fused_per_xcd(a), 256) &&
                grid_fits(8 * (per_max + (per_max < kExpandSplit ? per_max : kExpandSplit)), 256);
     }
     return grid_fits((a.L.T_pad * 2 * a.r + 255) / 256, 256) &&
@@ -1430,7 +1670,10 @@ hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
     // at most one wave of rows and no K-slice sum launch: the shrink and
     // expand workgroups order the rows themselves, no segmentation launch
     static_assert(kSgmmInlineRows <= kWave, "inline ordering: one row per lane");
-    const bool inl = dtype == 1 && a.T <= kSgmmInlineRows &&
+    const bool fold = a.L.r_pad / 16 <= kExpandFoldR16;
+    const bool fused = dtype == 1 && fold && a.L.max_ks <= kSgmmFusedMaxKs && kSgmmFused > 0 &&
+                       (kSgmmFused > 1 || a.T > kSgmmInlineRows);
+    const bool inl = !fused && dtype == 1 && a.T <= kSgmmInlineRows &&
                      !(a.L.r_pad / 16 > kExpandFoldR16 && a.total_ks > a.n_prob);
     if (inl) {
         SgmmArgs b = a;
@@ -1446,9 +1689,11 @@ hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
         if (e0 != hipSuccess) return e0;
     }
     hipLaunchKernelGGL(sgmm_seg_place, dim3((unsigned)n_chunks), dim3(kSegThreads), 0, s, a.idx, a.g, a.T, a.E,
-                       a.ws, a.L, a.status_out);
+                       a.ws, a.L, a.status_out, a.descs, a.single, a.n_prob, a.total_ks, a.total_cb,
+                       fused ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (fused) return launch_fused_r(a, s);
     if (dtype == 1) return launch_mfma_r(a, s);
     // fp32: element-wise kernels, grid sized for the most rows possible
     const dim3 g1((unsigned)((a.L.T_pad * 2 * a.r + 255) / 256), (unsigned)a.n_prob);

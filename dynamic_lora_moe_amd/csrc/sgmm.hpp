@@ -28,7 +28,9 @@ struct SgLayout {
     // (slot 0 in the low 16 bits, slot 1 in the high, -1 = empty); gpk: its two
     // gates; hist, cerr: each segmentation chunk's key counts and bad-set flag;
     // v: the shrink's results
-    size_t hdr, perm, epk, gpk, hist, cerr, v, total;
+    // dep, xcd: the one-launch shrink + expand's per-(problem, tile) counts of
+    // finished shrink items and its per-XCD work ranges
+    size_t hdr, perm, epk, gpk, hist, cerr, v, dep, xcd, total;
     int64_t T, T_pad, tiles_max, n_chunks;
     int r_pad;
     int max_ks;  // K slices of the widest problem
@@ -63,6 +65,18 @@ constexpr int kSgmmInlineRows = 64;
 
 // Header words of the workspace.
 enum { SG_ERR = 0, SG_NPOS = 1, SG_NTILES = 2 };
+// Words per XCD of the one-launch shrink + expand's work ranges.
+constexpr int kSgmmXcdWords = 16;
+// One-launch shrink + expand after the segmentation (bf16, ranks up to
+// kSgmmFoldRank): 0 off, 1 for segmented batches, 2 also for batches of up to
+// kSgmmInlineRows rows (segmented first instead of ordered in the kernels).
+#ifndef DLM_SGMM_FUSED
+#define DLM_SGMM_FUSED 2
+#endif
+constexpr int kSgmmFused = DLM_SGMM_FUSED;
+// Its counts hold K slices in 16 bits and K slices x (XCD id + 1) in 15: up to
+// this many K slices per problem.
+constexpr int kSgmmFusedMaxKs = 4095;
 
 struct SgmmArgs {
     const SgDesc* descs;    // device table, or nullptr to use `single`
@@ -84,6 +98,7 @@ struct SgmmArgs {
     SgLayout L;
     int32_t* status_out;   // device word that also receives the set-validity flag, or nullptr
     int32_t inline_seg;    // 1: the shrink and expand order the rows themselves (launch_sgmm sets it)
+    int32_t w_max;         // largest K slices + column groups of one problem
 };
 
 hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s);

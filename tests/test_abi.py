@@ -128,22 +128,23 @@ def test_sgmm_launch_count(lib):
     assert f(1, 4096, 16, 1, dlm.DLM_BF16) == 1
     assert f(4, 11008, 64, 1, dlm.DLM_BF16) == 1
     assert f(1, 4096, 128, 7, dlm.DLM_BF16) == 2
-    # 5..64 rows: the shrink and expand order the rows themselves (no
-    # segmentation launch) unless a K-slice sum launch is needed
+    # from 5 rows up to rank 64: the segmentation, then the shrink and expand
+    # in one launch
     assert f(5, 4096, 16, 1, dlm.DLM_BF16) == 2
     assert f(64, 11008, 64, 7, dlm.DLM_BF16) == 2
+    assert f(65, 4096, 16, 1, dlm.DLM_BF16) == 2
+    assert f(1024, 4096, 64, 7, dlm.DLM_BF16) == 2
+    # above rank 64, 5..64 rows: the shrink and expand order the rows
+    # themselves (no segmentation launch) unless a K-slice sum launch is needed
     assert f(64, 2048, 128, 1, dlm.DLM_BF16) == 2
-    # segment, shrink, expand; the expand adds the K slices up to rank 64
-    assert f(65, 4096, 16, 1, dlm.DLM_BF16) == 3
-    assert f(1024, 4096, 64, 7, dlm.DLM_BF16) == 3
     # above rank 64 a K-slice sum launch runs when there are several slices
     assert f(64, 4096, 65, 1, dlm.DLM_BF16) == 4
     assert f(65, 2048, 128, 1, dlm.DLM_BF16) == 3
     assert f(64, 2049, 128, 1, dlm.DLM_BF16) == 4
     # one segmentation launch up to 8192 rows, a count launch before the
     # placement above
-    assert f(8192, 4096, 16, 1, dlm.DLM_BF16) == 3
-    assert f(8193, 4096, 16, 1, dlm.DLM_BF16) == 4
+    assert f(8192, 4096, 16, 1, dlm.DLM_BF16) == 2
+    assert f(8193, 4096, 16, 1, dlm.DLM_BF16) == 3
     assert f(8193, 4096, 80, 1, dlm.DLM_BF16) == 5
     assert f(1, 64, 16, 1, dlm.DLM_F32) == 3
     assert f(4096, 64, 16, 1, dlm.DLM_F32) == 3
@@ -157,7 +158,7 @@ def test_sgmm_launch_count(lib):
     assert dlm.sgmm_launches(1, 11008, 16) == 1
     assert dlm.sgmm_launches(1, 11008, 16, 7) == 2
     assert dlm.sgmm_launches(64, 11008, 16) == 2
-    assert dlm.sgmm_launches(65, 11008, 16) == 3
+    assert dlm.sgmm_launches(65, 11008, 16) == 2
     assert dlm.sgmm_launches(64, 11008, 128) == 4
 
 
