@@ -869,7 +869,8 @@ int dlm_sgmm_launches(int64_t T, int64_t d_in_max, int32_t r, int32_t n_problems
     const int vsum = d_in_max > kSgmmKSlice && r > kSgmmFoldRank ? 1 : 0;
     const bool fold = (r + 15) / 16 * 16 <= kSgmmFoldRank;
     const bool fused_ks = (d_in_max + kSgmmKSlice - 1) / kSgmmKSlice <= kSgmmFusedMaxKs;
-    if (fold && fused_ks && kSgmmFused > 0 && (kSgmmFused > 1 || T > kSgmmInlineRows))
+    const bool fused_pairs = (int64_t)n_problems * ((T + 31) / 32) >= kSgmmFusedMinPairs;
+    if (fold && fused_ks && fused_pairs && kSgmmFused > 0 && (kSgmmFused > 1 || T > kSgmmInlineRows))
         return seg + 1;  // one launch after the segmentation
     if (T <= kSgmmInlineRows && !vsum) return 2;  // the rows ordered inside the shrink and expand
     return seg + 2 + vsum;

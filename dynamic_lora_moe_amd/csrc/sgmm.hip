@@ -1672,6 +1672,7 @@ hipError_t launch_sgmm(const SgmmArgs& a, int dtype, hipStream_t s) {
     static_assert(kSgmmInlineRows <= kWave, "inline ordering: one row per lane");
     const bool fold = a.L.r_pad / 16 <= kExpandFoldR16;
     const bool fused = dtype == 1 && fold && a.L.max_ks <= kSgmmFusedMaxKs && kSgmmFused > 0 &&
+                       (int64_t)a.n_prob * a.L.tiles_max >= kSgmmFusedMinPairs &&
                        (kSgmmFused > 1 || a.T > kSgmmInlineRows);
     const bool inl = !fused && dtype == 1 && a.T <= kSgmmInlineRows &&
                      !(a.L.r_pad / 16 > kExpandFoldR16 && a.total_ks > a.n_prob);

@@ -77,6 +77,9 @@ constexpr int kSgmmFused = DLM_SGMM_FUSED;
 // Its counts hold K slices in 16 bits and K slices x (XCD id + 1) in 15: up to
 // this many K slices per problem.
 constexpr int kSgmmFusedMaxKs = 4095;
+// It pays from this many (problem, tile) pairs on (32 per XCD); smaller batches,
+// whose few items would mostly wait on each other, keep two launches.
+constexpr int64_t kSgmmFusedMinPairs = 256;
 
 struct SgmmArgs {
     const SgDesc* descs;    // device table, or nullptr to use `single`

@@ -378,11 +378,12 @@ int dlm_sgmm_status(void* workspace, int32_t* code, void* stream);
  * Number of kernel launches one dlm_sgmm, dlm_sgmm_noalloc or
  * dlm_sgmm_group_run call makes for T rows and n_problems problems of rank r
  * with d_in up to d_in_max: 0 for T = 0; for bf16 with T <= 4, 1 (one problem)
- * or 2; for bf16 up to rank 64 (and d_in_max up to 4095 x 2048), the
- * segmentation (2 launches when T > 8192, else 1) and one launch running the
- * shrink and the expand; for bf16 above rank 64 with T <= 64 and no K-slice
- * sum, 2 (shrink and expand); else the segmentation, the shrink, the K-slice
- * sum (bf16 with d_in_max > 2048 and r > 64 only) and the expand.  Returns -1 (with the last
+ * or 2; for bf16 up to rank 64 with n_problems x ceil(T / 32) >= 256 (and
+ * d_in_max up to 4095 x 2048), the segmentation (2 launches when T > 8192,
+ * else 1) and one launch running the shrink and the expand; otherwise for bf16
+ * with T <= 64 and no K-slice sum, 2 (shrink and expand); else the
+ * segmentation, the shrink, the K-slice sum (bf16 with d_in_max > 2048 and
+ * r > 64 only) and the expand.  Returns -1 (with the last
  * error set) for a negative T, d_in_max < 1, r outside [1, DLM_MAX_RANK],
  * n_problems < 1 or an unknown dtype.
  */

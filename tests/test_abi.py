@@ -128,15 +128,19 @@ def test_sgmm_launch_count(lib):
     assert f(1, 4096, 16, 1, dlm.DLM_BF16) == 1
     assert f(4, 11008, 64, 1, dlm.DLM_BF16) == 1
     assert f(1, 4096, 128, 7, dlm.DLM_BF16) == 2
-    # from 5 rows up to rank 64: the segmentation, then the shrink and expand
-    # in one launch
+    # 5..64 rows and fewer than 256 (problem, tile) pairs: the shrink and
+    # expand order the rows themselves (no segmentation launch) unless a
+    # K-slice sum launch is needed
     assert f(5, 4096, 16, 1, dlm.DLM_BF16) == 2
     assert f(64, 11008, 64, 7, dlm.DLM_BF16) == 2
-    assert f(65, 4096, 16, 1, dlm.DLM_BF16) == 2
-    assert f(1024, 4096, 64, 7, dlm.DLM_BF16) == 2
-    # above rank 64, 5..64 rows: the shrink and expand order the rows
-    # themselves (no segmentation launch) unless a K-slice sum launch is needed
     assert f(64, 2048, 128, 1, dlm.DLM_BF16) == 2
+    # segment, shrink, expand below 256 pairs; from 256 pairs up to rank 64 the
+    # segmentation and one launch for the shrink and expand
+    assert f(65, 4096, 16, 1, dlm.DLM_BF16) == 3
+    assert f(1024, 4096, 64, 7, dlm.DLM_BF16) == 3
+    assert f(1024, 4096, 64, 8, dlm.DLM_BF16) == 2
+    assert f(64, 4096, 16, 128, dlm.DLM_BF16) == 2
+    assert f(64, 4096, 16, 127, dlm.DLM_BF16) == 2
     # above rank 64 a K-slice sum launch runs when there are several slices
     assert f(64, 4096, 65, 1, dlm.DLM_BF16) == 4
     assert f(65, 2048, 128, 1, dlm.DLM_BF16) == 3
@@ -158,7 +162,7 @@ def test_sgmm_launch_count(lib):
     assert dlm.sgmm_launches(1, 11008, 16) == 1
     assert dlm.sgmm_launches(1, 11008, 16, 7) == 2
     assert dlm.sgmm_launches(64, 11008, 16) == 2
-    assert dlm.sgmm_launches(65, 11008, 16) == 2
+    assert dlm.sgmm_launches(65, 11008, 16) == 3
     assert dlm.sgmm_launches(64, 11008, 128) == 4
 
 

@@ -234,8 +234,9 @@ def _captured(fn) -> int:
 @pytest.mark.parametrize("T,shapes,E,r,dt,group,want", [
     (2, [(4104, 1032)], 8, 16, torch.bfloat16, False, 1),                       # few rows, one launch
     (3, [(4104, 1032), (200, 264), (11008, 4096)], 8, 16, torch.bfloat16, True, 2),  # few rows, a group
-    (64, [(4104, 200), (2056, 64)], 8, 16, torch.bfloat16, True, 2),           # segment, then shrink + expand
-    (65, [(4104, 200), (2056, 64)], 8, 16, torch.bfloat16, True, 2),           # segment, then shrink + expand
+    (64, [(4104, 200), (2056, 64)], 8, 16, torch.bfloat16, True, 2),           # rows ordered in the kernels
+    (65, [(4104, 200), (2056, 64)], 8, 16, torch.bfloat16, True, 3),           # segment, shrink, expand
+    (8192, [(4104, 200)], 8, 16, torch.bfloat16, False, 2),                    # 256 pairs: segment, shrink + expand
     (64, [(4104, 72)], 4, 80, torch.bfloat16, False, 4),                        # + the K-slice sum (r > 64)
     (9000, [(64, 72)], 8, 16, torch.bfloat16, False, 3),                        # + the count launch (T > 8192)
     (40, [(72, 40)], 4, 8, torch.float32, False, 3),                            # fp32

@@ -321,18 +321,18 @@ def test_segment_order_equals_host_stable_sort(T, E, seed):
 @pytest.mark.parametrize("T,d_in,d_out,E,r,seed", [(64, 4104, 520, 8, 16, 1), (37, 200, 72, 16, 40, 2),
                                                    (64, 136, 64, 4, 128, 3), (6, 64, 1096, 2, 24, 4)])
 def test_inline_row_order_equals_the_segmentation(T, d_in, d_out, E, r, seed):
-    """Above rank 64, up to 64 rows, the shrink and expand order the rows
-    themselves (no segmentation launch); up to rank 64 every batch of 5 rows or
-    more is segmented and runs its shrink and expand in one launch.  The same
-    rows followed by released rows up to 65 (segmented, and released rows take
-    no position) must give bitwise the same y for the first T rows, leave the
-    released rows alone, and agree with the oracle; the header words match."""
+    """Up to 64 rows (and fewer than 256 (problem, tile) pairs) the shrink and
+    expand order the rows themselves (no segmentation launch).  The same rows
+    followed by released rows up to 65 (the segmentation launch runs, and
+    released rows take no position) must give bitwise the same y for the first
+    T rows, leave the released rows alone, and agree with the oracle; the
+    header words the shrink publishes match the segmentation's."""
     print(f"[sgmm] inline order T={T} d_in={d_in} r={r}", flush=True)
     T2 = 65
     x, A, B, y = _problem(T2, d_in, d_out, E, r, torch.bfloat16, 3600 + seed)
     idx, g = _sets(T2, E, np.random.default_rng(200 + seed))
     idx[T:] = -1
-    assert dlm.sgmm_launches(T, d_in, r) == 2 and dlm.sgmm_launches(T2, d_in, r) == (3 if r > 64 else 2)
+    assert dlm.sgmm_launches(T, d_in, r) == 2 and dlm.sgmm_launches(T2, d_in, r) == 3
     y0 = y.clone()
     ya, yb = y[:T].clone(), y.clone()
     ws = dlm.sgmm_workspace(T2, d_in, E, r)
