@@ -290,3 +290,58 @@ def test_switch_launch_counts_match_captured_kernels():
     assert _captured(lambda: L.gemv_unmerged(new)) == L.launches_per_gemv_unmerged() == 2
     assert L.status() == dlm.DLM_OK
     L.close()
+
+
+@pytest.mark.parametrize("T,n_prob", [(64, 128), (300, 26)])
+def test_sgmm_one_launch_group_in_graph_matches_eager(T, n_prob):
+    """A group of at least 256 (problem, tile) pairs runs its shrink and expand
+    in one launch, each XCD's expand items waiting on that XCD's shrink items.
+    Captured in a HIP graph and replayed (where the device starts the launch's
+    workgroups on another XCD than eagerly), every replay, with eager work in
+    between, must give the eager launch's bits and leave the status word clear
+    (it is set if an expand item's shrink items ran on another XCD)."""
+    E, r = 8, 16
+    assert n_prob * ((T + 31) // 32) >= 256
+    print(f"[graph] one-launch SGMM group T={T} problems={n_prob}", flush=True)
+    shapes = [(136, 64), (64, 1032), (2056, 72)]
+    probs = []
+    for p in range(n_prob):
+        n, o = shapes[p % len(shapes)]
+        key = (6100, T, p)
+        probs.append((synth.normal_device((T, n), 1.0, torch.bfloat16, "cuda", *key, "x"),
+                      synth.normal_device((E, r, n), 0.02, torch.bfloat16, "cuda", *key, "A"),
+                      synth.normal_device((E, o, r), 0.02, torch.bfloat16, "cuda", *key, "B"),
+                      synth.normal_device((T, o), 0.3, torch.bfloat16, "cuda", *key, "y")))
+    assert dlm.sgmm_launches(T, 2056, r, n_prob) == 2
+    y0 = [p[3].clone() for p in probs]
+    grp = dlm.SgmmGroup(probs, E, r, 1.0)
+    ws = grp.workspace(T)
+    idx_s = torch.zeros(T, 2, dtype=torch.int32, device="cuda")
+    g_s = torch.zeros(T, 2, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            grp.run(idx_s, g_s, T, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    for rep in range(3):
+        idx, g = _sets(T, E, rng)
+        idx_s.copy_(idx)
+        g_s.copy_(g)
+        for (_, _, _, y), y00 in zip(probs, y0):
+            y.copy_(y00)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert dlm.sgmm_status(ws) == dlm.DLM_OK, rep
+        got = [p[3].clone() for p in probs]
+        for (_, _, _, y), y00 in zip(probs, y0):
+            y.copy_(y00)
+        grp.run(idx_s, g_s, T, workspace=ws)
+        torch.cuda.synchronize()
+        assert dlm.sgmm_status(ws) == dlm.DLM_OK, rep
+        for k, (p, gy) in enumerate(zip(probs, got)):
+            assert torch.equal(p[3], gy), (rep, k)
+    grp.close()
